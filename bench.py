@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Forest Cascade Attention decode benchmark (one MI355X).
+
+One step = one ``fca_decode`` of a whole batch (grouped prefix pass,
+per-request suffix pass, log-sum-exp merge) for one attention layer.  The
+batch is a seeded synthetic shared-prefix rollout batch (default: the
+Llama-3-8B layer shape, 64 requests = 8 prompts x 8 samples, prefix 4096,
+suffix U{256..1024}, GQA 32/8, head dim 128, 16-token blocks).  Steps cycle
+through ``--layers`` independent KV pools that share one plan, as the layers
+of a model do, so each step reads KV that is not resident in L2 / MALL.
+
+Printed (one JSON line on stdout): logical-KV tokens/s (the value), unique-KV
+GB/s and its share of the 8 TB/s HBM peak, per-pass times measured with HIP
+events on the kernels' stream, the roofline of the dominant kernel, the
+non-cascade baseline (same kernels, every request read whole) and the CPU
+oracle timed on a bounded sample.  Progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama3_8b")
+    ap.add_argument("--layers", type=int, default=8, help="independent KV pools cycled by the steps")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-noncascade", action="store_true")
+    ap.add_argument("--profile-only", action="store_true", help="few steps, no baselines (for rocprofv3)")
+    return ap.parse_args()
+
+
+def pass_bytes(batch, plan, sched):
+    """Algorithmic bytes each pass must move (per launch)."""
+    sh = batch.shape
+    bs = sh.block_size
+    tok_bytes = (sh.num_kv_heads * sh.head_dim_qk * 2) if sh.v_aliases_k else sh.num_kv_heads * (sh.head_dim_qk + sh.head_dim_v) * 2
+    ex = plan.export()
+    prefix_tokens = sum((g["block_end"] - g["block_begin"]) * bs for g in ex["groups"])
+    suffix_tokens = sum(r[1] for r in ex["requests"])
+    row_bytes = sh.head_dim_v * 4 + 8
+    rows_g = sum(it["col1"] - it["col0"] for it in sched["grouped"])
+    rows_s = sum(it["col1"] - it["col0"] for it in sched["suffix"])
+    q_row = sh.head_dim_qk * 2
+    q_g = sum(len(g["members"]) for g in ex["groups"]) * sh.num_q_heads * q_row
+    q_s = sum(1 for r in ex["requests"] if r[1] > 0) * sh.num_q_heads * q_row
+    grouped = prefix_tokens * tok_bytes + q_g + rows_g * row_bytes
+    suffix = suffix_tokens * tok_bytes + q_s + rows_s * row_bytes
+    merge = (rows_g + rows_s) * row_bytes + batch.batch * sh.num_q_heads * (sh.head_dim_v * 2 + 4)
+    flops_g = sum(
+        (g["block_end"] - g["block_begin"]) * bs * len(g["members"]) * sh.num_q_heads * 2 * (sh.head_dim_qk + sh.head_dim_v)
+        for g in ex["groups"]
+    )
+    return dict(
+        grouped=grouped,
+        suffix=suffix,
+        merge=merge,
+        prefix_tokens=prefix_tokens,
+        suffix_tokens=suffix_tokens,
+        tok_bytes=tok_bytes,
+        grouped_flops=flops_g,
+    )
+
+
+def time_steps(plan, q, pools, out, lse, steps, torch, fca):
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(steps):
+        k, v = pools[s % len(pools)]
+        fca.fca_decode(q[s % len(q)], k, v, plan, out=out, lse=lse)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1000.0 / steps
+    return start.elapsed_time(stop) / steps, wall
+
+
+def cpu_baseline(batch, vals, budget_s):
+    """The fp64 oracle on a bounded sample of the same batch, one thread."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as A
+    from tests.helpers import to_bits
+    import torch
+
+    sh = batch.shape
+    bs = sh.block_size
+    q_bits = to_bits(vals["q"])
+    tokens = 0
+    done = 0
+    elapsed = 0.0
+    with threadpool_limits(limits=1):
+        for i in range(batch.batch):
+            L = int(batch.seq_lens[i])
+            nblk = -(-L // bs)
+            blocks = torch.from_numpy(batch.block_tables[i, :nblk].astype(np.int64)).to(vals["k"].device)
+            k = to_bits(vals["k"].index_select(0, blocks))
+            v = None if sh.v_aliases_k else to_bits(vals["v"].index_select(0, blocks))
+            table = np.arange(nblk, dtype=np.int32)
+            t0 = time.perf_counter()
+            K, V = A.gather_kv(k, v, table, L, bs, sh.head_dim_v, sh.v_aliases_k)
+            A.attend_one(A.widen_bf16(q_bits[i]), K, V, sh.scale, sh.num_kv_heads)
+            elapsed += time.perf_counter() - t0
+            tokens += L
+            done += 1
+            if elapsed >= budget_s:
+                break
+    return dict(
+        value=tokens / elapsed,
+        unit="logical KV tokens/s",
+        cores=1,
+        kind="oracle",
+        sample=f"first {done} of {batch.batch} requests ({tokens} logical tokens), fp64 numpy oracle, 1 thread, {elapsed:.1f} s",
+    )
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(
+            "bench.py measures one GPU: this decode path runs on a single MI355X and "
+            "has no multi-GPU mode (--gpus must be 1).",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import torch
+
+    import shared_prefix_kv_amd as fca
+    from workloads import CONFIGS, build_batch
+    from workloads.values import fill_values_torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fca.lib()
+    cfg = CONFIGS[args.config]
+    batch = build_batch(cfg)
+    sh = batch.shape
+    log(f"config {cfg.name}: B={batch.batch} pool={batch.num_blocks} blocks, layers={args.layers}")
+
+    pools = []
+    qs = []
+    for layer in range(args.layers):
+        vals = fill_values_torch(batch, "cuda", seed=cfg.seed * 1000 + layer, poison=False)
+        pools.append((vals["k"], vals["v"]))
+        qs.append(vals["q"])
+        if layer == 0:
+            vals0 = vals
+    torch.cuda.synchronize()
+    log("pools ready")
+
+    bt = torch.from_numpy(batch.block_tables).cuda()
+    sl = torch.from_numpy(batch.seq_lens).cuda()
+    desc = fca.desc_from_shape(sh, batch.num_blocks)
+    t0 = time.perf_counter()
+    plan = fca.fca_plan(bt, sl, desc)
+    torch.cuda.synchronize()
+    plan_ms_first = (time.perf_counter() - t0) * 1000
+    t0 = time.perf_counter()
+    for _ in range(5):
+        plan = fca.fca_plan(bt, sl, desc)
+    torch.cuda.synchronize()
+    plan_ms = (time.perf_counter() - t0) * 1000 / 5
+    info = plan.info
+    sched = plan.export_schedule()
+    pb = pass_bytes(batch, plan, sched)
+    log(f"plan: {info.num_groups} groups, {info.num_grouped_items} grouped + {info.num_suffix_items} suffix items, {plan_ms:.2f} ms")
+
+    out = torch.empty((batch.batch, sh.num_q_heads, sh.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((batch.batch, sh.num_q_heads), dtype=torch.float32, device="cuda")
+    plan.decode_workspace(out.device)
+
+    steps, warmup = args.steps, args.warmup
+    if args.profile_only:
+        steps, warmup = min(steps, 10), min(warmup, 2)
+    time_steps(plan, qs, pools, out, lse, warmup, torch, fca)
+    ms, wall_ms = time_steps(plan, qs, pools, out, lse, steps, torch, fca)
+    log(f"fca decode: {ms * 1000:.1f} us/step (events), {wall_ms * 1000:.1f} us/step (wall)")
+
+    plan.profile(True)
+    time_steps(plan, qs, pools, out, lse, steps, torch, fca)
+    prof = plan.read_profile()
+    plan.profile(False)
+    n = max(prof["calls"], 1)
+    per = {k: prof[f"{k}_ms"] / n for k in ("grouped", "suffix", "merge", "decode")}
+    log("per pass (ms):", {k: round(v, 4) for k, v in per.items()})
+
+    logical = int(info.logical_tokens)
+    unique_bytes = int(info.unique_tokens) * pb["tok_bytes"]
+    value = logical / (ms / 1000.0)
+    unique_gbps = unique_bytes / (ms / 1000.0) / 1e9
+
+    kernels = {
+        "fca_grouped_prefix_kernel": ("grouped", pb["grouped"]),
+        "fca_suffix_decode_kernel": ("suffix", pb["suffix"]),
+        "fca_merge_kernel_d128" if sh.head_dim_v == 128 else "fca_merge_kernel_d512": ("merge", pb["merge"]),
+    }
+    dom_name, (dom_pass, dom_bytes) = max(kernels.items(), key=lambda kv: per[kv[1][0]])
+    achieved = dom_bytes / (per[dom_pass] / 1000.0) / 1e9
+    roofline = {
+        "kernel": dom_name,
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": None,
+        "bytes_per_launch": int(dom_bytes),
+        "avg_launch_ms": round(per[dom_pass], 5),
+    }
+    sfx_merge_gbps = (pb["suffix"] + pb["merge"]) / ((per["suffix"] + per["merge"]) / 1000.0) / 1e9
+    grouped_tflops = pb["grouped_flops"] / (per["grouped"] / 1000.0) / 1e12 if per["grouped"] > 0 else 0.0
+
+    result = {
+        "metric": "decode attn: unique-KV HBM GB/s (% of peak) + logical KV tokens/s",
+        "value": round(value, 1),
+        "unit": "logical KV tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}",
+            "batch": batch.batch,
+            "logical_kv_tokens": logical,
+            "unique_kv_tokens": int(info.unique_tokens),
+            "groups": int(info.num_groups),
+            "kv_pools_cycled": args.layers,
+        },
+        "unique_kv_GBps": round(unique_gbps, 1),
+        "unique_kv_frac_of_hbm_peak": round(unique_gbps / HBM_PEAK_GBPS, 4),
+        "wall_ms_per_step": round(wall_ms, 5),
+        "per_pass_ms": {k: round(v, 5) for k, v in per.items()},
+        "pass_GBps": {
+            "grouped": round(pb["grouped"] / (per["grouped"] / 1000.0) / 1e9, 1) if per["grouped"] > 0 else None,
+            "suffix": round(pb["suffix"] / (per["suffix"] / 1000.0) / 1e9, 1) if per["suffix"] > 0 else None,
+            "merge": round(pb["merge"] / (per["merge"] / 1000.0) / 1e9, 1) if per["merge"] > 0 else None,
+            "suffix_plus_merge": round(sfx_merge_gbps, 1),
+        },
+        "grouped_mfma_TFLOPs": round(grouped_tflops, 1),
+        "grouped_mfma_frac_of_peak": round(grouped_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "plan_ms": round(plan_ms, 3),
+        "plan_ms_first_call": round(plan_ms_first, 3),
+        "roofline": roofline,
+    }
+
+    if not args.no_noncascade and not args.profile_only:
+        desc_nc = fca.desc_from_shape(sh, batch.num_blocks, cascade=False)
+        plan_nc = fca.fca_plan(bt, sl, desc_nc)
+        plan_nc.decode_workspace(out.device)
+        time_steps(plan_nc, qs, pools, out, lse, warmup, torch, fca)
+        ms_nc, _ = time_steps(plan_nc, qs, pools, out, lse, steps, torch, fca)
+        log(f"non-cascade: {ms_nc * 1000:.1f} us/step")
+        result["non_cascade"] = {
+            "ms_per_step": round(ms_nc, 5),
+            "value": round(logical / (ms_nc / 1000.0), 1),
+            "speedup_fca": round(ms_nc / ms, 3),
+            "byte_ratio_R": round(logical / max(int(info.unique_tokens), 1), 3),
+        }
+        del plan_nc
+
+    if not args.no_cpu_baseline and not args.profile_only:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(batch, vals0, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

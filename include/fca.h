@@ -1,0 +1,248 @@
+/*
+ * fca.h -- Forest Cascade Attention decode on gfx950 (MI355X), C ABI.
+ *
+ * Batched single-token decode attention over a paged bf16 KV cache, split the
+ * way the ZoRRo Inference & Forest Cascade Attention page describes it
+ * ("Overview" and "Core Mechanism"):
+ *
+ *   1. discover the groups of requests whose block tables share a prefix of
+ *      physical block IDs (fca_plan_create);
+ *   2. read each shared prefix block once per group in a grouped pass,
+ *   3. read each request's own suffix blocks in a per-request pass, and
+ *   4. combine the partial results exactly by log-sum-exp weighting
+ *      (fca_decode runs 2-4).
+ *
+ * The result equals standard per-request softmax attention (the page states
+ * the method is mathematically equivalent to it), up to floating-point
+ * rounding: bf16 inputs, fp32 accumulation, bf16 output.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev are device pointers; everything else is host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - The caller owns every buffer it passes in.  The library never frees
+ *     caller memory and never keeps a pointer to it past the call, except
+ *     the plan workspace, which must outlive the plan.
+ *   - Nothing throws or aborts across this boundary.  Every call returns an
+ *     fca_status; on failure fca_last_error() gives a message (per thread).
+ */
+#ifndef FCA_H_
+#define FCA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fca_status {
+  FCA_OK = 0,
+  FCA_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shape */
+  FCA_ERR_UNSUPPORTED = 2, /* head dims / block size / ratio not built */
+  FCA_ERR_WORKSPACE = 3,   /* workspace too small or misaligned */
+  FCA_ERR_BAD_TABLE = 4,   /* found on the device: block ID outside the pool
+                              in a used slot, or seq_len outside
+                              [0, max_blocks * block_size] */
+  FCA_ERR_HIP = 5,         /* a HIP runtime call failed */
+  FCA_ERR_HOST_ALLOC = 6   /* host memory for the plan could not be had */
+} fca_status;
+
+/* fca_attn_desc.flags */
+#define FCA_PLAN_DISABLE_CASCADE 1u /* no groups: every request is read whole
+                                       by the per-request pass (the
+                                       non-cascade paged-decode baseline) */
+
+/*
+ * Shape and cache layout of one attention layer.
+ *
+ * Cache layout (bf16, elements, d = head-dim index, t = slot in the block):
+ *   key  (blk, h, t, d) at k_cache[blk*k_stride_block + h*k_stride_head
+ *                                  + (d/8)*(block_size*8) + t*8 + d%8]
+ *   value(blk, h, t, d) at v_cache[blk*v_stride_block + h*v_stride_head
+ *                                  + d*block_size + t]
+ * i.e. inside one (block, head) tile keys are stored in 16-byte chunks of 8
+ * head dims, chunk-major, and values are stored transposed (one row of
+ * block_size tokens per value dim).  With v_aliases_k = 1 (latent caches)
+ * the values are the first head_dim_v key dims of the same tile and v_cache
+ * is ignored.  Strides are in elements; a tile must not straddle strides
+ * (k_stride_head >= head_dim_qk*block_size, and so on), and every tile must
+ * start on a 16-byte boundary.
+ *
+ * Supported (others return FCA_ERR_UNSUPPORTED):
+ *   - GQA:  head_dim_qk = head_dim_v = 128, block_size = 16,
+ *           num_q_heads / num_kv_heads in [1, 16], v_aliases_k = 0.
+ *   - MLA:  head_dim_qk = 576, head_dim_v = 512, block_size = 64,
+ *           num_kv_heads = 1, v_aliases_k = 1.
+ *
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * `scale` multiplies q.k before the softmax.
+ */
+typedef struct fca_attn_desc {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim_qk;
+  int32_t head_dim_v;
+  int32_t block_size;
+  int32_t num_blocks; /* pool size: valid block IDs are [0, num_blocks) */
+  int64_t k_stride_block;
+  int64_t k_stride_head;
+  int64_t v_stride_block;
+  int64_t v_stride_head;
+  int32_t v_aliases_k;
+  float scale;
+  uint32_t flags; /* FCA_PLAN_* */
+  int32_t reserved; /* must be 0 */
+} fca_attn_desc;
+
+typedef struct fca_plan_s* fca_plan; /* opaque, host-side */
+
+/* Counts of a built plan. */
+typedef struct fca_plan_info {
+  int32_t batch;
+  int32_t num_groups;        /* groups found by discovery */
+  int32_t max_depth;         /* deepest group depth (roots are 0), -1 if none */
+  int32_t num_grouped_items; /* work items of the grouped pass */
+  int32_t num_suffix_items;  /* work items of the per-request pass */
+  int32_t num_merge_sources; /* partial triples the merge reads per q head */
+  int64_t num_partial_rows;  /* (o, m, l) rows written per decode */
+  int64_t logical_tokens;    /* sum of seq_lens */
+  int64_t unique_tokens;     /* group ranges once + every suffix */
+  size_t decode_workspace_bytes; /* bytes fca_decode needs */
+} fca_plan_info;
+
+/*
+ * Bytes of device workspace fca_plan_create needs for a batch of `batch`
+ * requests with block tables `max_blocks` wide.  Depends only on the
+ * arguments.  Returns FCA_ERR_INVALID_ARG / FCA_ERR_UNSUPPORTED for a bad
+ * descriptor or sizes (batch in [0, 8192], max_blocks in [1, 2^20]).
+ */
+fca_status fca_plan_workspace_size(int32_t batch, int32_t max_blocks, const fca_attn_desc* desc,
+                                   size_t* bytes);
+
+/*
+ * Discover the prefix forest of a batch and build the decode schedule
+ * (the "discovers groups of requests sharing a KV-cache prefix" step of
+ * "Core Mechanism").
+ *
+ *   block_tables_dev  int32 [batch, >= max_blocks], row stride bt_row_stride
+ *                     (elements).  Row i maps request i's logical block j to
+ *                     a physical block; only j < ceil(seq_lens[i]/block_size)
+ *                     is read, the rest may hold anything.
+ *   seq_lens_dev      int32 [batch]: cached tokens of each request, the
+ *                     decode token's own key/value included.
+ *   workspace_dev     >= fca_plan_workspace_size bytes, 256-byte aligned;
+ *                     owned by the caller, must outlive the plan.
+ *
+ * Enqueues the discovery kernels on `stream`, then waits once for a small
+ * read-back (group records, counts and the device error flag).  The plan
+ * copies the tables and lengths it needs into the workspace: the caller may
+ * change or free block_tables_dev / seq_lens_dev once this returns.
+ * batch == 0 gives a valid, empty plan.  *out is set only on FCA_OK.
+ */
+fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_stride, const int32_t* seq_lens_dev,
+                           int32_t batch, int32_t max_blocks, const fca_attn_desc* desc, void* workspace_dev,
+                           size_t workspace_bytes, void* stream, fca_plan* out);
+
+fca_status fca_plan_get_info(fca_plan plan, fca_plan_info* info);
+
+/*
+ * Decode attention for the planned batch (grouped pass, per-request pass,
+ * exact log-sum-exp merge; "Core Mechanism", steps 2-3).
+ *
+ *   q_dev        bf16 [batch, num_q_heads, head_dim_qk], contiguous.
+ *   k_cache_dev  bf16 pool, layout above.  v_cache_dev likewise (ignored
+ *                when v_aliases_k).
+ *   out_dev      bf16 [batch, num_q_heads, head_dim_v], contiguous; row i is
+ *                request i.  A request with seq_len 0 gets zeros.
+ *   lse_dev      float [batch, num_q_heads] natural-log sum of exp(scores),
+ *                or NULL.  -inf for seq_len 0.
+ *   workspace_dev >= info.decode_workspace_bytes, 256-byte aligned: holds the
+ *                partial (o, max, denominator) triples of this call.
+ *
+ * Asynchronous on `stream`: no host synchronisation and no allocation.
+ * Calls that share a decode workspace must not overlap; a plan itself is
+ * read-only and may serve calls on several streams with separate decode
+ * workspaces.
+ */
+fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                      void* out_dev, float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* One discovered group, canonical order: sorted by (smallest member, depth). */
+typedef struct fca_group_record {
+  int32_t depth;        /* number of groups strictly above; roots are 0 */
+  int32_t parent;       /* canonical index of the nearest group above, or -1 */
+  int32_t block_begin;  /* logical block range [block_begin, block_end) */
+  int32_t block_end;
+  int32_t member_begin; /* offset of its ascending member list in `members` */
+  int32_t member_count;
+} fca_group_record;
+
+/*
+ * Canonical form of the plan's grouping, for tests and tools (host copies):
+ *   groups   [num_groups]
+ *   members  [sum of member_count]  request indices
+ *   requests [batch * 3]  per request: suffix_block_begin, suffix_tokens,
+ *                         deepest group (canonical index) or -1
+ * Any pointer may be NULL to skip that part.
+ */
+fca_status fca_plan_export(fca_plan plan, fca_group_record* groups, int32_t* members, int32_t* requests);
+
+/* One unit of work of the grouped or per-request pass (host copy). */
+typedef struct fca_work_item {
+  int32_t request;    /* block-table row the item's block IDs come from */
+  int32_t tok_begin;  /* logical token range [tok_begin, tok_end) */
+  int32_t tok_end;
+  int32_t kv_head;
+  int32_t member_off; /* grouped: offset of the group's range in the
+                         depth-first member order; -1: suffix item */
+  int32_t ncols;      /* query rows of the unit: members * (Hq/Hkv) */
+  int32_t col0;       /* query rows [col0, col1) of the unit */
+  int32_t col1;
+  int32_t part_base;  /* partial row of query row 0 of this (unit, kv head) */
+  int32_t reserved[3];
+} fca_work_item;
+
+/*
+ * The decode schedule, for tests and tools (host copies):
+ *   grouped [num_grouped_items], suffix [num_suffix_items]
+ *   src_off [batch + 1], src [2 * num_merge_sources]
+ * Request i merges the partial rows  a + (h / r) * b + h % r  for every
+ * pair (a, b) = (src[2s], src[2s+1]), s in [src_off[i], src_off[i+1]), for
+ * query head h (r = num_q_heads / num_kv_heads).
+ */
+fca_status fca_plan_export_schedule(fca_plan plan, fca_work_item* grouped, fca_work_item* suffix,
+                                    int32_t* src_off, int32_t* src);
+
+/* Summed GPU time of the passes of profiled fca_decode calls. */
+typedef struct fca_profile {
+  double grouped_ms; /* grouped prefix pass */
+  double suffix_ms;  /* per-request suffix pass */
+  double merge_ms;   /* log-sum-exp merge */
+  double decode_ms;  /* whole call, first launch to last */
+  int64_t calls;
+} fca_profile;
+
+/*
+ * Measurement hook.  While enabled, every fca_decode on this plan records HIP
+ * events on its stream before and after each pass.  fca_profile_read waits
+ * for the recorded events, returns the sums since the previous read and
+ * resets them.  Events are created on first use and freed with the plan.
+ * Not thread-safe; meant for benchmarks and profilers, not serving loops.
+ */
+fca_status fca_profile_enable(fca_plan plan, int32_t enable);
+fca_status fca_profile_read(fca_plan plan, fca_profile* out);
+
+/* Frees the host-side plan.  The workspace stays the caller's.  NULL is ok. */
+void fca_plan_destroy(fca_plan plan);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* fca_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* fca_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FCA_H_ */

@@ -1,0 +1,369 @@
+"""Python binding of libfca (Forest Cascade Attention decode on gfx950).
+
+Argument marshalling only: every step of the decode path (discovery, grouped
+pass, per-request pass, merge) runs in the HIP kernels of libfca.so; torch is
+used for device memory and the current stream.  Importing works without a
+GPU; calls that reach the device need one.  There is no fallback: if
+libfca.so is missing, ``lib()`` raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfca.so")
+
+FCA_OK = 0
+STATUS_NAMES = {
+    0: "FCA_OK",
+    1: "FCA_ERR_INVALID_ARG",
+    2: "FCA_ERR_UNSUPPORTED",
+    3: "FCA_ERR_WORKSPACE",
+    4: "FCA_ERR_BAD_TABLE",
+    5: "FCA_ERR_HIP",
+    6: "FCA_ERR_HOST_ALLOC",
+}
+FCA_PLAN_DISABLE_CASCADE = 1
+
+EXPORTED = [
+    "fca_plan_workspace_size",
+    "fca_plan_create",
+    "fca_plan_get_info",
+    "fca_decode",
+    "fca_plan_export",
+    "fca_plan_export_schedule",
+    "fca_profile_enable",
+    "fca_profile_read",
+    "fca_plan_destroy",
+    "fca_last_error",
+    "fca_version",
+]
+
+
+class FcaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim_qk", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("k_stride_block", ctypes.c_int64),
+        ("k_stride_head", ctypes.c_int64),
+        ("v_stride_block", ctypes.c_int64),
+        ("v_stride_head", ctypes.c_int64),
+        ("v_aliases_k", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_groups", ctypes.c_int32),
+        ("max_depth", ctypes.c_int32),
+        ("num_grouped_items", ctypes.c_int32),
+        ("num_suffix_items", ctypes.c_int32),
+        ("num_merge_sources", ctypes.c_int32),
+        ("num_partial_rows", ctypes.c_int64),
+        ("logical_tokens", ctypes.c_int64),
+        ("unique_tokens", ctypes.c_int64),
+        ("decode_workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class GroupRecord(ctypes.Structure):
+    _fields_ = [
+        ("depth", ctypes.c_int32),
+        ("parent", ctypes.c_int32),
+        ("block_begin", ctypes.c_int32),
+        ("block_end", ctypes.c_int32),
+        ("member_begin", ctypes.c_int32),
+        ("member_count", ctypes.c_int32),
+    ]
+
+
+class WorkItem(ctypes.Structure):
+    _fields_ = [
+        ("request", ctypes.c_int32),
+        ("tok_begin", ctypes.c_int32),
+        ("tok_end", ctypes.c_int32),
+        ("kv_head", ctypes.c_int32),
+        ("member_off", ctypes.c_int32),
+        ("ncols", ctypes.c_int32),
+        ("col0", ctypes.c_int32),
+        ("col1", ctypes.c_int32),
+        ("part_base", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
+    ]
+
+
+class Profile(ctypes.Structure):
+    _fields_ = [
+        ("grouped_ms", ctypes.c_double),
+        ("suffix_ms", ctypes.c_double),
+        ("merge_ms", ctypes.c_double),
+        ("decode_ms", ctypes.c_double),
+        ("calls", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libfca.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(
+                f"{LIB_PATH} is missing: build it with `python -m shared_prefix_kv_amd.build`"
+            )
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.fca_plan_workspace_size.argtypes = [i32, i32, ctypes.POINTER(AttnDesc), ctypes.POINTER(sz)]
+        L.fca_plan_create.argtypes = [vp, i64, vp, i32, i32, ctypes.POINTER(AttnDesc), vp, sz, vp, ctypes.POINTER(vp)]
+        L.fca_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+        L.fca_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.fca_plan_export.argtypes = [vp, vp, vp, vp]
+        L.fca_plan_export_schedule.argtypes = [vp, vp, vp, vp, vp]
+        L.fca_profile_enable.argtypes = [vp, i32]
+        L.fca_profile_read.argtypes = [vp, ctypes.POINTER(Profile)]
+        L.fca_plan_destroy.argtypes = [vp]
+        L.fca_plan_destroy.restype = None
+        L.fca_last_error.restype = ctypes.c_char_p
+        L.fca_version.restype = ctypes.c_char_p
+        for name in EXPORTED:
+            if name not in ("fca_plan_destroy", "fca_last_error", "fca_version"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != FCA_OK:
+        raise FcaError(status, lib().fca_last_error().decode())
+
+
+def make_desc(
+    num_q_heads,
+    num_kv_heads,
+    head_dim_qk,
+    head_dim_v,
+    block_size,
+    num_blocks,
+    scale,
+    v_aliases_k=False,
+    cascade=True,
+    k_strides=None,
+    v_strides=None,
+) -> AttnDesc:
+    """Descriptor for the documented cache layout (default: dense pools)."""
+    d = AttnDesc()
+    d.num_q_heads, d.num_kv_heads = num_q_heads, num_kv_heads
+    d.head_dim_qk, d.head_dim_v = head_dim_qk, head_dim_v
+    d.block_size, d.num_blocks = block_size, num_blocks
+    ksh = head_dim_qk * block_size
+    d.k_stride_block, d.k_stride_head = k_strides if k_strides else (num_kv_heads * ksh, ksh)
+    vsh = head_dim_v * block_size
+    if v_aliases_k:
+        d.v_stride_block, d.v_stride_head = d.k_stride_block, d.k_stride_head
+    else:
+        d.v_stride_block, d.v_stride_head = v_strides if v_strides else (num_kv_heads * vsh, vsh)
+    d.v_aliases_k = int(bool(v_aliases_k))
+    d.scale = float(scale)
+    d.flags = 0 if cascade else FCA_PLAN_DISABLE_CASCADE
+    d.reserved = 0
+    return d
+
+
+def desc_from_shape(shape, num_blocks, cascade=True) -> AttnDesc:
+    return make_desc(
+        shape.num_q_heads,
+        shape.num_kv_heads,
+        shape.head_dim_qk,
+        shape.head_dim_v,
+        shape.block_size,
+        num_blocks,
+        shape.scale,
+        v_aliases_k=shape.v_aliases_k,
+        cascade=cascade,
+    )
+
+
+def plan_workspace_size(batch: int, max_blocks: int, desc: AttnDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().fca_plan_workspace_size(batch, max_blocks, ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def _stream_ptr(stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+class Plan:
+    """A planned batch: prefix forest + decode schedule (fca_plan_create)."""
+
+    def __init__(self, block_tables, seq_lens, desc: AttnDesc, workspace=None, stream=None):
+        import torch
+
+        assert block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32
+        assert block_tables.dim() == 2 and block_tables.stride(1) == 1
+        B, W = block_tables.shape
+        self.desc = desc
+        self.batch, self.max_blocks = int(B), int(W)
+        nbytes = plan_workspace_size(self.batch, self.max_blocks, desc)
+        if workspace is None:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=block_tables.device)
+        self.workspace = workspace  # must outlive the plan
+        h = ctypes.c_void_p()
+        _check(
+            lib().fca_plan_create(
+                _ptr(block_tables),
+                block_tables.stride(0),
+                _ptr(seq_lens),
+                self.batch,
+                self.max_blocks,
+                ctypes.byref(desc),
+                _ptr(workspace),
+                workspace.numel() * workspace.element_size(),
+                _stream_ptr(stream),
+                ctypes.byref(h),
+            )
+        )
+        self._h = h
+        info = PlanInfo()
+        _check(lib().fca_plan_get_info(self._h, ctypes.byref(info)))
+        self.info = info
+        self._decode_ws = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib().fca_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def decode_workspace(self, device):
+        import torch
+
+        need = max(int(self.info.decode_workspace_bytes), 256)
+        if self._decode_ws is None or self._decode_ws.numel() < need:
+            self._decode_ws = torch.empty(need, dtype=torch.uint8, device=device)
+        return self._decode_ws
+
+    def decode(self, q, k_cache, v_cache, out=None, lse=None, workspace=None, stream=None):
+        import torch
+
+        d = self.desc
+        assert q.dtype == torch.bfloat16 and q.is_contiguous()
+        assert tuple(q.shape) == (self.batch, d.num_q_heads, d.head_dim_qk)
+        if out is None:
+            out = torch.empty((self.batch, d.num_q_heads, d.head_dim_v), dtype=torch.bfloat16, device=q.device)
+        assert out.dtype == torch.bfloat16 and out.is_contiguous()
+        if lse is not None:
+            assert lse.dtype == torch.float32 and lse.is_contiguous()
+        ws = workspace if workspace is not None else self.decode_workspace(q.device)
+        _check(
+            lib().fca_decode(
+                self._h,
+                _ptr(q),
+                _ptr(k_cache),
+                _ptr(v_cache),
+                _ptr(out),
+                _ptr(lse),
+                _ptr(ws),
+                ws.numel() * ws.element_size(),
+                _stream_ptr(stream),
+            )
+        )
+        return out
+
+    def profile(self, enable: bool):
+        """Record per-pass HIP events in later decode calls (measurement)."""
+        _check(lib().fca_profile_enable(self._h, int(bool(enable))))
+
+    def read_profile(self) -> dict:
+        p = Profile()
+        _check(lib().fca_profile_read(self._h, ctypes.byref(p)))
+        return {f: getattr(p, f) for f, _ in Profile._fields_}
+
+    def export(self):
+        """Canonical grouping: dict(groups=[...], requests=[...])."""
+        G, B = self.info.num_groups, self.batch
+        groups = (GroupRecord * max(G, 1))()
+        counts = None
+        # members: sum of member_count <= B * (depth + 1); fetch groups first
+        _check(lib().fca_plan_export(self._h, groups, None, None))
+        total = sum(groups[g].member_count for g in range(G))
+        members = (ctypes.c_int32 * max(total, 1))()
+        reqs = (ctypes.c_int32 * max(3 * B, 1))()
+        _check(lib().fca_plan_export(self._h, None, members, reqs))
+        del counts
+        out = []
+        for g in range(G):
+            rec = groups[g]
+            mem = tuple(members[rec.member_begin + k] for k in range(rec.member_count))
+            out.append(
+                dict(
+                    depth=rec.depth,
+                    parent=rec.parent,
+                    block_begin=rec.block_begin,
+                    block_end=rec.block_end,
+                    members=mem,
+                )
+            )
+        requests = [(reqs[3 * i], reqs[3 * i + 1], reqs[3 * i + 2]) for i in range(B)]
+        return dict(groups=out, requests=requests)
+
+    def export_schedule(self):
+        """Work items of both passes and per-request merge sources."""
+        ng, ns, B = self.info.num_grouped_items, self.info.num_suffix_items, self.batch
+        gi = (WorkItem * max(ng, 1))()
+        si = (WorkItem * max(ns, 1))()
+        off = (ctypes.c_int32 * (B + 1))()
+        src = (ctypes.c_int32 * max(2 * self.info.num_merge_sources, 1))()
+        _check(lib().fca_plan_export_schedule(self._h, gi, si, off, src))
+
+        def items(arr, n):
+            names = [f[0] for f in WorkItem._fields_ if f[0] != "reserved"]
+            return [{k: getattr(arr[j], k) for k in names} for j in range(n)]
+
+        sources = [[(src[2 * s], src[2 * s + 1]) for s in range(off[i], off[i + 1])] for i in range(B)]
+        return dict(grouped=items(gi, ng), suffix=items(si, ns), sources=sources)
+
+
+def fca_plan(block_tables, seq_lens, desc: AttnDesc, workspace=None, stream=None) -> Plan:
+    """Discover the prefix forest of a batch and schedule its decode."""
+    return Plan(block_tables, seq_lens, desc, workspace=workspace, stream=stream)
+
+
+def fca_decode(q, k_cache, v_cache, plan: Plan, out=None, lse=None, stream=None):
+    """Forest Cascade Attention decode for a planned batch; returns `out`."""
+    return plan.decode(q, k_cache, v_cache, out=out, lse=lse, stream=stream)
+
+
+def version() -> str:
+    return lib().fca_version().decode()

@@ -1,0 +1,705 @@
+// Host side of the C ABI: validation, plan construction, launches.
+//
+// fca_plan_create runs the discovery kernels, reads back one small region
+// (counters, error flags, group records, per-request deepest group and
+// suffix start), and turns it into:
+//   * the canonical group order (smallest member, depth),
+//   * a depth-first member order in which every group is a contiguous range,
+//   * the split schedule of the grouped and per-request passes,
+//   * the per-request / per-group metadata the merge walks.
+// These are uploaded into the caller's plan workspace.  fca_decode only
+// launches kernels.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <cstdlib>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "fca_internal.h"
+
+using namespace fca;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fca_status fail(fca_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fca_status hip_fail(hipError_t e, const char* what) {
+  return fail(FCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  const int v = atoi(s);
+  return v > 0 ? v : dflt;
+}
+
+// Split-schedule targets (developer tuning knobs; read the same way for the
+// workspace bound and for planning).
+struct Tuning {
+  int grouped_items;     // aim for about this many grouped work items
+  int grouped_min_work;  // min work per grouped item, in (32-column tile x token)
+  int suffix_items;
+  int suffix_min_tokens;
+};
+
+Tuning tuning() {
+  Tuning t;
+  t.grouped_items = env_int("FCA_TUNE_GROUPED_ITEMS", 1024);
+  t.grouped_min_work = env_int("FCA_TUNE_GROUPED_MIN_WORK", 1024);
+  t.suffix_items = env_int("FCA_TUNE_SUFFIX_ITEMS", 2048);
+  t.suffix_min_tokens = env_int("FCA_TUNE_SUFFIX_MIN_TOKENS", 512);
+  return t;
+}
+
+constexpr int kGroupedCols = 32;  // query rows per grouped wave pass
+
+enum Kind { kGqa = 0, kMla = 1 };
+
+fca_status check_desc(const fca_attn_desc* d, Kind* kind) {
+  if (!d) return fail(FCA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->reserved != 0) return fail(FCA_ERR_INVALID_ARG, "desc.reserved must be 0");
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads)
+    return fail(FCA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->num_blocks <= 0) return fail(FCA_ERR_INVALID_ARG, "num_blocks must be positive");
+  if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return fail(FCA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (d->flags & ~FCA_PLAN_DISABLE_CASCADE) return fail(FCA_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
+  const int r = d->num_q_heads / d->num_kv_heads;
+  if (d->head_dim_qk == 128 && d->head_dim_v == 128 && d->block_size == 16 && !d->v_aliases_k) {
+    if (r > 16) return fail(FCA_ERR_UNSUPPORTED, "GQA ratio %d > 16 is not built", r);
+    if (d->k_stride_head < 128 * 16 || d->v_stride_head < 128 * 16 ||
+        d->k_stride_block < (int64_t)d->num_kv_heads * d->k_stride_head ||
+        d->v_stride_block < (int64_t)d->num_kv_heads * d->v_stride_head)
+      return fail(FCA_ERR_INVALID_ARG, "cache strides overlap tiles");
+    if ((d->k_stride_head | d->k_stride_block | d->v_stride_head | d->v_stride_block) % 8)
+      return fail(FCA_ERR_INVALID_ARG, "cache strides must keep 16-byte tile alignment");
+    *kind = kGqa;
+    return FCA_OK;
+  }
+  return fail(FCA_ERR_UNSUPPORTED, "unsupported shape: head_dim_qk=%d head_dim_v=%d block_size=%d v_aliases_k=%d",
+              d->head_dim_qk, d->head_dim_v, d->block_size, d->v_aliases_k);
+}
+
+struct Layout {
+  size_t header, lens, deepest, sfx_begin, records, readback_bytes;
+  size_t bt, state;
+  size_t items_g, items_s, perm, req, grp;
+  int64_t cap_g, cap_s;
+  size_t total;
+};
+
+Layout make_layout(int B, int W, const fca_attn_desc* d, const Tuning& t) {
+  Layout L{};
+  const size_t b = (size_t)B;
+  size_t off = 0;
+  L.header = off;
+  L.lens = L.header + kHdrWords * 4;
+  L.deepest = L.lens + b * 4;
+  L.sfx_begin = L.deepest + b * 4;
+  L.records = L.sfx_begin + b * 4;
+  L.readback_bytes = L.records + b * kRecordInts * 4 - L.header;
+  off = align_up(L.header + L.readback_bytes);
+  L.bt = off;
+  off = align_up(off + b * (size_t)W * 4);
+  L.state = off;
+  off = align_up(off + 11 * b * 4);
+  const int64_t hkv = d->num_kv_heads;
+  L.cap_g = 2LL * t.grouped_items + hkv * B + 16;
+  L.cap_s = (int64_t)t.suffix_items + hkv * B + 16;
+  L.items_g = off;
+  off = align_up(off + (size_t)L.cap_g * sizeof(WorkItem));
+  L.items_s = off;
+  off = align_up(off + (size_t)L.cap_s * sizeof(WorkItem));
+  L.perm = off;
+  off = align_up(off + b * 4);
+  L.req = off;
+  off = align_up(off + b * sizeof(ReqMeta));
+  L.grp = off;
+  off = align_up(off + std::max<size_t>(b, 1) * sizeof(GroupMeta));
+  L.total = off;
+  return L;
+}
+
+DiscoveryPtrs discovery_ptrs(char* ws, const Layout& L, int B) {
+  DiscoveryPtrs p;
+  p.header = reinterpret_cast<int32_t*>(ws + L.header);
+  p.lens = reinterpret_cast<int32_t*>(ws + L.lens);
+  p.deepest = reinterpret_cast<int32_t*>(ws + L.deepest);
+  p.sfx_begin = reinterpret_cast<int32_t*>(ws + L.sfx_begin);
+  p.records = reinterpret_cast<int32_t*>(ws + L.records);
+  p.bt = reinterpret_cast<int32_t*>(ws + L.bt);
+  int32_t* st = reinterpret_cast<int32_t*>(ws + L.state);
+  int32_t** arr[] = {&p.nfull,  &p.root,   &p.depth_at, &p.node, &p.gdepth, &p.gparent,
+                     &p.active, &p.ndstar, &p.ncount,   &p.ngid, &p.newnode};
+  for (int a = 0; a < 11; ++a) *arr[a] = st + (size_t)a * B;
+  return p;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
+
+}  // namespace
+
+struct fca_plan_s {
+  fca_attn_desc desc;
+  Kind kind;
+  int B, W, r;
+  char* ws;
+  Layout L;
+  // host copies
+  std::vector<fca_group_record> groups;
+  std::vector<int32_t> members;   // ascending per group
+  std::vector<int32_t> req3;      // per request: suffix_block_begin, suffix_tokens, deepest
+  std::vector<WorkItem> items_g, items_s;
+  std::vector<int32_t> perm;
+  std::vector<ReqMeta> req;
+  std::vector<GroupMeta> grp;
+  fca_plan_info info;
+  // measurement hook
+  bool profiling = false;
+  std::vector<hipEvent_t> event_pool;
+  std::vector<hipEvent_t> pending;  // 4 per profiled call
+  ~fca_plan_s() {
+    for (hipEvent_t e : pending) (void)hipEventDestroy(e);
+    for (hipEvent_t e : event_pool) (void)hipEventDestroy(e);
+  }
+};
+
+extern "C" {
+
+const char* fca_last_error(void) { return g_last_error.c_str(); }
+
+const char* fca_version(void) { return "0.1.0"; }
+
+fca_status fca_plan_workspace_size(int32_t batch, int32_t max_blocks, const fca_attn_desc* desc, size_t* bytes) {
+  try {
+    if (!bytes) return fail(FCA_ERR_INVALID_ARG, "bytes is NULL");
+    Kind kind;
+    fca_status st = check_desc(desc, &kind);
+    if (st != FCA_OK) return st;
+    if (batch < 0 || batch > kMaxBatch) return fail(FCA_ERR_INVALID_ARG, "batch %d outside [0, %d]", batch, kMaxBatch);
+    if (max_blocks < 1 || max_blocks > kMaxTableWidth)
+      return fail(FCA_ERR_INVALID_ARG, "max_blocks %d outside [1, %d]", max_blocks, kMaxTableWidth);
+    *bytes = make_layout(batch, max_blocks, desc, tuning()).total;
+    return FCA_OK;
+  } catch (...) {
+    return fail(FCA_ERR_HOST_ALLOC, "host allocation failed");
+  }
+}
+
+static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb) {
+  const int B = P->B;
+  const int bs = P->desc.block_size;
+  const int hkv = P->desc.num_kv_heads;
+  const int hq = P->desc.num_q_heads;
+  const int r = P->r;
+  const Layout& L = P->L;
+  const int32_t* hdr = rb.data();
+  const int32_t* lens = hdr + (L.lens - L.header) / 4;
+  const int32_t* deep = hdr + (L.deepest - L.header) / 4;
+  const int32_t* sfxb = hdr + (L.sfx_begin - L.header) / 4;
+  const int32_t* rec = hdr + (L.records - L.header) / 4;
+  const int G = hdr[kHdrGroups];
+  if (G < 0 || G > std::max(B - 1, 0)) return fail(FCA_ERR_HIP, "discovery produced %d groups for %d requests", G, B);
+
+  // Canonical order: (leader = smallest member, depth).
+  std::vector<int> order(G);
+  for (int g = 0; g < G; ++g) order[g] = g;
+  std::sort(order.begin(), order.end(), [&](int a, int b) {
+    const int32_t* ra = rec + (size_t)a * kRecordInts;
+    const int32_t* rb2 = rec + (size_t)b * kRecordInts;
+    return ra[0] != rb2[0] ? ra[0] < rb2[0] : ra[1] < rb2[1];
+  });
+  std::vector<int> canon(G);
+  for (int c = 0; c < G; ++c) canon[order[c]] = c;
+
+  P->groups.assign(G, fca_group_record{});
+  P->grp.assign(G, GroupMeta{});
+  std::vector<int> count(G);
+  std::vector<std::vector<int>> children(G), direct(G);
+  std::vector<int> roots;
+  int max_depth = -1;
+  for (int c = 0; c < G; ++c) {
+    const int32_t* x = rec + (size_t)order[c] * kRecordInts;
+    fca_group_record& gr = P->groups[c];
+    gr.depth = x[1];
+    gr.parent = x[2] >= 0 ? canon[x[2]] : -1;
+    gr.block_begin = x[3];
+    gr.block_end = x[4];
+    count[c] = x[5];
+    max_depth = std::max(max_depth, gr.depth);
+    if (gr.parent >= 0)
+      children[gr.parent].push_back(c);
+    else
+      roots.push_back(c);
+  }
+  std::vector<int> deepest_c(B);
+  for (int i = 0; i < B; ++i) {
+    deepest_c[i] = deep[i] >= 0 ? canon[deep[i]] : -1;
+    if (deepest_c[i] >= 0) direct[deepest_c[i]].push_back(i);
+  }
+
+  // Depth-first member order: every group is the contiguous range [r0, r1).
+  P->perm.clear();
+  P->perm.reserve(B);
+  std::vector<int> r0(G), r1(G);
+  {
+    std::vector<std::pair<int, size_t>> stack;  // (group, next child)
+    for (int root : roots) {
+      stack.push_back({root, 0});
+      r0[root] = (int)P->perm.size();
+      for (int i : direct[root]) P->perm.push_back(i);
+      while (!stack.empty()) {
+        auto& top = stack.back();
+        const int c = top.first;
+        if (top.second < children[c].size()) {
+          const int ch = children[c][top.second++];
+          r0[ch] = (int)P->perm.size();
+          for (int i : direct[ch]) P->perm.push_back(i);
+          stack.push_back({ch, 0});
+        } else {
+          r1[c] = (int)P->perm.size();
+          stack.pop_back();
+        }
+      }
+    }
+    for (int i = 0; i < B; ++i)
+      if (deepest_c[i] < 0) P->perm.push_back(i);
+  }
+  if ((int)P->perm.size() != B) return fail(FCA_ERR_HIP, "inconsistent discovery output (member order)");
+  std::vector<int> pos(B);
+  for (int k = 0; k < B; ++k) pos[P->perm[k]] = k;
+
+  P->members.clear();
+  for (int c = 0; c < G; ++c) {
+    if (r1[c] - r0[c] != count[c] || count[c] < 2)
+      return fail(FCA_ERR_HIP, "inconsistent discovery output (group %d: %d members, range %d)", c, count[c],
+                  r1[c] - r0[c]);
+    P->groups[c].member_begin = (int32_t)P->members.size();
+    P->groups[c].member_count = count[c];
+    std::vector<int> m(P->perm.begin() + r0[c], P->perm.begin() + r1[c]);
+    std::sort(m.begin(), m.end());
+    P->members.insert(P->members.end(), m.begin(), m.end());
+  }
+
+  P->req3.assign((size_t)B * 3, 0);
+  int64_t logical = 0, unique = 0;
+  std::vector<int> sfx_tokens(B);
+  for (int i = 0; i < B; ++i) {
+    const int sb = sfxb[i];
+    sfx_tokens[i] = lens[i] - bs * sb;
+    P->req3[3 * i + 0] = sb;
+    P->req3[3 * i + 1] = sfx_tokens[i];
+    P->req3[3 * i + 2] = deepest_c[i];
+    logical += lens[i];
+    unique += sfx_tokens[i];
+    if (sfx_tokens[i] < 0) return fail(FCA_ERR_HIP, "inconsistent discovery output (suffix of request %d)", i);
+  }
+
+  // Split schedule, grouped pass.
+  const Tuning t = tuning();
+  P->items_g.clear();
+  P->items_s.clear();
+  int64_t row = 0;
+  {
+    int64_t work = 0;
+    for (int c = 0; c < G; ++c) {
+      const int64_t T = (int64_t)(P->groups[c].block_end - P->groups[c].block_begin) * bs;
+      const int64_t ncols = (int64_t)count[c] * r;
+      work += (int64_t)hkv * ceil_div(ncols, kGroupedCols) * T;
+      unique += T;
+    }
+    const int64_t wt = std::max<int64_t>(ceil_div(work, t.grouped_items), t.grouped_min_work);
+    for (int c = 0; c < G; ++c) {
+      const fca_group_record& gr = P->groups[c];
+      const int64_t T = (int64_t)(gr.block_end - gr.block_begin) * bs;
+      const int ncols = count[c] * r;
+      const int64_t mtiles = ceil_div(ncols, kGroupedCols);
+      int64_t splits = 1, mchunk = mtiles;
+      if (mtiles * T > wt) {
+        if (T <= wt) {
+          mchunk = std::max<int64_t>(1, wt / T);
+        } else {
+          mchunk = 1;
+          splits = ceil_div(T, wt);
+        }
+      }
+      const int64_t chunk = round_up(ceil_div(T, splits), kTileTokens);
+      splits = ceil_div(T, chunk);
+      GroupMeta& gm = P->grp[c];
+      gm.parent = gr.parent;
+      gm.r0 = r0[c];
+      gm.ncols = ncols;
+      gm.unit = (int32_t)row;
+      gm.splits = (int32_t)splits;
+      for (int64_t s = 0; s < splits; ++s) {
+        const int tb = (int)(gr.block_begin * (int64_t)bs + s * chunk);
+        const int te = (int)std::min<int64_t>(tb + chunk, (int64_t)gr.block_end * bs);
+        for (int h = 0; h < hkv; ++h)
+          for (int64_t m0 = 0; m0 < mtiles; m0 += mchunk) {
+            WorkItem it{};
+            it.request = P->perm[r0[c]];
+            it.tok_begin = tb;
+            it.tok_end = te;
+            it.kv_head = h;
+            it.member_off = r0[c];
+            it.ncols = ncols;
+            it.col0 = (int)(m0 * kGroupedCols);
+            it.col1 = (int)std::min<int64_t>((m0 + mchunk) * kGroupedCols, ncols);
+            it.part_base = (int32_t)(row + (s * hkv + h) * (int64_t)ncols);
+            P->items_g.push_back(it);
+          }
+      }
+      row += splits * hkv * (int64_t)ncols;
+      if (row > INT32_MAX) return fail(FCA_ERR_UNSUPPORTED, "too many partial rows");
+    }
+  }
+  // Split schedule, per-request pass.
+  P->req.assign(B, ReqMeta{});
+  {
+    int64_t work = 0;
+    for (int i = 0; i < B; ++i) work += (int64_t)hkv * sfx_tokens[i];
+    const int64_t wt = round_up(std::max<int64_t>(ceil_div(work, t.suffix_items), t.suffix_min_tokens), kTileTokens);
+    for (int i = 0; i < B; ++i) {
+      ReqMeta& rq = P->req[i];
+      rq.pos = pos[i];
+      rq.deepest = deepest_c[i];
+      rq.sfx_unit = (int32_t)row;
+      rq.sfx_splits = 0;
+      const int64_t T = sfx_tokens[i];
+      if (T == 0) continue;
+      int64_t splits = ceil_div(T, wt);
+      const int64_t chunk = round_up(ceil_div(T, splits), kTileTokens);
+      splits = ceil_div(T, chunk);
+      rq.sfx_splits = (int32_t)splits;
+      const int base = P->req3[3 * i] * bs;
+      for (int64_t s = 0; s < splits; ++s) {
+        const int tb = (int)(base + s * chunk);
+        const int te = (int)std::min<int64_t>(tb + chunk, lens[i]);
+        for (int h = 0; h < hkv; ++h) {
+          WorkItem it{};
+          it.request = i;
+          it.tok_begin = tb;
+          it.tok_end = te;
+          it.kv_head = h;
+          it.member_off = -1;
+          it.ncols = r;
+          it.col0 = 0;
+          it.col1 = r;
+          it.part_base = (int32_t)(row + s * hq + (int64_t)h * r);
+          P->items_s.push_back(it);
+        }
+      }
+      row += splits * hq;
+      if (row > INT32_MAX) return fail(FCA_ERR_UNSUPPORTED, "too many partial rows");
+    }
+  }
+  // Longest items first; ties keep their order.
+  auto work_of = [](const WorkItem& a) {
+    return (int64_t)(a.tok_end - a.tok_begin) * ((a.col1 - a.col0 + kGroupedCols - 1) / kGroupedCols);
+  };
+  std::stable_sort(P->items_g.begin(), P->items_g.end(),
+                   [&](const WorkItem& a, const WorkItem& b) { return work_of(a) > work_of(b); });
+  std::stable_sort(P->items_s.begin(), P->items_s.end(), [](const WorkItem& a, const WorkItem& b) {
+    return a.tok_end - a.tok_begin > b.tok_end - b.tok_begin;
+  });
+  if ((int64_t)P->items_g.size() > L.cap_g || (int64_t)P->items_s.size() > L.cap_s)
+    return fail(FCA_ERR_WORKSPACE, "schedule exceeds the workspace bound (tuning changed between calls?)");
+
+  int64_t sources = 0;
+  for (int i = 0; i < B; ++i) {
+    for (int g = deepest_c[i]; g >= 0; g = P->grp[g].parent) sources += P->grp[g].splits;
+    sources += P->req[i].sfx_splits;
+  }
+
+  fca_plan_info& info = P->info;
+  info.batch = B;
+  info.num_groups = G;
+  info.max_depth = max_depth;
+  info.num_grouped_items = (int32_t)P->items_g.size();
+  info.num_suffix_items = (int32_t)P->items_s.size();
+  info.num_merge_sources = (int32_t)std::min<int64_t>(sources, INT32_MAX);
+  info.num_partial_rows = row;
+  info.logical_tokens = logical;
+  info.unique_tokens = unique;
+  const size_t dv = (size_t)P->desc.head_dim_v;
+  info.decode_workspace_bytes = align_up((size_t)row * dv * 4) + 2 * align_up((size_t)row * 4) + kAlign;
+  return FCA_OK;
+}
+
+fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_stride, const int32_t* seq_lens_dev,
+                           int32_t batch, int32_t max_blocks, const fca_attn_desc* desc, void* workspace_dev,
+                           size_t workspace_bytes, void* stream, fca_plan* out) {
+  fca_plan_s* P = nullptr;
+  try {
+    if (!out) return fail(FCA_ERR_INVALID_ARG, "out is NULL");
+    Kind kind;
+    fca_status st = check_desc(desc, &kind);
+    if (st != FCA_OK) return st;
+    if (batch < 0 || batch > kMaxBatch) return fail(FCA_ERR_INVALID_ARG, "batch %d outside [0, %d]", batch, kMaxBatch);
+    if (max_blocks < 1 || max_blocks > kMaxTableWidth)
+      return fail(FCA_ERR_INVALID_ARG, "max_blocks %d outside [1, %d]", max_blocks, kMaxTableWidth);
+    if (batch > 0 && (!block_tables_dev || !seq_lens_dev))
+      return fail(FCA_ERR_INVALID_ARG, "block_tables / seq_lens is NULL");
+    if (batch > 0 && bt_row_stride < max_blocks)
+      return fail(FCA_ERR_INVALID_ARG, "bt_row_stride %lld < max_blocks %d", (long long)bt_row_stride, max_blocks);
+    if (!workspace_dev) return fail(FCA_ERR_INVALID_ARG, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace_dev) % kAlign)
+      return fail(FCA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+    const Tuning t = tuning();
+    const Layout L = make_layout(batch, max_blocks, desc, t);
+    if (workspace_bytes < L.total)
+      return fail(FCA_ERR_WORKSPACE, "plan workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+
+    P = new fca_plan_s();
+    P->desc = *desc;
+    P->kind = kind;
+    P->B = batch;
+    P->W = max_blocks;
+    P->r = desc->num_q_heads / desc->num_kv_heads;
+    P->ws = static_cast<char*>(workspace_dev);
+    P->L = L;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool cascade = !(desc->flags & FCA_PLAN_DISABLE_CASCADE);
+    DiscoveryPtrs dp = discovery_ptrs(P->ws, L, batch);
+    hipError_t e = launch_discovery(block_tables_dev, bt_row_stride, seq_lens_dev, batch, max_blocks,
+                                    desc->block_size, desc->num_blocks, cascade, dp, s);
+    if (e != hipSuccess) {
+      delete P;
+      return hip_fail(e, "discovery launch");
+    }
+    std::vector<int32_t> rb(L.readback_bytes / 4);
+    e = hipMemcpyAsync(rb.data(), P->ws + L.header, L.readback_bytes, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      delete P;
+      return hip_fail(e, "discovery read-back");
+    }
+    if (rb[kHdrErr]) {
+      const int bad = rb[kHdrBadReq];
+      const int err = rb[kHdrErr];
+      delete P;
+      return fail(FCA_ERR_BAD_TABLE, "request %d: %s", bad,
+                  (err & kErrBadLen) ? "seq_len outside [0, max_blocks * block_size]"
+                                     : "block ID outside [0, num_blocks) in a used slot");
+    }
+    st = build_plan(P, rb);
+    if (st != FCA_OK) {
+      delete P;
+      return st;
+    }
+    // Upload the schedule (pageable copies: the runtime stages them before returning).
+    struct Up {
+      const void* src;
+      size_t off, bytes;
+    } ups[] = {
+        {P->items_g.data(), L.items_g, P->items_g.size() * sizeof(WorkItem)},
+        {P->items_s.data(), L.items_s, P->items_s.size() * sizeof(WorkItem)},
+        {P->perm.data(), L.perm, P->perm.size() * 4},
+        {P->req.data(), L.req, P->req.size() * sizeof(ReqMeta)},
+        {P->grp.data(), L.grp, P->grp.size() * sizeof(GroupMeta)},
+    };
+    for (const Up& u : ups) {
+      if (!u.bytes) continue;
+      e = hipMemcpyAsync(P->ws + u.off, u.src, u.bytes, hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) {
+        delete P;
+        return hip_fail(e, "schedule upload");
+      }
+    }
+    *out = P;
+    return FCA_OK;
+  } catch (const std::bad_alloc&) {
+    delete P;
+    return fail(FCA_ERR_HOST_ALLOC, "host allocation failed");
+  } catch (...) {
+    delete P;
+    return fail(FCA_ERR_HOST_ALLOC, "unexpected host exception");
+  }
+}
+
+fca_status fca_plan_get_info(fca_plan plan, fca_plan_info* info) {
+  if (!plan || !info) return fail(FCA_ERR_INVALID_ARG, "plan / info is NULL");
+  *info = plan->info;
+  return FCA_OK;
+}
+
+fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                      void* out_dev, float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
+  const fca_plan_s* P = plan;
+  if (P->B == 0) return FCA_OK;
+  if (!q_dev || !k_cache_dev || !out_dev || (!P->desc.v_aliases_k && !v_cache_dev))
+    return fail(FCA_ERR_INVALID_ARG, "q / k_cache / v_cache / out is NULL");
+  if (P->info.num_partial_rows > 0) {
+    if (!workspace_dev) return fail(FCA_ERR_INVALID_ARG, "decode workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace_dev) % kAlign)
+      return fail(FCA_ERR_WORKSPACE, "decode workspace must be %zu-byte aligned", kAlign);
+    if (workspace_bytes < P->info.decode_workspace_bytes)
+      return fail(FCA_ERR_WORKSPACE, "decode workspace has %zu bytes, needs %zu", workspace_bytes,
+                  P->info.decode_workspace_bytes);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t rows = P->info.num_partial_rows;
+  const size_t dv = (size_t)P->desc.head_dim_v;
+  char* w = static_cast<char*>(workspace_dev);
+  PartialPtrs part;
+  part.o = reinterpret_cast<float*>(w);
+  part.m = reinterpret_cast<float*>(w + align_up((size_t)rows * dv * 4));
+  part.l = reinterpret_cast<float*>(w + align_up((size_t)rows * dv * 4) + align_up((size_t)rows * 4));
+
+  const Layout& L = P->L;
+  GqaParams gp;
+  gp.perm = reinterpret_cast<const int32_t*>(P->ws + L.perm);
+  gp.bt = reinterpret_cast<const int32_t*>(P->ws + L.bt);
+  gp.W = P->W;
+  gp.Hq = P->desc.num_q_heads;
+  gp.r = P->r;
+  gp.scale_log2 = P->desc.scale * 1.4426950408889634f;
+  gp.q = q_dev;
+  gp.k = k_cache_dev;
+  gp.v = v_cache_dev;
+  gp.k_stride_block = P->desc.k_stride_block;
+  gp.k_stride_head = P->desc.k_stride_head;
+  gp.v_stride_block = P->desc.v_stride_block;
+  gp.v_stride_head = P->desc.v_stride_head;
+  gp.part = part;
+  hipError_t e;
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  if (P->profiling) {
+    fca_plan_s* M = plan;
+    for (int j = 0; j < 4; ++j) {
+      if (M->event_pool.empty()) {
+        e = hipEventCreate(&ev[j]);
+        if (e != hipSuccess) return hip_fail(e, "profiling event");
+      } else {
+        ev[j] = M->event_pool.back();
+        M->event_pool.pop_back();
+      }
+      M->pending.push_back(ev[j]);
+    }
+  }
+  auto mark = [&](int j) -> hipError_t { return ev[j] ? hipEventRecord(ev[j], s) : hipSuccess; };
+  if ((e = mark(0)) != hipSuccess) return hip_fail(e, "event record");
+  gp.items = reinterpret_cast<const WorkItem*>(P->ws + L.items_g);
+  e = launch_gqa_partial(0, gp, (int)P->items_g.size(), s);
+  if (e != hipSuccess) return hip_fail(e, "grouped pass launch");
+  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "event record");
+  gp.items = reinterpret_cast<const WorkItem*>(P->ws + L.items_s);
+  e = launch_gqa_partial(1, gp, (int)P->items_s.size(), s);
+  if (e != hipSuccess) return hip_fail(e, "suffix pass launch");
+  if ((e = mark(2)) != hipSuccess) return hip_fail(e, "event record");
+
+  MergeParams mp;
+  mp.req = reinterpret_cast<const ReqMeta*>(P->ws + L.req);
+  mp.grp = reinterpret_cast<const GroupMeta*>(P->ws + L.grp);
+  mp.B = P->B;
+  mp.Hq = P->desc.num_q_heads;
+  mp.Hkv = P->desc.num_kv_heads;
+  mp.r = P->r;
+  mp.Dv = P->desc.head_dim_v;
+  mp.part = part;
+  mp.out = out_dev;
+  mp.lse = lse_dev;
+  e = launch_merge(mp, s);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "event record");
+  return FCA_OK;
+}
+
+fca_status fca_profile_enable(fca_plan plan, int32_t enable) {
+  if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
+  plan->profiling = enable != 0;
+  return FCA_OK;
+}
+
+fca_status fca_profile_read(fca_plan plan, fca_profile* out) {
+  if (!plan || !out) return fail(FCA_ERR_INVALID_ARG, "plan / out is NULL");
+  fca_profile acc{};
+  hipError_t err = hipSuccess;
+  for (size_t c = 0; c + 4 <= plan->pending.size(); c += 4) {
+    hipEvent_t* ev = plan->pending.data() + c;
+    float t[4] = {0, 0, 0, 0};
+    if (err == hipSuccess) err = hipEventSynchronize(ev[3]);
+    if (err == hipSuccess) err = hipEventElapsedTime(&t[0], ev[0], ev[1]);
+    if (err == hipSuccess) err = hipEventElapsedTime(&t[1], ev[1], ev[2]);
+    if (err == hipSuccess) err = hipEventElapsedTime(&t[2], ev[2], ev[3]);
+    if (err == hipSuccess) err = hipEventElapsedTime(&t[3], ev[0], ev[3]);
+    acc.grouped_ms += t[0];
+    acc.suffix_ms += t[1];
+    acc.merge_ms += t[2];
+    acc.decode_ms += t[3];
+    acc.calls += 1;
+  }
+  plan->event_pool.insert(plan->event_pool.end(), plan->pending.begin(), plan->pending.end());
+  plan->pending.clear();
+  if (err != hipSuccess) return hip_fail(err, "profiling events");
+  *out = acc;
+  return FCA_OK;
+}
+
+fca_status fca_plan_export(fca_plan plan, fca_group_record* groups, int32_t* members, int32_t* requests) {
+  if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
+  if (groups) std::copy(plan->groups.begin(), plan->groups.end(), groups);
+  if (members) std::copy(plan->members.begin(), plan->members.end(), members);
+  if (requests) std::copy(plan->req3.begin(), plan->req3.end(), requests);
+  return FCA_OK;
+}
+
+fca_status fca_plan_export_schedule(fca_plan plan, fca_work_item* grouped, fca_work_item* suffix, int32_t* src_off,
+                                    int32_t* src) {
+  if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
+  const fca_plan_s* P = plan;
+  if (grouped) std::memcpy(grouped, P->items_g.data(), P->items_g.size() * sizeof(WorkItem));
+  if (suffix) std::memcpy(suffix, P->items_s.data(), P->items_s.size() * sizeof(WorkItem));
+  if (src_off || src) {
+    int64_t n = 0;
+    for (int i = 0; i < P->B; ++i) {
+      if (src_off) src_off[i] = (int32_t)n;
+      const ReqMeta& rq = P->req[i];
+      for (int g = rq.deepest; g >= 0; g = P->grp[g].parent) {
+        const GroupMeta& gm = P->grp[g];
+        const int k = rq.pos - gm.r0;
+        for (int s = 0; s < gm.splits; ++s) {
+          if (src) {
+            src[2 * n] = gm.unit + s * P->desc.num_kv_heads * gm.ncols + k * P->r;
+            src[2 * n + 1] = gm.ncols;
+          }
+          ++n;
+        }
+      }
+      for (int s = 0; s < rq.sfx_splits; ++s) {
+        if (src) {
+          src[2 * n] = rq.sfx_unit + s * P->desc.num_q_heads;
+          src[2 * n + 1] = P->r;
+        }
+        ++n;
+      }
+    }
+    if (src_off) src_off[P->B] = (int32_t)n;
+  }
+  return FCA_OK;
+}
+
+void fca_plan_destroy(fca_plan plan) { delete plan; }
+
+}  // extern "C"

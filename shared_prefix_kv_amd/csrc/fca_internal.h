@@ -1,0 +1,117 @@
+// Internal declarations shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/fca.h"
+
+namespace fca {
+
+constexpr int kMaxBatch = 8192;
+constexpr int kMaxTableWidth = 1 << 20;
+constexpr int kTileTokens = 32;  // tokens per MFMA tile step of the attention kernels
+
+// A unit of work of the grouped or per-request pass; same layout as the
+// public fca_work_item.
+struct WorkItem {
+  int32_t request;
+  int32_t tok_begin;
+  int32_t tok_end;
+  int32_t kv_head;
+  int32_t member_off;
+  int32_t ncols;
+  int32_t col0;
+  int32_t col1;
+  int32_t part_base;
+  int32_t pad0, pad1, pad2;
+};
+static_assert(sizeof(WorkItem) == sizeof(fca_work_item), "work item layout");
+
+// Per-request data the merge reads.
+struct ReqMeta {
+  int32_t pos;         // position in the depth-first member order
+  int32_t deepest;     // canonical index of the deepest group, -1 if none
+  int32_t sfx_unit;    // partial row of (split 0, q head 0) of the suffix
+  int32_t sfx_splits;  // number of suffix splits (0: no suffix tokens)
+};
+
+// Per-group data the merge reads (canonical order).
+struct GroupMeta {
+  int32_t parent;  // canonical index or -1
+  int32_t r0;      // first position of the group's members in `perm`
+  int32_t ncols;   // members * (Hq / Hkv)
+  int32_t unit;    // partial row of (split 0, kv head 0, column 0)
+  int32_t splits;  // token splits of the group's range
+  int32_t pad0, pad1, pad2;
+};
+
+// Discovery header words.
+enum { kHdrGroups = 0, kHdrErr = 1, kHdrBadReq = 2, kHdrWords = 64 };
+enum { kErrBadBlock = 1, kErrBadLen = 2 };
+constexpr int kRecordInts = 8;  // leader, depth, parent gid, begin, end, count, 0, 0
+
+// Device arrays of the discovery step (all inside the plan workspace).
+struct DiscoveryPtrs {
+  int32_t* header;     // [kHdrWords]   -- read back
+  int32_t* lens;       // [B]           -- read back
+  int32_t* deepest;    // [B] device group id, -1   -- read back
+  int32_t* sfx_begin;  // [B] first suffix block    -- read back
+  int32_t* records;    // [B * kRecordInts]         -- read back
+  int32_t* bt;         // [B * W] copy of the used table entries (-1 elsewhere)
+  int32_t* nfull;
+  int32_t* root;
+  int32_t* depth_at;   // current node's first block
+  int32_t* node;
+  int32_t* gdepth;
+  int32_t* gparent;
+  int32_t* active;
+  int32_t* ndstar;
+  int32_t* ncount;
+  int32_t* ngid;
+  int32_t* newnode;
+};
+
+hipError_t launch_discovery(const int32_t* bt_in, int64_t bt_stride, const int32_t* lens_in, int B, int W,
+                            int block_size, int num_blocks, bool cascade, const DiscoveryPtrs& p, hipStream_t s);
+
+// Partial (o, m, l) rows: o unnormalised w.r.t. its own running max m
+// (log2 domain), l the matching denominator.
+struct PartialPtrs {
+  float* o;
+  float* m;
+  float* l;
+};
+
+struct GqaParams {
+  const WorkItem* items;
+  const int32_t* perm;
+  const int32_t* bt;
+  int32_t W;
+  int32_t Hq;
+  int32_t r;
+  float scale_log2;
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t k_stride_block, k_stride_head, v_stride_block, v_stride_head;
+  PartialPtrs part;
+};
+
+// kind 0: grouped pass (32 query rows per wave), 1: per-request pass (16).
+hipError_t launch_gqa_partial(int kind, const GqaParams& p, int n_items, hipStream_t s);
+
+struct MergeParams {
+  const ReqMeta* req;
+  const GroupMeta* grp;
+  int32_t B, Hq, Hkv, r, Dv;
+  PartialPtrs part;
+  void* out;
+  float* lse;
+};
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+
+}  // namespace fca

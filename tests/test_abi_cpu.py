@@ -1,0 +1,148 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects bad arguments before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import shared_prefix_kv_amd as fca
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fca.LIB_PATH), reason="libfca.so not built")
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "fca.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fca_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = fca.lib()
+    decl = declared_symbols()
+    assert decl, "no declarations parsed"
+    for name in decl:
+        assert hasattr(L, name), name
+    assert sorted(decl) == sorted(fca.EXPORTED)
+    assert fca.version() == "0.1.0"
+
+
+def gqa_desc(**kw):
+    args = dict(
+        num_q_heads=32, num_kv_heads=8, head_dim_qk=128, head_dim_v=128, block_size=16, num_blocks=100, scale=0.088
+    )
+    args.update(kw)
+    return fca.make_desc(**args)
+
+
+def status_of(fn, *a):
+    return fn(*a)
+
+
+def test_workspace_size_and_validation():
+    n = fca.plan_workspace_size(64, 320, gqa_desc())
+    assert n > 64 * 320 * 4
+    assert fca.plan_workspace_size(0, 1, gqa_desc()) > 0
+    with pytest.raises(fca.FcaError) as e:
+        fca.plan_workspace_size(64, 320, gqa_desc(head_dim_qk=96, head_dim_v=96))
+    assert e.value.status == 2
+    with pytest.raises(fca.FcaError) as e:
+        fca.plan_workspace_size(64, 320, gqa_desc(num_q_heads=30))
+    assert e.value.status == 1
+    with pytest.raises(fca.FcaError) as e:
+        fca.plan_workspace_size(64, 320, gqa_desc(num_q_heads=64, num_kv_heads=2))  # ratio 32
+    assert e.value.status == 2
+    with pytest.raises(fca.FcaError) as e:
+        fca.plan_workspace_size(-1, 320, gqa_desc())
+    assert e.value.status == 1
+    with pytest.raises(fca.FcaError) as e:
+        fca.plan_workspace_size(9000, 320, gqa_desc())
+    assert e.value.status == 1
+    with pytest.raises(fca.FcaError) as e:
+        fca.plan_workspace_size(4, 0, gqa_desc())
+    assert e.value.status == 1
+    d = gqa_desc()
+    d.reserved = 3
+    with pytest.raises(fca.FcaError):
+        fca.plan_workspace_size(4, 4, d)
+    d = gqa_desc(scale=float("nan"))
+    with pytest.raises(fca.FcaError):
+        fca.plan_workspace_size(4, 4, d)
+    d = gqa_desc()
+    d.flags = 8
+    with pytest.raises(fca.FcaError):
+        fca.plan_workspace_size(4, 4, d)
+    d = gqa_desc()
+    d.k_stride_head = 100  # tiles would overlap
+    with pytest.raises(fca.FcaError):
+        fca.plan_workspace_size(4, 4, d)
+
+
+def test_create_rejects_bad_args_before_device():
+    L = fca.lib()
+    d = gqa_desc()
+    h = ctypes.c_void_p()
+    fake = ctypes.c_void_p(0x1000)
+    # NULL tables with batch > 0
+    st = L.fca_plan_create(None, 4, fake, 2, 4, ctypes.byref(d), fake, 1 << 20, None, ctypes.byref(h))
+    assert st == 1 and b"NULL" in L.fca_last_error()
+    # stride smaller than width
+    st = L.fca_plan_create(fake, 2, fake, 2, 4, ctypes.byref(d), fake, 1 << 20, None, ctypes.byref(h))
+    assert st == 1
+    # misaligned workspace
+    st = L.fca_plan_create(fake, 4, fake, 2, 4, ctypes.byref(d), ctypes.c_void_p(0x1004), 1 << 20, None, ctypes.byref(h))
+    assert st == 3
+    # workspace too small
+    st = L.fca_plan_create(fake, 4, fake, 2, 4, ctypes.byref(d), fake, 16, None, ctypes.byref(h))
+    assert st == 3 and b"needs" in L.fca_last_error()
+    # NULL out handle
+    st = L.fca_plan_create(fake, 4, fake, 2, 4, ctypes.byref(d), fake, 1 << 20, None, None)
+    assert st == 1
+    assert not h.value
+
+
+def test_decode_and_info_reject_null_plan():
+    L = fca.lib()
+    assert L.fca_decode(None, None, None, None, None, None, None, 0, None) == 1
+    info = fca.PlanInfo()
+    assert L.fca_plan_get_info(None, ctypes.byref(info)) == 1
+    assert L.fca_plan_export(None, None, None, None) == 1
+    assert L.fca_plan_export_schedule(None, None, None, None, None) == 1
+    assert L.fca_profile_enable(None, 1) == 1
+    assert L.fca_profile_read(None, None) == 1
+    L.fca_plan_destroy(None)  # no-op
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """ctypes mirrors have the sizes and field offsets a C compiler gives the header."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {
+        "fca_attn_desc": fca.AttnDesc,
+        "fca_plan_info": fca.PlanInfo,
+        "fca_group_record": fca.GroupRecord,
+        "fca_work_item": fca.WorkItem,
+        "fca_profile": fca.Profile,
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "fca.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname}.{fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("  return 0; }")
+    src = tmp_path / "sizes.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "sizes"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines())
+    for cname, py in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert int(got[f"{cname}.{fname}"]) == getattr(py, fname).offset, (cname, fname)

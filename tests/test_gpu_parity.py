@@ -1,0 +1,371 @@
+"""GPU parity: plans (bit-exact) and decode outputs (tolerance) of libfca
+against the CPU oracle, through the C ABI.  Needs an MI355X."""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle.grouping import group
+from tests.helpers import (
+    assert_close,
+    assert_lse_close,
+    bf16_tensor_to_f64,
+    oracle_requests_from_device,
+    to_device_bf16,
+)
+from workloads import CONFIGS, build_batch, fill_values_numpy
+from workloads.forest import AttnShape
+from workloads.values import BF16_NAN, fill_values_torch, f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import shared_prefix_kv_amd as fca  # noqa: E402
+
+GQA_CONFIGS = ["tiny", "llama3_8b", "long_rl", "forest_mixed"]
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fca.lib()
+
+
+def dev_tables(batch):
+    return (
+        torch.from_numpy(batch.block_tables).cuda(),
+        torch.from_numpy(batch.seq_lens).cuda(),
+    )
+
+
+def plan_for(batch, cascade=True):
+    bt, sl = dev_tables(batch)
+    desc = fca.desc_from_shape(batch.shape, batch.num_blocks, cascade=cascade)
+    return fca.fca_plan(bt, sl, desc)
+
+
+def with_block_ids(exported, tables):
+    groups = []
+    for g in exported["groups"]:
+        first = g["members"][0]
+        groups.append(dict(g, block_ids=tuple(int(x) for x in tables[first][g["block_begin"] : g["block_end"]])))
+    return dict(groups=groups, requests=exported["requests"])
+
+
+# ---------------------------------------------------------------- plans ----
+
+
+@pytest.mark.parametrize("name", GQA_CONFIGS)
+def test_plan_matches_oracle(name):
+    b = build_batch(CONFIGS[name])
+    say("plan", name, "B", b.batch)
+    p = plan_for(b)
+    got = with_block_ids(p.export(), b.block_tables)
+    assert got == group(b.block_tables, b.seq_lens, b.shape.block_size)
+    assert p.info.unique_tokens == sum((g["block_end"] - g["block_begin"]) * b.shape.block_size for g in got["groups"]) + sum(r[1] for r in got["requests"])
+    pn = plan_for(b, cascade=False)
+    assert with_block_ids(pn.export(), b.block_tables) == group(b.block_tables, b.seq_lens, b.shape.block_size, cascade=False)
+
+
+def random_forest(rng, B, width, bs, alphabet):
+    rows = []
+    for i in range(B):
+        if rows and rng.random() < 0.6:
+            base = rows[int(rng.integers(0, len(rows)))]
+            cut = int(rng.integers(0, width + 1))
+            row = list(base[:cut]) + list(rng.integers(0, alphabet, size=width - cut))
+        else:
+            row = list(rng.integers(0, alphabet, size=width))
+        rows.append(row)
+    tables = np.array(rows, dtype=np.int32).reshape(B, width)
+    lens = rng.integers(0, width * bs + 1, size=B).astype(np.int32)
+    for i in range(B):
+        nb = -(-int(lens[i]) // bs)
+        tables[i, nb:] = rng.integers(-(2**31), 2**31, size=width - nb, dtype=np.int64).astype(np.int32)
+    return tables, lens
+
+
+def test_plan_fuzz_forests():
+    rng = np.random.default_rng(1234)
+    shape = AttnShape(8, 2, 128, 128, 16, 0.1)
+    cases = 0
+    for B in [1, 2, 3, 5, 8, 17, 40, 100, 300]:
+        for width in [1, 3, 8, 70]:
+            for alphabet in [1, 2, 3, 50]:
+                tables, lens = random_forest(rng, B, width, 16, alphabet)
+                desc = fca.desc_from_shape(shape, 64)
+                p = fca.fca_plan(torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), desc)
+                got = with_block_ids(p.export(), tables)
+                exp = group(tables, lens, 16)
+                assert got == exp, (B, width, alphabet)
+                cases += 1
+    say("fuzz plans", cases)
+
+
+def test_plan_deep_chain_and_duplicates():
+    # caterpillar: request i shares i+1 blocks with request i+1
+    B, W = 40, 48
+    t = np.arange(B * W, dtype=np.int32).reshape(B, W) + 1000
+    for i in range(1, B):
+        t[i, :i] = t[i - 1, :i]
+    lens = np.full(B, W * 16, np.int32)
+    tables = np.concatenate([t, t[:5]])  # plus exact duplicates
+    lens = np.concatenate([lens, lens[:5]])
+    desc = fca.desc_from_shape(AttnShape(4, 4, 128, 128, 16, 0.1), 10**6)
+    p = fca.fca_plan(torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), desc)
+    assert with_block_ids(p.export(), tables) == group(tables, lens, 16)
+    assert p.info.max_depth > 10
+
+
+def test_plan_copies_tables_and_bad_tables():
+    b = build_batch(CONFIGS["tiny"])
+    bt, sl = dev_tables(b)
+    desc = fca.desc_from_shape(b.shape, b.num_blocks)
+    p = fca.fca_plan(bt, sl, desc)
+    before = with_block_ids(p.export(), b.block_tables)
+    bt.fill_(0)
+    sl.fill_(0)
+    torch.cuda.synchronize()
+    assert with_block_ids(p.export(), b.block_tables) == before
+    # block ID outside the pool in a used slot
+    bad = b.block_tables.copy()
+    bad[3, 1] = b.num_blocks
+    with pytest.raises(fca.FcaError) as e:
+        fca.fca_plan(torch.from_numpy(bad).cuda(), torch.from_numpy(b.seq_lens).cuda(), desc)
+    assert e.value.status == 4 and "request 3" in str(e.value)
+    bad[3, 1] = -1
+    with pytest.raises(fca.FcaError):
+        fca.fca_plan(torch.from_numpy(bad).cuda(), torch.from_numpy(b.seq_lens).cuda(), desc)
+    # seq_len longer than the table can hold
+    lens = b.seq_lens.copy()
+    lens[5] = b.max_blocks * 16 + 1
+    with pytest.raises(fca.FcaError) as e:
+        fca.fca_plan(torch.from_numpy(b.block_tables).cuda(), torch.from_numpy(lens).cuda(), desc)
+    assert e.value.status == 4
+    # an out-of-pool ID past the last used block is fine (padding)
+    ok = b.block_tables.copy()
+    ok[0, -1] = 10**9
+    if b.seq_lens[0] <= (b.max_blocks - 1) * 16:
+        fca.fca_plan(torch.from_numpy(ok).cuda(), torch.from_numpy(b.seq_lens).cuda(), desc)
+
+
+@pytest.mark.parametrize("name", GQA_CONFIGS)
+def test_schedule_covers_each_token_once(name):
+    b = build_batch(CONFIGS[name])
+    p = plan_for(b)
+    sh = b.shape
+    r = sh.gqa_ratio
+    ex = p.export()
+    sc = p.export_schedule()
+    bs = sh.block_size
+    # grouped: every (group, head, query row, token) of each range exactly once
+    cover = {}
+    for it in sc["grouped"]:
+        assert it["tok_begin"] < it["tok_end"] and it["col0"] < it["col1"] <= it["ncols"]
+        assert (it["tok_begin"] - sc["grouped"][0]["tok_begin"]) % 1 == 0
+        key = (it["member_off"], it["kv_head"])
+        cover.setdefault(key, []).append((it["tok_begin"], it["tok_end"], it["col0"], it["col1"]))
+    assert len(cover) == len(ex["groups"]) * sh.num_kv_heads
+    for key, spans in cover.items():
+        toks = {}
+        for t0, t1, c0, c1 in spans:
+            toks.setdefault((t0, t1), []).append((c0, c1))
+        ranges = sorted(toks)
+        for (a0, a1), (b0, _) in zip(ranges, ranges[1:]):
+            assert a1 == b0
+        for cols in toks.values():
+            cols.sort()
+            assert cols[0][0] == 0
+            for (a0, a1), (b0, _) in zip(cols, cols[1:]):
+                assert a1 == b0
+    # suffix: each request's suffix tokens exactly once per head
+    per_req = {}
+    for it in sc["suffix"]:
+        per_req.setdefault((it["request"], it["kv_head"]), []).append((it["tok_begin"], it["tok_end"]))
+        assert it["col0"] == 0 and it["col1"] == r and it["member_off"] == -1
+    for i, (sb, st, _) in enumerate(ex["requests"]):
+        for h in range(sh.num_kv_heads):
+            spans = sorted(per_req.get((i, h), []))
+            total = sum(e - s for s, e in spans)
+            assert total == st
+            if st:
+                assert spans[0][0] == sb * bs and spans[-1][1] == int(b.seq_lens[i])
+    # merge sources: every partial row read once per (request, head)
+    rows_seen = np.zeros(p.info.num_partial_rows, dtype=np.int64)
+    for i in range(b.batch):
+        for h in range(sh.num_q_heads):
+            for a, bb in sc["sources"][i]:
+                rows_seen[a + (h // r) * bb + h % r] += 1
+    assert (rows_seen == 1).all()
+
+
+# --------------------------------------------------------------- decode ----
+
+
+def run_decode(batch, vals, cascade=True, lse=True):
+    p = plan_for(batch, cascade=cascade)
+    out = torch.empty((batch.batch, batch.shape.num_q_heads, batch.shape.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    l = torch.empty((batch.batch, batch.shape.num_q_heads), dtype=torch.float32, device="cuda") if lse else None
+    fca.fca_decode(vals["q"], vals["k"], vals["v"], p, out=out, lse=l)
+    torch.cuda.synchronize()
+    return p, out, l
+
+
+def upload(vals_np):
+    return {k: (to_device_bf16(v) if v is not None else None) for k, v in vals_np.items()}
+
+
+@pytest.mark.parametrize("cascade", [True, False])
+def test_decode_tiny_full(cascade):
+    b = build_batch(CONFIGS["tiny"])
+    vn = fill_values_numpy(b, poison=True)
+    say("decode tiny cascade", cascade)
+    ref, ref_lse = A.attend(vn["q"], vn["k"], vn["v"], b.block_tables, b.seq_lens, b.shape)
+    _, out, lse = run_decode(b, upload(vn), cascade=cascade)
+    rep = assert_close(bf16_tensor_to_f64(out), ref, f"tiny cascade={cascade}")
+    assert_lse_close(lse.cpu().numpy(), ref_lse, "tiny")
+    say("tiny", rep)
+
+
+def test_decode_llama3_8b_full():
+    b = build_batch(CONFIGS["llama3_8b"])
+    vn = fill_values_numpy(b, poison=True)
+    say("decode llama3_8b (all 64 requests vs oracle)")
+    ref, ref_lse = A.attend(vn["q"], vn["k"], vn["v"], b.block_tables, b.seq_lens, b.shape)
+    vals = upload(vn)
+    p, out, lse = run_decode(b, vals)
+    rep = assert_close(bf16_tensor_to_f64(out), ref, "llama3_8b")
+    assert_lse_close(lse.cpu().numpy(), ref_lse, "llama3_8b")
+    say("llama3_8b cascade", rep, "groups", p.info.num_groups)
+    _, out_nc, _ = run_decode(b, vals, cascade=False)
+    rep2 = assert_close(bf16_tensor_to_f64(out_nc), ref, "llama3_8b non-cascade")
+    say("llama3_8b non-cascade", rep2)
+    # bitwise determinism
+    _, out2, lse2 = run_decode(b, vals)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("name", ["long_rl", "forest_mixed"])
+def test_decode_sampled_full_size(name):
+    b = build_batch(CONFIGS[name])
+    say("decode", name, "full size, sampled oracle")
+    vals = fill_values_torch(b, "cuda", seed=CONFIGS[name].seed, poison=True)
+    p, out, lse = run_decode(b, vals)
+    # every output finite; sample longest, shortest and a spread of requests
+    assert torch.isfinite(out.float()).all()
+    order = np.argsort(b.seq_lens)
+    pick = sorted(set([int(order[0]), int(order[-1])] + [int(x) for x in np.linspace(0, b.batch - 1, 6).astype(int)]))
+    ref, ref_lse = oracle_requests_from_device(b, vals, pick)
+    rep = assert_close(bf16_tensor_to_f64(out[pick]), ref, name)
+    assert_lse_close(lse[pick].cpu().numpy(), ref_lse, name)
+    say(name, rep, "groups", p.info.num_groups, "items", p.info.num_grouped_items, p.info.num_suffix_items)
+    del vals
+    torch.cuda.empty_cache()
+
+
+def small_case(shape, tables, lens, num_blocks, seed=0):
+    rng = np.random.default_rng(seed)
+    k = f32_to_bf16_bits(rng.standard_normal((num_blocks, shape.num_kv_heads, shape.head_dim_qk // 8, shape.block_size, 8), dtype=np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((num_blocks, shape.num_kv_heads, shape.head_dim_v, shape.block_size), dtype=np.float32))
+    q = f32_to_bf16_bits(rng.standard_normal((len(lens), shape.num_q_heads, shape.head_dim_qk), dtype=np.float32))
+    bs = shape.block_size
+    used = np.zeros(num_blocks, bool)
+    for i, L in enumerate(lens):
+        nb = -(-int(L) // bs)
+        used[tables[i, :nb]] = True
+        if L % bs:
+            blk = tables[i, L // bs]
+            k[blk, :, :, L % bs :, :] = BF16_NAN
+            v[blk, :, :, L % bs :] = BF16_NAN
+    k[~used] = BF16_NAN
+    v[~used] = BF16_NAN
+    return dict(q=q, k=k, v=v)
+
+
+class _B:
+    def __init__(self, shape, tables, lens, num_blocks):
+        self.shape, self.block_tables, self.seq_lens, self.num_blocks = shape, tables, lens, num_blocks
+        self.batch = len(lens)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (16, 2), (16, 1), (12, 4)])
+def test_decode_edge_lengths_and_ratios(hq, hkv):
+    """Lengths 0, 1, block and tile boundaries, nested sharing, duplicates."""
+    shape = AttnShape(hq, hkv, 128, 128, 16, 1 / math.sqrt(128))
+    lens = np.array([0, 1, 15, 16, 17, 31, 32, 33, 47, 48, 200, 513, 513, 530, 700, 64], np.int32)
+    W = 48
+    B = len(lens)
+    nb = 4096
+    rng = np.random.default_rng(hq * 100 + hkv)
+    perm = rng.permutation(nb)
+    tables = perm[: B * W].reshape(B, W).astype(np.int32)
+    # requests 10..15 share 12 blocks; 11..13 share 32 blocks; 11 and 12 identical
+    tables[11:16, :12] = tables[10, :12]
+    tables[12:14, :32] = tables[11, :32]
+    tables[12] = tables[11]
+    tables[15, :4] = tables[10, :4]
+    case = small_case(shape, tables, lens, nb, seed=hq + hkv)
+    ref, ref_lse = A.attend(case["q"], case["k"], case["v"], tables, lens, shape)
+    b = _B(shape, tables, lens, nb)
+    vals = upload(case)
+    for cascade in (True, False):
+        p, out, lse = run_decode(b, vals, cascade=cascade)
+        assert_close(bf16_tensor_to_f64(out), ref, f"edge hq={hq} hkv={hkv} cascade={cascade}")
+        assert_lse_close(lse.cpu().numpy(), ref_lse, "edge")
+        o = bf16_tensor_to_f64(out)
+        assert (o[0] == 0).all() and np.isneginf(lse[0].cpu().numpy()).all()
+    say("edge", hq, hkv, "groups", p.info.num_groups)
+
+
+def test_decode_empty_batch_and_all_empty():
+    shape = AttnShape(8, 2, 128, 128, 16, 0.1)
+    desc = fca.desc_from_shape(shape, 8)
+    p = fca.fca_plan(torch.zeros((0, 4), dtype=torch.int32, device="cuda"), torch.zeros(0, dtype=torch.int32, device="cuda"), desc)
+    assert p.info.batch == 0
+    q = torch.zeros((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((8, 2, 16, 16, 8), dtype=torch.bfloat16, device="cuda")
+    out = fca.fca_decode(q, kv, kv, p)
+    assert out.shape == (0, 8, 128)
+    # all requests empty
+    p = fca.fca_plan(torch.zeros((3, 4), dtype=torch.int32, device="cuda"), torch.zeros(3, dtype=torch.int32, device="cuda"), desc)
+    q = torch.ones((3, 8, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((3, 8), dtype=torch.float32, device="cuda")
+    out = fca.fca_decode(q, kv, kv, p, lse=lse)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all() and torch.isneginf(lse).all()
+
+
+def test_decode_strided_pool():
+    """Pools that are slices of a larger buffer (head/block strides)."""
+    b = build_batch(CONFIGS["tiny"])
+    vn = fill_values_numpy(b, poison=True)
+    sh = b.shape
+    ref, _ = A.attend(vn["q"], vn["k"], vn["v"], b.block_tables, b.seq_lens, sh)
+    # embed each pool in a buffer with 3 extra heads per block
+    nb = b.num_blocks
+    kbig = np.full((nb, sh.num_kv_heads + 3, 16, 16, 8), BF16_NAN, np.uint16)
+    vbig = np.full((nb, sh.num_kv_heads + 3, 128, 16), BF16_NAN, np.uint16)
+    kbig[:, 1 : 1 + sh.num_kv_heads] = vn["k"]
+    vbig[:, 2 : 2 + sh.num_kv_heads] = vn["v"]
+    kd, vd = to_device_bf16(kbig), to_device_bf16(vbig)
+    ksh = 128 * 16
+    desc = fca.make_desc(
+        sh.num_q_heads, sh.num_kv_heads, 128, 128, 16, nb, sh.scale,
+        k_strides=((sh.num_kv_heads + 3) * ksh, ksh), v_strides=((sh.num_kv_heads + 3) * ksh, ksh),
+    )
+    bt, sl = dev_tables(b)
+    p = fca.fca_plan(bt, sl, desc)
+    out = fca.fca_decode(to_device_bf16(vn["q"]), kd[:, 1:], vd[:, 2:], p)
+    torch.cuda.synchronize()
+    assert_close(bf16_tensor_to_f64(out), ref, "strided pool")
