@@ -51,6 +51,13 @@ typedef enum fca_status {
 #define FCA_PLAN_DISABLE_CASCADE 1u /* no groups: every request is read whole
                                        by the per-request pass (the
                                        non-cascade paged-decode baseline) */
+#define FCA_PLAN_CONCURRENT_PASSES 2u /* run the grouped pass on a
+                                       library-owned side stream, forked from
+                                       and joined back into the caller's
+                                       stream with events, concurrently with
+                                       the per-request pass.  By default the
+                                       passes run one after the other on the
+                                       caller's stream. */
 
 /*
  * Shape and cache layout of one attention layer.
@@ -160,9 +167,10 @@ fca_status fca_plan_get_info(fca_plan plan, fca_plan_info* info);
  *                partial (o, max, denominator) triples of this call.
  *
  * Asynchronous on `stream`: no host synchronisation and no allocation.
- * Calls that share a decode workspace must not overlap; a plan itself is
- * read-only and may serve calls on several streams with separate decode
- * workspaces.
+ * Calls that share a decode workspace must not overlap.  Calls on one plan
+ * must be issued from one host thread at a time (with
+ * FCA_PLAN_CONCURRENT_PASSES they reuse the plan's fork/join events); they
+ * may target different streams if each has its own decode workspace.
  */
 fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
                       void* out_dev, float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream);

@@ -28,6 +28,7 @@ STATUS_NAMES = {
     6: "FCA_ERR_HOST_ALLOC",
 }
 FCA_PLAN_DISABLE_CASCADE = 1
+FCA_PLAN_CONCURRENT_PASSES = 2
 
 EXPORTED = [
     "fca_plan_workspace_size",
@@ -169,6 +170,7 @@ def make_desc(
     cascade=True,
     k_strides=None,
     v_strides=None,
+    concurrent_passes=False,
 ) -> AttnDesc:
     """Descriptor for the documented cache layout (default: dense pools)."""
     d = AttnDesc()
@@ -184,12 +186,12 @@ def make_desc(
         d.v_stride_block, d.v_stride_head = v_strides if v_strides else (num_kv_heads * vsh, vsh)
     d.v_aliases_k = int(bool(v_aliases_k))
     d.scale = float(scale)
-    d.flags = 0 if cascade else FCA_PLAN_DISABLE_CASCADE
+    d.flags = (0 if cascade else FCA_PLAN_DISABLE_CASCADE) | (FCA_PLAN_CONCURRENT_PASSES if concurrent_passes else 0)
     d.reserved = 0
     return d
 
 
-def desc_from_shape(shape, num_blocks, cascade=True) -> AttnDesc:
+def desc_from_shape(shape, num_blocks, cascade=True, concurrent_passes=False) -> AttnDesc:
     return make_desc(
         shape.num_q_heads,
         shape.num_kv_heads,
@@ -200,6 +202,7 @@ def desc_from_shape(shape, num_blocks, cascade=True) -> AttnDesc:
         shape.scale,
         v_aliases_k=shape.v_aliases_k,
         cascade=cascade,
+        concurrent_passes=concurrent_passes,
     )
 
 

@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <cstring>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -82,7 +83,8 @@ fca_status check_desc(const fca_attn_desc* d, Kind* kind) {
                 d->num_q_heads, d->num_kv_heads);
   if (d->num_blocks <= 0) return fail(FCA_ERR_INVALID_ARG, "num_blocks must be positive");
   if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return fail(FCA_ERR_INVALID_ARG, "scale must be finite and > 0");
-  if (d->flags & ~FCA_PLAN_DISABLE_CASCADE) return fail(FCA_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
+  if (d->flags & ~(FCA_PLAN_DISABLE_CASCADE | FCA_PLAN_CONCURRENT_PASSES))
+    return fail(FCA_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
   const int r = d->num_q_heads / d->num_kv_heads;
   if (d->head_dim_qk == 128 && d->head_dim_v == 128 && d->block_size == 16 && !d->v_aliases_k) {
     if (r > 16) return fail(FCA_ERR_UNSUPPORTED, "GQA ratio %d > 16 is not built", r);
@@ -154,6 +156,26 @@ DiscoveryPtrs discovery_ptrs(char* ws, const Layout& L, int B) {
   return p;
 }
 
+// One side stream per device for the grouped pass, default priority,
+// created on first use and kept for the life of the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+hipStream_t g_side[kMaxDevices] = {};
+
+hipError_t side_stream(hipStream_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  if (!g_side[dev]) {
+    e = hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+  }
+  *out = g_side[dev];
+  return hipSuccess;
+}
+
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
 
@@ -174,11 +196,16 @@ struct fca_plan_s {
   std::vector<ReqMeta> req;
   std::vector<GroupMeta> grp;
   fca_plan_info info;
+  // concurrent passes
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
   // measurement hook
   bool profiling = false;
   std::vector<hipEvent_t> event_pool;
-  std::vector<hipEvent_t> pending;  // 4 per profiled call
+  std::vector<hipEvent_t> pending;  // kProfEvents per profiled call
   ~fca_plan_s() {
+    if (fork) (void)hipEventDestroy(fork);
+    if (join) (void)hipEventDestroy(join);
     for (hipEvent_t e : pending) (void)hipEventDestroy(e);
     for (hipEvent_t e : event_pool) (void)hipEventDestroy(e);
   }
@@ -526,6 +553,15 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
         return hip_fail(e, "schedule upload");
       }
     }
+    if ((desc->flags & FCA_PLAN_CONCURRENT_PASSES) && !P->items_g.empty() && !P->items_s.empty()) {
+      e = side_stream(&P->side);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&P->fork, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&P->join, hipEventDisableTiming);
+      if (e != hipSuccess) {
+        delete P;
+        return hip_fail(e, "side stream / events");
+      }
+    }
     *out = P;
     return FCA_OK;
   } catch (const std::bad_alloc&) {
@@ -584,10 +620,11 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   gp.v_stride_head = P->desc.v_stride_head;
   gp.part = part;
   hipError_t e;
-  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  fca_plan_s* M = plan;
+  constexpr int kProf = 7;
+  hipEvent_t ev[kProf] = {};
   if (P->profiling) {
-    fca_plan_s* M = plan;
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kProf; ++j) {
       if (M->event_pool.empty()) {
         e = hipEventCreate(&ev[j]);
         if (e != hipSuccess) return hip_fail(e, "profiling event");
@@ -598,16 +635,32 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
       M->pending.push_back(ev[j]);
     }
   }
-  auto mark = [&](int j) -> hipError_t { return ev[j] ? hipEventRecord(ev[j], s) : hipSuccess; };
-  if ((e = mark(0)) != hipSuccess) return hip_fail(e, "event record");
+  const bool overlap = P->side != nullptr;
+  hipStream_t sg = overlap ? P->side : s;
+  auto mark = [&](int j, hipStream_t st) -> hipError_t { return ev[j] ? hipEventRecord(ev[j], st) : hipSuccess; };
+#define FCA_TRY(expr, what)             \
+  do {                                  \
+    e = (expr);                         \
+    if (e != hipSuccess) return hip_fail(e, what); \
+  } while (0)
+  FCA_TRY(mark(0, s), "event record");
+  if (overlap) {
+    FCA_TRY(hipEventRecord(P->fork, s), "fork record");
+    FCA_TRY(hipStreamWaitEvent(sg, P->fork, 0), "fork wait");
+  }
+  FCA_TRY(mark(1, sg), "event record");
   gp.items = reinterpret_cast<const WorkItem*>(P->ws + L.items_g);
-  e = launch_gqa_partial(0, gp, (int)P->items_g.size(), s);
-  if (e != hipSuccess) return hip_fail(e, "grouped pass launch");
-  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "event record");
+  FCA_TRY(launch_gqa_partial(0, gp, (int)P->items_g.size(), sg), "grouped pass launch");
+  FCA_TRY(mark(2, sg), "event record");
+  FCA_TRY(mark(3, s), "event record");
   gp.items = reinterpret_cast<const WorkItem*>(P->ws + L.items_s);
-  e = launch_gqa_partial(1, gp, (int)P->items_s.size(), s);
-  if (e != hipSuccess) return hip_fail(e, "suffix pass launch");
-  if ((e = mark(2)) != hipSuccess) return hip_fail(e, "event record");
+  FCA_TRY(launch_gqa_partial(1, gp, (int)P->items_s.size(), s), "suffix pass launch");
+  FCA_TRY(mark(4, s), "event record");
+  if (overlap) {
+    FCA_TRY(hipEventRecord(P->join, sg), "join record");
+    FCA_TRY(hipStreamWaitEvent(s, P->join, 0), "join wait");
+  }
+  FCA_TRY(mark(5, s), "event record");
 
   MergeParams mp;
   mp.req = reinterpret_cast<const ReqMeta*>(P->ws + L.req);
@@ -620,9 +673,9 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   mp.part = part;
   mp.out = out_dev;
   mp.lse = lse_dev;
-  e = launch_merge(mp, s);
-  if (e != hipSuccess) return hip_fail(e, "merge launch");
-  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "event record");
+  FCA_TRY(launch_merge(mp, s), "merge launch");
+  FCA_TRY(mark(6, s), "event record");
+#undef FCA_TRY
   return FCA_OK;
 }
 
@@ -636,14 +689,15 @@ fca_status fca_profile_read(fca_plan plan, fca_profile* out) {
   if (!plan || !out) return fail(FCA_ERR_INVALID_ARG, "plan / out is NULL");
   fca_profile acc{};
   hipError_t err = hipSuccess;
-  for (size_t c = 0; c + 4 <= plan->pending.size(); c += 4) {
+  // events per call: start, grouped begin/end, suffix begin/end, merge begin/end
+  for (size_t c = 0; c + 7 <= plan->pending.size(); c += 7) {
     hipEvent_t* ev = plan->pending.data() + c;
     float t[4] = {0, 0, 0, 0};
-    if (err == hipSuccess) err = hipEventSynchronize(ev[3]);
-    if (err == hipSuccess) err = hipEventElapsedTime(&t[0], ev[0], ev[1]);
-    if (err == hipSuccess) err = hipEventElapsedTime(&t[1], ev[1], ev[2]);
-    if (err == hipSuccess) err = hipEventElapsedTime(&t[2], ev[2], ev[3]);
-    if (err == hipSuccess) err = hipEventElapsedTime(&t[3], ev[0], ev[3]);
+    if (err == hipSuccess) err = hipEventSynchronize(ev[6]);
+    if (err == hipSuccess) err = hipEventElapsedTime(&t[0], ev[1], ev[2]);
+    if (err == hipSuccess) err = hipEventElapsedTime(&t[1], ev[3], ev[4]);
+    if (err == hipSuccess) err = hipEventElapsedTime(&t[2], ev[5], ev[6]);
+    if (err == hipSuccess) err = hipEventElapsedTime(&t[3], ev[0], ev[6]);
     acc.grouped_ms += t[0];
     acc.suffix_ms += t[1];
     acc.merge_ms += t[2];

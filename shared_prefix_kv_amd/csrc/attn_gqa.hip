@@ -48,22 +48,40 @@ constexpr int kLdsPad = 4;  // floats of padding per LDS row
 __device__ __forceinline__ float wave_xor_max(float x, int mask) { return fmaxf(x, __shfl_xor(x, mask)); }
 __device__ __forceinline__ float wave_xor_sum(float x, int mask) { return x + __shfl_xor(x, mask); }
 
+// K/V registers of one 32-token step of one wave.
+struct StepRegs {
+  bf16x8 ka[2][4];
+  bf16x4 va[2][8];
+};
+
 template <int NCT>
 __device__ __forceinline__ void run_item(const GqaParams& P, const WorkItem& it, float* lds_o, float* lds_m,
                                          float* lds_l) {
   constexpr int NC = 16 * NCT;  // columns per wave pass
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int c16 = lane & 15;
 
   const int ntok = it.tok_end - it.tok_begin;
   const int ntiles = (ntok + kTileTokens - 1) / kTileTokens;
-  const int32_t* btrow = P.bt + (int64_t)it.request * P.W;
+  // steps of this wave: tiles wave, wave + 4, ...
+  const int nsteps = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  const int32_t* btrow = P.bt + (int64_t)it.request * P.W + it.tok_begin / kBS;
+  const int nblk_item = (ntok + kBS - 1) / kBS;
   const __bf16* kbase = static_cast<const __bf16*>(P.k) + (int64_t)it.kv_head * P.k_stride_head;
   const __bf16* vbase = static_cast<const __bf16*>(P.v) + (int64_t)it.kv_head * P.v_stride_head;
   const __bf16* qbase = static_cast<const __bf16*>(P.q);
   const float NEG_INF = -INFINITY;
+
+  // Block IDs of 32 consecutive steps of this wave, two per step: lane l
+  // holds the ID of block 2*(wave + 4*(k0 + l/2)) + l%2 of the item.  Slots
+  // past the item read as block 0, which always exists; every token they
+  // stand for is masked.
+  auto load_ids = [&](int k0) -> int {
+    const int b = 2 * (wave + kWaves * (k0 + (lane >> 1))) + (lane & 1);
+    return b < nblk_item ? btrow[b] : 0;
+  };
 
   for (int mc0 = it.col0; mc0 < it.col1; mc0 += NC) {
     // Q^T operand: column 16*c + c16 of this pass, d-chunk ks*32 + 8*g.
@@ -93,32 +111,33 @@ __device__ __forceinline__ void run_item(const GqaParams& P, const WorkItem& it,
       for (int dt = 0; dt < 8; ++dt) o[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (int tile = wave; tile < ntiles; tile += kWaves) {
-      const int t0 = it.tok_begin + tile * kTileTokens;
-      const int blk = t0 / kBS;
-      const bool has1 = t0 + kBS < it.tok_end;
-      const int id0 = btrow[blk];
-      const int id1 = has1 ? btrow[blk + 1] : id0;
+    // Issue the loads of wave-local step k into R (both blocks always: a
+    // step whose second block lies past the range reads block 0 and masks
+    // all of its tokens).
+    auto load_step = [&](int k, StepRegs& R, int idv) {
+      const int id0 = __builtin_amdgcn_readlane(idv, 2 * (k & 31));
+      const int id1 = __builtin_amdgcn_readlane(idv, 2 * (k & 31) + 1);
       const __bf16* k0 = kbase + (int64_t)id0 * P.k_stride_block;
       const __bf16* k1 = kbase + (int64_t)id1 * P.k_stride_block;
       const __bf16* v0 = vbase + (int64_t)id0 * P.v_stride_block;
       const __bf16* v1 = vbase + (int64_t)id1 * P.v_stride_block;
-
-      bf16x8 ka[2][4];
-      bf16x4 va[2][8];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int off = ((4 * ks + g) * kBS + c16) * 8;
-        ka[0][ks] = *reinterpret_cast<const bf16x8*>(k0 + off);
-        ka[1][ks] = has1 ? *reinterpret_cast<const bf16x8*>(k1 + off) : bf16x8{};
+        R.ka[0][ks] = *reinterpret_cast<const bf16x8*>(k0 + off);
+        R.ka[1][ks] = *reinterpret_cast<const bf16x8*>(k1 + off);
       }
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const int off = (16 * dt + c16) * kBS + 4 * g;
-        va[0][dt] = *reinterpret_cast<const bf16x4*>(v0 + off);
-        va[1][dt] = has1 ? *reinterpret_cast<const bf16x4*>(v1 + off) : bf16x4{};
+        R.va[0][dt] = *reinterpret_cast<const bf16x4*>(v0 + off);
+        R.va[1][dt] = *reinterpret_cast<const bf16x4*>(v1 + off);
       }
+    };
 
+    // Scores, online softmax and PV of wave-local step k held in R.
+    auto compute_step = [&](int k, StepRegs& R) {
+      const int t0 = it.tok_begin + (wave + kWaves * k) * kTileTokens;
       // S^T = K Q^T for the two blocks of the step.
       f32x4 s[2][NCT];
 #pragma unroll
@@ -127,7 +146,8 @@ __device__ __forceinline__ void run_item(const GqaParams& P, const WorkItem& it,
         for (int c = 0; c < NCT; ++c) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[mt][ks], qb[c][ks], acc, 0, 0, 0);
+          for (int ks = 0; ks < 4; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(R.ka[mt][ks], qb[c][ks], acc, 0, 0, 0);
           s[mt][c] = acc;
         }
 
@@ -145,7 +165,7 @@ __device__ __forceinline__ void run_item(const GqaParams& P, const WorkItem& it,
           for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              if (!valid[mt][j]) va[mt][dt][j] = (__bf16)0.f;
+              if (!valid[mt][j]) R.va[mt][dt][j] = (__bf16)0.f;
       }
 
       // Online softmax per column, P^T operand in bf16.
@@ -173,9 +193,9 @@ __device__ __forceinline__ void run_item(const GqaParams& P, const WorkItem& it,
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const __bf16 pbf = (__bf16)exp2f(sv[mt][j] - muse);
-            pb[c][4 * mt + j] = pbf;
-            ps += (float)pbf;
+            const float p = exp2f(sv[mt][j] - muse);
+            pb[c][4 * mt + j] = (__bf16)p;
+            ps += p;
           }
         lsum[c] = lsum[c] * alpha + ps;
 #pragma unroll
@@ -185,11 +205,34 @@ __device__ __forceinline__ void run_item(const GqaParams& P, const WorkItem& it,
       // O^T += V^T P^T.
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const bf16x8 a = {va[0][dt][0], va[0][dt][1], va[0][dt][2], va[0][dt][3],
-                          va[1][dt][0], va[1][dt][1], va[1][dt][2], va[1][dt][3]};
+        const bf16x8 a = {R.va[0][dt][0], R.va[0][dt][1], R.va[0][dt][2], R.va[0][dt][3],
+                          R.va[1][dt][0], R.va[1][dt][1], R.va[1][dt][2], R.va[1][dt][3]};
 #pragma unroll
         for (int c = 0; c < NCT; ++c) o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[c], o[dt][c], 0, 0, 0);
       }
+    };
+
+    // Two register sets in ping-pong: the loads of step k+1 are in flight
+    // while step k is computed.  The prefetch is issued unconditionally (the
+    // last step re-reads its own addresses, which hit the caches) so that
+    // every wait before a step's math is the same static count.  Block IDs
+    // are refreshed once per 32 steps, outside the inner loop.
+    StepRegs A, B;
+    for (int kc = 0; kc < nsteps; kc += 32) {
+      const int kend = min(nsteps, kc + 32);
+      const int idv = load_ids(kc);
+      int k = kc;
+      load_step(k, A, idv);
+      while (k + 1 < kend) {
+        load_step(k + 1, B, idv);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+        compute_step(k, A);
+        load_step(min(k + 2, kend - 1), A, idv);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_step(k + 1, B);
+        k += 2;
+      }
+      if (k < kend) compute_step(k, A);
     }
 
     // Fold the four waves' triples through LDS.
@@ -251,7 +294,7 @@ __device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
 __global__ __launch_bounds__(256) void fca_grouped_prefix_kernel(GqaParams P) { partial_kernel_body<2>(P); }
 
 // Per-request suffix pass: the Hq/Hkv rows of one request.
-__global__ __launch_bounds__(256) void fca_suffix_decode_kernel(GqaParams P) { partial_kernel_body<1>(P); }
+__global__ __launch_bounds__(256, 2) void fca_suffix_decode_kernel(GqaParams P) { partial_kernel_body<1>(P); }
 
 hipError_t launch_gqa_partial(int kind, const GqaParams& p, int n_items, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;

@@ -11,12 +11,11 @@
 //
 // which is the weighting of the partial results in "Core Mechanism", step 3
 // of the ZoRRo Inference & Forest Cascade Attention page, folding the
-// split-K pieces and the depth levels in one pass.  The running maximum is
-// updated as rows arrive (accumulators rescaled on a new maximum); the order
-// of rows is fixed, so results are bit-reproducible.  A request with no
-// tokens gets zeros and -inf.
-//
-// One half-wave (32 lanes x 4 floats) per (request, head) and 128 value dims.
+// split-K pieces and the depth levels in one pass.  Rows are taken 64 at a
+// time (one per lane); the running maximum is updated per batch of rows and
+// the accumulators rescaled when it grows.  The order of rows is fixed, so
+// results are bit-reproducible.  A request with no tokens gets zeros and
+// -inf.
 
 #include <cmath>
 
@@ -25,53 +24,104 @@
 namespace fca {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// One wave per (request, head); lane j resolves the j-th partial row of the
+// request's path so that all (m, l) loads are issued at once, then the value
+// rows are accumulated with the broadcast weights.  Each lane owns DV/64
+// value dims.
 template <int DV>
 __device__ __forceinline__ void merge_body(const MergeParams& P) {
-  constexpr int LANES = DV / 4;  // lanes per (request, head)
-  constexpr int PER_WG = 256 / LANES;
-  const int64_t pair = (int64_t)blockIdx.x * PER_WG + threadIdx.x / LANES;
+  constexpr int VPL = DV / 64;  // floats per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= (int64_t)P.B * P.Hq) return;
-  const int sub = threadIdx.x % LANES;
   const int i = (int)(pair / P.Hq);
   const int h = (int)(pair % P.Hq);
   const int kvh = h / P.r;
   const int rr = h % P.r;
+  const ReqMeta rq = P.req[i];
+
+  int n_src = rq.sfx_splits;
+  for (int g = rq.deepest; g >= 0; g = P.grp[g].parent) n_src += P.grp[g].splits;
 
   float M = -INFINITY, L = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto add = [&](int64_t row) {
-    const float l = P.part.l[row];
-    if (!(l > 0.f)) return;
-    const float m = P.part.m[row];
-    if (m > M) {
-      const float sc = exp2f(M - m);
-      acc *= sc;
-      L *= sc;
-      M = m;
+  float acc[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) acc[v] = 0.f;
+
+  for (int base = 0; base < n_src; base += 64) {
+    // Row of source j: splits of the deepest group first, then its
+    // ancestors, then the suffix splits.
+    const int j = base + lane;
+    int64_t row = -1;
+    if (j < n_src) {
+      int rem = j;
+      for (int g = rq.deepest; g >= 0;) {
+        const GroupMeta gm = P.grp[g];
+        if (rem < gm.splits) {
+          row = (int64_t)gm.unit + ((int64_t)rem * P.Hkv + kvh) * gm.ncols + (int64_t)(rq.pos - gm.r0) * P.r + rr;
+          break;
+        }
+        rem -= gm.splits;
+        g = gm.parent;
+      }
+      if (row < 0) row = (int64_t)rq.sfx_unit + (int64_t)rem * P.Hq + h;
     }
-    const float w = exp2f(m - M);
-    L += w * l;
-    acc += w * *reinterpret_cast<const f32x4*>(P.part.o + row * DV + 4 * sub);
-  };
-
-  const ReqMeta rq = P.req[i];
-  for (int g = rq.deepest; g >= 0;) {
-    const GroupMeta gm = P.grp[g];
-    const int k = rq.pos - gm.r0;
-    for (int s = 0; s < gm.splits; ++s)
-      add((int64_t)gm.unit + ((int64_t)s * P.Hkv + kvh) * gm.ncols + (int64_t)k * P.r + rr);
-    g = gm.parent;
+    float m = -INFINITY, l = 0.f;
+    if (row >= 0) {
+      l = P.part.l[row];
+      m = P.part.m[row];
+      if (!(l > 0.f)) {
+        l = 0.f;
+        m = -INFINITY;
+      }
+    }
+    const float Mn = fmaxf(M, wave_max(m));
+    const float muse = Mn == -INFINITY ? 0.f : Mn;
+    const float sc = exp2f(M - muse);
+    L *= sc;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) acc[v] *= sc;
+    const float w = l > 0.f ? exp2f(m - muse) : 0.f;
+    L += wave_sum(w * l);
+    M = Mn;
+    const int cnt = min(64, n_src - base);
+    const int row_lo = (int)(row & 0xffffffff), row_hi = (int)(row >> 32);
+    for (int s = 0; s < cnt; ++s) {
+      const float ws = __shfl(w, s);
+      const int64_t rs = ((int64_t)__shfl(row_hi, s) << 32) | (uint32_t)__shfl(row_lo, s);
+      if (ws > 0.f) {
+        const float* src = P.part.o + rs * DV + lane * VPL;
+#pragma unroll
+        for (int v = 0; v < VPL; v += 2) {
+          const float2 x = *reinterpret_cast<const float2*>(src + v);
+          acc[v] += ws * x.x;
+          acc[v + 1] += ws * x.y;
+        }
+      }
+    }
   }
-  for (int s = 0; s < rq.sfx_splits; ++s) add((int64_t)rq.sfx_unit + (int64_t)s * P.Hq + h);
 
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  if (L > 0.f) o = acc * (1.f / L);
-  bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-  *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(P.out) + pair * DV + 4 * sub) = ob;
-  if (P.lse && sub == 0) P.lse[pair] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  __bf16* dst = static_cast<__bf16*>(P.out) + pair * DV + lane * VPL;
+#pragma unroll
+  for (int v = 0; v < VPL; v += 2) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ob = {(__bf16)(acc[v] * inv), (__bf16)(acc[v + 1] * inv)};
+    *reinterpret_cast<bf16x2*>(dst + v) = ob;
+  }
+  if (P.lse && lane == 0) P.lse[pair] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 }  // namespace
@@ -82,10 +132,11 @@ __global__ __launch_bounds__(256) void fca_merge_kernel_d512(MergeParams P) { me
 hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
   const int64_t pairs = (int64_t)p.B * p.Hq;
   if (pairs == 0) return hipSuccess;
+  const dim3 grid((unsigned)((pairs + 3) / 4));
   if (p.Dv == 128) {
-    hipLaunchKernelGGL(fca_merge_kernel_d128, dim3((unsigned)((pairs + 7) / 8)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(fca_merge_kernel_d128, grid, dim3(256), 0, s, p);
   } else if (p.Dv == 512) {
-    hipLaunchKernelGGL(fca_merge_kernel_d512, dim3((unsigned)((pairs + 1) / 2)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(fca_merge_kernel_d512, grid, dim3(256), 0, s, p);
   } else {
     return hipErrorInvalidValue;
   }
