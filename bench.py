@@ -61,8 +61,8 @@ def pass_bytes(batch, plan, sched):
     prefix_tokens = sum((g["block_end"] - g["block_begin"]) * bs for g in ex["groups"])
     suffix_tokens = sum(r[1] for r in ex["requests"])
     row_bytes = sh.head_dim_v * 4 + 8
-    rows_g = sum(it["col1"] - it["col0"] for it in sched["grouped"])
-    rows_s = sum(it["col1"] - it["col0"] for it in sched["suffix"])
+    rows_g = sum((it["col1"] - it["col0"]) * it["kv_heads"] for it in sched["grouped"])
+    rows_s = sum((it["col1"] - it["col0"]) * it["kv_heads"] for it in sched["suffix"])
     q_row = sh.head_dim_qk * 2
     q_g = sum(len(g["members"]) for g in ex["groups"]) * sh.num_q_heads * q_row
     q_s = sum(1 for r in ex["requests"] if r[1] > 0) * sh.num_q_heads * q_row

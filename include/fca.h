@@ -206,8 +206,10 @@ typedef struct fca_work_item {
   int32_t ncols;      /* query rows of the unit: members * (Hq/Hkv) */
   int32_t col0;       /* query rows [col0, col1) of the unit */
   int32_t col1;
-  int32_t part_base;  /* partial row of query row 0 of this (unit, kv head) */
-  int32_t reserved[3];
+  int32_t part_base;  /* partial row of (KV head 0, query row 0) of the unit's
+                         token split; head h, row n is part_base + h*ncols + n */
+  int32_t kv_heads;   /* the item covers KV heads kv_head .. kv_head+kv_heads-1 */
+  int32_t reserved[2];
 } fca_work_item;
 
 /*

@@ -107,7 +107,8 @@ class WorkItem(ctypes.Structure):
         ("col0", ctypes.c_int32),
         ("col1", ctypes.c_int32),
         ("part_base", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("kv_heads", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 

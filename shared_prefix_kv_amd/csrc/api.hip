@@ -18,6 +18,7 @@
 #include <cstdlib>
 #include <mutex>
 #include <new>
+#include <queue>
 #include <string>
 #include <vector>
 
@@ -53,25 +54,23 @@ int env_int(const char* name, int dflt) {
   return v > 0 ? v : dflt;
 }
 
-// Split-schedule targets (developer tuning knobs; read the same way for the
-// workspace bound and for planning).
+// Split-schedule targets (developer tuning knobs).
 struct Tuning {
-  int grouped_items;     // aim for about this many grouped work items
-  int grouped_min_work;  // min work per grouped item, in (32-column tile x token)
-  int suffix_items;
-  int suffix_min_tokens;
+  int items_per_bin;  // aim for about this many work items per persistent workgroup
+  int min_stages;     // shortest token split, in stages (4 (head, block) tiles each)
+  int wg_per_cu;      // persistent workgroups per compute unit
 };
 
 Tuning tuning() {
   Tuning t;
-  t.grouped_items = env_int("FCA_TUNE_GROUPED_ITEMS", 1024);
-  t.grouped_min_work = env_int("FCA_TUNE_GROUPED_MIN_WORK", 1024);
-  t.suffix_items = env_int("FCA_TUNE_SUFFIX_ITEMS", 2048);
-  t.suffix_min_tokens = env_int("FCA_TUNE_SUFFIX_MIN_TOKENS", 512);
+  t.items_per_bin = env_int("FCA_TUNE_ITEMS_PER_BIN", 3);
+  t.min_stages = env_int("FCA_TUNE_MIN_STAGES", 4);
+  t.wg_per_cu = env_int("FCA_TUNE_WG_PER_CU", 2);
   return t;
 }
 
-constexpr int kGroupedCols = 32;  // query rows per grouped wave pass
+constexpr int kItemCols = 64;  // query rows one attention work item covers at most
+constexpr int kItemWaves = 4;  // waves per attention workgroup: heads x 16-row column tiles
 
 enum Kind { kGqa = 0, kMla = 1 };
 
@@ -101,45 +100,36 @@ fca_status check_desc(const fca_attn_desc* d, Kind* kind) {
               d->head_dim_qk, d->head_dim_v, d->block_size, d->v_aliases_k);
 }
 
+// Caller-owned plan workspace: discovery read-back region, table copy and
+// discovery state.  Its size depends only on (batch, max_blocks).
 struct Layout {
   size_t header, lens, deepest, sfx_begin, records, readback_bytes;
   size_t bt, state;
-  size_t items_g, items_s, perm, req, grp;
-  int64_t cap_g, cap_s;
   size_t total;
 };
 
-Layout make_layout(int B, int W, const fca_attn_desc* d, const Tuning& t) {
+Layout make_layout(int B, int W) {
   Layout L{};
   const size_t b = (size_t)B;
-  size_t off = 0;
-  L.header = off;
+  L.header = 0;
   L.lens = L.header + kHdrWords * 4;
   L.deepest = L.lens + b * 4;
   L.sfx_begin = L.deepest + b * 4;
   L.records = L.sfx_begin + b * 4;
   L.readback_bytes = L.records + b * kRecordInts * 4 - L.header;
-  off = align_up(L.header + L.readback_bytes);
+  size_t off = align_up(L.header + L.readback_bytes);
   L.bt = off;
   off = align_up(off + b * (size_t)W * 4);
   L.state = off;
   off = align_up(off + 11 * b * 4);
-  const int64_t hkv = d->num_kv_heads;
-  L.cap_g = 2LL * t.grouped_items + hkv * B + 16;
-  L.cap_s = (int64_t)t.suffix_items + hkv * B + 16;
-  L.items_g = off;
-  off = align_up(off + (size_t)L.cap_g * sizeof(WorkItem));
-  L.items_s = off;
-  off = align_up(off + (size_t)L.cap_s * sizeof(WorkItem));
-  L.perm = off;
-  off = align_up(off + b * 4);
-  L.req = off;
-  off = align_up(off + b * sizeof(ReqMeta));
-  L.grp = off;
-  off = align_up(off + std::max<size_t>(b, 1) * sizeof(GroupMeta));
   L.total = off;
   return L;
 }
+
+// Plan-owned device buffer holding the schedule.
+struct SchedLayout {
+  size_t items_g, items_s, bins_g, bins_s, perm, req, grp, total;
+};
 
 DiscoveryPtrs discovery_ptrs(char* ws, const Layout& L, int B) {
   DiscoveryPtrs p;
@@ -191,11 +181,15 @@ struct fca_plan_s {
   std::vector<fca_group_record> groups;
   std::vector<int32_t> members;   // ascending per group
   std::vector<int32_t> req3;      // per request: suffix_block_begin, suffix_tokens, deepest
-  std::vector<WorkItem> items_g, items_s;
+  std::vector<WorkItem> items_g, items_s;  // in bin order
+  std::vector<int32_t> bins_g, bins_s;     // bin offsets (n_bins + 1)
   std::vector<int32_t> perm;
   std::vector<ReqMeta> req;
   std::vector<GroupMeta> grp;
   fca_plan_info info;
+  // plan-owned device copy of the schedule
+  char* sched = nullptr;
+  SchedLayout SL{};
   // concurrent passes
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
@@ -204,6 +198,7 @@ struct fca_plan_s {
   std::vector<hipEvent_t> event_pool;
   std::vector<hipEvent_t> pending;  // kProfEvents per profiled call
   ~fca_plan_s() {
+    if (sched) (void)hipFree(sched);
     if (fork) (void)hipEventDestroy(fork);
     if (join) (void)hipEventDestroy(join);
     for (hipEvent_t e : pending) (void)hipEventDestroy(e);
@@ -226,18 +221,17 @@ fca_status fca_plan_workspace_size(int32_t batch, int32_t max_blocks, const fca_
     if (batch < 0 || batch > kMaxBatch) return fail(FCA_ERR_INVALID_ARG, "batch %d outside [0, %d]", batch, kMaxBatch);
     if (max_blocks < 1 || max_blocks > kMaxTableWidth)
       return fail(FCA_ERR_INVALID_ARG, "max_blocks %d outside [1, %d]", max_blocks, kMaxTableWidth);
-    *bytes = make_layout(batch, max_blocks, desc, tuning()).total;
+    *bytes = make_layout(batch, max_blocks).total;
     return FCA_OK;
   } catch (...) {
     return fail(FCA_ERR_HOST_ALLOC, "host allocation failed");
   }
 }
 
-static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb) {
+static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int n_cu_) {
   const int B = P->B;
   const int bs = P->desc.block_size;
   const int hkv = P->desc.num_kv_heads;
-  const int hq = P->desc.num_q_heads;
   const int r = P->r;
   const Layout& L = P->L;
   const int32_t* hdr = rb.data();
@@ -342,115 +336,152 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb) {
     if (sfx_tokens[i] < 0) return fail(FCA_ERR_HIP, "inconsistent discovery output (suffix of request %d)", i);
   }
 
-  // Split schedule, grouped pass.
+  // ---- Work items ----
+  // An item covers a token split of one unit (a group's prefix range or a
+  // request's suffix), H KV heads and up to 64 query rows, with H x (16-row
+  // column tiles) <= 4 waves.  Splits are chosen per unit, in whole stages
+  // (4 (head, block) tiles), so that each pass has about items_per_bin items
+  // per persistent workgroup.
   const Tuning t = tuning();
-  P->items_g.clear();
-  P->items_s.clear();
-  int64_t row = 0;
-  {
-    int64_t work = 0;
-    for (int c = 0; c < G; ++c) {
-      const int64_t T = (int64_t)(P->groups[c].block_end - P->groups[c].block_begin) * bs;
-      const int64_t ncols = (int64_t)count[c] * r;
-      work += (int64_t)hkv * ceil_div(ncols, kGroupedCols) * T;
-      unique += T;
-    }
-    const int64_t wt = std::max<int64_t>(ceil_div(work, t.grouped_items), t.grouped_min_work);
-    for (int c = 0; c < G; ++c) {
-      const fca_group_record& gr = P->groups[c];
-      const int64_t T = (int64_t)(gr.block_end - gr.block_begin) * bs;
-      const int ncols = count[c] * r;
-      const int64_t mtiles = ceil_div(ncols, kGroupedCols);
-      int64_t splits = 1, mchunk = mtiles;
-      if (mtiles * T > wt) {
-        if (T <= wt) {
-          mchunk = std::max<int64_t>(1, wt / T);
-        } else {
-          mchunk = 1;
-          splits = ceil_div(T, wt);
-        }
-      }
-      const int64_t chunk = round_up(ceil_div(T, splits), kTileTokens);
-      splits = ceil_div(T, chunk);
-      GroupMeta& gm = P->grp[c];
-      gm.parent = gr.parent;
-      gm.r0 = r0[c];
-      gm.ncols = ncols;
-      gm.unit = (int32_t)row;
-      gm.splits = (int32_t)splits;
-      for (int64_t s = 0; s < splits; ++s) {
-        const int tb = (int)(gr.block_begin * (int64_t)bs + s * chunk);
-        const int te = (int)std::min<int64_t>(tb + chunk, (int64_t)gr.block_end * bs);
-        for (int h = 0; h < hkv; ++h)
-          for (int64_t m0 = 0; m0 < mtiles; m0 += mchunk) {
-            WorkItem it{};
-            it.request = P->perm[r0[c]];
-            it.tok_begin = tb;
-            it.tok_end = te;
-            it.kv_head = h;
-            it.member_off = r0[c];
-            it.ncols = ncols;
-            it.col0 = (int)(m0 * kGroupedCols);
-            it.col1 = (int)std::min<int64_t>((m0 + mchunk) * kGroupedCols, ncols);
-            it.part_base = (int32_t)(row + (s * hkv + h) * (int64_t)ncols);
-            P->items_g.push_back(it);
-          }
-      }
-      row += splits * hkv * (int64_t)ncols;
-      if (row > INT32_MAX) return fail(FCA_ERR_UNSUPPORTED, "too many partial rows");
-    }
-  }
-  // Split schedule, per-request pass.
-  P->req.assign(B, ReqMeta{});
-  {
-    int64_t work = 0;
-    for (int i = 0; i < B; ++i) work += (int64_t)hkv * sfx_tokens[i];
-    const int64_t wt = round_up(std::max<int64_t>(ceil_div(work, t.suffix_items), t.suffix_min_tokens), kTileTokens);
-    for (int i = 0; i < B; ++i) {
-      ReqMeta& rq = P->req[i];
-      rq.pos = pos[i];
-      rq.deepest = deepest_c[i];
-      rq.sfx_unit = (int32_t)row;
-      rq.sfx_splits = 0;
-      const int64_t T = sfx_tokens[i];
-      if (T == 0) continue;
-      int64_t splits = ceil_div(T, wt);
-      const int64_t chunk = round_up(ceil_div(T, splits), kTileTokens);
-      splits = ceil_div(T, chunk);
-      rq.sfx_splits = (int32_t)splits;
-      const int base = P->req3[3 * i] * bs;
-      for (int64_t s = 0; s < splits; ++s) {
-        const int tb = (int)(base + s * chunk);
-        const int te = (int)std::min<int64_t>(tb + chunk, lens[i]);
-        for (int h = 0; h < hkv; ++h) {
-          WorkItem it{};
-          it.request = i;
-          it.tok_begin = tb;
-          it.tok_end = te;
-          it.kv_head = h;
-          it.member_off = -1;
-          it.ncols = r;
-          it.col0 = 0;
-          it.col1 = r;
-          it.part_base = (int32_t)(row + s * hq + (int64_t)h * r);
-          P->items_s.push_back(it);
-        }
-      }
-      row += splits * hq;
-      if (row > INT32_MAX) return fail(FCA_ERR_UNSUPPORTED, "too many partial rows");
-    }
-  }
-  // Longest items first; ties keep their order.
-  auto work_of = [](const WorkItem& a) {
-    return (int64_t)(a.tok_end - a.tok_begin) * ((a.col1 - a.col0 + kGroupedCols - 1) / kGroupedCols);
+  auto heads_for = [&](int nct) {  // KV heads per item for nct column tiles
+    for (int H = kItemWaves / nct; H > 1; H /= 2)
+      if (hkv % H == 0) return H;
+    return 1;
   };
-  std::stable_sort(P->items_g.begin(), P->items_g.end(),
-                   [&](const WorkItem& a, const WorkItem& b) { return work_of(a) > work_of(b); });
-  std::stable_sort(P->items_s.begin(), P->items_s.end(), [](const WorkItem& a, const WorkItem& b) {
-    return a.tok_end - a.tok_begin > b.tok_end - b.tok_begin;
-  });
-  if ((int64_t)P->items_g.size() > L.cap_g || (int64_t)P->items_s.size() > L.cap_s)
-    return fail(FCA_ERR_WORKSPACE, "schedule exceeds the workspace bound (tuning changed between calls?)");
+  struct Unit {
+    int64_t T;        // tokens of the range
+    int tok0;         // first token
+    int request;      // block-table row
+    int member_off;   // -1 for a suffix
+    int ncols;
+    int H;            // KV heads per item
+    int chunks;       // 64-row column chunks
+    int64_t stages;   // stages of one (head group, chunk) stream over the whole range
+    int64_t base;     // partial row of (split 0, head 0, row 0)
+    int64_t split_stride;  // partial rows per split
+    int splits;
+    int64_t chunk_tok;
+  };
+  auto make_unit = [&](int64_t T, int tok0, int request, int member_off, int ncols) {
+    Unit u{};
+    u.T = T;
+    u.tok0 = tok0;
+    u.request = request;
+    u.member_off = member_off;
+    u.ncols = ncols;
+    const int nct = (int)std::min<int64_t>(ceil_div(ncols, 16), kItemWaves);
+    u.H = heads_for(nct);
+    u.chunks = (int)ceil_div(ncols, kItemCols);
+    const int bps = kItemWaves / u.H;
+    u.stages = ceil_div(ceil_div(T, bs), bps);
+    return u;
+  };
+  auto split_units = [&](std::vector<Unit>& units, int64_t& row) {
+    int64_t work = 0;
+    for (const Unit& u : units) work += u.stages * (hkv / u.H) * u.chunks;
+    const int64_t target_items = (int64_t)t.items_per_bin * n_cu_ * t.wg_per_cu;
+    const int64_t st = std::max<int64_t>(t.min_stages, ceil_div(work, std::max<int64_t>(target_items, 1)));
+    for (Unit& u : units) {
+      const int bps = kItemWaves / u.H;
+      int64_t k = std::max<int64_t>(1, ceil_div(u.stages, st));
+      k = std::max<int64_t>(k, ceil_div(u.T, (int64_t)kMaxItemBlocks * bs));
+      u.chunk_tok = ceil_div(u.stages, k) * bps * bs;  // whole stages, a multiple of 32 tokens
+      u.splits = (int)ceil_div(u.T, u.chunk_tok);
+      u.base = row;
+      u.split_stride = (int64_t)hkv * u.ncols;
+      row += u.splits * u.split_stride;
+    }
+  };
+  auto emit_items = [&](const std::vector<Unit>& units, std::vector<WorkItem>& out) {
+    for (const Unit& u : units)
+      for (int s = 0; s < u.splits; ++s)
+        for (int h0 = 0; h0 < hkv; h0 += u.H)
+          for (int c = 0; c < u.chunks; ++c) {
+            WorkItem it{};
+            it.request = u.request;
+            it.tok_begin = (int)(u.tok0 + s * u.chunk_tok);
+            it.tok_end = (int)std::min<int64_t>(it.tok_begin + u.chunk_tok, u.tok0 + u.T);
+            it.kv_head = h0;
+            it.kv_heads = u.H;
+            it.member_off = u.member_off;
+            it.ncols = u.ncols;
+            it.col0 = c * kItemCols;
+            it.col1 = std::min(u.ncols, (c + 1) * kItemCols);
+            it.part_base = (int32_t)(u.base + s * u.split_stride);
+            out.push_back(it);
+          }
+  };
+  // Longest-first packing into n_bins persistent workgroups (least-loaded
+  // bin, ties to the lower index); items are then stored bin by bin.
+  auto pack_bins = [&](std::vector<WorkItem>& items, std::vector<int32_t>& bins) {
+    auto stages_of = [](const WorkItem& w) {
+      const int64_t nblk = (w.tok_end - w.tok_begin + 15) / 16;
+      const int bps = kItemWaves / w.kv_heads;
+      return (nblk + bps - 1) / bps;
+    };
+    std::vector<int> order(items.size());
+    for (size_t k = 0; k < order.size(); ++k) order[k] = (int)k;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return stages_of(items[a]) > stages_of(items[b]); });
+    const int nb = (int)std::min<int64_t>((int64_t)items.size(), (int64_t)n_cu_ * t.wg_per_cu);
+    std::vector<std::vector<int>> per(nb);
+    std::priority_queue<std::pair<int64_t, int>, std::vector<std::pair<int64_t, int>>, std::greater<>> heap;
+    for (int b = 0; b < nb; ++b) heap.push({0, b});
+    for (int k : order) {
+      auto top = heap.top();
+      heap.pop();
+      per[top.second].push_back(k);
+      heap.push({top.first + stages_of(items[k]), top.second});
+    }
+    std::vector<WorkItem> sorted;
+    sorted.reserve(items.size());
+    bins.assign(nb + 1, 0);
+    for (int b = 0; b < nb; ++b) {
+      bins[b] = (int32_t)sorted.size();
+      for (int k : per[b]) sorted.push_back(items[k]);
+    }
+    bins[nb] = (int32_t)sorted.size();
+    items.swap(sorted);
+  };
+
+  int64_t row = 0;
+  std::vector<Unit> gunits, sunits;
+  for (int c = 0; c < G; ++c) {
+    const fca_group_record& gr = P->groups[c];
+    const int64_t T = (int64_t)(gr.block_end - gr.block_begin) * bs;
+    gunits.push_back(make_unit(T, gr.block_begin * bs, P->perm[r0[c]], r0[c], count[c] * r));
+    unique += T;
+  }
+  split_units(gunits, row);
+  P->items_g.clear();
+  emit_items(gunits, P->items_g);
+  for (int c = 0; c < G; ++c) {
+    GroupMeta& gm = P->grp[c];
+    gm.parent = P->groups[c].parent;
+    gm.r0 = r0[c];
+    gm.ncols = count[c] * r;
+    gm.unit = (int32_t)gunits[c].base;
+    gm.splits = gunits[c].splits;
+  }
+  std::vector<int> sunit_of(B, -1);
+  for (int i = 0; i < B; ++i)
+    if (sfx_tokens[i] > 0) {
+      sunit_of[i] = (int)sunits.size();
+      sunits.push_back(make_unit(sfx_tokens[i], P->req3[3 * i] * bs, i, -1, r));
+    }
+  split_units(sunits, row);
+  P->items_s.clear();
+  emit_items(sunits, P->items_s);
+  if (row > INT32_MAX) return fail(FCA_ERR_UNSUPPORTED, "too many partial rows");
+  P->req.assign(B, ReqMeta{});
+  for (int i = 0; i < B; ++i) {
+    ReqMeta& rq = P->req[i];
+    rq.pos = pos[i];
+    rq.deepest = deepest_c[i];
+    rq.sfx_unit = sunit_of[i] >= 0 ? (int32_t)sunits[sunit_of[i]].base : 0;
+    rq.sfx_splits = sunit_of[i] >= 0 ? sunits[sunit_of[i]].splits : 0;
+  }
+  pack_bins(P->items_g, P->bins_g);
+  pack_bins(P->items_s, P->bins_s);
 
   int64_t sources = 0;
   for (int i = 0; i < B; ++i) {
@@ -492,8 +523,7 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
     if (!workspace_dev) return fail(FCA_ERR_INVALID_ARG, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace_dev) % kAlign)
       return fail(FCA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
-    const Tuning t = tuning();
-    const Layout L = make_layout(batch, max_blocks, desc, t);
+    const Layout L = make_layout(batch, max_blocks);
     if (workspace_bytes < L.total)
       return fail(FCA_ERR_WORKSPACE, "plan workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
 
@@ -529,25 +559,56 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
                   (err & kErrBadLen) ? "seq_len outside [0, max_blocks * block_size]"
                                      : "block ID outside [0, num_blocks) in a used slot");
     }
-    st = build_plan(P, rb);
+    int dev = 0, n_cu = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n_cu <= 0) {
+      delete P;
+      return hip_fail(e, "compute-unit count");
+    }
+    st = build_plan(P, rb, n_cu);
     if (st != FCA_OK) {
       delete P;
       return st;
     }
-    // Upload the schedule (pageable copies: the runtime stages them before returning).
+    // Plan-owned device copy of the schedule (pageable copies: the runtime
+    // stages them before returning).
+    SchedLayout& S = P->SL;
+    size_t off = 0;
+    auto place = [&](size_t bytes) {
+      const size_t at = off;
+      off = align_up(off + std::max<size_t>(bytes, 1));
+      return at;
+    };
+    S.items_g = place(P->items_g.size() * sizeof(WorkItem));
+    S.items_s = place(P->items_s.size() * sizeof(WorkItem));
+    S.bins_g = place(P->bins_g.size() * 4);
+    S.bins_s = place(P->bins_s.size() * 4);
+    S.perm = place(P->perm.size() * 4);
+    S.req = place(P->req.size() * sizeof(ReqMeta));
+    S.grp = place(P->grp.size() * sizeof(GroupMeta));
+    S.total = off;
+    e = hipMalloc(&P->sched, S.total);
+    if (e != hipSuccess) {
+      P->sched = nullptr;
+      delete P;
+      return hip_fail(e, "schedule buffer");
+    }
     struct Up {
       const void* src;
       size_t off, bytes;
     } ups[] = {
-        {P->items_g.data(), L.items_g, P->items_g.size() * sizeof(WorkItem)},
-        {P->items_s.data(), L.items_s, P->items_s.size() * sizeof(WorkItem)},
-        {P->perm.data(), L.perm, P->perm.size() * 4},
-        {P->req.data(), L.req, P->req.size() * sizeof(ReqMeta)},
-        {P->grp.data(), L.grp, P->grp.size() * sizeof(GroupMeta)},
+        {P->items_g.data(), S.items_g, P->items_g.size() * sizeof(WorkItem)},
+        {P->items_s.data(), S.items_s, P->items_s.size() * sizeof(WorkItem)},
+        {P->bins_g.data(), S.bins_g, P->bins_g.size() * 4},
+        {P->bins_s.data(), S.bins_s, P->bins_s.size() * 4},
+        {P->perm.data(), S.perm, P->perm.size() * 4},
+        {P->req.data(), S.req, P->req.size() * sizeof(ReqMeta)},
+        {P->grp.data(), S.grp, P->grp.size() * sizeof(GroupMeta)},
     };
     for (const Up& u : ups) {
       if (!u.bytes) continue;
-      e = hipMemcpyAsync(P->ws + u.off, u.src, u.bytes, hipMemcpyHostToDevice, s);
+      e = hipMemcpyAsync(P->sched + u.off, u.src, u.bytes, hipMemcpyHostToDevice, s);
       if (e != hipSuccess) {
         delete P;
         return hip_fail(e, "schedule upload");
@@ -604,8 +665,9 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   part.l = reinterpret_cast<float*>(w + align_up((size_t)rows * dv * 4) + align_up((size_t)rows * 4));
 
   const Layout& L = P->L;
+  const SchedLayout& S = P->SL;
   GqaParams gp;
-  gp.perm = reinterpret_cast<const int32_t*>(P->ws + L.perm);
+  gp.perm = reinterpret_cast<const int32_t*>(P->sched + S.perm);
   gp.bt = reinterpret_cast<const int32_t*>(P->ws + L.bt);
   gp.W = P->W;
   gp.Hq = P->desc.num_q_heads;
@@ -649,12 +711,14 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
     FCA_TRY(hipStreamWaitEvent(sg, P->fork, 0), "fork wait");
   }
   FCA_TRY(mark(1, sg), "event record");
-  gp.items = reinterpret_cast<const WorkItem*>(P->ws + L.items_g);
-  FCA_TRY(launch_gqa_partial(0, gp, (int)P->items_g.size(), sg), "grouped pass launch");
+  gp.items = reinterpret_cast<const WorkItem*>(P->sched + S.items_g);
+  gp.bin_off = reinterpret_cast<const int32_t*>(P->sched + S.bins_g);
+  FCA_TRY(launch_gqa_partial(0, gp, (int)P->bins_g.size() - 1, sg), "grouped pass launch");
   FCA_TRY(mark(2, sg), "event record");
   FCA_TRY(mark(3, s), "event record");
-  gp.items = reinterpret_cast<const WorkItem*>(P->ws + L.items_s);
-  FCA_TRY(launch_gqa_partial(1, gp, (int)P->items_s.size(), s), "suffix pass launch");
+  gp.items = reinterpret_cast<const WorkItem*>(P->sched + S.items_s);
+  gp.bin_off = reinterpret_cast<const int32_t*>(P->sched + S.bins_s);
+  FCA_TRY(launch_gqa_partial(1, gp, (int)P->bins_s.size() - 1, s), "suffix pass launch");
   FCA_TRY(mark(4, s), "event record");
   if (overlap) {
     FCA_TRY(hipEventRecord(P->join, sg), "join record");
@@ -663,8 +727,8 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   FCA_TRY(mark(5, s), "event record");
 
   MergeParams mp;
-  mp.req = reinterpret_cast<const ReqMeta*>(P->ws + L.req);
-  mp.grp = reinterpret_cast<const GroupMeta*>(P->ws + L.grp);
+  mp.req = reinterpret_cast<const ReqMeta*>(P->sched + S.req);
+  mp.grp = reinterpret_cast<const GroupMeta*>(P->sched + S.grp);
   mp.B = P->B;
   mp.Hq = P->desc.num_q_heads;
   mp.Hkv = P->desc.num_kv_heads;

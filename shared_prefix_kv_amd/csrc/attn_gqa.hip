@@ -1,33 +1,48 @@
 // Grouped prefix pass and per-request suffix pass for GQA caches, gfx950.
 //
-// Both passes compute, for a set of query rows and a run of cached tokens,
-// the partial softmax triple (o, max, denominator) that the merge combines
+// Both passes compute, for sets of query rows and runs of cached tokens, the
+// partial softmax triples (o, max, denominator) that the merge combines
 // ("Core Mechanism" of the ZoRRo Inference & Forest Cascade Attention page,
 // step 2: one pass over each group's shared prefix blocks, read once per
 // group, and one pass per request over its own suffix blocks).
 //
-// Work item = (token range, KV head, column range).  Columns are the query
-// rows: grouped items cover members x (Hq/Hkv) rows that all read the same
-// KV tiles, so QK^T and PV are real matrix products and run on bf16 MFMA
-// (v_mfma_f32_16x16x32_bf16).  A per-request item has Hq/Hkv <= 16 rows and
-// uses the same code with one 16-column tile.
+// Work item = (token range, H consecutive KV heads, up to 16 * n_ct query
+// rows) with H * n_ct <= 4.  Query rows ("columns") of a grouped item are
+// members x (Hq/Hkv) rows that all read the same KV tiles, so QK^T and PV are
+// real matrix products and run on bf16 MFMA.  A per-request item has
+// Hq/Hkv <= 16 rows per head and takes up to 4 heads of one request.
 //
-// Data flow of one 32-token step (two 16-token blocks) of one wave:
-//   * keys of the step are the A operand of S^T = K Q^T: lane (g, c) loads
-//     the 16-byte d-chunk 4*ks + g of token c of block mt; in the chunked key
-//     layout those are 1 KiB contiguous per instruction.
-//   * S^T lands with token 4*g + j of block mt in lane group g, register j,
-//     column c: exactly the P^T operand of the PV product once rounded to
-//     bf16 (token order inside a 32-token step is free as long as V uses it).
-//   * values of the step are the A operand of O^T = V^T P^T: lane (g, c)
-//     loads tokens 4g..4g+3 of block mt at value dim 16*dt + c, 8 bytes that
-//     are contiguous in the transposed value layout (512 B per instruction).
-//   * online softmax per column in the log2 domain; the row max is reduced
-//     across the four lane groups that share a column.
-// The four waves of a workgroup take interleaved 32-token steps of the item
-// and fold their triples through LDS before one partial row per column is
-// written.  Tokens at or past the end of the range are masked: their scores
-// become -inf and their (possibly NaN) value entries are zeroed before PV.
+// Persistent workgroups of 4 waves: the planner packs items into one bin per
+// workgroup (longest first, least-loaded bin); a workgroup walks its bin as
+// one stream of stages, so the copy of the next stage -- possibly the first
+// stage of the next item -- is always in flight while the current one is
+// computed.
+//
+// Stage = 4 (head, block) tiles of the current item: tile t is block
+// (4/H)*s + t % (4/H) of head h0 + t / (4/H).  Wave t copies tile t straight
+// from HBM into LDS with global_load_lds_dwordx4 (16 bytes per lane, 1 KiB
+// contiguous per instruction: the K tile then the V tile, 4 KiB each), so
+// every KV byte crosses the vector-memory front end once per workgroup.  Two
+// 32 KiB stage slots alternate; one barrier per stage hands a landed stage to
+// all waves and frees the other slot for the next copy.  Block IDs and item
+// descriptors come in through scalar loads.
+//
+// Wave w < H * n_ct owns head h0 + w / n_ct and column tile w % n_ct and
+// computes the 4/H blocks of its head in each stage; its columns' triples are
+// written straight from registers when the item ends (no cross-wave fold).
+//
+// Math of one 16-token block of one wave, operands read from LDS:
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: lane (g, c) reads d-chunk
+//     4*ks + g of token c (the chunked key layout makes this 1 KiB contiguous);
+//   * S^T lands with token 4*g + j in lane group g, register j, column c --
+//     exactly the B operand (P^T) of v_mfma_f32_16x16x16_bf16 once rounded;
+//   * O^T += V^T P^T: lane (g, c) reads tokens 4g..4g+3 at value dim
+//     16*dt + c, 8 contiguous bytes of the transposed value tile;
+//   * online softmax per column in the log2 domain; the column max is reduced
+//     across the four lane groups with permlane swaps; accumulators are
+//     rescaled only when some column's max grew (a wave-uniform test).
+// Tokens at or past the end of the range are masked: their scores become
+// -inf and their (possibly NaN) values are zeroed before PV.
 
 #include <cmath>
 
@@ -39,269 +54,276 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const int32_t cint32;
 
-constexpr int kD = 128;   // head dim (keys and values)
-constexpr int kBS = 16;   // tokens per cache block
-constexpr int kWaves = 4;
-constexpr int kLdsPad = 4;  // floats of padding per LDS row
+constexpr int kD = 128;                              // head dim (keys and values)
+constexpr int kBS = 16;                              // tokens per cache block
+constexpr int kWaves = 4;                            // waves per workgroup = tiles per stage
+constexpr int kTileBytes = kBS * kD * 2;             // one (block, head) K or V tile: 4 KiB
+constexpr int kSlotBytes = kWaves * 2 * kTileBytes;  // 32 KiB per stage
 
-__device__ __forceinline__ float wave_xor_max(float x, int mask) { return fmaxf(x, __shfl_xor(x, mask)); }
-__device__ __forceinline__ float wave_xor_sum(float x, int mask) { return x + __shfl_xor(x, mask); }
+// x op x' where x' is the value of lane ^ 16 (resp. ^ 32).
+__device__ __forceinline__ float xmax16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xsum16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-// K/V registers of one 32-token step of one wave.
-struct StepRegs {
-  bf16x8 ka[2][4];
-  bf16x4 va[2][8];
-};
+// s_waitcnt until no vector-memory operation of this wave is outstanding
+// (gfx9 encoding: vmcnt 0, expcnt and lgkmcnt at their no-wait maxima).
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
 
-template <int NCT>
-__device__ __forceinline__ void run_item(const GqaParams& P, const WorkItem& it, float* lds_o, float* lds_m,
-                                         float* lds_l) {
-  constexpr int NC = 16 * NCT;  // columns per wave pass
+// Work item i read through the scalar path.
+__device__ __forceinline__ WorkItem load_item(cint32* items, int i) {
+  static_assert(sizeof(WorkItem) == 12 * 4, "work item layout");
+  cint32* p = items + 12 * i;
+  WorkItem w;
+  w.request = p[0];
+  w.tok_begin = p[1];
+  w.tok_end = p[2];
+  w.kv_head = p[3];
+  w.member_off = p[4];
+  w.ncols = p[5];
+  w.col0 = p[6];
+  w.col1 = p[7];
+  w.part_base = p[8];
+  w.kv_heads = p[9];
+  w.pad1 = w.pad2 = 0;
+  return w;
+}
+
+__device__ __forceinline__ int item_blocks(const WorkItem& it) { return (it.tok_end - it.tok_begin + kBS - 1) / kBS; }
+
+__device__ __forceinline__ int item_stages(const WorkItem& it) {
+  const int bps = kWaves / it.kv_heads;
+  return (item_blocks(it) + bps - 1) / bps;
+}
+
+__device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kSlotBytes];
+
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int c16 = lane & 15;
-
-  const int ntok = it.tok_end - it.tok_begin;
-  const int ntiles = (ntok + kTileTokens - 1) / kTileTokens;
-  // steps of this wave: tiles wave, wave + 4, ...
-  const int nsteps = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-  const int32_t* btrow = P.bt + (int64_t)it.request * P.W + it.tok_begin / kBS;
-  const int nblk_item = (ntok + kBS - 1) / kBS;
-  const __bf16* kbase = static_cast<const __bf16*>(P.k) + (int64_t)it.kv_head * P.k_stride_head;
-  const __bf16* vbase = static_cast<const __bf16*>(P.v) + (int64_t)it.kv_head * P.v_stride_head;
-  const __bf16* qbase = static_cast<const __bf16*>(P.q);
   const float NEG_INF = -INFINITY;
+  const float sc = P.scale_log2;
 
-  // Block IDs of 32 consecutive steps of this wave, two per step: lane l
-  // holds the ID of block 2*(wave + 4*(k0 + l/2)) + l%2 of the item.  Slots
-  // past the item read as block 0, which always exists; every token they
-  // stand for is masked.
-  auto load_ids = [&](int k0) -> int {
-    const int b = 2 * (wave + kWaves * (k0 + (lane >> 1))) + (lane & 1);
-    return b < nblk_item ? btrow[b] : 0;
+  cint32* bin_off = (cint32*)(P.bin_off);
+  cint32* items = (cint32*)(P.items);
+  cint32* bt = (cint32*)(P.bt);
+  const int i_begin = bin_off[blockIdx.x];
+  const int i_end = bin_off[blockIdx.x + 1];
+  if (i_begin >= i_end) return;
+
+  const char* kpool = static_cast<const char*>(P.k);
+  const char* vpool = static_cast<const char*>(P.v);
+  const __bf16* qbase = static_cast<const __bf16*>(P.q);
+
+  // ---- copy cursor: item di, stage ds ----
+  int di = i_begin, ds = 0;
+  WorkItem dit = load_item(items, di);
+  int dnst = item_stages(dit);
+
+  // Q^T operand of this wave for an item: column tile w % n_ct of head
+  // h0 + w / n_ct (d-chunk ks*32 + 8*g); zeros for columns past the item and
+  // for idle waves.  Issued while the next stage's copy is in flight, and
+  // only consumed after the next stage barrier.
+  bf16x8 qn[4];
+  cint32* perm = (cint32*)(P.perm);
+  auto load_q = [&](const WorkItem& it) {
+    const int nct = (it.col1 - it.col0 + 15) / 16;
+    const int cb = it.col0 + 16 * (wave % nct);  // first column of this wave's tile
+    const int col = cb + c16;
+    const int h = wave / nct;
+    int member = it.request;
+    if (it.member_off >= 0 && cb < it.col1) {
+      // The tile's columns belong to members (cb / r) .. (last / r); their
+      // request indices come in through scalar loads, one select per member.
+      const int last = min(cb + 15, it.col1 - 1);
+      const int m0 = cb / P.r;
+      const int mine = min(col, last) / P.r - m0;
+      for (int k = 0; k <= last / P.r - m0; ++k) {
+        const int pk = perm[it.member_off + m0 + k];
+        member = mine == k ? pk : member;
+      }
+    }
+    if (h < it.kv_heads && col < it.col1) {
+      const int qh = (it.kv_head + h) * P.r + col % P.r;
+      const __bf16* qp = qbase + ((int64_t)member * P.Hq + qh) * kD + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qn[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qn[ks] = bf16x8{};
+    }
   };
 
-  for (int mc0 = it.col0; mc0 < it.col1; mc0 += NC) {
-    // Q^T operand: column 16*c + c16 of this pass, d-chunk ks*32 + 8*g.
-    bf16x8 qb[NCT][4];
+  // Copy stage (di, ds) into a slot: this wave's tile is block
+  // bps*ds + wave % bps of head h0 + wave / bps.  Blocks past the item copy
+  // block 0, which always exists; they are never used in the math.
+  auto issue = [&](int slot) {
+    const int bps = kWaves / dit.kv_heads;
+    const int b = bps * ds + wave % bps;
+    const int id = b < item_blocks(dit) ? bt[(int64_t)dit.request * P.W + dit.tok_begin / kBS + b] : 0;
+    const int head = dit.kv_head + wave / bps;
+    const char* ksrc = kpool + ((int64_t)id * P.k_stride_block + (int64_t)head * P.k_stride_head) * 2 + lane * 16;
+    const char* vsrc = vpool + ((int64_t)id * P.v_stride_block + (int64_t)head * P.v_stride_head) * 2 + lane * 16;
+    char* dst = lds + slot * kSlotBytes + wave * 2 * kTileBytes;
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      const int col = mc0 + 16 * c + c16;
-      if (col < it.col1) {
-        const int member = it.member_off >= 0 ? P.perm[it.member_off + col / P.r] : it.request;
-        const int qh = it.kv_head * P.r + col % P.r;
-        const __bf16* qp = qbase + ((int64_t)member * P.Hq + qh) * kD + 8 * g;
+    for (int i = 0; i < kTileBytes / 1024; ++i)
+      __builtin_amdgcn_global_load_lds(ksrc + i * 1024, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
+                                       0, 0);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qb[c][ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qb[c][ks] = bf16x8{};
+    for (int i = 0; i < kTileBytes / 1024; ++i)
+      __builtin_amdgcn_global_load_lds(vsrc + i * 1024,
+                                       (__attribute__((address_space(3))) void*)(dst + kTileBytes + i * 1024), 16, 0,
+                                       0);
+    if (++ds == dnst) {  // on to the next item: its descriptor and its Q
+      ds = 0;
+      if (++di < i_end) {
+        dit = load_item(items, di);
+        dnst = item_stages(dit);
+        load_q(dit);
       }
     }
+  };
 
-    f32x4 o[8][NCT];
-    float mrow[NCT], lsum[NCT];
+  // ---- compute cursor: item ci, stage cs ----
+  WorkItem cit = dit;
+  int ci = i_begin, cs = 0, cnst = dnst;
+  int hh = 0, ct = 0, bps = 1;
+  bool active = false;
+  bf16x8 qb[4];
+  f32x4 o[8];
+  float mrow = NEG_INF, lsum = 0.f;
+
+  auto begin_item = [&]() {
+    const int nct = (cit.col1 - cit.col0 + 15) / 16;
+    bps = kWaves / cit.kv_heads;
+    hh = wave / nct;
+    ct = wave % nct;
+    active = hh < cit.kv_heads;
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      mrow[c] = NEG_INF;
-      lsum[c] = 0.f;
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = qn[ks];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mrow = NEG_INF;
+    lsum = 0.f;
+  };
+
+  // One 16-token block from LDS: S^T = K Q^T (16x16x32, K = head dim),
+  // online softmax, O^T += V^T P^T (16x16x16, K = the block's tokens).
+  auto compute_block = [&](const char* kt, int t0) {
+    const char* vt = kt + kTileBytes;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + ((4 * ks + g) * kBS + c16) * 16);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], s, 0, 0, 0);
     }
-
-    // Issue the loads of wave-local step k into R (both blocks always: a
-    // step whose second block lies past the range reads block 0 and masks
-    // all of its tokens).
-    auto load_step = [&](int k, StepRegs& R, int idv) {
-      const int id0 = __builtin_amdgcn_readlane(idv, 2 * (k & 31));
-      const int id1 = __builtin_amdgcn_readlane(idv, 2 * (k & 31) + 1);
-      const __bf16* k0 = kbase + (int64_t)id0 * P.k_stride_block;
-      const __bf16* k1 = kbase + (int64_t)id1 * P.k_stride_block;
-      const __bf16* v0 = vbase + (int64_t)id0 * P.v_stride_block;
-      const __bf16* v1 = vbase + (int64_t)id1 * P.v_stride_block;
+    const bool partial = t0 + kBS > cit.tok_end;  // only the last block of a range
+    if (partial) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int off = ((4 * ks + g) * kBS + c16) * 8;
-        R.ka[0][ks] = *reinterpret_cast<const bf16x8*>(k0 + off);
-        R.ka[1][ks] = *reinterpret_cast<const bf16x8*>(k1 + off);
-      }
+      for (int j = 0; j < 4; ++j)
+        if (t0 + 4 * g + j >= cit.tok_end) s[j] = NEG_INF;
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = xmax32(xmax16(mx));
+    const float mnew = fmaxf(mrow, mx * sc);
+    if (__builtin_amdgcn_ballot_w64(mnew > mrow)) {  // some column's max grew
+      const float alpha = exp2f(mrow - mnew);           // 0 on the first block
+      lsum *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int off = (16 * dt + c16) * kBS + 4 * g;
-        R.va[0][dt] = *reinterpret_cast<const bf16x4*>(v0 + off);
-        R.va[1][dt] = *reinterpret_cast<const bf16x4*>(v1 + off);
-      }
-    };
-
-    // Scores, online softmax and PV of wave-local step k held in R.
-    auto compute_step = [&](int k, StepRegs& R) {
-      const int t0 = it.tok_begin + (wave + kWaves * k) * kTileTokens;
-      // S^T = K Q^T for the two blocks of the step.
-      f32x4 s[2][NCT];
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+      mrow = mnew;
+    }
+    bf16x4 pb;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+    for (int j = 0; j < 4; ++j) {
+      const float p = exp2f(fmaf(s[j], sc, -mrow));
+      pb[j] = (__bf16)p;
+      lsum += p;
+    }
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(R.ka[mt][ks], qb[c][ks], acc, 0, 0, 0);
-          s[mt][c] = acc;
-        }
-
-      // Token validity (only the last step of a range can be partial).
-      const bool partial = t0 + kTileTokens > it.tok_end;
-      bool valid[2][4];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) valid[mt][j] = !partial || (t0 + 16 * mt + 4 * g + j < it.tok_end);
+    for (int dt = 0; dt < 8; ++dt) {
+      bf16x4 a = *reinterpret_cast<const bf16x4*>(vt + ((16 * dt + c16) * kBS + 4 * g) * 2);
       if (partial) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (!valid[mt][j]) R.va[mt][dt][j] = (__bf16)0.f;
+        for (int j = 0; j < 4; ++j)
+          if (t0 + 4 * g + j >= cit.tok_end) a[j] = (__bf16)0.f;  // NaN-safe tail
       }
-
-      // Online softmax per column, P^T operand in bf16.
-      bf16x8 pb[NCT];
-#pragma unroll
-      for (int c = 0; c < NCT; ++c) {
-        float sv[2][4];
-        float mx = NEG_INF;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = valid[mt][j] ? s[mt][c][j] * P.scale_log2 : NEG_INF;
-            sv[mt][j] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = wave_xor_max(mx, 16);
-        mx = wave_xor_max(mx, 32);
-        const float mnew = fmaxf(mrow[c], mx);
-        const float muse = (mnew == NEG_INF) ? 0.f : mnew;
-        const float alpha = exp2f(mrow[c] - muse);
-        mrow[c] = mnew;
-        float ps = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p = exp2f(sv[mt][j] - muse);
-            pb[c][4 * mt + j] = (__bf16)p;
-            ps += p;
-          }
-        lsum[c] = lsum[c] * alpha + ps;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[dt][c] *= alpha;
-      }
-
-      // O^T += V^T P^T.
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const bf16x8 a = {R.va[0][dt][0], R.va[0][dt][1], R.va[0][dt][2], R.va[0][dt][3],
-                          R.va[1][dt][0], R.va[1][dt][1], R.va[1][dt][2], R.va[1][dt][3]};
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[c], o[dt][c], 0, 0, 0);
-      }
-    };
-
-    // Two register sets in ping-pong: the loads of step k+1 are in flight
-    // while step k is computed.  The prefetch is issued unconditionally (the
-    // last step re-reads its own addresses, which hit the caches) so that
-    // every wait before a step's math is the same static count.  Block IDs
-    // are refreshed once per 32 steps, outside the inner loop.
-    StepRegs A, B;
-    for (int kc = 0; kc < nsteps; kc += 32) {
-      const int kend = min(nsteps, kc + 32);
-      const int idv = load_ids(kc);
-      int k = kc;
-      load_step(k, A, idv);
-      while (k + 1 < kend) {
-        load_step(k + 1, B, idv);
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-        compute_step(k, A);
-        load_step(min(k + 2, kend - 1), A, idv);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_step(k + 1, B);
-        k += 2;
-      }
-      if (k < kend) compute_step(k, A);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[dt], 0, 0, 0);
     }
+  };
 
-    // Fold the four waves' triples through LDS.
+  // Triples of this wave's columns, straight from registers.
+  auto finish_item = [&]() {
+    const float l = xsum32(xsum16(lsum));
+    const int col = cit.col0 + 16 * ct + c16;
+    if (!active || col >= cit.col1) return;
+    const int64_t prow = (int64_t)cit.part_base + (int64_t)(cit.kv_head + hh) * cit.ncols + col;
+    float* dst = P.part.o + prow * kD + 4 * g;
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      lsum[c] = wave_xor_sum(lsum[c], 16);
-      lsum[c] = wave_xor_sum(lsum[c], 32);
-      const int col = 16 * c + c16;
-      float* row = lds_o + (wave * NC + col) * (kD + kLdsPad);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(row + 16 * dt + 4 * g) = o[dt][c];
-      if (g == 0) {
-        lds_m[wave * NC + col] = mrow[c];
-        lds_l[wave * NC + col] = lsum[c];
-      }
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt];
+    if (g == 0) {
+      P.part.m[prow] = mrow;
+      P.part.l[prow] = l;
     }
+  };
+
+  load_q(dit);
+  issue(0);
+  for (int it = 0;; ++it) {
+    // Stage `it` has landed for every wave, and every wave is done with
+    // stage it - 1, whose slot the next copy reuses.
+    wait_vm_all();
     __syncthreads();
-    for (int idx = threadIdx.x; idx < NC * (kD / 4); idx += kWaves * 64) {
-      const int col = idx / (kD / 4);
-      const int d4 = idx % (kD / 4);
-      const int n = mc0 + col;
-      if (n >= it.col1) continue;
-      float M = NEG_INF;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_m[w * NC + col]);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      float L = 0.f;
-      if (M != NEG_INF) {
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float sc = exp2f(lds_m[w * NC + col] - M);
-          L += sc * lds_l[w * NC + col];
-          acc += sc * *reinterpret_cast<const f32x4*>(lds_o + (w * NC + col) * (kD + kLdsPad) + 4 * d4);
-        }
-      }
-      const int64_t prow = (int64_t)it.part_base + n;
-      *reinterpret_cast<f32x4*>(P.part.o + prow * kD + 4 * d4) = acc;
-      if (d4 == 0) {
-        P.part.m[prow] = M;
-        P.part.l[prow] = L;
+    if (cs == 0) begin_item();
+    if (di < i_end) issue((it + 1) & 1);
+    if (active) {
+      const char* slot = lds + (it & 1) * kSlotBytes + hh * bps * 2 * kTileBytes;
+      const int nblk = item_blocks(cit);
+      for (int b = 0; b < bps; ++b) {
+        const int blk = bps * cs + b;
+        if (blk < nblk) compute_block(slot + b * 2 * kTileBytes, cit.tok_begin + blk * kBS);
       }
     }
-    __syncthreads();
+    if (++cs == cnst) {
+      finish_item();
+      if (++ci == i_end) break;
+      cit = load_item(items, ci);
+      cnst = item_stages(cit);
+      cs = 0;
+    }
   }
-}
-
-template <int NCT>
-__device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
-  __shared__ float lds_o[kWaves * 16 * NCT * (kD + kLdsPad)];
-  __shared__ float lds_m[kWaves * 16 * NCT];
-  __shared__ float lds_l[kWaves * 16 * NCT];
-  const WorkItem it = P.items[blockIdx.x];
-  run_item<NCT>(P, it, lds_o, lds_m, lds_l);
 }
 
 }  // namespace
 
-// Grouped prefix pass: 32 query rows (members x Hq/Hkv) per wave pass.
-__global__ __launch_bounds__(256) void fca_grouped_prefix_kernel(GqaParams P) { partial_kernel_body<2>(P); }
+// Grouped prefix pass: members x Hq/Hkv query rows per item.
+__global__ __launch_bounds__(256, 2) void fca_grouped_prefix_kernel(GqaParams P) { partial_kernel_body(P); }
 
-// Per-request suffix pass: the Hq/Hkv rows of one request.
-__global__ __launch_bounds__(256, 2) void fca_suffix_decode_kernel(GqaParams P) { partial_kernel_body<1>(P); }
+// Per-request suffix pass: the Hq/Hkv rows of up to 4 KV heads of a request.
+__global__ __launch_bounds__(256, 2) void fca_suffix_decode_kernel(GqaParams P) { partial_kernel_body(P); }
 
-hipError_t launch_gqa_partial(int kind, const GqaParams& p, int n_items, hipStream_t s) {
-  if (n_items <= 0) return hipSuccess;
+hipError_t launch_gqa_partial(int kind, const GqaParams& p, int n_bins, hipStream_t s) {
+  if (n_bins <= 0) return hipSuccess;
   if (kind == 0)
-    hipLaunchKernelGGL(fca_grouped_prefix_kernel, dim3(n_items), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(fca_grouped_prefix_kernel, dim3(n_bins), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(fca_suffix_decode_kernel, dim3(n_items), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(fca_suffix_decode_kernel, dim3(n_bins), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -6,13 +6,14 @@
 #include <cstddef>
 #include <cstdint>
 
-#include "../../include/fca.h"
+#include "fca.h"
 
 namespace fca {
 
 constexpr int kMaxBatch = 8192;
 constexpr int kMaxTableWidth = 1 << 20;
-constexpr int kTileTokens = 32;  // tokens per MFMA tile step of the attention kernels
+constexpr int kTileTokens = 32;     // split boundaries are multiples of this many tokens
+constexpr int kMaxItemBlocks = 1024;  // cache blocks one attention work item may span
 
 // A unit of work of the grouped or per-request pass; same layout as the
 // public fca_work_item.
@@ -26,7 +27,8 @@ struct WorkItem {
   int32_t col0;
   int32_t col1;
   int32_t part_base;
-  int32_t pad0, pad1, pad2;
+  int32_t kv_heads;  // KV heads the item covers: kv_head .. kv_head + kv_heads - 1
+  int32_t pad1, pad2;
 };
 static_assert(sizeof(WorkItem) == sizeof(fca_work_item), "work item layout");
 
@@ -86,7 +88,8 @@ struct PartialPtrs {
 };
 
 struct GqaParams {
-  const WorkItem* items;
+  const WorkItem* items;    // grouped by bin
+  const int32_t* bin_off;   // items of workgroup b: [bin_off[b], bin_off[b + 1])
   const int32_t* perm;
   const int32_t* bt;
   int32_t W;
@@ -100,8 +103,8 @@ struct GqaParams {
   PartialPtrs part;
 };
 
-// kind 0: grouped pass (32 query rows per wave), 1: per-request pass (16).
-hipError_t launch_gqa_partial(int kind, const GqaParams& p, int n_items, hipStream_t s);
+// kind 0: grouped pass, 1: per-request pass; one persistent workgroup per bin.
+hipError_t launch_gqa_partial(int kind, const GqaParams& p, int n_bins, hipStream_t s);
 
 struct MergeParams {
   const ReqMeta* req;

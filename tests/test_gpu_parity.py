@@ -162,53 +162,70 @@ def test_plan_copies_tables_and_bad_tables():
 
 @pytest.mark.parametrize("name", GQA_CONFIGS)
 def test_schedule_covers_each_token_once(name):
+    """Every (group or suffix, KV head, query row, token) is computed by
+    exactly one work item, every partial row is written once, and the merge
+    reads each partial row once per (request, query head)."""
     b = build_batch(CONFIGS[name])
     p = plan_for(b)
     sh = b.shape
     r = sh.gqa_ratio
+    hkv = sh.num_kv_heads
+    bs = sh.block_size
     ex = p.export()
     sc = p.export_schedule()
-    bs = sh.block_size
-    # grouped: every (group, head, query row, token) of each range exactly once
-    cover = {}
+    rows = np.zeros(p.info.num_partial_rows, dtype=np.int64)
+    # grouped: coverage counted per (group, head, column, token)
+    group_of = {}
+    for k, g in enumerate(ex["groups"]):
+        group_of[(g["block_begin"], len(g["members"]) * r, g["members"])] = k
+    cov_g = {}
     for it in sc["grouped"]:
-        assert it["tok_begin"] < it["tok_end"] and it["col0"] < it["col1"] <= it["ncols"]
-        # nested groups can start at the same depth-first position; their
-        # member counts differ, so (position, query rows) names a group
-        key = (it["member_off"], it["ncols"], it["kv_head"])
-        cover.setdefault(key, []).append((it["tok_begin"], it["tok_end"], it["col0"], it["col1"]))
-    assert len(cover) == len(ex["groups"]) * sh.num_kv_heads
-    for key, spans in cover.items():
-        toks = {}
-        for t0, t1, c0, c1 in spans:
-            toks.setdefault((t0, t1), []).append((c0, c1))
-        ranges = sorted(toks)
-        for (a0, a1), (b0, _) in zip(ranges, ranges[1:]):
+        assert it["member_off"] >= 0 and it["tok_begin"] < it["tok_end"]
+        assert 0 <= it["col0"] < it["col1"] <= it["ncols"] and it["col1"] - it["col0"] <= 64
+        assert it["kv_heads"] in (1, 2, 4) and it["kv_head"] % it["kv_heads"] == 0
+        assert it["kv_heads"] * -(-(it["col1"] - it["col0"]) // 16) <= 4
+        key = (it["member_off"], it["ncols"])
+        arr = cov_g.setdefault(key, {})
+        for h in range(it["kv_head"], it["kv_head"] + it["kv_heads"]):
+            for c in range(it["col0"], it["col1"]):
+                arr.setdefault((h, c), []).append((it["tok_begin"], it["tok_end"]))
+            for c in range(it["col0"], it["col1"]):
+                rows[it["part_base"] + h * it["ncols"] + c] += 1
+    assert len(cov_g) == len(ex["groups"])
+    ranges = sorted((g["block_begin"] * bs, g["block_end"] * bs, len(g["members"]) * r) for g in ex["groups"])
+    for key, arr in cov_g.items():
+        ncols = key[1]
+        assert len(arr) == hkv * ncols
+        spans_set = {tuple(sorted(v)) for v in arr.values()}
+        assert len(spans_set) == 1  # every (head, column) sees the same token splits
+        spans = next(iter(spans_set))
+        for (a0, a1), (b0, _) in zip(spans, spans[1:]):
             assert a1 == b0
-        for cols in toks.values():
-            cols.sort()
-            assert cols[0][0] == 0 and cols[-1][1] == key[1]
-            for (a0, a1), (b0, _) in zip(cols, cols[1:]):
-                assert a1 == b0
-    # suffix: each request's suffix tokens exactly once per head
+        assert any(lo == spans[0][0] and hi == spans[-1][1] and n == ncols for lo, hi, n in ranges)
+    # suffix: each request's suffix tokens once per head
     per_req = {}
     for it in sc["suffix"]:
-        per_req.setdefault((it["request"], it["kv_head"]), []).append((it["tok_begin"], it["tok_end"]))
-        assert it["col0"] == 0 and it["col1"] == r and it["member_off"] == -1
+        assert it["member_off"] == -1 and it["col0"] == 0 and it["col1"] == r and it["ncols"] == r
+        for h in range(it["kv_head"], it["kv_head"] + it["kv_heads"]):
+            per_req.setdefault((it["request"], h), []).append((it["tok_begin"], it["tok_end"]))
+            for c in range(r):
+                rows[it["part_base"] + h * r + c] += 1
     for i, (sb, st, _) in enumerate(ex["requests"]):
-        for h in range(sh.num_kv_heads):
+        for h in range(hkv):
             spans = sorted(per_req.get((i, h), []))
-            total = sum(e - s for s, e in spans)
-            assert total == st
+            assert sum(e - s for s, e in spans) == st
             if st:
                 assert spans[0][0] == sb * bs and spans[-1][1] == int(b.seq_lens[i])
+                for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+                    assert a1 == b0
+    assert (rows == 1).all()
     # merge sources: every partial row read once per (request, head)
-    rows_seen = np.zeros(p.info.num_partial_rows, dtype=np.int64)
+    seen = np.zeros(p.info.num_partial_rows, dtype=np.int64)
     for i in range(b.batch):
         for h in range(sh.num_q_heads):
             for a, bb in sc["sources"][i]:
-                rows_seen[a + (h // r) * bb + h % r] += 1
-    assert (rows_seen == 1).all()
+                seen[a + (h // r) * bb + h % r] += 1
+    assert (seen == 1).all()
 
 
 # --------------------------------------------------------------- decode ----
