@@ -110,7 +110,8 @@ typedef struct fca_plan_info {
   int32_t max_depth;         /* deepest group depth (roots are 0), -1 if none */
   int32_t num_grouped_items; /* work items of the grouped pass */
   int32_t num_suffix_items;  /* work items of the per-request pass */
-  int32_t num_merge_sources; /* partial triples the merge reads per q head */
+  int32_t num_merge_sources; /* partial triples the merge reads, summed over
+                                (request, query head) */
   int64_t num_partial_rows;  /* (o, m, l) rows written per decode */
   int64_t logical_tokens;    /* sum of seq_lens */
   int64_t unique_tokens;     /* group ranges once + every suffix */
@@ -206,8 +207,9 @@ typedef struct fca_work_item {
   int32_t ncols;      /* query rows of the unit: members * (Hq/Hkv) */
   int32_t col0;       /* query rows [col0, col1) of the unit */
   int32_t col1;
-  int32_t part_base;  /* partial row of (KV head 0, query row 0) of the unit's
-                         token split; head h, row n is part_base + h*ncols + n */
+  int32_t part_base;  /* partial row of (kv_head, col0) of the item; head h,
+                         row n is part_base + (h - kv_head)*(col1 - col0)
+                         + (n - col0) */
   int32_t kv_heads;   /* the item covers KV heads kv_head .. kv_head+kv_heads-1 */
   int32_t reserved[2];
 } fca_work_item;
@@ -215,10 +217,9 @@ typedef struct fca_work_item {
 /*
  * The decode schedule, for tests and tools (host copies):
  *   grouped [num_grouped_items], suffix [num_suffix_items]
- *   src_off [batch + 1], src [2 * num_merge_sources]
- * Request i merges the partial rows  a + (h / r) * b + h % r  for every
- * pair (a, b) = (src[2s], src[2s+1]), s in [src_off[i], src_off[i+1]), for
- * query head h (r = num_q_heads / num_kv_heads).
+ *   src_off [batch * num_q_heads + 1], src [num_merge_sources]
+ * Query head h of request i merges the partial rows
+ *   src[s], s in [src_off[i * num_q_heads + h], src_off[i * num_q_heads + h + 1]).
  */
 fca_status fca_plan_export_schedule(fca_plan plan, fca_work_item* grouped, fca_work_item* suffix,
                                     int32_t* src_off, int32_t* src);

@@ -343,19 +343,21 @@ class Plan:
         return dict(groups=out, requests=requests)
 
     def export_schedule(self):
-        """Work items of both passes and per-request merge sources."""
+        """Work items of both passes and the merge sources: ``sources[i][h]``
+        lists the partial rows query head h of request i merges."""
         ng, ns, B = self.info.num_grouped_items, self.info.num_suffix_items, self.batch
+        hq = self.desc.num_q_heads
         gi = (WorkItem * max(ng, 1))()
         si = (WorkItem * max(ns, 1))()
-        off = (ctypes.c_int32 * (B + 1))()
-        src = (ctypes.c_int32 * max(2 * self.info.num_merge_sources, 1))()
+        off = (ctypes.c_int32 * (B * hq + 1))()
+        src = (ctypes.c_int32 * max(self.info.num_merge_sources, 1))()
         _check(lib().fca_plan_export_schedule(self._h, gi, si, off, src))
 
         def items(arr, n):
             names = [f[0] for f in WorkItem._fields_ if f[0] != "reserved"]
             return [{k: getattr(arr[j], k) for k in names} for j in range(n)]
 
-        sources = [[(src[2 * s], src[2 * s + 1]) for s in range(off[i], off[i + 1])] for i in range(B)]
+        sources = [[list(src[off[i * hq + h] : off[i * hq + h + 1]]) for h in range(hq)] for i in range(B)]
         return dict(grouped=items(gi, ng), suffix=items(si, ns), sources=sources)
 
 

@@ -56,15 +56,11 @@ int env_int(const char* name, int dflt) {
 
 // Split-schedule targets (developer tuning knobs).
 struct Tuning {
-  int items_per_bin;  // aim for about this many work items per persistent workgroup
-  int min_stages;     // shortest token split, in stages (4 (head, block) tiles each)
-  int wg_per_cu;      // persistent workgroups per compute unit
+  int wg_per_cu;  // persistent workgroups per compute unit
 };
 
 Tuning tuning() {
   Tuning t;
-  t.items_per_bin = env_int("FCA_TUNE_ITEMS_PER_BIN", 3);
-  t.min_stages = env_int("FCA_TUNE_MIN_STAGES", 4);
   t.wg_per_cu = env_int("FCA_TUNE_WG_PER_CU", 2);
   return t;
 }
@@ -128,7 +124,7 @@ Layout make_layout(int B, int W) {
 
 // Plan-owned device buffer holding the schedule.
 struct SchedLayout {
-  size_t items_g, items_s, bins_g, bins_s, perm, req, grp, total;
+  size_t items_g, items_s, bins_g, bins_s, perm, req, grp, lanes, total;
 };
 
 DiscoveryPtrs discovery_ptrs(char* ws, const Layout& L, int B) {
@@ -186,6 +182,7 @@ struct fca_plan_s {
   std::vector<int32_t> perm;
   std::vector<ReqMeta> req;
   std::vector<GroupMeta> grp;
+  std::vector<LaneMeta> lanes;  // grouped lanes, then suffix lanes
   fca_plan_info info;
   // plan-owned device copy of the schedule
   char* sched = nullptr;
@@ -205,6 +202,33 @@ struct fca_plan_s {
     for (hipEvent_t e : event_pool) (void)hipEventDestroy(e);
   }
 };
+
+// Partial rows request i merges for query head h, in the merge's order:
+// every split of the deepest group's lane, then of its ancestors' lanes, then
+// of the suffix lane.
+template <class F>
+void for_each_source(const fca_plan_s& P, int i, int h, F&& f) {
+  const int r = P.r;
+  const int kvh = h / r, rr = h % r;
+  const ReqMeta& rq = P.req[i];
+  auto lane_rows = [&](int lane, int col) {
+    const LaneMeta& L = P.lanes[lane];
+    for (int s = 0; s < L.splits; ++s)
+      f((int64_t)L.base + (int64_t)s * L.H * L.ccols + (int64_t)(kvh - L.kv0) * L.ccols + (col - L.col0));
+  };
+  for (int g = rq.deepest; g >= 0; g = P.grp[g].parent) {
+    const GroupMeta& gm = P.grp[g];
+    const int col = (rq.pos - gm.r0) * r + rr;
+    lane_rows(gm.lane0 + (kvh / gm.H) * gm.chunks + col / kItemCols, col);
+  }
+  if (rq.sfx_lane >= 0) lane_rows(rq.sfx_lane + kvh / rq.sfx_H, rr);
+}
+
+int64_t count_sources(const fca_plan_s& P, int i, int h) {
+  int64_t n = 0;
+  for_each_source(P, i, h, [&](int64_t) { ++n; });
+  return n;
+}
 
 extern "C" {
 
@@ -232,6 +256,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   const int B = P->B;
   const int bs = P->desc.block_size;
   const int hkv = P->desc.num_kv_heads;
+  const int hq = P->desc.num_q_heads;
   const int r = P->r;
   const Layout& L = P->L;
   const int32_t* hdr = rb.data();
@@ -337,157 +362,131 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   }
 
   // ---- Work items ----
-  // An item covers a token split of one unit (a group's prefix range or a
-  // request's suffix), H KV heads and up to 64 query rows, with H x (16-row
-  // column tiles) <= 4 waves.  Splits are chosen per unit, in whole stages
-  // (4 (head, block) tiles), so that each pass has about items_per_bin items
-  // per persistent workgroup.
+  // A lane is one (unit, head block, column chunk) stream of stages: a unit
+  // is a group's prefix range or a request's suffix, a head block H KV heads,
+  // a column chunk up to 64 query rows, with H x (16-row column tiles) <= 4
+  // waves; one stage is 4 / H blocks of each of the H heads.  Each pass lays
+  // its lanes end to end and cuts the stream into one equal run of stages per
+  // persistent workgroup; a lane cut k times yields k + 1 items (token
+  // splits), each with its own partial rows.
   const Tuning t = tuning();
   auto heads_for = [&](int nct) {  // KV heads per item for nct column tiles
     for (int H = kItemWaves / nct; H > 1; H /= 2)
       if (hkv % H == 0) return H;
     return 1;
   };
-  struct Unit {
-    int64_t T;        // tokens of the range
-    int tok0;         // first token
-    int request;      // block-table row
-    int member_off;   // -1 for a suffix
-    int ncols;
-    int H;            // KV heads per item
-    int chunks;       // 64-row column chunks
-    int64_t stages;   // stages of one (head group, chunk) stream over the whole range
-    int64_t base;     // partial row of (split 0, head 0, row 0)
-    int64_t split_stride;  // partial rows per split
+  struct Lane {
+    int request, member_off, ncols, tok0, tok_end;
+    int kv0, H, col0, col1;
+    int64_t stages;
+    int64_t base;
     int splits;
-    int64_t chunk_tok;
   };
-  auto make_unit = [&](int64_t T, int tok0, int request, int member_off, int ncols) {
-    Unit u{};
-    u.T = T;
-    u.tok0 = tok0;
-    u.request = request;
-    u.member_off = member_off;
-    u.ncols = ncols;
+  // Appends the lanes of one unit; returns the index of its first lane.
+  auto add_lanes = [&](std::vector<Lane>& lanes, int tok0, int tok_end, int request, int member_off,
+                       int ncols, int* H_out, int* chunks_out) {
+    const int first = (int)lanes.size();
     const int nct = (int)std::min<int64_t>(ceil_div(ncols, 16), kItemWaves);
-    u.H = heads_for(nct);
-    u.chunks = (int)ceil_div(ncols, kItemCols);
-    const int bps = kItemWaves / u.H;
-    u.stages = ceil_div(ceil_div(T, bs), bps);
-    return u;
+    const int H = heads_for(nct);
+    const int chunks = (int)ceil_div(ncols, kItemCols);
+    const int bps = kItemWaves / H;
+    const int64_t stages = ceil_div(ceil_div((int64_t)tok_end - tok0, bs), bps);
+    for (int hb = 0; hb < hkv / H; ++hb)
+      for (int c = 0; c < chunks; ++c)
+        lanes.push_back(Lane{request, member_off, ncols, tok0, tok_end, hb * H, H, c * kItemCols,
+                             std::min(ncols, (c + 1) * kItemCols), stages, 0, 0});
+    *H_out = H;
+    *chunks_out = chunks;
+    return first;
   };
-  auto split_units = [&](std::vector<Unit>& units, int64_t& row) {
-    int64_t work = 0;
-    for (const Unit& u : units) work += u.stages * (hkv / u.H) * u.chunks;
-    const int64_t target_items = (int64_t)t.items_per_bin * n_cu_ * t.wg_per_cu;
-    const int64_t st = std::max<int64_t>(t.min_stages, ceil_div(work, std::max<int64_t>(target_items, 1)));
-    for (Unit& u : units) {
-      const int bps = kItemWaves / u.H;
-      int64_t k = std::max<int64_t>(1, ceil_div(u.stages, st));
-      k = std::max<int64_t>(k, ceil_div(u.T, (int64_t)kMaxItemBlocks * bs));
-      u.chunk_tok = ceil_div(u.stages, k) * bps * bs;  // whole stages, a multiple of 32 tokens
-      u.splits = (int)ceil_div(u.T, u.chunk_tok);
-      u.base = row;
-      u.split_stride = (int64_t)hkv * u.ncols;
-      row += u.splits * u.split_stride;
-    }
-  };
-  auto emit_items = [&](const std::vector<Unit>& units, std::vector<WorkItem>& out) {
-    for (const Unit& u : units)
-      for (int s = 0; s < u.splits; ++s)
-        for (int h0 = 0; h0 < hkv; h0 += u.H)
-          for (int c = 0; c < u.chunks; ++c) {
-            WorkItem it{};
-            it.request = u.request;
-            it.tok_begin = (int)(u.tok0 + s * u.chunk_tok);
-            it.tok_end = (int)std::min<int64_t>(it.tok_begin + u.chunk_tok, u.tok0 + u.T);
-            it.kv_head = h0;
-            it.kv_heads = u.H;
-            it.member_off = u.member_off;
-            it.ncols = u.ncols;
-            it.col0 = c * kItemCols;
-            it.col1 = std::min(u.ncols, (c + 1) * kItemCols);
-            it.part_base = (int32_t)(u.base + s * u.split_stride);
-            out.push_back(it);
-          }
-  };
-  // Longest-first packing into n_bins persistent workgroups (least-loaded
-  // bin, ties to the lower index); items are then stored bin by bin.
-  auto pack_bins = [&](std::vector<WorkItem>& items, std::vector<int32_t>& bins) {
-    auto stages_of = [](const WorkItem& w) {
-      const int64_t nblk = (w.tok_end - w.tok_begin + 15) / 16;
-      const int bps = kItemWaves / w.kv_heads;
-      return (nblk + bps - 1) / bps;
-    };
-    std::vector<int> order(items.size());
-    for (size_t k = 0; k < order.size(); ++k) order[k] = (int)k;
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return stages_of(items[a]) > stages_of(items[b]); });
-    const int nb = (int)std::min<int64_t>((int64_t)items.size(), (int64_t)n_cu_ * t.wg_per_cu);
-    std::vector<std::vector<int>> per(nb);
-    std::priority_queue<std::pair<int64_t, int>, std::vector<std::pair<int64_t, int>>, std::greater<>> heap;
-    for (int b = 0; b < nb; ++b) heap.push({0, b});
-    for (int k : order) {
-      auto top = heap.top();
-      heap.pop();
-      per[top.second].push_back(k);
-      heap.push({top.first + stages_of(items[k]), top.second});
-    }
-    std::vector<WorkItem> sorted;
-    sorted.reserve(items.size());
+  auto cut = [&](std::vector<Lane>& lanes, std::vector<WorkItem>& items, std::vector<int32_t>& bins,
+                 int64_t& row) {
+    int64_t W = 0;
+    for (const Lane& L : lanes) W += L.stages;
+    const int64_t nb = std::min<int64_t>(W, (int64_t)n_cu_ * t.wg_per_cu);
+    items.clear();
     bins.assign(nb + 1, 0);
-    for (int b = 0; b < nb; ++b) {
-      bins[b] = (int32_t)sorted.size();
-      for (int k : per[b]) sorted.push_back(items[k]);
+    std::vector<int> lane_of;
+    size_t li = 0;
+    int64_t lpos = 0, pos = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+      bins[b] = (int32_t)items.size();
+      const int64_t end = (b + 1) * W / nb;
+      while (pos < end) {
+        Lane& L = lanes[li];
+        const int64_t take = std::min(L.stages - lpos, end - pos);
+        const int64_t stok = (int64_t)(kItemWaves / L.H) * bs;  // tokens per stage
+        WorkItem it{};
+        it.request = L.request;
+        it.tok_begin = (int)(L.tok0 + lpos * stok);
+        it.tok_end = (int)std::min<int64_t>(L.tok0 + (lpos + take) * stok, L.tok_end);
+        it.kv_head = L.kv0;
+        it.kv_heads = L.H;
+        it.member_off = L.member_off;
+        it.ncols = L.ncols;
+        it.col0 = L.col0;
+        it.col1 = L.col1;
+        it.part_base = L.splits++;  // split index until the lane bases are known
+        items.push_back(it);
+        lane_of.push_back((int)li);
+        pos += take;
+        lpos += take;
+        if (lpos == L.stages) {
+          ++li;
+          lpos = 0;
+        }
+      }
     }
-    bins[nb] = (int32_t)sorted.size();
-    items.swap(sorted);
+    bins[nb] = (int32_t)items.size();
+    for (Lane& L : lanes) {
+      L.base = row;
+      row += (int64_t)L.splits * L.H * (L.col1 - L.col0);
+    }
+    for (size_t k = 0; k < items.size(); ++k) {
+      const Lane& L = lanes[lane_of[k]];
+      items[k].part_base = (int32_t)std::min<int64_t>(L.base + (int64_t)items[k].part_base * L.H * (L.col1 - L.col0),
+                                                      INT32_MAX);
+    }
   };
 
   int64_t row = 0;
-  std::vector<Unit> gunits, sunits;
+  std::vector<Lane> glanes, slanes;
   for (int c = 0; c < G; ++c) {
     const fca_group_record& gr = P->groups[c];
-    const int64_t T = (int64_t)(gr.block_end - gr.block_begin) * bs;
-    gunits.push_back(make_unit(T, gr.block_begin * bs, P->perm[r0[c]], r0[c], count[c] * r));
-    unique += T;
-  }
-  split_units(gunits, row);
-  P->items_g.clear();
-  emit_items(gunits, P->items_g);
-  for (int c = 0; c < G; ++c) {
     GroupMeta& gm = P->grp[c];
-    gm.parent = P->groups[c].parent;
+    gm.parent = gr.parent;
     gm.r0 = r0[c];
     gm.ncols = count[c] * r;
-    gm.unit = (int32_t)gunits[c].base;
-    gm.splits = gunits[c].splits;
+    gm.lane0 = add_lanes(glanes, gr.block_begin * bs, gr.block_end * bs, P->perm[r0[c]], r0[c], count[c] * r,
+                         &gm.H, &gm.chunks);
+    unique += (int64_t)(gr.block_end - gr.block_begin) * bs;
   }
-  std::vector<int> sunit_of(B, -1);
-  for (int i = 0; i < B; ++i)
-    if (sfx_tokens[i] > 0) {
-      sunit_of[i] = (int)sunits.size();
-      sunits.push_back(make_unit(sfx_tokens[i], P->req3[3 * i] * bs, i, -1, r));
-    }
-  split_units(sunits, row);
-  P->items_s.clear();
-  emit_items(sunits, P->items_s);
-  if (row > INT32_MAX) return fail(FCA_ERR_UNSUPPORTED, "too many partial rows");
   P->req.assign(B, ReqMeta{});
   for (int i = 0; i < B; ++i) {
     ReqMeta& rq = P->req[i];
     rq.pos = pos[i];
     rq.deepest = deepest_c[i];
-    rq.sfx_unit = sunit_of[i] >= 0 ? (int32_t)sunits[sunit_of[i]].base : 0;
-    rq.sfx_splits = sunit_of[i] >= 0 ? sunits[sunit_of[i]].splits : 0;
+    rq.sfx_lane = -1;
+    rq.sfx_H = 1;
+    if (sfx_tokens[i] > 0) {
+      int chunks;
+      rq.sfx_lane = add_lanes(slanes, P->req3[3 * i] * bs, lens[i], i, -1, r, &rq.sfx_H, &chunks);
+    }
   }
-  pack_bins(P->items_g, P->bins_g);
-  pack_bins(P->items_s, P->bins_s);
+  cut(glanes, P->items_g, P->bins_g, row);
+  cut(slanes, P->items_s, P->bins_s, row);
+  if (row > INT32_MAX) return fail(FCA_ERR_UNSUPPORTED, "too many partial rows");
+  P->lanes.clear();
+  for (const std::vector<Lane>* v : {&glanes, &slanes})
+    for (const Lane& L : *v)
+      P->lanes.push_back(LaneMeta{(int32_t)L.base, L.splits, L.kv0, L.H, L.col0, L.col1 - L.col0, 0, 0});
+  for (int i = 0; i < B; ++i)
+    if (P->req[i].sfx_lane >= 0) P->req[i].sfx_lane += (int)glanes.size();
 
+  // Merge sources: one per (request, query head, token split on its path).
   int64_t sources = 0;
-  for (int i = 0; i < B; ++i) {
-    for (int g = deepest_c[i]; g >= 0; g = P->grp[g].parent) sources += P->grp[g].splits;
-    sources += P->req[i].sfx_splits;
-  }
+  for (int i = 0; i < B; ++i)
+    for (int h = 0; h < hq; ++h) sources += count_sources(*P, i, h);
 
   fca_plan_info& info = P->info;
   info.batch = B;
@@ -587,6 +586,7 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
     S.perm = place(P->perm.size() * 4);
     S.req = place(P->req.size() * sizeof(ReqMeta));
     S.grp = place(P->grp.size() * sizeof(GroupMeta));
+    S.lanes = place(P->lanes.size() * sizeof(LaneMeta));
     S.total = off;
     e = hipMalloc(&P->sched, S.total);
     if (e != hipSuccess) {
@@ -605,6 +605,7 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
         {P->perm.data(), S.perm, P->perm.size() * 4},
         {P->req.data(), S.req, P->req.size() * sizeof(ReqMeta)},
         {P->grp.data(), S.grp, P->grp.size() * sizeof(GroupMeta)},
+        {P->lanes.data(), S.lanes, P->lanes.size() * sizeof(LaneMeta)},
     };
     for (const Up& u : ups) {
       if (!u.bytes) continue;
@@ -729,6 +730,7 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   MergeParams mp;
   mp.req = reinterpret_cast<const ReqMeta*>(P->sched + S.req);
   mp.grp = reinterpret_cast<const GroupMeta*>(P->sched + S.grp);
+  mp.lanes = reinterpret_cast<const LaneMeta*>(P->sched + S.lanes);
   mp.B = P->B;
   mp.Hq = P->desc.num_q_heads;
   mp.Hkv = P->desc.num_kv_heads;
@@ -790,30 +792,17 @@ fca_status fca_plan_export_schedule(fca_plan plan, fca_work_item* grouped, fca_w
   if (grouped) std::memcpy(grouped, P->items_g.data(), P->items_g.size() * sizeof(WorkItem));
   if (suffix) std::memcpy(suffix, P->items_s.data(), P->items_s.size() * sizeof(WorkItem));
   if (src_off || src) {
+    const int hq = P->desc.num_q_heads;
     int64_t n = 0;
-    for (int i = 0; i < P->B; ++i) {
-      if (src_off) src_off[i] = (int32_t)n;
-      const ReqMeta& rq = P->req[i];
-      for (int g = rq.deepest; g >= 0; g = P->grp[g].parent) {
-        const GroupMeta& gm = P->grp[g];
-        const int k = rq.pos - gm.r0;
-        for (int s = 0; s < gm.splits; ++s) {
-          if (src) {
-            src[2 * n] = gm.unit + s * P->desc.num_kv_heads * gm.ncols + k * P->r;
-            src[2 * n + 1] = gm.ncols;
-          }
+    for (int i = 0; i < P->B; ++i)
+      for (int h = 0; h < hq; ++h) {
+        if (src_off) src_off[(int64_t)i * hq + h] = (int32_t)n;
+        for_each_source(*P, i, h, [&](int64_t row) {
+          if (src) src[n] = (int32_t)row;
           ++n;
-        }
+        });
       }
-      for (int s = 0; s < rq.sfx_splits; ++s) {
-        if (src) {
-          src[2 * n] = rq.sfx_unit + s * P->desc.num_q_heads;
-          src[2 * n + 1] = P->r;
-        }
-        ++n;
-      }
-    }
-    if (src_off) src_off[P->B] = (int32_t)n;
+    if (src_off) src_off[(int64_t)P->B * hq] = (int32_t)n;
   }
   return FCA_OK;
 }

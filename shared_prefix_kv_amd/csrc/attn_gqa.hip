@@ -105,9 +105,12 @@ __device__ __forceinline__ WorkItem load_item(cint32* items, int i) {
 
 __device__ __forceinline__ int item_blocks(const WorkItem& it) { return (it.tok_end - it.tok_begin + kBS - 1) / kBS; }
 
+// log2 of the blocks per stage of an item: 4 / kv_heads with kv_heads in {1, 2, 4}.
+__device__ __forceinline__ int item_lg_bps(const WorkItem& it) { return it.kv_heads == 1 ? 2 : it.kv_heads == 2 ? 1 : 0; }
+
 __device__ __forceinline__ int item_stages(const WorkItem& it) {
-  const int bps = kWaves / it.kv_heads;
-  return (item_blocks(it) + bps - 1) / bps;
+  const int lg = item_lg_bps(it);
+  return (item_blocks(it) + (1 << lg) - 1) >> lg;
 }
 
 __device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
@@ -123,6 +126,7 @@ __device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
   cint32* bin_off = (cint32*)(P.bin_off);
   cint32* items = (cint32*)(P.items);
   cint32* bt = (cint32*)(P.bt);
+  cint32* perm = (cint32*)(P.perm);
   const int i_begin = bin_off[blockIdx.x];
   const int i_end = bin_off[blockIdx.x + 1];
   if (i_begin >= i_end) return;
@@ -131,22 +135,17 @@ __device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
   const char* vpool = static_cast<const char*>(P.v);
   const __bf16* qbase = static_cast<const __bf16*>(P.q);
 
-  // ---- copy cursor: item di, stage ds ----
-  int di = i_begin, ds = 0;
-  WorkItem dit = load_item(items, di);
-  int dnst = item_stages(dit);
-
   // Q^T operand of this wave for an item: column tile w % n_ct of head
-  // h0 + w / n_ct (d-chunk ks*32 + 8*g); zeros for columns past the item and
-  // for idle waves.  Issued while the next stage's copy is in flight, and
-  // only consumed after the next stage barrier.
+  // h0 + w / n_ct (d-chunk ks*32 + 8*g).  The Q of item k + 1 is loaded into
+  // qn while item k is begun (right after its first stage copy is issued)
+  // and taken into the MFMA operand when item k + 1 begins, after a stage
+  // wait; one buffer suffices however short the items are.
   bf16x8 qn[4];
-  cint32* perm = (cint32*)(P.perm);
   auto load_q = [&](const WorkItem& it) {
-    const int nct = (it.col1 - it.col0 + 15) / 16;
-    const int cb = it.col0 + 16 * (wave % nct);  // first column of this wave's tile
-    const int col = cb + c16;
+    const int nct = (it.col1 - it.col0 + 15) >> 4;
     const int h = wave / nct;
+    const int cb = it.col0 + 16 * (wave - h * nct);  // first column of this wave's tile
+    const int col = cb + c16;
     int member = it.request;
     if (it.member_off >= 0 && cb < it.col1) {
       // The tile's columns belong to members (cb / r) .. (last / r); their
@@ -159,27 +158,47 @@ __device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
         member = mine == k ? pk : member;
       }
     }
-    if (h < it.kv_heads && col < it.col1) {
-      const int qh = (it.kv_head + h) * P.r + col % P.r;
-      const __bf16* qp = qbase + ((int64_t)member * P.Hq + qh) * kD + 8 * g;
+    const bool use = h < it.kv_heads && col < it.col1;
+    const int qh = (it.kv_head + h) * P.r + col % P.r;
+    // Idle lanes read row 0 of the item (always in bounds) and are zeroed
+    // when the operand is taken.
+    const __bf16* qp =
+        qbase + ((int64_t)(use ? member : it.request) * P.Hq + (use ? qh : it.kv_head * P.r)) * kD + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qn[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qn[ks] = bf16x8{};
-    }
+    for (int ks = 0; ks < 4; ++ks) qn[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
   };
 
+  // ---- copy cursor: item di, stage ds ----
+  // The descriptor of item di + 1 and the block ID of this wave's next tile
+  // are loaded one step ahead, so issuing a stage waits on nothing.
+  int di = i_begin, ds = 0;
+  WorkItem dit = load_item(items, di);
+  WorkItem dnx = dit;
+  if (di + 1 < i_end) dnx = load_item(items, di + 1);
+  int dnst, dlg, dsub, dhead, dnblk;
+  auto copy_item = [&]() {  // per-item constants of the copy cursor
+    dnst = item_stages(dit);
+    dlg = item_lg_bps(dit);
+    dsub = wave & ((1 << dlg) - 1);
+    dhead = dit.kv_head + (wave >> dlg);
+    dnblk = item_blocks(dit);
+  };
+  copy_item();
+  // Tiles past the item copy block 0, which always exists; the math never
+  // reads them.
+  auto tile_id = [&]() {
+    const int b = (ds << dlg) + dsub;
+    return b < dnblk ? bt[(int64_t)dit.request * P.W + dit.tok_begin / kBS + b] : 0;
+  };
+  int cur_id = tile_id();
+
   // Copy stage (di, ds) into a slot: this wave's tile is block
-  // bps*ds + wave % bps of head h0 + wave / bps.  Blocks past the item copy
-  // block 0, which always exists; they are never used in the math.
+  // bps*ds + wave % bps of head h0 + wave / bps.
   auto issue = [&](int slot) {
-    const int bps = kWaves / dit.kv_heads;
-    const int b = bps * ds + wave % bps;
-    const int id = b < item_blocks(dit) ? bt[(int64_t)dit.request * P.W + dit.tok_begin / kBS + b] : 0;
-    const int head = dit.kv_head + wave / bps;
-    const char* ksrc = kpool + ((int64_t)id * P.k_stride_block + (int64_t)head * P.k_stride_head) * 2 + lane * 16;
-    const char* vsrc = vpool + ((int64_t)id * P.v_stride_block + (int64_t)head * P.v_stride_head) * 2 + lane * 16;
+    const char* ksrc =
+        kpool + ((int64_t)cur_id * P.k_stride_block + (int64_t)dhead * P.k_stride_head) * 2 + lane * 16;
+    const char* vsrc =
+        vpool + ((int64_t)cur_id * P.v_stride_block + (int64_t)dhead * P.v_stride_head) * 2 + lane * 16;
     char* dst = lds + slot * kSlotBytes + wave * 2 * kTileBytes;
 #pragma unroll
     for (int i = 0; i < kTileBytes / 1024; ++i)
@@ -190,33 +209,40 @@ __device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
       __builtin_amdgcn_global_load_lds(vsrc + i * 1024,
                                        (__attribute__((address_space(3))) void*)(dst + kTileBytes + i * 1024), 16, 0,
                                        0);
-    if (++ds == dnst) {  // on to the next item: its descriptor and its Q
+    if (++ds == dnst) {  // on to the next item: its descriptor, its Q, the one after
       ds = 0;
       if (++di < i_end) {
-        dit = load_item(items, di);
-        dnst = item_stages(dit);
-        load_q(dit);
+        dit = dnx;
+        copy_item();
+        if (di + 1 < i_end) dnx = load_item(items, di + 1);
       }
     }
+    if (di < i_end) cur_id = tile_id();
   };
 
   // ---- compute cursor: item ci, stage cs ----
-  WorkItem cit = dit;
+  WorkItem cit = dit, cnx = dnx;
   int ci = i_begin, cs = 0, cnst = dnst;
-  int hh = 0, ct = 0, bps = 1;
+  int hh = 0, ct = 0, lg = 0;
   bool active = false;
+  bool q_pending = false;  // qn is free and the next item's Q is still to be loaded
   bf16x8 qb[4];
   f32x4 o[8];
   float mrow = NEG_INF, lsum = 0.f;
 
   auto begin_item = [&]() {
-    const int nct = (cit.col1 - cit.col0 + 15) / 16;
-    bps = kWaves / cit.kv_heads;
+    const int nct = (cit.col1 - cit.col0 + 15) >> 4;
+    lg = item_lg_bps(cit);
     hh = wave / nct;
-    ct = wave % nct;
+    ct = wave - hh * nct;
     active = hh < cit.kv_heads;
+    const bool use = active && cit.col0 + 16 * ct + c16 < cit.col1;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[ks] = qn[ks];
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = use ? qn[ks] : bf16x8{};
+    if (ci + 1 < i_end) {
+      if (ci > i_begin) cnx = load_item(items, ci + 1);
+      q_pending = true;
+    }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     mrow = NEG_INF;
@@ -224,20 +250,25 @@ __device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
   };
 
   // One 16-token block from LDS: S^T = K Q^T (16x16x32, K = head dim),
-  // online softmax, O^T += V^T P^T (16x16x16, K = the block's tokens).
+  // online softmax, O^T += V^T P^T (16x16x16, K = the block's tokens).  All
+  // twelve LDS reads are issued first; V is consumed after the softmax.
   auto compute_block = [&](const char* kt, int t0) {
     const char* vt = kt + kTileBytes;
+    bf16x8 ka[4];
+    bf16x4 va[8];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(kt + ((4 * ks + g) * kBS + c16) * 16);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) va[dt] = *reinterpret_cast<const bf16x4*>(vt + ((16 * dt + c16) * kBS + 4 * g) * 2);
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + ((4 * ks + g) * kBS + c16) * 16);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], s, 0, 0, 0);
-    }
-    const bool partial = t0 + kBS > cit.tok_end;  // only the last block of a range
-    if (partial) {
+    for (int ks = 0; ks < 4; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[ks], s, 0, 0, 0);
+    // Tokens at or past the end of the range: score -inf, value zeroed
+    // (the tail of a block may hold NaN).
+    const int nvalid = cit.tok_end - t0 - 4 * g;  // valid tokens of this lane's 4
+    if (t0 + kBS > cit.tok_end) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (t0 + 4 * g + j >= cit.tok_end) s[j] = NEG_INF;
+      for (int j = 0; j < 4; ++j) s[j] = j < nvalid ? s[j] : NEG_INF;
     }
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mx = xmax32(xmax16(mx));
@@ -256,30 +287,34 @@ __device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
       pb[j] = (__bf16)p;
       lsum += p;
     }
+    if (t0 + kBS > cit.tok_end) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 keep = {(nvalid > 0 ? 0xffffu : 0u) | (nvalid > 1 ? 0xffff0000u : 0u),
+                          (nvalid > 2 ? 0xffffu : 0u) | (nvalid > 3 ? 0xffff0000u : 0u)};
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      bf16x4 a = *reinterpret_cast<const bf16x4*>(vt + ((16 * dt + c16) * kBS + 4 * g) * 2);
-      if (partial) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (t0 + 4 * g + j >= cit.tok_end) a[j] = (__bf16)0.f;  // NaN-safe tail
+      for (int dt = 0; dt < 8; ++dt) {
+        u32x2 w = __builtin_bit_cast(u32x2, va[dt]);
+        w &= keep;
+        va[dt] = __builtin_bit_cast(bf16x4, w);
       }
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[dt], 0, 0, 0);
     }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb, o[dt], 0, 0, 0);
   };
 
-  // Triples of this wave's columns, straight from registers.
-  auto finish_item = [&]() {
-    const float l = xsum32(xsum16(lsum));
-    const int col = cit.col0 + 16 * ct + c16;
-    if (!active || col >= cit.col1) return;
-    const int64_t prow = (int64_t)cit.part_base + (int64_t)(cit.kv_head + hh) * cit.ncols + col;
-    float* dst = P.part.o + prow * kD + 4 * g;
+  // Triple of this lane's column of the finished item, straight from
+  // registers.  It is stored after the next stage barrier, beside the next
+  // copy, so the stores never hold up a stage wait on their own.
+  bool fin = false;
+  int64_t fin_row = 0;
+  float fin_l = 0.f;
+  auto store_partial = [&]() {
+    float* dst = P.part.o + fin_row * kD + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt];
     if (g == 0) {
-      P.part.m[prow] = mrow;
-      P.part.l[prow] = l;
+      P.part.m[fin_row] = mrow;
+      P.part.l[fin_row] = fin_l;
     }
   };
 
@@ -290,9 +325,18 @@ __device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
     // stage it - 1, whose slot the next copy reuses.
     wait_vm_all();
     __syncthreads();
+    if (fin) {
+      store_partial();
+      fin = false;
+    }
     if (cs == 0) begin_item();
     if (di < i_end) issue((it + 1) & 1);
+    if (q_pending) {
+      load_q(cnx);
+      q_pending = false;
+    }
     if (active) {
+      const int bps = 1 << lg;
       const char* slot = lds + (it & 1) * kSlotBytes + hh * bps * 2 * kTileBytes;
       const int nblk = item_blocks(cit);
       for (int b = 0; b < bps; ++b) {
@@ -301,13 +345,18 @@ __device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
       }
     }
     if (++cs == cnst) {
-      finish_item();
+      // Row of head kv_head + hh, column col of the item's token split.
+      fin_l = xsum32(xsum16(lsum));
+      const int col = cit.col0 + 16 * ct + c16;
+      fin = active && col < cit.col1;
+      fin_row = (int64_t)cit.part_base + (int64_t)hh * (cit.col1 - cit.col0) + (col - cit.col0);
       if (++ci == i_end) break;
-      cit = load_item(items, ci);
+      cit = cnx;
       cnst = item_stages(cit);
       cs = 0;
     }
   }
+  if (fin) store_partial();
 }
 
 }  // namespace

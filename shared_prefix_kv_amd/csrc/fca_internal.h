@@ -13,7 +13,6 @@ namespace fca {
 constexpr int kMaxBatch = 8192;
 constexpr int kMaxTableWidth = 1 << 20;
 constexpr int kTileTokens = 32;     // split boundaries are multiples of this many tokens
-constexpr int kMaxItemBlocks = 1024;  // cache blocks one attention work item may span
 
 // A unit of work of the grouped or per-request pass; same layout as the
 // public fca_work_item.
@@ -34,10 +33,10 @@ static_assert(sizeof(WorkItem) == sizeof(fca_work_item), "work item layout");
 
 // Per-request data the merge reads.
 struct ReqMeta {
-  int32_t pos;         // position in the depth-first member order
-  int32_t deepest;     // canonical index of the deepest group, -1 if none
-  int32_t sfx_unit;    // partial row of (split 0, q head 0) of the suffix
-  int32_t sfx_splits;  // number of suffix splits (0: no suffix tokens)
+  int32_t pos;       // position in the depth-first member order
+  int32_t deepest;   // canonical index of the deepest group, -1 if none
+  int32_t sfx_lane;  // first lane of the suffix (-1: no suffix tokens)
+  int32_t sfx_H;     // KV heads per suffix lane
 };
 
 // Per-group data the merge reads (canonical order).
@@ -45,9 +44,23 @@ struct GroupMeta {
   int32_t parent;  // canonical index or -1
   int32_t r0;      // first position of the group's members in `perm`
   int32_t ncols;   // members * (Hq / Hkv)
-  int32_t unit;    // partial row of (split 0, kv head 0, column 0)
-  int32_t splits;  // token splits of the group's range
-  int32_t pad0, pad1, pad2;
+  int32_t lane0;   // lane of (head block 0, column chunk 0)
+  int32_t H;       // KV heads per lane; lane of (kv head h, column n) is
+  int32_t chunks;  //   lane0 + (h / H) * chunks + n / 64
+  int32_t pad0, pad1;
+};
+
+// One (unit, head block, column chunk) stream of a pass and its partial
+// rows: token split s, KV head h, column n is row
+//   base + s * H * ccols + (h - kv0) * ccols + (n - col0).
+struct LaneMeta {
+  int32_t base;
+  int32_t splits;
+  int32_t kv0;
+  int32_t H;
+  int32_t col0;
+  int32_t ccols;
+  int32_t pad0, pad1;
 };
 
 // Discovery header words.
@@ -109,6 +122,7 @@ hipError_t launch_gqa_partial(int kind, const GqaParams& p, int n_bins, hipStrea
 struct MergeParams {
   const ReqMeta* req;
   const GroupMeta* grp;
+  const LaneMeta* lanes;
   int32_t B, Hq, Hkv, r, Dv;
   PartialPtrs part;
   void* out;

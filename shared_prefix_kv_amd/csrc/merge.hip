@@ -36,14 +36,28 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One wave per (request, head); lane j resolves the j-th partial row of the
-// request's path so that all (m, l) loads are issued at once, then the value
-// rows are accumulated with the broadcast weights.  Each lane owns DV/64
-// value dims.
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// x + x' where x' is the value of lane ^ 32.
+__device__ __forceinline__ float xsum32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One wave per (request, head).  Lane j resolves the j-th partial row of the
+// request's path so that all (m, l) loads are issued at once; the value rows
+// are then accumulated two at a time (lanes 0-31 take even sources, lanes
+// 32-63 odd ones, each lane DV/32 value dims), eight rows in flight per
+// wave, and the two halves are added at the end.
 template <int DV>
 __device__ __forceinline__ void merge_body(const MergeParams& P) {
-  constexpr int VPL = DV / 64;  // floats per lane
+  constexpr int VPL = DV / 32;  // floats per lane
+  constexpr int U = 4;          // row pairs per batch of loads
   const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int hl = lane & 31;
   const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= (int64_t)P.B * P.Hq) return;
   const int i = (int)(pair / P.Hq);
@@ -52,8 +66,19 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
   const int rr = h % P.r;
   const ReqMeta rq = P.req[i];
 
-  int n_src = rq.sfx_splits;
-  for (int g = rq.deepest; g >= 0; g = P.grp[g].parent) n_src += P.grp[g].splits;
+  // Lanes on the request's path for this head: deepest group first, then
+  // its ancestors, then the suffix.
+  auto lane_of = [&](int g, int* col) {
+    const GroupMeta gm = P.grp[g];
+    *col = (rq.pos - gm.r0) * P.r + rr;
+    return gm.lane0 + (kvh / gm.H) * gm.chunks + *col / 64;
+  };
+  int n_src = 0;
+  for (int g = rq.deepest; g >= 0; g = P.grp[g].parent) {
+    int col;
+    n_src += P.lanes[lane_of(g, &col)].splits;
+  }
+  if (rq.sfx_lane >= 0) n_src += P.lanes[rq.sfx_lane + kvh / rq.sfx_H].splits;
 
   float M = -INFINITY, L = 0.f;
   float acc[VPL];
@@ -61,22 +86,29 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
   for (int v = 0; v < VPL; ++v) acc[v] = 0.f;
 
   for (int base = 0; base < n_src; base += 64) {
-    // Row of source j: splits of the deepest group first, then its
-    // ancestors, then the suffix splits.
+    // Row of source j: splits of the deepest group's lane first, then its
+    // ancestors', then the suffix lane's.
     const int j = base + lane;
-    int64_t row = -1;
+    int row = -1;
     if (j < n_src) {
       int rem = j;
-      for (int g = rq.deepest; g >= 0;) {
-        const GroupMeta gm = P.grp[g];
-        if (rem < gm.splits) {
-          row = (int64_t)gm.unit + ((int64_t)rem * P.Hkv + kvh) * gm.ncols + (int64_t)(rq.pos - gm.r0) * P.r + rr;
+      int g = rq.deepest;
+      for (;;) {
+        int ln, col;
+        if (g >= 0) {
+          ln = lane_of(g, &col);
+        } else {
+          ln = rq.sfx_lane + kvh / rq.sfx_H;
+          col = rr;
+        }
+        const LaneMeta lm = P.lanes[ln];
+        if (rem < lm.splits || g < 0) {
+          row = lm.base + rem * lm.H * lm.ccols + (kvh - lm.kv0) * lm.ccols + (col - lm.col0);
           break;
         }
-        rem -= gm.splits;
-        g = gm.parent;
+        rem -= lm.splits;
+        g = P.grp[g].parent;
       }
-      if (row < 0) row = (int64_t)rq.sfx_unit + (int64_t)rem * P.Hq + h;
     }
     float m = -INFINITY, l = 0.f;
     if (row >= 0) {
@@ -97,29 +129,47 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
     L += wave_sum(w * l);
     M = Mn;
     const int cnt = min(64, n_src - base);
-    const int row_lo = (int)(row & 0xffffffff), row_hi = (int)(row >> 32);
-    for (int s = 0; s < cnt; ++s) {
-      const float ws = __shfl(w, s);
-      const int64_t rs = ((int64_t)__shfl(row_hi, s) << 32) | (uint32_t)__shfl(row_lo, s);
-      if (ws > 0.f) {
-        const float* src = P.part.o + rs * DV + lane * VPL;
+    const int row0 = __builtin_amdgcn_readlane(row, 0);  // a valid row for idle slots
+    for (int s = 0; s < cnt; s += 2 * U) {
+      float x[U][VPL];
+      float ws[U];
 #pragma unroll
-        for (int v = 0; v < VPL; v += 2) {
-          const float2 x = *reinterpret_cast<const float2*>(src + v);
-          acc[v] += ws * x.x;
-          acc[v + 1] += ws * x.y;
+      for (int u = 0; u < U; ++u) {
+        const int se = s + 2 * u;  // even source; odd one is se + 1 (wave-uniform indices)
+        const float we = se < cnt ? lane_f(w, se) : 0.f;
+        const float wo = se + 1 < cnt ? lane_f(w, se + 1) : 0.f;
+        const int re = se < cnt ? __builtin_amdgcn_readlane(row, se) : row0;
+        const int ro = se + 1 < cnt ? __builtin_amdgcn_readlane(row, se + 1) : row0;
+        ws[u] = half ? wo : we;
+        const float* src = P.part.o + (int64_t)(half ? ro : re) * DV + hl * VPL;
+#pragma unroll
+        for (int v = 0; v < VPL; v += 4) {
+          const float4 t = *reinterpret_cast<const float4*>(src + v);
+          x[u][v] = t.x;
+          x[u][v + 1] = t.y;
+          x[u][v + 2] = t.z;
+          x[u][v + 3] = t.w;
         }
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) acc[v] += ws[u] > 0.f ? ws[u] * x[u][v] : 0.f;  // NaN-safe for w = 0
     }
   }
 
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  __bf16* dst = static_cast<__bf16*>(P.out) + pair * DV + lane * VPL;
 #pragma unroll
-  for (int v = 0; v < VPL; v += 2) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 ob = {(__bf16)(acc[v] * inv), (__bf16)(acc[v + 1] * inv)};
-    *reinterpret_cast<bf16x2*>(dst + v) = ob;
+  for (int v = 0; v < VPL; ++v) acc[v] = xsum32(acc[v]);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (half == 0) {
+    __bf16* dst = static_cast<__bf16*>(P.out) + pair * DV + hl * VPL;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int v = 0; v < VPL; v += 4) {
+      const bf16x4 ob = {(__bf16)(acc[v] * inv), (__bf16)(acc[v + 1] * inv), (__bf16)(acc[v + 2] * inv),
+                         (__bf16)(acc[v + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(dst + v) = ob;
+    }
   }
   if (P.lse && lane == 0) P.lse[pair] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }

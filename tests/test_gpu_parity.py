@@ -163,8 +163,9 @@ def test_plan_copies_tables_and_bad_tables():
 @pytest.mark.parametrize("name", GQA_CONFIGS)
 def test_schedule_covers_each_token_once(name):
     """Every (group or suffix, KV head, query row, token) is computed by
-    exactly one work item, every partial row is written once, and the merge
-    reads each partial row once per (request, query head)."""
+    exactly one work item, every partial row is written once, and query head
+    h of request i merges exactly the rows of its path's units for its own KV
+    head and column, each row read by one (request, head)."""
     b = build_batch(CONFIGS[name])
     p = plan_for(b)
     sh = b.shape
@@ -173,58 +174,92 @@ def test_schedule_covers_each_token_once(name):
     bs = sh.block_size
     ex = p.export()
     sc = p.export_schedule()
-    rows = np.zeros(p.info.num_partial_rows, dtype=np.int64)
-    # grouped: coverage counted per (group, head, column, token)
-    group_of = {}
-    for k, g in enumerate(ex["groups"]):
-        group_of[(g["block_begin"], len(g["members"]) * r, g["members"])] = k
-    cov_g = {}
-    for it in sc["grouped"]:
-        assert it["member_off"] >= 0 and it["tok_begin"] < it["tok_end"]
+    nrows = p.info.num_partial_rows
+    written = np.zeros(nrows, dtype=np.int64)
+    row_info = {}  # row -> (unit key, kv head, column, tok_begin, tok_end)
+
+    def record(it, key):
+        assert it["tok_begin"] < it["tok_end"]
         assert 0 <= it["col0"] < it["col1"] <= it["ncols"] and it["col1"] - it["col0"] <= 64
         assert it["kv_heads"] in (1, 2, 4) and it["kv_head"] % it["kv_heads"] == 0
         assert it["kv_heads"] * -(-(it["col1"] - it["col0"]) // 16) <= 4
-        key = (it["member_off"], it["ncols"])
-        arr = cov_g.setdefault(key, {})
+        w = it["col1"] - it["col0"]
         for h in range(it["kv_head"], it["kv_head"] + it["kv_heads"]):
             for c in range(it["col0"], it["col1"]):
-                arr.setdefault((h, c), []).append((it["tok_begin"], it["tok_end"]))
+                row = it["part_base"] + (h - it["kv_head"]) * w + (c - it["col0"])
+                assert 0 <= row < nrows
+                written[row] += 1
+                row_info[row] = (key, h, c, it["tok_begin"], it["tok_end"])
+
+    # grouped items: unit key (member_off, ncols); the group is the one whose
+    # member list holds the item's request and whose range and width match.
+    spans_g = {}
+    first_req = {}
+    for it in sc["grouped"]:
+        assert it["member_off"] >= 0
+        key = ("g", it["member_off"], it["ncols"])
+        first_req.setdefault(key, it["request"])
+        assert first_req[key] == it["request"]
+        record(it, key)
+        for h in range(it["kv_head"], it["kv_head"] + it["kv_heads"]):
             for c in range(it["col0"], it["col1"]):
-                rows[it["part_base"] + h * it["ncols"] + c] += 1
-    assert len(cov_g) == len(ex["groups"])
-    ranges = sorted((g["block_begin"] * bs, g["block_end"] * bs, len(g["members"]) * r) for g in ex["groups"])
-    for key, arr in cov_g.items():
-        ncols = key[1]
-        assert len(arr) == hkv * ncols
-        spans_set = {tuple(sorted(v)) for v in arr.values()}
-        assert len(spans_set) == 1  # every (head, column) sees the same token splits
-        spans = next(iter(spans_set))
-        for (a0, a1), (b0, _) in zip(spans, spans[1:]):
-            assert a1 == b0
-        assert any(lo == spans[0][0] and hi == spans[-1][1] and n == ncols for lo, hi, n in ranges)
-    # suffix: each request's suffix tokens once per head
-    per_req = {}
+                spans_g.setdefault(key, {}).setdefault((h, c), []).append((it["tok_begin"], it["tok_end"]))
+    group_key = {}
+    for key, arr in spans_g.items():
+        assert len(arr) == hkv * key[2]
+        lo = min(s0 for v in arr.values() for s0, _ in v)
+        hi = max(s1 for v in arr.values() for _, s1 in v)
+        for v in arr.values():  # each (head, column) tiles the whole range once
+            v = sorted(v)
+            assert v[0][0] == lo and v[-1][1] == hi
+            assert all(x1 == y0 for (_, x1), (y0, _) in zip(v, v[1:]))
+        match = [k for k, g in enumerate(ex["groups"])
+                 if (g["block_begin"] * bs, g["block_end"] * bs, len(g["members"]) * r) == (lo, hi, key[2])
+                 and first_req[key] in g["members"]]
+        assert len(match) == 1
+        group_key[match[0]] = key
+    assert len(group_key) == len(ex["groups"])
+
+    # suffix items: each request's suffix tokens once per (head, column)
+    spans_s = {}
     for it in sc["suffix"]:
         assert it["member_off"] == -1 and it["col0"] == 0 and it["col1"] == r and it["ncols"] == r
+        key = ("s", it["request"])
+        record(it, key)
         for h in range(it["kv_head"], it["kv_head"] + it["kv_heads"]):
-            per_req.setdefault((it["request"], h), []).append((it["tok_begin"], it["tok_end"]))
-            for c in range(r):
-                rows[it["part_base"] + h * r + c] += 1
+            spans_s.setdefault((it["request"], h), []).append((it["tok_begin"], it["tok_end"]))
     for i, (sb, st, _) in enumerate(ex["requests"]):
         for h in range(hkv):
-            spans = sorted(per_req.get((i, h), []))
-            assert sum(e - s for s, e in spans) == st
+            v = sorted(spans_s.get((i, h), []))
+            assert sum(e - s0 for s0, e in v) == st
             if st:
-                assert spans[0][0] == sb * bs and spans[-1][1] == int(b.seq_lens[i])
-                for (a0, a1), (b0, _) in zip(spans, spans[1:]):
-                    assert a1 == b0
-    assert (rows == 1).all()
-    # merge sources: every partial row read once per (request, head)
-    seen = np.zeros(p.info.num_partial_rows, dtype=np.int64)
-    for i in range(b.batch):
+                assert v[0][0] == sb * bs and v[-1][1] == int(b.seq_lens[i])
+                assert all(x1 == y0 for (_, x1), (y0, _) in zip(v, v[1:]))
+    assert (written == 1).all()
+
+    # merge sources
+    seen = np.zeros(nrows, dtype=np.int64)
+    for i, (sb, st, deepest) in enumerate(ex["requests"]):
+        path = []
+        g = deepest
+        while g >= 0:
+            path.append(group_key[g])
+            g = ex["groups"][g]["parent"]
+        if st:
+            path.append(("s", i))
         for h in range(sh.num_q_heads):
-            for a, bb in sc["sources"][i]:
-                seen[a + (h // r) * bb + h % r] += 1
+            rows = sc["sources"][i][h]
+            per_unit = {}
+            for row in rows:
+                seen[row] += 1
+                key, kvh, col, t0, t1 = row_info[row]
+                assert kvh == h // r and col % r == h % r
+                per_unit.setdefault(key, []).append((col, t0, t1))
+            assert list(per_unit) == path  # deepest group first, suffix last
+            for key, v in per_unit.items():
+                assert len({c for c, _, _ in v}) == 1  # one column per unit
+                v = sorted((t0, t1) for _, t0, t1 in v)
+                assert all(x1 == y0 for (_, x1), (y0, _) in zip(v, v[1:]))
     assert (seen == 1).all()
 
 
