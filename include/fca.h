@@ -51,13 +51,11 @@ typedef enum fca_status {
 #define FCA_PLAN_DISABLE_CASCADE 1u /* no groups: every request is read whole
                                        by the per-request pass (the
                                        non-cascade paged-decode baseline) */
-#define FCA_PLAN_CONCURRENT_PASSES 2u /* run the grouped pass on a
-                                       library-owned side stream, forked from
-                                       and joined back into the caller's
-                                       stream with events, concurrently with
-                                       the per-request pass.  By default the
-                                       passes run one after the other on the
-                                       caller's stream. */
+#define FCA_PLAN_SEPARATE_PASSES 2u /* launch the grouped pass and the
+                                       per-request pass one after the other
+                                       (for per-pass timing).  By default one
+                                       launch of persistent workgroups runs
+                                       the work items of both passes. */
 
 /*
  * Shape and cache layout of one attention layer.
@@ -169,9 +167,8 @@ fca_status fca_plan_get_info(fca_plan plan, fca_plan_info* info);
  *
  * Asynchronous on `stream`: no host synchronisation and no allocation.
  * Calls that share a decode workspace must not overlap.  Calls on one plan
- * must be issued from one host thread at a time (with
- * FCA_PLAN_CONCURRENT_PASSES they reuse the plan's fork/join events); they
- * may target different streams if each has its own decode workspace.
+ * may target different streams if each has its own decode workspace; with
+ * profiling enabled they must come from one host thread at a time.
  */
 fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
                       void* out_dev, float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
@@ -224,18 +221,19 @@ typedef struct fca_work_item {
 fca_status fca_plan_export_schedule(fca_plan plan, fca_work_item* grouped, fca_work_item* suffix,
                                     int32_t* src_off, int32_t* src);
 
-/* Summed GPU time of the passes of profiled fca_decode calls. */
+/* Summed GPU time of the launches of profiled fca_decode calls. */
 typedef struct fca_profile {
-  double grouped_ms; /* grouped prefix pass */
-  double suffix_ms;  /* per-request suffix pass */
-  double merge_ms;   /* log-sum-exp merge */
-  double decode_ms;  /* whole call, first launch to last */
+  double attention_ms; /* grouped and per-request passes */
+  double grouped_ms;   /* grouped pass alone (FCA_PLAN_SEPARATE_PASSES, else 0) */
+  double suffix_ms;    /* per-request pass alone (FCA_PLAN_SEPARATE_PASSES, else 0) */
+  double merge_ms;     /* log-sum-exp merge */
+  double decode_ms;    /* whole call, first launch to last */
   int64_t calls;
 } fca_profile;
 
 /*
  * Measurement hook.  While enabled, every fca_decode on this plan records HIP
- * events on its stream before and after each pass.  fca_profile_read waits
+ * events on its stream before and after each launch.  fca_profile_read waits
  * for the recorded events, returns the sums since the previous read and
  * resets them.  Events are created on first use and freed with the plan.
  * Not thread-safe; meant for benchmarks and profilers, not serving loops.

@@ -28,7 +28,7 @@ STATUS_NAMES = {
     6: "FCA_ERR_HOST_ALLOC",
 }
 FCA_PLAN_DISABLE_CASCADE = 1
-FCA_PLAN_CONCURRENT_PASSES = 2
+FCA_PLAN_SEPARATE_PASSES = 2
 
 EXPORTED = [
     "fca_plan_workspace_size",
@@ -114,6 +114,7 @@ class WorkItem(ctypes.Structure):
 
 class Profile(ctypes.Structure):
     _fields_ = [
+        ("attention_ms", ctypes.c_double),
         ("grouped_ms", ctypes.c_double),
         ("suffix_ms", ctypes.c_double),
         ("merge_ms", ctypes.c_double),
@@ -171,7 +172,7 @@ def make_desc(
     cascade=True,
     k_strides=None,
     v_strides=None,
-    concurrent_passes=False,
+    separate_passes=False,
 ) -> AttnDesc:
     """Descriptor for the documented cache layout (default: dense pools)."""
     d = AttnDesc()
@@ -187,12 +188,12 @@ def make_desc(
         d.v_stride_block, d.v_stride_head = v_strides if v_strides else (num_kv_heads * vsh, vsh)
     d.v_aliases_k = int(bool(v_aliases_k))
     d.scale = float(scale)
-    d.flags = (0 if cascade else FCA_PLAN_DISABLE_CASCADE) | (FCA_PLAN_CONCURRENT_PASSES if concurrent_passes else 0)
+    d.flags = (0 if cascade else FCA_PLAN_DISABLE_CASCADE) | (FCA_PLAN_SEPARATE_PASSES if separate_passes else 0)
     d.reserved = 0
     return d
 
 
-def desc_from_shape(shape, num_blocks, cascade=True, concurrent_passes=False) -> AttnDesc:
+def desc_from_shape(shape, num_blocks, cascade=True, separate_passes=False) -> AttnDesc:
     return make_desc(
         shape.num_q_heads,
         shape.num_kv_heads,
@@ -203,7 +204,7 @@ def desc_from_shape(shape, num_blocks, cascade=True, concurrent_passes=False) ->
         shape.scale,
         v_aliases_k=shape.v_aliases_k,
         cascade=cascade,
-        concurrent_passes=concurrent_passes,
+        separate_passes=separate_passes,
     )
 
 

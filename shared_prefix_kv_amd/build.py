@@ -33,6 +33,9 @@ FLAGS = [
     "-target-feature",
     "-Xclang",
     "-packed-fp32-ops",
+    # The leading pointer arguments of the kernels arrive in scalar registers.
+    "-mllvm",
+    "-amdgpu-kernarg-preload-count=16",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

@@ -19,6 +19,7 @@
 #include <mutex>
 #include <new>
 #include <queue>
+#include <stdexcept>
 #include <string>
 #include <vector>
 
@@ -61,7 +62,7 @@ struct Tuning {
 
 Tuning tuning() {
   Tuning t;
-  t.wg_per_cu = env_int("FCA_TUNE_WG_PER_CU", 2);
+  t.wg_per_cu = env_int("FCA_TUNE_WG_PER_CU", 1);
   return t;
 }
 
@@ -78,7 +79,7 @@ fca_status check_desc(const fca_attn_desc* d, Kind* kind) {
                 d->num_q_heads, d->num_kv_heads);
   if (d->num_blocks <= 0) return fail(FCA_ERR_INVALID_ARG, "num_blocks must be positive");
   if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return fail(FCA_ERR_INVALID_ARG, "scale must be finite and > 0");
-  if (d->flags & ~(FCA_PLAN_DISABLE_CASCADE | FCA_PLAN_CONCURRENT_PASSES))
+  if (d->flags & ~(FCA_PLAN_DISABLE_CASCADE | FCA_PLAN_SEPARATE_PASSES))
     return fail(FCA_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
   const int r = d->num_q_heads / d->num_kv_heads;
   if (d->head_dim_qk == 128 && d->head_dim_v == 128 && d->block_size == 16 && !d->v_aliases_k) {
@@ -124,7 +125,13 @@ Layout make_layout(int B, int W) {
 
 // Plan-owned device buffer holding the schedule.
 struct SchedLayout {
-  size_t items_g, items_s, bins_g, bins_s, perm, req, grp, lanes, total;
+  size_t items, heads, perm, req, grp, lanes, total;
+};
+
+// One launch of the attention kernel: bins [bin0, bin0 + n_bins) of the
+// plan's bins, nct column tiles per wave.
+struct Launch {
+  int bin0, n_bins, nct;
 };
 
 DiscoveryPtrs discovery_ptrs(char* ws, const Layout& L, int B) {
@@ -142,26 +149,6 @@ DiscoveryPtrs discovery_ptrs(char* ws, const Layout& L, int B) {
   return p;
 }
 
-// One side stream per device for the grouped pass, default priority,
-// created on first use and kept for the life of the process.
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-hipStream_t g_side[kMaxDevices] = {};
-
-hipError_t side_stream(hipStream_t* out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  if (!g_side[dev]) {
-    e = hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking);
-    if (e != hipSuccess) return e;
-  }
-  *out = g_side[dev];
-  return hipSuccess;
-}
-
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
 
@@ -177,8 +164,10 @@ struct fca_plan_s {
   std::vector<fca_group_record> groups;
   std::vector<int32_t> members;   // ascending per group
   std::vector<int32_t> req3;      // per request: suffix_block_begin, suffix_tokens, deepest
-  std::vector<WorkItem> items_g, items_s;  // in bin order
-  std::vector<int32_t> bins_g, bins_s;     // bin offsets (n_bins + 1)
+  std::vector<WorkItem> items_g, items_s;  // host copies of each pass's items, in bin order
+  std::vector<WorkItem> items;             // what the device runs: all launches' items
+  std::vector<int32_t> bins;               // bin b runs items [bins[b], bins[b + 1])
+  std::vector<Launch> launches;            // one (both passes) or two (grouped, suffix)
   std::vector<int32_t> perm;
   std::vector<ReqMeta> req;
   std::vector<GroupMeta> grp;
@@ -187,17 +176,12 @@ struct fca_plan_s {
   // plan-owned device copy of the schedule
   char* sched = nullptr;
   SchedLayout SL{};
-  // concurrent passes
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
   // measurement hook
   bool profiling = false;
   std::vector<hipEvent_t> event_pool;
   std::vector<hipEvent_t> pending;  // kProfEvents per profiled call
   ~fca_plan_s() {
     if (sched) (void)hipFree(sched);
-    if (fork) (void)hipEventDestroy(fork);
-    if (join) (void)hipEventDestroy(join);
     for (hipEvent_t e : pending) (void)hipEventDestroy(e);
     for (hipEvent_t e : event_pool) (void)hipEventDestroy(e);
   }
@@ -363,18 +347,15 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
 
   // ---- Work items ----
   // A lane is one (unit, head block, column chunk) stream of stages: a unit
-  // is a group's prefix range or a request's suffix, a head block H KV heads,
-  // a column chunk up to 64 query rows, with H x (16-row column tiles) <= 4
-  // waves; one stage is 4 / H blocks of each of the H heads.  Each pass lays
-  // its lanes end to end and cuts the stream into one equal run of stages per
-  // persistent workgroup; a lane cut k times yields k + 1 items (token
-  // splits), each with its own partial rows.
+  // is a group's prefix range or a request's suffix, a head block H KV heads
+  // (H = 4, 2 or 1, dividing Hkv), a column chunk up to 64 query rows.  The 4
+  // waves of a workgroup take the H heads x 4/H block stripes of an item, so
+  // one stage is 4/H blocks of each head.  Each pass lays its lanes end to
+  // end and cuts the stream into one equal run of stages per persistent
+  // workgroup; a lane cut k times yields k + 1 items (token pieces).  Every
+  // piece has 4/H stripe splits, each with its own partial rows.
   const Tuning t = tuning();
-  auto heads_for = [&](int nct) {  // KV heads per item for nct column tiles
-    for (int H = kItemWaves / nct; H > 1; H /= 2)
-      if (hkv % H == 0) return H;
-    return 1;
-  };
+  const int H_all = hkv % 4 == 0 ? 4 : hkv % 2 == 0 ? 2 : 1;
   struct Lane {
     int request, member_off, ncols, tok0, tok_end;
     int kv0, H, col0, col1;
@@ -386,8 +367,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   auto add_lanes = [&](std::vector<Lane>& lanes, int tok0, int tok_end, int request, int member_off,
                        int ncols, int* H_out, int* chunks_out) {
     const int first = (int)lanes.size();
-    const int nct = (int)std::min<int64_t>(ceil_div(ncols, 16), kItemWaves);
-    const int H = heads_for(nct);
+    const int H = H_all;
     const int chunks = (int)ceil_div(ncols, kItemCols);
     const int bps = kItemWaves / H;
     const int64_t stages = ceil_div(ceil_div((int64_t)tok_end - tok0, bs), bps);
@@ -399,21 +379,30 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
     *chunks_out = chunks;
     return first;
   };
-  auto cut = [&](std::vector<Lane>& lanes, std::vector<WorkItem>& items, std::vector<int32_t>& bins,
-                 int64_t& row) {
+  // Cuts lanes [l0, l1) of `all` into one launch: its bins are appended to
+  // P->bins / P->items.  An item's part_base holds its piece index until the
+  // lane bases are known.
+  std::vector<Lane> all;
+  std::vector<int> item_lane;
+  P->items.clear();
+  P->bins.assign(1, 0);
+  P->launches.clear();
+  auto cut = [&](size_t l0, size_t l1) {
     int64_t W = 0;
-    for (const Lane& L : lanes) W += L.stages;
+    int nct = 1;
+    for (size_t k = l0; k < l1; ++k) {
+      W += all[k].stages;
+      nct = std::max(nct, (int)ceil_div(all[k].col1 - all[k].col0, 16));
+    }
     const int64_t nb = std::min<int64_t>(W, (int64_t)n_cu_ * t.wg_per_cu);
-    items.clear();
-    bins.assign(nb + 1, 0);
-    std::vector<int> lane_of;
-    size_t li = 0;
+    if (nb == 0) return;
+    P->launches.push_back(Launch{(int)P->bins.size() - 1, (int)nb, nct});
+    size_t li = l0;
     int64_t lpos = 0, pos = 0;
     for (int64_t b = 0; b < nb; ++b) {
-      bins[b] = (int32_t)items.size();
       const int64_t end = (b + 1) * W / nb;
       while (pos < end) {
-        Lane& L = lanes[li];
+        Lane& L = all[li];
         const int64_t take = std::min(L.stages - lpos, end - pos);
         const int64_t stok = (int64_t)(kItemWaves / L.H) * bs;  // tokens per stage
         WorkItem it{};
@@ -426,9 +415,9 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
         it.ncols = L.ncols;
         it.col0 = L.col0;
         it.col1 = L.col1;
-        it.part_base = L.splits++;  // split index until the lane bases are known
-        items.push_back(it);
-        lane_of.push_back((int)li);
+        it.part_base = L.splits++;
+        P->items.push_back(it);
+        item_lane.push_back((int)li);
         pos += take;
         lpos += take;
         if (lpos == L.stages) {
@@ -436,31 +425,23 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
           lpos = 0;
         }
       }
-    }
-    bins[nb] = (int32_t)items.size();
-    for (Lane& L : lanes) {
-      L.base = row;
-      row += (int64_t)L.splits * L.H * (L.col1 - L.col0);
-    }
-    for (size_t k = 0; k < items.size(); ++k) {
-      const Lane& L = lanes[lane_of[k]];
-      items[k].part_base = (int32_t)std::min<int64_t>(L.base + (int64_t)items[k].part_base * L.H * (L.col1 - L.col0),
-                                                      INT32_MAX);
+      P->bins.push_back((int32_t)P->items.size());
+      if (P->bins.back() == P->bins[P->bins.size() - 2]) throw std::logic_error("empty bin");
     }
   };
 
   int64_t row = 0;
-  std::vector<Lane> glanes, slanes;
   for (int c = 0; c < G; ++c) {
     const fca_group_record& gr = P->groups[c];
     GroupMeta& gm = P->grp[c];
     gm.parent = gr.parent;
     gm.r0 = r0[c];
     gm.ncols = count[c] * r;
-    gm.lane0 = add_lanes(glanes, gr.block_begin * bs, gr.block_end * bs, P->perm[r0[c]], r0[c], count[c] * r,
+    gm.lane0 = add_lanes(all, gr.block_begin * bs, gr.block_end * bs, P->perm[r0[c]], r0[c], count[c] * r,
                          &gm.H, &gm.chunks);
     unique += (int64_t)(gr.block_end - gr.block_begin) * bs;
   }
+  const size_t n_glanes = all.size();
   P->req.assign(B, ReqMeta{});
   for (int i = 0; i < B; ++i) {
     ReqMeta& rq = P->req[i];
@@ -470,18 +451,32 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
     rq.sfx_H = 1;
     if (sfx_tokens[i] > 0) {
       int chunks;
-      rq.sfx_lane = add_lanes(slanes, P->req3[3 * i] * bs, lens[i], i, -1, r, &rq.sfx_H, &chunks);
+      rq.sfx_lane = add_lanes(all, P->req3[3 * i] * bs, lens[i], i, -1, r, &rq.sfx_H, &chunks);
     }
   }
-  cut(glanes, P->items_g, P->bins_g, row);
-  cut(slanes, P->items_s, P->bins_s, row);
+  if (P->desc.flags & FCA_PLAN_SEPARATE_PASSES) {
+    cut(0, n_glanes);
+    cut(n_glanes, all.size());
+  } else {
+    cut(0, all.size());
+  }
+  for (Lane& L : all) {
+    L.splits *= kItemWaves / L.H;  // stripe splits of every piece
+    L.base = row;
+    row += (int64_t)L.splits * L.H * (L.col1 - L.col0);
+  }
   if (row > INT32_MAX) return fail(FCA_ERR_UNSUPPORTED, "too many partial rows");
+  P->items_g.clear();
+  P->items_s.clear();
+  for (size_t k = 0; k < P->items.size(); ++k) {
+    WorkItem& it = P->items[k];
+    const Lane& L = all[item_lane[k]];
+    it.part_base = (int32_t)(L.base + (int64_t)it.part_base * kItemWaves * (L.col1 - L.col0));
+    (it.member_off >= 0 ? P->items_g : P->items_s).push_back(it);
+  }
   P->lanes.clear();
-  for (const std::vector<Lane>* v : {&glanes, &slanes})
-    for (const Lane& L : *v)
-      P->lanes.push_back(LaneMeta{(int32_t)L.base, L.splits, L.kv0, L.H, L.col0, L.col1 - L.col0, 0, 0});
-  for (int i = 0; i < B; ++i)
-    if (P->req[i].sfx_lane >= 0) P->req[i].sfx_lane += (int)glanes.size();
+  for (const Lane& L : all)
+    P->lanes.push_back(LaneMeta{(int32_t)L.base, L.splits, L.kv0, L.H, L.col0, L.col1 - L.col0, 0, 0});
 
   // Merge sources: one per (request, query head, token split on its path).
   int64_t sources = 0;
@@ -579,10 +574,16 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
       off = align_up(off + std::max<size_t>(bytes, 1));
       return at;
     };
-    S.items_g = place(P->items_g.size() * sizeof(WorkItem));
-    S.items_s = place(P->items_s.size() * sizeof(WorkItem));
-    S.bins_g = place(P->bins_g.size() * 4);
-    S.bins_s = place(P->bins_s.size() * 4);
+    std::vector<BinHead> heads(P->bins.size() - 1);
+    for (size_t b = 0; b + 1 < P->bins.size(); ++b) {
+      BinHead& h = heads[b];
+      h = BinHead{};
+      h.i_begin = P->bins[b];
+      h.i_end = P->bins[b + 1];
+      h.first = P->items[h.i_begin];
+    }
+    S.items = place(P->items.size() * sizeof(WorkItem));
+    S.heads = place(heads.size() * sizeof(BinHead));
     S.perm = place(P->perm.size() * 4);
     S.req = place(P->req.size() * sizeof(ReqMeta));
     S.grp = place(P->grp.size() * sizeof(GroupMeta));
@@ -598,10 +599,8 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
       const void* src;
       size_t off, bytes;
     } ups[] = {
-        {P->items_g.data(), S.items_g, P->items_g.size() * sizeof(WorkItem)},
-        {P->items_s.data(), S.items_s, P->items_s.size() * sizeof(WorkItem)},
-        {P->bins_g.data(), S.bins_g, P->bins_g.size() * 4},
-        {P->bins_s.data(), S.bins_s, P->bins_s.size() * 4},
+        {P->items.data(), S.items, P->items.size() * sizeof(WorkItem)},
+        {heads.data(), S.heads, heads.size() * sizeof(BinHead)},
         {P->perm.data(), S.perm, P->perm.size() * 4},
         {P->req.data(), S.req, P->req.size() * sizeof(ReqMeta)},
         {P->grp.data(), S.grp, P->grp.size() * sizeof(GroupMeta)},
@@ -615,20 +614,20 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
         return hip_fail(e, "schedule upload");
       }
     }
-    if ((desc->flags & FCA_PLAN_CONCURRENT_PASSES) && !P->items_g.empty() && !P->items_s.empty()) {
-      e = side_stream(&P->side);
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&P->fork, hipEventDisableTiming);
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&P->join, hipEventDisableTiming);
-      if (e != hipSuccess) {
-        delete P;
-        return hip_fail(e, "side stream / events");
-      }
+    e = launch_bin_heads(reinterpret_cast<BinHead*>(P->sched + S.heads), (int)heads.size(),
+                         reinterpret_cast<const int32_t*>(P->ws + P->L.bt), P->W, P->desc.block_size, s);
+    if (e != hipSuccess) {
+      delete P;
+      return hip_fail(e, "bin heads");
     }
     *out = P;
     return FCA_OK;
   } catch (const std::bad_alloc&) {
     delete P;
     return fail(FCA_ERR_HOST_ALLOC, "host allocation failed");
+  } catch (const std::logic_error& x) {
+    delete P;
+    return fail(FCA_ERR_HIP, "internal planner error: %s", x.what());
   } catch (...) {
     delete P;
     return fail(FCA_ERR_HOST_ALLOC, "unexpected host exception");
@@ -684,6 +683,8 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   gp.part = part;
   hipError_t e;
   fca_plan_s* M = plan;
+  // Profiling events: start, then begin/end of each attention launch (up to
+  // two), then begin/end of the merge.
   constexpr int kProf = 7;
   hipEvent_t ev[kProf] = {};
   if (P->profiling) {
@@ -698,34 +699,24 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
       M->pending.push_back(ev[j]);
     }
   }
-  const bool overlap = P->side != nullptr;
-  hipStream_t sg = overlap ? P->side : s;
-  auto mark = [&](int j, hipStream_t st) -> hipError_t { return ev[j] ? hipEventRecord(ev[j], st) : hipSuccess; };
+  auto mark = [&](int j) -> hipError_t { return ev[j] ? hipEventRecord(ev[j], s) : hipSuccess; };
 #define FCA_TRY(expr, what)             \
   do {                                  \
     e = (expr);                         \
     if (e != hipSuccess) return hip_fail(e, what); \
   } while (0)
-  FCA_TRY(mark(0, s), "event record");
-  if (overlap) {
-    FCA_TRY(hipEventRecord(P->fork, s), "fork record");
-    FCA_TRY(hipStreamWaitEvent(sg, P->fork, 0), "fork wait");
+  FCA_TRY(mark(0), "event record");
+  gp.items = reinterpret_cast<const WorkItem*>(P->sched + S.items);
+  for (int k = 0; k < 2; ++k) {
+    FCA_TRY(mark(1 + 2 * k), "event record");
+    if (k < (int)P->launches.size()) {
+      const Launch& ln = P->launches[k];
+      gp.bins = reinterpret_cast<const BinHead*>(P->sched + S.heads) + ln.bin0;
+      FCA_TRY(launch_attention(gp, ln.n_bins, ln.nct, s), "attention launch");
+    }
+    FCA_TRY(mark(2 + 2 * k), "event record");
   }
-  FCA_TRY(mark(1, sg), "event record");
-  gp.items = reinterpret_cast<const WorkItem*>(P->sched + S.items_g);
-  gp.bin_off = reinterpret_cast<const int32_t*>(P->sched + S.bins_g);
-  FCA_TRY(launch_gqa_partial(0, gp, (int)P->bins_g.size() - 1, sg), "grouped pass launch");
-  FCA_TRY(mark(2, sg), "event record");
-  FCA_TRY(mark(3, s), "event record");
-  gp.items = reinterpret_cast<const WorkItem*>(P->sched + S.items_s);
-  gp.bin_off = reinterpret_cast<const int32_t*>(P->sched + S.bins_s);
-  FCA_TRY(launch_gqa_partial(1, gp, (int)P->bins_s.size() - 1, s), "suffix pass launch");
-  FCA_TRY(mark(4, s), "event record");
-  if (overlap) {
-    FCA_TRY(hipEventRecord(P->join, sg), "join record");
-    FCA_TRY(hipStreamWaitEvent(s, P->join, 0), "join wait");
-  }
-  FCA_TRY(mark(5, s), "event record");
+  FCA_TRY(mark(5), "event record");
 
   MergeParams mp;
   mp.req = reinterpret_cast<const ReqMeta*>(P->sched + S.req);
@@ -740,7 +731,7 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   mp.out = out_dev;
   mp.lse = lse_dev;
   FCA_TRY(launch_merge(mp, s), "merge launch");
-  FCA_TRY(mark(6, s), "event record");
+  FCA_TRY(mark(6), "event record");
 #undef FCA_TRY
   return FCA_OK;
 }
@@ -755,17 +746,22 @@ fca_status fca_profile_read(fca_plan plan, fca_profile* out) {
   if (!plan || !out) return fail(FCA_ERR_INVALID_ARG, "plan / out is NULL");
   fca_profile acc{};
   hipError_t err = hipSuccess;
-  // events per call: start, grouped begin/end, suffix begin/end, merge begin/end
+  // events per call: start, launch 1 begin/end, launch 2 begin/end, merge begin/end
+  const bool separate = plan->launches.size() == 2;
   for (size_t c = 0; c + 7 <= plan->pending.size(); c += 7) {
     hipEvent_t* ev = plan->pending.data() + c;
-    float t[4] = {0, 0, 0, 0};
+    float t[5] = {0, 0, 0, 0, 0};
     if (err == hipSuccess) err = hipEventSynchronize(ev[6]);
     if (err == hipSuccess) err = hipEventElapsedTime(&t[0], ev[1], ev[2]);
     if (err == hipSuccess) err = hipEventElapsedTime(&t[1], ev[3], ev[4]);
     if (err == hipSuccess) err = hipEventElapsedTime(&t[2], ev[5], ev[6]);
     if (err == hipSuccess) err = hipEventElapsedTime(&t[3], ev[0], ev[6]);
-    acc.grouped_ms += t[0];
-    acc.suffix_ms += t[1];
+    if (err == hipSuccess) err = hipEventElapsedTime(&t[4], ev[1], ev[4]);
+    acc.attention_ms += t[4];
+    if (separate) {
+      acc.grouped_ms += t[0];
+      acc.suffix_ms += t[1];
+    }
     acc.merge_ms += t[2];
     acc.decode_ms += t[3];
     acc.calls += 1;

@@ -6,30 +6,29 @@
 // step 2: one pass over each group's shared prefix blocks, read once per
 // group, and one pass per request over its own suffix blocks).
 //
-// Work item = (token range, H consecutive KV heads, up to 16 * n_ct query
-// rows) with H * n_ct <= 4.  Query rows ("columns") of a grouped item are
-// members x (Hq/Hkv) rows that all read the same KV tiles, so QK^T and PV are
-// real matrix products and run on bf16 MFMA.  A per-request item has
-// Hq/Hkv <= 16 rows per head and takes up to 4 heads of one request.
+// Work item = (token range, H consecutive KV heads, up to 64 query rows).
+// Query rows ("columns") of a grouped item are members x (Hq/Hkv) rows that
+// all read the same KV tiles, so QK^T and PV are real matrix products and run
+// on bf16 MFMA; a per-request item has the Hq/Hkv <= 16 rows of each head.
 //
-// Persistent workgroups of 4 waves: the planner packs items into one bin per
-// workgroup (longest first, least-loaded bin); a workgroup walks its bin as
-// one stream of stages, so the copy of the next stage -- possibly the first
-// stage of the next item -- is always in flight while the current one is
-// computed.
+// Persistent workgroups of 4 independent waves, one per SIMD: the planner
+// cuts each pass into one equal run of work per workgroup (its bin).  In an
+// item, wave w takes head kv_head + w % H and block stripe w / H: blocks
+// stripe, stripe + 4/H, ... of the range, for all of the item's columns.
+// Each stripe writes its own partial triples (the merge folds them like
+// token splits), so waves never wait for one another: no barrier anywhere.
 //
-// Stage = 4 (head, block) tiles of the current item: tile t is block
-// (4/H)*s + t % (4/H) of head h0 + t / (4/H).  Wave t copies tile t straight
-// from HBM into LDS with global_load_lds_dwordx4 (16 bytes per lane, 1 KiB
-// contiguous per instruction: the K tile then the V tile, 4 KiB each), so
-// every KV byte crosses the vector-memory front end once per workgroup.  Two
-// 32 KiB stage slots alternate; one barrier per stage hands a landed stage to
-// all waves and frees the other slot for the next copy.  Block IDs and item
-// descriptors come in through scalar loads.
-//
-// Wave w < H * n_ct owns head h0 + w / n_ct and column tile w % n_ct and
-// computes the 4/H blocks of its head in each stage; its columns' triples are
-// written straight from registers when the item ends (no cross-wave fold).
+// Each wave streams its (block, head) tiles through its own ring of P LDS
+// slots with global_load_lds_dwordx4 (16 bytes per lane, 1 KiB contiguous per
+// instruction: K tile then V tile, 4 KiB each), P - 1 tiles ahead of the
+// math, and waits with explicit vmcnt counts.  Every tile copy is exactly 8
+// instructions; any other vector-memory operation (Q copies, partial stores)
+// only adds to the count of operations issued after a tile, so waiting for
+// "8 x tiles issued after it" is always a lower bound and correct.  The Q
+// rows of the next item the wave computes are copied into a per-wave LDS
+// slot while the current item begins, so beginning an item never waits for
+// memory issued after it.  Block IDs and item descriptors come in through
+// scalar loads, a step ahead.
 //
 // Math of one 16-token block of one wave, operands read from LDS:
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: lane (g, c) reads d-chunk
@@ -54,13 +53,17 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(4))) const int32_t cint32;
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kD = 128;                              // head dim (keys and values)
-constexpr int kBS = 16;                              // tokens per cache block
-constexpr int kWaves = 4;                            // waves per workgroup = tiles per stage
-constexpr int kTileBytes = kBS * kD * 2;             // one (block, head) K or V tile: 4 KiB
-constexpr int kSlotBytes = kWaves * 2 * kTileBytes;  // 32 KiB per stage
+constexpr int kD = 128;                   // head dim (keys and values)
+constexpr int kBS = 16;                   // tokens per cache block
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kTileBytes = kBS * kD * 2;  // one (block, head) K or V tile: 4 KiB
+constexpr int kSlotBytes = 2 * kTileBytes;
+constexpr int kTileOps = 2 * kTileBytes / 1024;  // vector-memory instructions per tile copy
+constexpr int kQRowBytes = kD * 2;
 
 // x op x' where x' is the value of lane ^ 16 (resp. ^ 32).
 __device__ __forceinline__ float xmax16(float x) {
@@ -80,9 +83,23 @@ __device__ __forceinline__ float xsum32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// s_waitcnt until no vector-memory operation of this wave is outstanding
-// (gfx9 encoding: vmcnt 0, expcnt and lgkmcnt at their no-wait maxima).
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8; a field at its maximum does not wait).
+constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kLgkmWait0 = 15 | (7 << 4) | (3 << 14);
+
+// Wait until at most 8 * n vector-memory operations of this wave are in
+// flight, n >= 0 (n above 3 waits as for 3, which is longer, still correct).
+__device__ __forceinline__ void wait_tiles_after(int n) {
+  if (n >= 3)
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(3 * kTileOps));
+  else if (n == 2)
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * kTileOps));
+  else if (n == 1)
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(kTileOps));
+  else
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+}
 
 // Work item i read through the scalar path.
 __device__ __forceinline__ WorkItem load_item(cint32* items, int i) {
@@ -103,276 +120,330 @@ __device__ __forceinline__ WorkItem load_item(cint32* items, int i) {
   return w;
 }
 
-__device__ __forceinline__ int item_blocks(const WorkItem& it) { return (it.tok_end - it.tok_begin + kBS - 1) / kBS; }
+// This wave's share of an item: head kv_head + hh, blocks stripe,
+// stripe + S, ... (S = 4 / kv_heads stripes, kv_heads in {1, 2, 4}).
+struct Role {
+  int lgh;     // log2 kv_heads
+  int hh;      // head within the item
+  int stripe;  // block stripe
+  int nblk;    // blocks of the stripe
+};
 
-// log2 of the blocks per stage of an item: 4 / kv_heads with kv_heads in {1, 2, 4}.
-__device__ __forceinline__ int item_lg_bps(const WorkItem& it) { return it.kv_heads == 1 ? 2 : it.kv_heads == 2 ? 1 : 0; }
-
-__device__ __forceinline__ int item_stages(const WorkItem& it) {
-  const int lg = item_lg_bps(it);
-  return (item_blocks(it) + (1 << lg) - 1) >> lg;
+__device__ __forceinline__ Role role_of(const WorkItem& it, int wave) {
+  Role r;
+  r.lgh = it.kv_heads == 4 ? 2 : it.kv_heads == 2 ? 1 : 0;
+  r.hh = wave & (it.kv_heads - 1);
+  r.stripe = wave >> r.lgh;
+  const int lgs = 2 - r.lgh;
+  const int nb = (it.tok_end - it.tok_begin + kBS - 1) / kBS;
+  r.nblk = nb > r.stripe ? ((nb - 1 - r.stripe) >> lgs) + 1 : 0;
+  return r;
 }
 
-__device__ __forceinline__ void partial_kernel_body(const GqaParams& P) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kSlotBytes];
+// Arguments the first tile copy needs, passed ahead of the parameter block
+// so that they arrive preloaded in scalar registers.
+struct CopyArgs {
+  const BinHead* bins;
+  const WorkItem* items;
+  const char* k;
+  const char* v;
+  int64_t ksb, ksh, vsb, vsh;  // strides in elements: key block / head, value block / head
+};
+
+template <int NCT, int P>
+__device__ __forceinline__ void stream_body(const CopyArgs& ca, const GqaParams& Pm) {
+  constexpr int kQBytes = NCT * 16 * kQRowBytes;
+  constexpr int kWaveBytes = P * kSlotBytes + kQBytes;
+  __shared__ __attribute__((aligned(1024))) char lds[kWaves * kWaveBytes];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int c16 = lane & 15;
   const float NEG_INF = -INFINITY;
-  const float sc = P.scale_log2;
+  const float sc = Pm.scale_log2;
+  char* ring = lds + wave * kWaveBytes;
+  char* qlds = ring + P * kSlotBytes;
 
-  cint32* bin_off = (cint32*)(P.bin_off);
-  cint32* items = (cint32*)(P.items);
-  cint32* bt = (cint32*)(P.bt);
-  cint32* perm = (cint32*)(P.perm);
-  const int i_begin = bin_off[blockIdx.x];
-  const int i_end = bin_off[blockIdx.x + 1];
-  if (i_begin >= i_end) return;
+  // The bin head: item range, first item, first block IDs (one line).
+  cint32* head = (cint32*)(ca.bins + blockIdx.x);
+  cint32* items = (cint32*)(ca.items);
+  cint32* bt = (cint32*)(Pm.bt);
+  cint32* perm = (cint32*)(Pm.perm);
+  // Every bin holds at least one item (the planner never makes an empty
+  // one), so nothing waits for the range before the first copy.
+  typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 h8 = *(__attribute__((address_space(4))) const i32x8*)head;  // one scalar load
+  const int i_begin = h8[0];
+  const int i_end = h8[1];
 
-  const char* kpool = static_cast<const char*>(P.k);
-  const char* vpool = static_cast<const char*>(P.v);
-  const __bf16* qbase = static_cast<const __bf16*>(P.q);
+  const char* kpool = ca.k;
+  const char* vpool = ca.v;
+  const char* qbase = static_cast<const char*>(Pm.q);
 
-  // Q^T operand of this wave for an item: column tile w % n_ct of head
-  // h0 + w / n_ct (d-chunk ks*32 + 8*g).  The Q of item k + 1 is loaded into
-  // qn while item k is begun (right after its first stage copy is issued)
-  // and taken into the MFMA operand when item k + 1 begins, after a stage
-  // wait; one buffer suffices however short the items are.
-  bf16x8 qn[4];
-  auto load_q = [&](const WorkItem& it) {
-    const int nct = (it.col1 - it.col0 + 15) >> 4;
-    const int h = wave / nct;
-    const int cb = it.col0 + 16 * (wave - h * nct);  // first column of this wave's tile
-    const int col = cb + c16;
-    int member = it.request;
-    if (it.member_off >= 0 && cb < it.col1) {
-      // The tile's columns belong to members (cb / r) .. (last / r); their
-      // request indices come in through scalar loads, one select per member.
-      const int last = min(cb + 15, it.col1 - 1);
-      const int m0 = cb / P.r;
-      const int mine = min(col, last) / P.r - m0;
-      for (int k = 0; k <= last / P.r - m0; ++k) {
-        const int pk = perm[it.member_off + m0 + k];
-        member = mine == k ? pk : member;
-      }
-    }
-    const bool use = h < it.kv_heads && col < it.col1;
-    const int qh = (it.kv_head + h) * P.r + col % P.r;
-    // Idle lanes read row 0 of the item (always in bounds) and are zeroed
-    // when the operand is taken.
-    const __bf16* qp =
-        qbase + ((int64_t)(use ? member : it.request) * P.Hq + (use ? qh : it.kv_head * P.r)) * kD + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qn[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
+  int n_iss = 0;  // tiles issued by this wave
+  int n_cmp = 0;  // tiles computed
+
+  // ---- copy cursor: item di, k-th block of this wave's stripe ----
+  int di = i_begin, dk = 0;
+  WorkItem dit = load_item(head + 8, 0);
+  Role dr = role_of(dit, wave);
+  // On to the next item with blocks for this wave.  Its descriptor load is
+  // the one round trip of an item change on the copy side; P - 1 tiles are
+  // in flight meanwhile.
+  auto copy_next_item = [&]() {
+    do {
+      dk = 0;
+      if (++di >= i_end) return;
+      dit = load_item(items, di);
+      dr = role_of(dit, wave);
+    } while (dr.nblk == 0);
   };
-
-  // ---- copy cursor: item di, stage ds ----
-  // The descriptor of item di + 1 and the block ID of this wave's next tile
-  // are loaded one step ahead, so issuing a stage waits on nothing.
-  int di = i_begin, ds = 0;
-  WorkItem dit = load_item(items, di);
-  WorkItem dnx = dit;
-  if (di + 1 < i_end) dnx = load_item(items, di + 1);
-  int dnst, dlg, dsub, dhead, dnblk;
-  auto copy_item = [&]() {  // per-item constants of the copy cursor
-    dnst = item_stages(dit);
-    dlg = item_lg_bps(dit);
-    dsub = wave & ((1 << dlg) - 1);
-    dhead = dit.kv_head + (wave >> dlg);
-    dnblk = item_blocks(dit);
-  };
-  copy_item();
-  // Tiles past the item copy block 0, which always exists; the math never
-  // reads them.
   auto tile_id = [&]() {
-    const int b = (ds << dlg) + dsub;
-    return b < dnblk ? bt[(int64_t)dit.request * P.W + dit.tok_begin / kBS + b] : 0;
+    const int b = dr.stripe + (dk << (2 - dr.lgh));
+    return bt[(int64_t)dit.request * Pm.W + dit.tok_begin / kBS + b];
   };
-  int cur_id = tile_id();
+  // Block IDs of the first item's blocks 0..3, loaded with the rest of the
+  // head; this wave's first tile is block `stripe`.
+  const int id0 = h8[2], id1 = h8[3], id2 = h8[4], id3 = h8[5];
+  int cur_id;
+  if (dr.nblk > 0) {
+    cur_id = dr.stripe == 0 ? id0 : dr.stripe == 1 ? id1 : dr.stripe == 2 ? id2 : id3;
+  } else {
+    copy_next_item();
+    cur_id = di < i_end ? tile_id() : 0;
+  }
 
-  // Copy stage (di, ds) into a slot: this wave's tile is block
-  // bps*ds + wave % bps of head h0 + wave / bps.
-  auto issue = [&](int slot) {
-    const char* ksrc =
-        kpool + ((int64_t)cur_id * P.k_stride_block + (int64_t)dhead * P.k_stride_head) * 2 + lane * 16;
-    const char* vsrc =
-        vpool + ((int64_t)cur_id * P.v_stride_block + (int64_t)dhead * P.v_stride_head) * 2 + lane * 16;
-    char* dst = lds + slot * kSlotBytes + wave * 2 * kTileBytes;
+  // Copy the next tile of the stream into ring slot n_iss % P.
+  auto issue_next = [&]() {
+    if (di >= i_end) return;
+    const int head = dit.kv_head + dr.hh;
+    const char* ksrc = kpool + ((int64_t)cur_id * ca.ksb + (int64_t)head * ca.ksh) * 2 + lane * 16;
+    const char* vsrc = vpool + ((int64_t)cur_id * ca.vsb + (int64_t)head * ca.vsh) * 2 + lane * 16;
+    char* dst = ring + (n_iss % P) * kSlotBytes;
 #pragma unroll
     for (int i = 0; i < kTileBytes / 1024; ++i)
-      __builtin_amdgcn_global_load_lds(ksrc + i * 1024, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds(ksrc + i * 1024, (lds_void*)(dst + i * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < kTileBytes / 1024; ++i)
-      __builtin_amdgcn_global_load_lds(vsrc + i * 1024,
-                                       (__attribute__((address_space(3))) void*)(dst + kTileBytes + i * 1024), 16, 0,
-                                       0);
-    if (++ds == dnst) {  // on to the next item: its descriptor, its Q, the one after
-      ds = 0;
-      if (++di < i_end) {
-        dit = dnx;
-        copy_item();
-        if (di + 1 < i_end) dnx = load_item(items, di + 1);
-      }
-    }
+      __builtin_amdgcn_global_load_lds(vsrc + i * 1024, (lds_void*)(dst + kTileBytes + i * 1024), 16, 0, 0);
+    ++n_iss;
+    if (++dk == dr.nblk) copy_next_item();
     if (di < i_end) cur_id = tile_id();
   };
 
-  // ---- compute cursor: item ci, stage cs ----
-  WorkItem cit = dit, cnx = dnx;
-  int ci = i_begin, cs = 0, cnst = dnst;
-  int hh = 0, ct = 0, lg = 0;
-  bool active = false;
-  bool q_pending = false;  // qn is free and the next item's Q is still to be loaded
-  bf16x8 qb[4];
-  f32x4 o[8];
-  float mrow = NEG_INF, lsum = 0.f;
-
-  auto begin_item = [&]() {
-    const int nct = (cit.col1 - cit.col0 + 15) >> 4;
-    lg = item_lg_bps(cit);
-    hh = wave / nct;
-    ct = wave - hh * nct;
-    active = hh < cit.kv_heads;
-    const bool use = active && cit.col0 + 16 * ct + c16 < cit.col1;
+  // Copy the Q rows of item `it` for this wave's head into the Q slot:
+  // row n (n < 16 * NCT) is query row col0 + n of the item; rows past col1
+  // repeat row col0 and are zeroed when read.
+  auto issue_q = [&](const WorkItem& it, const Role& r) {
+    const int head_q0 = (it.kv_head + r.hh) * Pm.r;  // first q head of the KV head
+    // Request of every row: for a grouped item all scalar loads go out
+    // before the first is used (one round trip).
+    int req[NCT * 16];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[ks] = use ? qn[ks] : bf16x8{};
-    if (ci + 1 < i_end) {
-      if (ci > i_begin) cnx = load_item(items, ci + 1);
-      q_pending = true;
+    for (int n = 0; n < NCT * 16; ++n) {
+      const int col = it.col0 + n < it.col1 ? it.col0 + n : it.col0;
+      req[n] = it.member_off >= 0 ? perm[it.member_off + col / Pm.r] : it.request;
     }
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mrow = NEG_INF;
-    lsum = 0.f;
+    for (int i = 0; i < NCT * 4; ++i) {
+      // Four rows per instruction, 16 lanes (256 bytes) per row.
+      const int x = lane >> 4;
+      const int rq = x == 0 ? req[4 * i] : x == 1 ? req[4 * i + 1] : x == 2 ? req[4 * i + 2] : req[4 * i + 3];
+      int col = it.col0 + 4 * i + x;
+      col = col < it.col1 ? col : it.col0;
+      const int hq = head_q0 + (it.member_off >= 0 ? col % Pm.r : col);
+      const char* src = qbase + ((int64_t)rq * Pm.Hq + hq) * kQRowBytes + c16 * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(qlds + i * 1024), 16, 0, 0);
+    }
   };
 
-  // One 16-token block from LDS: S^T = K Q^T (16x16x32, K = head dim),
-  // online softmax, O^T += V^T P^T (16x16x16, K = the block's tokens).  All
-  // twelve LDS reads are issued first; V is consumed after the softmax.
-  auto compute_block = [&](const char* kt, int t0) {
-    const char* vt = kt + kTileBytes;
-    bf16x8 ka[4];
-    bf16x4 va[8];
+  // ---- compute cursor ----
+  // The first tile, the Q of the first item this wave computes, then the
+  // next P - 2 tiles.
+  int q_iss = 0;  // n_iss when the pending Q copy was issued
+  const WorkItem qit = dit;
+  const Role qr = dr;
+  const bool have_q = di < i_end;
+  issue_next();
+  if (have_q) {
+    issue_q(qit, qr);
+    q_iss = n_iss;
+  }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(kt + ((4 * ks + g) * kBS + c16) * 16);
+  for (int p = 1; p < P - 1; ++p) issue_next();
+
+  f32x4 o[NCT][8];
+  float mrow[NCT], lsum[NCT];
+  bf16x8 qb[NCT][4];
+
+  WorkItem cnx = load_item(head + 8, 0);
+  for (int ci = i_begin; ci < i_end; ++ci) {
+    const WorkItem cit = cnx;
+    if (ci + 1 < i_end) cnx = load_item(items, ci + 1);
+    const Role cr = role_of(cit, wave);
+    const int ccols = cit.col1 - cit.col0;
+    const int64_t row0 = (int64_t)cit.part_base + (int64_t)(cr.stripe << cr.lgh) * ccols + (int64_t)cr.hh * ccols;
+
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) va[dt] = *reinterpret_cast<const bf16x4*>(vt + ((16 * dt + c16) * kBS + 4 * g) * 2);
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < NCT; ++ct) {
+      mrow[ct] = NEG_INF;
+      lsum[ct] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[ks], s, 0, 0, 0);
-    // Tokens at or past the end of the range: score -inf, value zeroed
-    // (the tail of a block may hold NaN).
-    const int nvalid = cit.tok_end - t0 - 4 * g;  // valid tokens of this lane's 4
-    if (t0 + kBS > cit.tok_end) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s[j] = j < nvalid ? s[j] : NEG_INF;
+      for (int dt = 0; dt < 8; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = xmax32(xmax16(mx));
-    const float mnew = fmaxf(mrow, mx * sc);
-    if (__builtin_amdgcn_ballot_w64(mnew > mrow)) {  // some column's max grew
-      const float alpha = exp2f(mrow - mnew);           // 0 on the first block
-      lsum *= alpha;
+
+    if (cr.nblk > 0) {
+      // Q of this item has landed once every tile issued before its copy
+      // has; take it into registers, then start the copy of the next item's.
+      wait_tiles_after(n_iss - q_iss);
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-      mrow = mnew;
-    }
-    bf16x4 pb;
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int col = 16 * ct + c16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float p = exp2f(fmaf(s[j], sc, -mrow));
-      pb[j] = (__bf16)p;
-      lsum += p;
-    }
-    if (t0 + kBS > cit.tok_end) {
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 keep = {(nvalid > 0 ? 0xffffu : 0u) | (nvalid > 1 ? 0xffff0000u : 0u),
-                          (nvalid > 2 ? 0xffffu : 0u) | (nvalid > 3 ? 0xffff0000u : 0u)};
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(qlds + col * kQRowBytes + (32 * ks + 8 * g) * 2);
+          qb[ct][ks] = col < ccols ? v : bf16x8{};
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kLgkmWait0);  // Q slot read before it is overwritten
+      for (int nj = ci + 1; nj < i_end; ++nj) {
+        const WorkItem nit = nj == ci + 1 ? cnx : load_item(items, nj);
+        const Role nr = role_of(nit, wave);
+        if (nr.nblk > 0) {
+          issue_q(nit, nr);
+          q_iss = n_iss;
+          break;
+        }
+      }
+
+      for (int k = 0; k < cr.nblk; ++k) {
+        issue_next();
+        wait_tiles_after(n_iss - n_cmp - 1);
+        const char* kt = ring + (n_cmp % P) * kSlotBytes;
+        const char* vt = kt + kTileBytes;
+        ++n_cmp;
+        const int t0 = cit.tok_begin + (cr.stripe + (k << (2 - cr.lgh))) * kBS;
+
+        // All twelve LDS reads first; V is consumed after the softmax.
+        bf16x8 ka[4];
+        bf16x4 va[8];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        u32x2 w = __builtin_bit_cast(u32x2, va[dt]);
-        w &= keep;
-        va[dt] = __builtin_bit_cast(bf16x4, w);
+        for (int ks = 0; ks < 4; ++ks)
+          ka[ks] = *reinterpret_cast<const bf16x8*>(kt + ((4 * ks + g) * kBS + c16) * 16);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          va[dt] = *reinterpret_cast<const bf16x4*>(vt + ((16 * dt + c16) * kBS + 4 * g) * 2);
+        f32x4 s[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          s[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            s[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[ct][ks], s[ct], 0, 0, 0);
+        }
+        // Tokens at or past the end of the range: score -inf, value zeroed
+        // (the tail of a block may hold NaN).
+        const int nvalid = cit.tok_end - t0 - 4 * g;  // valid tokens of this lane's 4
+        const bool partial = t0 + kBS > cit.tok_end;
+        if (partial) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[ct][j] = j < nvalid ? s[ct][j] : NEG_INF;
+        }
+        bf16x4 pb[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          float mx = fmaxf(fmaxf(s[ct][0], s[ct][1]), fmaxf(s[ct][2], s[ct][3]));
+          mx = xmax32(xmax16(mx));
+          const float mnew = fmaxf(mrow[ct], mx * sc);
+          if (__builtin_amdgcn_ballot_w64(mnew > mrow[ct])) {  // some column's max grew
+            const float alpha = exp2f(mrow[ct] - mnew);        // 0 on the first block
+            lsum[ct] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) o[ct][dt] *= alpha;
+            mrow[ct] = mnew;
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p = exp2f(fmaf(s[ct][j], sc, -mrow[ct]));
+            pb[ct][j] = (__bf16)p;
+            lsum[ct] += p;
+          }
+        }
+        if (partial) {
+          const u32x2 keep = {(nvalid > 0 ? 0xffffu : 0u) | (nvalid > 1 ? 0xffff0000u : 0u),
+                              (nvalid > 2 ? 0xffffu : 0u) | (nvalid > 3 ? 0xffff0000u : 0u)};
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            va[dt] = __builtin_bit_cast(bf16x4, __builtin_bit_cast(u32x2, va[dt]) & keep);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb[ct], o[ct][dt], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb, o[dt], 0, 0, 0);
-  };
 
-  // Triple of this lane's column of the finished item, straight from
-  // registers.  It is stored after the next stage barrier, beside the next
-  // copy, so the stores never hold up a stage wait on their own.
-  bool fin = false;
-  int64_t fin_row = 0;
-  float fin_l = 0.f;
-  auto store_partial = [&]() {
-    float* dst = P.part.o + fin_row * kD + 4 * g;
+    // Triples of this wave's columns (empty if the stripe had no block):
+    // row of (stripe, head, column).
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt];
-    if (g == 0) {
-      P.part.m[fin_row] = mrow;
-      P.part.l[fin_row] = fin_l;
-    }
-  };
-
-  load_q(dit);
-  issue(0);
-  for (int it = 0;; ++it) {
-    // Stage `it` has landed for every wave, and every wave is done with
-    // stage it - 1, whose slot the next copy reuses.
-    wait_vm_all();
-    __syncthreads();
-    if (fin) {
-      store_partial();
-      fin = false;
-    }
-    if (cs == 0) begin_item();
-    if (di < i_end) issue((it + 1) & 1);
-    if (q_pending) {
-      load_q(cnx);
-      q_pending = false;
-    }
-    if (active) {
-      const int bps = 1 << lg;
-      const char* slot = lds + (it & 1) * kSlotBytes + hh * bps * 2 * kTileBytes;
-      const int nblk = item_blocks(cit);
-      for (int b = 0; b < bps; ++b) {
-        const int blk = bps * cs + b;
-        if (blk < nblk) compute_block(slot + b * 2 * kTileBytes, cit.tok_begin + blk * kBS);
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float l = xsum32(xsum16(lsum[ct]));
+      const int col = 16 * ct + c16;
+      if (col < ccols) {
+        const int64_t row = row0 + col;
+        float* dst = Pm.part.o + row * kD + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[ct][dt];
+        if (g == 0) {
+          Pm.part.m[row] = mrow[ct];
+          Pm.part.l[row] = l;
+        }
       }
-    }
-    if (++cs == cnst) {
-      // Row of head kv_head + hh, column col of the item's token split.
-      fin_l = xsum32(xsum16(lsum));
-      const int col = cit.col0 + 16 * ct + c16;
-      fin = active && col < cit.col1;
-      fin_row = (int64_t)cit.part_base + (int64_t)hh * (cit.col1 - cit.col0) + (col - cit.col0);
-      if (++ci == i_end) break;
-      cit = cnx;
-      cnst = item_stages(cit);
-      cs = 0;
     }
   }
-  if (fin) store_partial();
 }
 
 }  // namespace
 
-// Grouped prefix pass: members x Hq/Hkv query rows per item.
-__global__ __launch_bounds__(256, 2) void fca_grouped_prefix_kernel(GqaParams P) { partial_kernel_body(P); }
+// Both passes: the work items of the bin of each workgroup, up to 16 * NCT
+// query rows per wave.  The bin heads and items come first among the
+// arguments so that they can be preloaded into scalar registers.
+template <int NCT, int P>
+__global__ __launch_bounds__(256, 1) void fca_attention_kernel(const BinHead* __restrict__ bins,
+                                                               const WorkItem* __restrict__ items, const char* k,
+                                                               const char* v, int64_t ksb, int64_t ksh, int64_t vsb,
+                                                               int64_t vsh, GqaParams p) {
+  const CopyArgs ca{bins, items, k, v, ksb, ksh, vsb, vsh};
+  stream_body<NCT, P>(ca, p);
+}
 
-// Per-request suffix pass: the Hq/Hkv rows of up to 4 KV heads of a request.
-__global__ __launch_bounds__(256, 2) void fca_suffix_decode_kernel(GqaParams P) { partial_kernel_body(P); }
-
-hipError_t launch_gqa_partial(int kind, const GqaParams& p, int n_bins, hipStream_t s) {
+hipError_t launch_attention(const GqaParams& p, int n_bins, int nct, hipStream_t s) {
   if (n_bins <= 0) return hipSuccess;
-  if (kind == 0)
-    hipLaunchKernelGGL(fca_grouped_prefix_kernel, dim3(n_bins), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(fca_suffix_decode_kernel, dim3(n_bins), dim3(256), 0, s, p);
+  const dim3 grid(n_bins), block(kWaves * 64);
+#define KARGS                                                                                          \
+  p.bins, p.items, static_cast<const char*>(p.k), static_cast<const char*>(p.v), p.k_stride_block, \
+      p.k_stride_head, p.v_stride_block, p.v_stride_head, p
+  switch (nct) {
+    case 1:
+      hipLaunchKernelGGL((fca_attention_kernel<1, 4>), grid, block, 0, s, KARGS);
+      break;
+    case 2:
+      hipLaunchKernelGGL((fca_attention_kernel<2, 4>), grid, block, 0, s, KARGS);
+      break;
+    case 3:
+      hipLaunchKernelGGL((fca_attention_kernel<3, 3>), grid, block, 0, s, KARGS);
+      break;
+    case 4:
+      hipLaunchKernelGGL((fca_attention_kernel<4, 3>), grid, block, 0, s, KARGS);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef KARGS
   return hipGetLastError();
 }
 

@@ -100,9 +100,25 @@ struct PartialPtrs {
   float* l;
 };
 
+// What a persistent attention workgroup needs first, in one 128-byte line:
+// its range of items, the first item, and the block IDs of that item's
+// first four blocks (each wave's first tile), so that the first copies go
+// out after a single memory round trip.
+struct BinHead {
+  int32_t i_begin, i_end;  // items of the bin: [i_begin, i_end) of the item array
+  int32_t id[4];           // block IDs of blocks 0..3 of the first item (0 past its end)
+  int32_t pad0, pad1;
+  WorkItem first;          // item i_begin
+  int32_t pad2[12];
+};
+static_assert(sizeof(BinHead) == 128, "bin head layout");
+
+// Fills id[] of every bin head from the block-table copy (plan time).
+hipError_t launch_bin_heads(BinHead* heads, int n_bins, const int32_t* bt, int W, int bs, hipStream_t s);
+
 struct GqaParams {
   const WorkItem* items;    // grouped by bin
-  const int32_t* bin_off;   // items of workgroup b: [bin_off[b], bin_off[b + 1])
+  const BinHead* bins;      // one per workgroup
   const int32_t* perm;
   const int32_t* bt;
   int32_t W;
@@ -116,8 +132,9 @@ struct GqaParams {
   PartialPtrs part;
 };
 
-// kind 0: grouped pass, 1: per-request pass; one persistent workgroup per bin.
-hipError_t launch_gqa_partial(int kind, const GqaParams& p, int n_bins, hipStream_t s);
+// Grouped and per-request work items, one persistent workgroup per bin
+// (bins [0, n_bins) of p.bins); nct = 16-row column tiles per wave (1..4).
+hipError_t launch_attention(const GqaParams& p, int n_bins, int nct, hipStream_t s);
 
 struct MergeParams {
   const ReqMeta* req;
