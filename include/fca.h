@@ -208,7 +208,10 @@ typedef struct fca_work_item {
                          row n is part_base + (h - kv_head)*(col1 - col0)
                          + (n - col0) */
   int32_t kv_heads;   /* the item covers KV heads kv_head .. kv_head+kv_heads-1 */
-  int32_t reserved[2];
+  int32_t stripes;    /* block stripes S: stripe t takes blocks t, t+S, ... of
+                         the range and writes rows part_base + t*kv_heads*
+                         (col1 - col0) + (as above) */
+  int32_t reserved;
 } fca_work_item;
 
 /*

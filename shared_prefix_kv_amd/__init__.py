@@ -108,7 +108,8 @@ class WorkItem(ctypes.Structure):
         ("col1", ctypes.c_int32),
         ("part_base", ctypes.c_int32),
         ("kv_heads", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("stripes", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

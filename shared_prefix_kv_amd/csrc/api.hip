@@ -57,17 +57,18 @@ int env_int(const char* name, int dflt) {
 
 // Split-schedule targets (developer tuning knobs).
 struct Tuning {
-  int wg_per_cu;  // persistent workgroups per compute unit
+  int bins_per_cu;  // attention workgroups per compute unit (the dispatcher balances them)
 };
 
 Tuning tuning() {
   Tuning t;
-  t.wg_per_cu = env_int("FCA_TUNE_WG_PER_CU", 1);
+  t.bins_per_cu = env_int("FCA_TUNE_BINS_PER_CU", 2);
   return t;
 }
 
 constexpr int kItemCols = 64;  // query rows one attention work item covers at most
-constexpr int kItemWaves = 4;  // waves per attention workgroup: heads x 16-row column tiles
+constexpr int kItemWaves = kAttnWaves;  // waves per work item: heads x column groups x block stripes
+constexpr int kWaveCols = 32;  // query rows one wave covers at most
 
 enum Kind { kGqa = 0, kMla = 1 };
 
@@ -129,9 +130,9 @@ struct SchedLayout {
 };
 
 // One launch of the attention kernel: bins [bin0, bin0 + n_bins) of the
-// plan's bins, nct column tiles per wave.
+// plan's bins.
 struct Launch {
-  int bin0, n_bins, nct;
+  int bin0, n_bins;
 };
 
 DiscoveryPtrs discovery_ptrs(char* ws, const Layout& L, int B) {
@@ -347,18 +348,21 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
 
   // ---- Work items ----
   // A lane is one (unit, head block, column chunk) stream of stages: a unit
-  // is a group's prefix range or a request's suffix, a head block H KV heads
-  // (H = 4, 2 or 1, dividing Hkv), a column chunk up to 64 query rows.  The 4
-  // waves of a workgroup take the H heads x 4/H block stripes of an item, so
-  // one stage is 4/H blocks of each head.  Each pass lays its lanes end to
-  // end and cuts the stream into one equal run of stages per persistent
-  // workgroup; a lane cut k times yields k + 1 items (token pieces).  Every
-  // piece has 4/H stripe splits, each with its own partial rows.
+  // is a group's prefix range or a request's suffix, a head block H KV heads,
+  // a column chunk up to 64 query rows.  The 8 waves of a workgroup take an
+  // item's H heads x C column groups (C = 2 for chunks wider than 32 rows) x
+  // S = 8 / (H C) block stripes, so one stage is S blocks of each head.  H is
+  // the largest power of two that divides Hkv with H x C <= 8 for the unit's
+  // widest chunk.  The lanes are laid end to end and the stream is cut into
+  // one equal run of stages per persistent workgroup; a lane cut k times
+  // yields k + 1 items (token pieces), and every piece has S stripe splits,
+  // each with its own partial rows.
   const Tuning t = tuning();
-  const int H_all = hkv % 4 == 0 ? 4 : hkv % 2 == 0 ? 2 : 1;
+  const int H_div = hkv % 8 == 0 ? 8 : hkv % 4 == 0 ? 4 : hkv % 2 == 0 ? 2 : 1;
   struct Lane {
     int request, member_off, ncols, tok0, tok_end;
     int kv0, H, col0, col1;
+    int S;  // block stripes
     int64_t stages;
     int64_t base;
     int splits;
@@ -367,14 +371,17 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   auto add_lanes = [&](std::vector<Lane>& lanes, int tok0, int tok_end, int request, int member_off,
                        int ncols, int* H_out, int* chunks_out) {
     const int first = (int)lanes.size();
-    const int H = H_all;
+    const int cmax = std::min(ncols, kItemCols) > kWaveCols ? 2 : 1;
+    const int H = std::min(H_div, kItemWaves / cmax);
     const int chunks = (int)ceil_div(ncols, kItemCols);
-    const int bps = kItemWaves / H;
-    const int64_t stages = ceil_div(ceil_div((int64_t)tok_end - tok0, bs), bps);
+    const int64_t nblk = ceil_div((int64_t)tok_end - tok0, bs);
     for (int hb = 0; hb < hkv / H; ++hb)
-      for (int c = 0; c < chunks; ++c)
-        lanes.push_back(Lane{request, member_off, ncols, tok0, tok_end, hb * H, H, c * kItemCols,
-                             std::min(ncols, (c + 1) * kItemCols), stages, 0, 0});
+      for (int c = 0; c < chunks; ++c) {
+        const int col0 = c * kItemCols, col1 = std::min(ncols, (c + 1) * kItemCols);
+        const int S = kItemWaves / (H * (col1 - col0 > kWaveCols ? 2 : 1));
+        lanes.push_back(Lane{request, member_off, ncols, tok0, tok_end, hb * H, H, col0, col1, S,
+                             ceil_div(nblk, S), 0, 0});
+      }
     *H_out = H;
     *chunks_out = chunks;
     return first;
@@ -389,14 +396,12 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   P->launches.clear();
   auto cut = [&](size_t l0, size_t l1) {
     int64_t W = 0;
-    int nct = 1;
     for (size_t k = l0; k < l1; ++k) {
       W += all[k].stages;
-      nct = std::max(nct, (int)ceil_div(all[k].col1 - all[k].col0, 16));
     }
-    const int64_t nb = std::min<int64_t>(W, (int64_t)n_cu_ * t.wg_per_cu);
+    const int64_t nb = std::min<int64_t>(W, (int64_t)n_cu_ * t.bins_per_cu);
     if (nb == 0) return;
-    P->launches.push_back(Launch{(int)P->bins.size() - 1, (int)nb, nct});
+    P->launches.push_back(Launch{(int)P->bins.size() - 1, (int)nb});
     size_t li = l0;
     int64_t lpos = 0, pos = 0;
     for (int64_t b = 0; b < nb; ++b) {
@@ -404,7 +409,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
       while (pos < end) {
         Lane& L = all[li];
         const int64_t take = std::min(L.stages - lpos, end - pos);
-        const int64_t stok = (int64_t)(kItemWaves / L.H) * bs;  // tokens per stage
+        const int64_t stok = (int64_t)L.S * bs;  // tokens per stage
         WorkItem it{};
         it.request = L.request;
         it.tok_begin = (int)(L.tok0 + lpos * stok);
@@ -416,6 +421,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
         it.col0 = L.col0;
         it.col1 = L.col1;
         it.part_base = L.splits++;
+        it.stripes = L.S;
         P->items.push_back(it);
         item_lane.push_back((int)li);
         pos += take;
@@ -461,7 +467,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
     cut(0, all.size());
   }
   for (Lane& L : all) {
-    L.splits *= kItemWaves / L.H;  // stripe splits of every piece
+    L.splits *= L.S;  // stripe splits of every piece
     L.base = row;
     row += (int64_t)L.splits * L.H * (L.col1 - L.col0);
   }
@@ -471,7 +477,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   for (size_t k = 0; k < P->items.size(); ++k) {
     WorkItem& it = P->items[k];
     const Lane& L = all[item_lane[k]];
-    it.part_base = (int32_t)(L.base + (int64_t)it.part_base * kItemWaves * (L.col1 - L.col0));
+    it.part_base = (int32_t)(L.base + (int64_t)it.part_base * L.S * L.H * (L.col1 - L.col0));
     (it.member_off >= 0 ? P->items_g : P->items_s).push_back(it);
   }
   P->lanes.clear();
@@ -712,7 +718,7 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
     if (k < (int)P->launches.size()) {
       const Launch& ln = P->launches[k];
       gp.bins = reinterpret_cast<const BinHead*>(P->sched + S.heads) + ln.bin0;
-      FCA_TRY(launch_attention(gp, ln.n_bins, ln.nct, s), "attention launch");
+      FCA_TRY(launch_attention(gp, ln.n_bins, s), "attention launch");
     }
     FCA_TRY(mark(2 + 2 * k), "event record");
   }

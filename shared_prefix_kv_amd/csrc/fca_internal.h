@@ -12,7 +12,8 @@ namespace fca {
 
 constexpr int kMaxBatch = 8192;
 constexpr int kMaxTableWidth = 1 << 20;
-constexpr int kTileTokens = 32;     // split boundaries are multiples of this many tokens
+constexpr int kAttnLgWaves = 2;                 // log2 of the waves of an attention workgroup
+constexpr int kAttnWaves = 1 << kAttnLgWaves;   // waves that share one work item
 
 // A unit of work of the grouped or per-request pass; same layout as the
 // public fca_work_item.
@@ -27,7 +28,8 @@ struct WorkItem {
   int32_t col1;
   int32_t part_base;
   int32_t kv_heads;  // KV heads the item covers: kv_head .. kv_head + kv_heads - 1
-  int32_t pad1, pad2;
+  int32_t stripes;   // block stripes (the kernel derives them; exported for tests)
+  int32_t pad2;
 };
 static_assert(sizeof(WorkItem) == sizeof(fca_work_item), "work item layout");
 
@@ -133,8 +135,8 @@ struct GqaParams {
 };
 
 // Grouped and per-request work items, one persistent workgroup per bin
-// (bins [0, n_bins) of p.bins); nct = 16-row column tiles per wave (1..4).
-hipError_t launch_attention(const GqaParams& p, int n_bins, int nct, hipStream_t s);
+// (bins [0, n_bins) of p.bins).
+hipError_t launch_attention(const GqaParams& p, int n_bins, hipStream_t s);
 
 struct MergeParams {
   const ReqMeta* req;

@@ -176,23 +176,26 @@ def test_schedule_covers_each_token_once(name):
     sc = p.export_schedule()
     nrows = p.info.num_partial_rows
     written = np.zeros(nrows, dtype=np.int64)
-    row_info = {}  # row -> (unit key, kv head, column, tok_begin, tok_end, stripe)
+    row_info = {}  # row -> (unit key, kv head, column, tok_begin, tok_end, stripe, stripes)
 
     def record(it, key):
-        # The item's 4 waves are kv_heads heads x S block stripes; stripe t
-        # of head h writes row part_base + (t * kv_heads + h - kv_head) * w + n - col0.
+        # The item's waves are kv_heads heads x C column groups (2 above 32
+        # rows) x S block stripes; stripe t of head h writes row
+        # part_base + (t * kv_heads + h - kv_head) * w + n - col0.
         assert it["tok_begin"] < it["tok_end"]
         assert 0 <= it["col0"] < it["col1"] <= it["ncols"] and it["col1"] - it["col0"] <= 64
-        assert it["kv_heads"] in (1, 2, 4) and it["kv_head"] % it["kv_heads"] == 0
+        assert it["kv_heads"] in (1, 2, 4, 8) and it["kv_head"] % it["kv_heads"] == 0
         w = it["col1"] - it["col0"]
-        S = 4 // it["kv_heads"]
+        C = 2 if w > 32 else 1
+        S = it["stripes"]
+        assert S >= 1 and S & (S - 1) == 0 and it["kv_heads"] * C * S in (4, 8)
         for t in range(S):
             for h in range(it["kv_head"], it["kv_head"] + it["kv_heads"]):
                 for c in range(it["col0"], it["col1"]):
                     row = it["part_base"] + (t * it["kv_heads"] + h - it["kv_head"]) * w + (c - it["col0"])
                     assert 0 <= row < nrows
                     written[row] += 1
-                    row_info[row] = (key, h, c, it["tok_begin"], it["tok_end"], t)
+                    row_info[row] = (key, h, c, it["tok_begin"], it["tok_end"], t, S)
 
     # grouped items: unit key (member_off, ncols); the group is the one whose
     # member list holds the item's request and whose range and width match.
@@ -255,18 +258,17 @@ def test_schedule_covers_each_token_once(name):
             per_unit = {}
             for row in rows:
                 seen[row] += 1
-                key, kvh, col, t0, t1, t = row_info[row]
+                key, kvh, col, t0, t1, t, S = row_info[row]
                 assert kvh == h // r and col % r == h % r
-                per_unit.setdefault(key, []).append((col, t0, t1, t))
+                per_unit.setdefault(key, []).append((col, t0, t1, t, S))
             assert list(per_unit) == path  # deepest group first, suffix last
             for key, v in per_unit.items():
                 assert len({x[0] for x in v}) == 1  # one column per unit
                 pieces = {}
-                for _, t0, t1, t in v:
-                    pieces.setdefault((t0, t1), set()).add(t)
-                S = 4 // (4 if hkv % 4 == 0 else 2 if hkv % 2 == 0 else 1)
-                assert all(len(ts) == S for ts in pieces.values())  # every stripe of every piece
-                spans = sorted(pieces)
+                for _, t0, t1, t, S in v:
+                    pieces.setdefault((t0, t1, S), set()).add(t)
+                assert all(len(ts) == S for (_, _, S), ts in pieces.items())  # every stripe of every piece
+                spans = sorted((t0, t1) for t0, t1, _ in pieces)
                 assert all(x1 == y0 for (_, x1), (y0, _) in zip(spans, spans[1:]))
     assert (seen == 1).all()
 
