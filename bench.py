@@ -31,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+COPY_BYTES = 1 << 30
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -49,33 +50,42 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-noncascade", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="few steps, no baselines (for rocprofv3)")
+    ap.add_argument(
+        "--copy-calibration",
+        action="store_true",
+        help="also run a plain elementwise copy of known size (scale of the HBM byte counters)",
+    )
     return ap.parse_args()
 
 
 def pass_bytes(batch, plan, sched):
-    """Algorithmic bytes each pass must move (per launch)."""
+    """Algorithmic bytes per launch.
+
+    Attention (both passes): every unique KV token row once (a group's prefix
+    range once for the group, each request's suffix once) plus each
+    request's Q row once.  Grouped / suffix alone: their share of that.
+    Merge: the partial triples it reads plus the output (and lse) it writes.
+    Partial-triple writes of the attention kernel are not counted: they
+    follow from the token splits, not from the method.
+    """
     sh = batch.shape
     bs = sh.block_size
     tok_bytes = (sh.num_kv_heads * sh.head_dim_qk * 2) if sh.v_aliases_k else sh.num_kv_heads * (sh.head_dim_qk + sh.head_dim_v) * 2
     ex = plan.export()
     prefix_tokens = sum((g["block_end"] - g["block_begin"]) * bs for g in ex["groups"])
     suffix_tokens = sum(r[1] for r in ex["requests"])
+    q_bytes = batch.batch * sh.num_q_heads * sh.head_dim_qk * 2
     row_bytes = sh.head_dim_v * 4 + 8
-    rows_g = sum((it["col1"] - it["col0"]) * it["kv_heads"] for it in sched["grouped"])
-    rows_s = sum((it["col1"] - it["col0"]) * it["kv_heads"] for it in sched["suffix"])
-    q_row = sh.head_dim_qk * 2
-    q_g = sum(len(g["members"]) for g in ex["groups"]) * sh.num_q_heads * q_row
-    q_s = sum(1 for r in ex["requests"] if r[1] > 0) * sh.num_q_heads * q_row
-    grouped = prefix_tokens * tok_bytes + q_g + rows_g * row_bytes
-    suffix = suffix_tokens * tok_bytes + q_s + rows_s * row_bytes
-    merge = (rows_g + rows_s) * row_bytes + batch.batch * sh.num_q_heads * (sh.head_dim_v * 2 + 4)
+    rows = plan.info.num_partial_rows
+    merge = rows * row_bytes + batch.batch * sh.num_q_heads * (sh.head_dim_v * 2 + 4)
     flops_g = sum(
         (g["block_end"] - g["block_begin"]) * bs * len(g["members"]) * sh.num_q_heads * 2 * (sh.head_dim_qk + sh.head_dim_v)
         for g in ex["groups"]
     )
     return dict(
-        grouped=grouped,
-        suffix=suffix,
+        attention=(prefix_tokens + suffix_tokens) * tok_bytes + q_bytes,
+        grouped=prefix_tokens * tok_bytes + q_bytes,
+        suffix=suffix_tokens * tok_bytes + q_bytes,
         merge=merge,
         prefix_tokens=prefix_tokens,
         suffix_tokens=suffix_tokens,
@@ -99,13 +109,17 @@ def time_steps(plan, q, pools, out, lse, steps, torch, fca):
     return start.elapsed_time(stop) / steps, wall
 
 
-def cpu_baseline(batch, vals, budget_s):
-    """The fp64 oracle on a bounded sample of the same batch, one thread."""
+def cpu_baseline(batch, vals, budget_s, threads):
+    """The fp64 oracle on a bounded sample of the same batch (its first
+    requests, in order, until the budget is spent), with `threads` BLAS
+    threads."""
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as A
-    from tests.helpers import to_bits
     import torch
+
+    def to_bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
     sh = batch.shape
     bs = sh.block_size
@@ -113,7 +127,7 @@ def cpu_baseline(batch, vals, budget_s):
     tokens = 0
     done = 0
     elapsed = 0.0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         for i in range(batch.batch):
             L = int(batch.seq_lens[i])
             nblk = -(-L // bs)
@@ -132,9 +146,10 @@ def cpu_baseline(batch, vals, budget_s):
     return dict(
         value=tokens / elapsed,
         unit="logical KV tokens/s",
-        cores=1,
+        cores=threads,
         kind="oracle",
-        sample=f"first {done} of {batch.batch} requests ({tokens} logical tokens), fp64 numpy oracle, 1 thread, {elapsed:.1f} s",
+        sample=f"first {done} of {batch.batch} requests ({tokens} logical tokens), fp64 numpy oracle, "
+        f"{threads} BLAS thread(s), {elapsed:.1f} s",
     )
 
 
@@ -210,6 +225,17 @@ def main():
         ms, wall_ms = time_steps(plan, qs, pools, out, lse, steps, torch, fca)
         log(f"fca decode: {ms * 1000:.1f} us/step (events), {wall_ms * 1000:.1f} us/step (wall)")
 
+    if args.copy_calibration:
+        # A plain bf16 copy (read + write COPY_BYTES each) whose FETCH_SIZE /
+        # WRITE_SIZE give the scale of those counters on this chip.
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {COPY_BYTES} bytes read and written per launch")
+        del src, dst
+
     # Kernel times: HIP events recorded around each launch on the kernels'
     # stream (separate loops, so the events do not touch `value`): the
     # attention launch and the merge of the timed plan, then the two passes
@@ -224,8 +250,12 @@ def main():
         return {k: pr[f"{k}_ms"] / n for k in ("attention", "grouped", "suffix", "merge", "decode")}
 
     per = profiled(plan)
-    per_sep = profiled(plan_sep)
-    per["grouped"], per["suffix"] = per_sep["grouped"], per_sep["suffix"]
+    if args.profile_only:
+        # only the timed plan's launches, so that counter runs see one kind
+        per["grouped"] = per["suffix"] = float("nan")
+    else:
+        per_sep = profiled(plan_sep)
+        per["grouped"], per["suffix"] = per_sep["grouped"], per_sep["suffix"]
     log("per launch (ms):", {k: round(v, 4) for k, v in per.items()})
     if args.profile_only:
         ms = per["decode"]
@@ -236,7 +266,7 @@ def main():
     unique_gbps = unique_bytes / (ms / 1000.0) / 1e9
 
     kernels = {
-        "fca_attention_kernel": ("attention", pb["grouped"] + pb["suffix"]),
+        "fca_attention_kernel": ("attention", pb["attention"]),
         "fca_merge_kernel_d128" if sh.head_dim_v == 128 else "fca_merge_kernel_d512": ("merge", pb["merge"]),
     }
     dom_name, (dom_pass, dom_bytes) = max(kernels.items(), key=lambda kv: per[kv[1][0]])
@@ -252,7 +282,24 @@ def main():
         "bytes_per_launch": int(dom_bytes),
         "avg_launch_ms": round(per[dom_pass], 5),
     }
-    sfx_merge_gbps = (pb["suffix"] + pb["merge"]) / ((per["suffix"] + per["merge"]) / 1000.0) / 1e9
+    # HBM bytes per launch measured with FETCH_SIZE / WRITE_SIZE (calibrated
+    # against a copy of known size) in the committed profile summary, used
+    # only while the library sources are the ones it was taken with.
+    from shared_prefix_kv_amd.profiling import load_traffic
+
+    tr = load_traffic(cfg.name)
+    if tr and dom_name == tr["kernel"] and dom_name in tr["traffic"]:
+        t = tr["traffic"][dom_name]
+        roofline["traffic"] = int(t["fetch_bytes"] + t["write_bytes"])
+        roofline["traffic_detail"] = {
+            "fetch_bytes": int(t["fetch_bytes"]),
+            "write_bytes": int(t["write_bytes"]),
+            "counter_scale": {"fetch": round(tr["fetch_factor"], 4), "write": round(tr["write_factor"], 4)},
+        }
+    def gbps(nbytes, ms_):
+        return round(nbytes / (ms_ / 1000.0) / 1e9, 1) if ms_ > 0 else None  # None for nan / 0
+
+    sfx_merge_gbps = gbps(pb["suffix"] + pb["merge"], per["suffix"] + per["merge"])
     grouped_tflops = pb["grouped_flops"] / (per["grouped"] / 1000.0) / 1e12 if per["grouped"] > 0 else 0.0
 
     result = {
@@ -279,13 +326,13 @@ def main():
         "unique_kv_GBps": round(unique_gbps, 1),
         "unique_kv_frac_of_hbm_peak": round(unique_gbps / HBM_PEAK_GBPS, 4),
         "wall_ms_per_step": round(wall_ms, 5),
-        "per_launch_ms": {k: round(v, 5) for k, v in per.items()},
+        "per_launch_ms": {k: (round(v, 5) if v == v else None) for k, v in per.items()},
         "pass_GBps": {
-            "attention": round((pb["grouped"] + pb["suffix"]) / (per["attention"] / 1000.0) / 1e9, 1),
-            "grouped": round(pb["grouped"] / (per["grouped"] / 1000.0) / 1e9, 1) if per["grouped"] > 0 else None,
-            "suffix": round(pb["suffix"] / (per["suffix"] / 1000.0) / 1e9, 1) if per["suffix"] > 0 else None,
-            "merge": round(pb["merge"] / (per["merge"] / 1000.0) / 1e9, 1) if per["merge"] > 0 else None,
-            "suffix_plus_merge": round(sfx_merge_gbps, 1),
+            "attention": gbps(pb["attention"], per["attention"]),
+            "grouped": gbps(pb["grouped"], per["grouped"]),
+            "suffix": gbps(pb["suffix"], per["suffix"]),
+            "merge": gbps(pb["merge"], per["merge"]),
+            "suffix_plus_merge": sfx_merge_gbps,
         },
         "grouped_mfma_TFLOPs": round(grouped_tflops, 1),
         "grouped_mfma_frac_of_peak": round(grouped_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -316,8 +363,10 @@ def main():
         del plan_nc
 
     if not args.no_cpu_baseline and not args.profile_only:
-        log("cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(batch, vals0, args.cpu_seconds)
+        ncpu = len(os.sched_getaffinity(0))
+        log(f"cpu baseline (oracle), {ncpu} threads then 1 ...")
+        result["cpu_baseline"] = cpu_baseline(batch, vals0, args.cpu_seconds / 2, ncpu)
+        result["cpu_baseline_1_thread"] = cpu_baseline(batch, vals0, args.cpu_seconds / 2, 1)
 
     print(json.dumps(result), flush=True)
 

@@ -1,0 +1,223 @@
+"""Summaries of rocprofv3 runs of bench.py (kernel times and HBM traffic).
+
+    python -m shared_prefix_kv_amd.profiling summarize \\
+        --stats DIR --fetch DIR --write DIR --config NAME --out FILE [--cmd "..."]...
+
+DIR are rocprofv3 output folders (``-f csv``): ``--stats`` from
+``--kernel-trace --stats``, ``--fetch`` / ``--write`` from ``--pmc FETCH_SIZE``
+and ``--pmc WRITE_SIZE`` runs of ``bench.py --profile-only --copy-calibration``.
+
+FETCH_SIZE and WRITE_SIZE are per-dispatch byte counters (KiB) whose scale
+on this chip is taken from the calibration copy that bench.py launches in the
+same process: an elementwise kernel that reads and writes a known number of
+bytes.  The factor (known bytes / counter bytes) is applied to every other
+kernel's counters.
+
+The summary ends with one ``json:`` line that bench.py reads back to fill in
+the roofline's measured traffic, but only while the sources that built the
+library are unchanged (``source_sha256``).
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+
+ATTENTION = "fca_attention_kernel"
+MERGE = "fca_merge_kernel"
+CALIBRATION = "mul"  # torch.mul elementwise kernel of the calibration copy
+
+
+def source_sha256() -> str:
+    """Hash of the HIP sources and the public header the library is built from."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + [os.path.join(ROOT, "include", "fca.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _one(dirpath: str, suffix: str) -> str:
+    found = sorted(glob.glob(os.path.join(dirpath, "**", f"*{suffix}"), recursive=True))
+    if not found:
+        raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+    return found[0]
+
+
+def _short(name: str) -> str:
+    """Kernel name without namespaces, template arguments or parameters."""
+    base = name.split("(")[0].replace("void ", "")
+    return base.split("::")[-1][:42]
+
+
+def kernel_stats(dirpath: str) -> list[dict]:
+    rows = []
+    with open(_one(dirpath, "kernel_stats.csv")) as fh:
+        for r in csv.DictReader(fh):
+            rows.append(
+                dict(
+                    name=r["Name"],
+                    calls=int(r["Calls"]),
+                    avg_us=float(r["AverageNs"]) / 1e3,
+                    min_us=float(r["MinNs"]) / 1e3,
+                    max_us=float(r["MaxNs"]) / 1e3,
+                    share=float(r["Percentage"]),
+                )
+            )
+    return rows
+
+
+def kernel_durations(dirpath: str, key: str) -> list[float]:
+    """Per-dispatch durations (us) of kernels whose name contains `key`."""
+    out = []
+    with open(_one(dirpath, "kernel_trace.csv")) as fh:
+        for r in csv.DictReader(fh):
+            if key in r["Kernel_Name"]:
+                out.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return out
+
+
+def counters(dirpath: str, counter: str) -> dict[str, list[float]]:
+    """Counter values (bytes) per dispatch, grouped by kernel name."""
+    by = {}
+    with open(_one(dirpath, "counter_collection.csv")) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+    return by
+
+
+def _pick(by: dict[str, list[float]], key: str) -> list[float]:
+    vals = []
+    for name, v in by.items():
+        if key == CALIBRATION:
+            if "vectorized_elementwise_kernel" in name and "MulFunctor" in name:
+                vals += v
+        elif key in name:
+            vals += v
+    return vals
+
+
+def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_bytes, cmds, out):
+    stats = kernel_stats(stats_dir)
+    att_us = kernel_durations(stats_dir, ATTENTION)
+    fetch = counters(fetch_dir, "FETCH_SIZE")
+    write = counters(write_dir, "WRITE_SIZE")
+    cal_f = _pick(fetch, CALIBRATION)
+    cal_w = _pick(write, CALIBRATION)
+    if not cal_f or not cal_w:
+        raise RuntimeError("calibration copy not found in the counter runs")
+    f_factor = copy_bytes / statistics.median(cal_f)
+    w_factor = copy_bytes / statistics.median(cal_w)
+    res = {}
+    for key in (ATTENTION, MERGE):
+        fv, wv = _pick(fetch, key), _pick(write, key)
+        if fv and wv:
+            res[key] = dict(
+                dispatches=len(fv),
+                fetch_counter_bytes=statistics.median(fv),
+                write_counter_bytes=statistics.median(wv),
+                fetch_bytes=statistics.median(fv) * f_factor,
+                write_bytes=statistics.median(wv) * w_factor,
+            )
+    att = res.get(ATTENTION)
+    lines = [
+        f"# {ATTENTION} on the {config} workload: kernel times and HBM traffic (rocprofv3)",
+        "",
+        "Commands (from the repository root on the GPU box):",
+    ]
+    lines += [f"  {c}" for c in cmds]
+    lines += [
+        "",
+        f"source_sha256: {source_sha256()}",
+        "",
+        "Kernel trace statistics (--kernel-trace --stats), fca kernels:",
+        f"  {'kernel':42s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}",
+    ]
+    for r in stats:
+        if "fca" in r["name"]:
+            lines.append(f"  {_short(r['name']):42s} {r['calls']:6d} {r['avg_us']:9.2f} {r['min_us']:9.2f} {r['max_us']:9.2f}")
+    if att_us:
+        lines.append(
+            f"  {ATTENTION}: median of {len(att_us)} dispatches {statistics.median(att_us):.2f} us"
+        )
+    lines += [
+        "",
+        f"Counter calibration: the copy reads and writes {copy_bytes} bytes per dispatch;",
+        f"  FETCH_SIZE reads {statistics.median(cal_f):.0f} bytes -> factor {f_factor:.4f}",
+        f"  WRITE_SIZE reads {statistics.median(cal_w):.0f} bytes -> factor {w_factor:.4f}",
+        "",
+        "HBM traffic per dispatch (median over dispatches, calibrated):",
+    ]
+    for key, v in res.items():
+        lines.append(
+            f"  {key:24s} fetch {v['fetch_bytes'] / 1e6:9.2f} MB  write {v['write_bytes'] / 1e6:8.2f} MB"
+            f"  (counters {v['fetch_counter_bytes'] / 1e6:.2f} / {v['write_counter_bytes'] / 1e6:.2f} MB,"
+            f" {v['dispatches']} dispatches)"
+        )
+    if att and algorithmic_bytes:
+        lines.append(
+            f"  algorithmic bytes per attention dispatch {algorithmic_bytes / 1e6:.2f} MB;"
+            f" measured / algorithmic = {(att['fetch_bytes'] + att['write_bytes']) / algorithmic_bytes:.3f}"
+        )
+    payload = dict(
+        config=config,
+        source_sha256=source_sha256(),
+        kernel=ATTENTION,
+        avg_launch_us=statistics.median(att_us) if att_us else None,
+        fetch_factor=f_factor,
+        write_factor=w_factor,
+        traffic=res,
+    )
+    lines += ["", "json: " + json.dumps(payload)]
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as fh:
+        fh.write(text)
+    return text
+
+
+def load_traffic(config: str):
+    """Calibrated traffic per attention dispatch from the committed summary,
+    or None if there is none or the sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{ATTENTION}.{config}.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("json: "):
+                d = json.loads(line[6:])
+                if d.get("source_sha256") != source_sha256():
+                    return None
+                return d
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("summarize")
+    s.add_argument("--stats", required=True)
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--config", required=True)
+    s.add_argument("--copy-bytes", type=int, required=True)
+    s.add_argument("--algorithmic-bytes", type=int, default=0)
+    s.add_argument("--cmd", action="append", default=[])
+    s.add_argument("--out", required=True)
+    a = ap.parse_args()
+    print(summarize(a.stats, a.fetch, a.write, a.config, a.copy_bytes, a.algorithmic_bytes, a.cmd, a.out), end="")
+
+
+if __name__ == "__main__":
+    main()
