@@ -66,7 +66,8 @@ Tuning tuning() {
   return t;
 }
 
-constexpr int kItemCols = 64;  // query rows one attention work item covers at most
+constexpr int kItemColsGqa = 64;   // query rows of one GQA work item at most
+constexpr int kItemColsMla = 64;   // query rows of one latent-cache work item at most
 constexpr int kItemWaves = kAttnWaves;  // waves per work item: heads x column groups x block stripes
 constexpr int kWaveCols = 32;  // query rows one wave covers at most
 
@@ -92,6 +93,14 @@ fca_status check_desc(const fca_attn_desc* d, Kind* kind) {
     if ((d->k_stride_head | d->k_stride_block | d->v_stride_head | d->v_stride_block) % 8)
       return fail(FCA_ERR_INVALID_ARG, "cache strides must keep 16-byte tile alignment");
     *kind = kGqa;
+    return FCA_OK;
+  }
+  if (d->head_dim_qk == 576 && d->head_dim_v == 512 && d->block_size == 64 && d->v_aliases_k) {
+    if (d->k_stride_head < 576 * 64 || d->k_stride_block < (int64_t)d->num_kv_heads * d->k_stride_head)
+      return fail(FCA_ERR_INVALID_ARG, "cache strides overlap tiles");
+    if ((d->k_stride_head | d->k_stride_block) % 8)
+      return fail(FCA_ERR_INVALID_ARG, "cache strides must keep 16-byte tile alignment");
+    *kind = kMla;
     return FCA_OK;
   }
   return fail(FCA_ERR_UNSUPPORTED, "unsupported shape: head_dim_qk=%d head_dim_v=%d block_size=%d v_aliases_k=%d",
@@ -173,6 +182,7 @@ struct fca_plan_s {
   std::vector<ReqMeta> req;
   std::vector<GroupMeta> grp;
   std::vector<LaneMeta> lanes;  // grouped lanes, then suffix lanes
+  int item_cols = kItemColsGqa;  // query rows per column chunk
   fca_plan_info info;
   // plan-owned device copy of the schedule
   char* sched = nullptr;
@@ -204,9 +214,9 @@ void for_each_source(const fca_plan_s& P, int i, int h, F&& f) {
   for (int g = rq.deepest; g >= 0; g = P.grp[g].parent) {
     const GroupMeta& gm = P.grp[g];
     const int col = (rq.pos - gm.r0) * r + rr;
-    lane_rows(gm.lane0 + (kvh / gm.H) * gm.chunks + col / kItemCols, col);
+    lane_rows(gm.lane0 + (kvh / gm.H) * gm.chunks + col / P.item_cols, col);
   }
-  if (rq.sfx_lane >= 0) lane_rows(rq.sfx_lane + kvh / rq.sfx_H, rr);
+  if (rq.sfx_lane >= 0) lane_rows(rq.sfx_lane + (kvh / rq.sfx_H) * rq.sfx_chunks + rr / P.item_cols, rr);
 }
 
 int64_t count_sources(const fca_plan_s& P, int i, int h) {
@@ -358,6 +368,8 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   // yields k + 1 items (token pieces), and every piece has S stripe splits,
   // each with its own partial rows.
   const Tuning t = tuning();
+  const bool mla = P->kind == kMla;
+  P->item_cols = mla ? kItemColsMla : kItemColsGqa;
   const int H_div = hkv % 8 == 0 ? 8 : hkv % 4 == 0 ? 4 : hkv % 2 == 0 ? 2 : 1;
   struct Lane {
     int request, member_off, ncols, tok0, tok_end;
@@ -371,14 +383,17 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   auto add_lanes = [&](std::vector<Lane>& lanes, int tok0, int tok_end, int request, int member_off,
                        int ncols, int* H_out, int* chunks_out) {
     const int first = (int)lanes.size();
-    const int cmax = std::min(ncols, kItemCols) > kWaveCols ? 2 : 1;
-    const int H = std::min(H_div, kItemWaves / cmax);
-    const int chunks = (int)ceil_div(ncols, kItemCols);
+    const int icols = P->item_cols;
+    const int cmax = std::min(ncols, icols) > kWaveCols ? 2 : 1;
+    // Latent cache: one head per item, its 4 waves split the item's up to
+    // 128 query rows and share every block (no stripes).
+    const int H = mla ? 1 : std::min(H_div, kItemWaves / cmax);
+    const int chunks = (int)ceil_div(ncols, icols);
     const int64_t nblk = ceil_div((int64_t)tok_end - tok0, bs);
     for (int hb = 0; hb < hkv / H; ++hb)
       for (int c = 0; c < chunks; ++c) {
-        const int col0 = c * kItemCols, col1 = std::min(ncols, (c + 1) * kItemCols);
-        const int S = kItemWaves / (H * (col1 - col0 > kWaveCols ? 2 : 1));
+        const int col0 = c * icols, col1 = std::min(ncols, (c + 1) * icols);
+        const int S = mla ? 1 : kItemWaves / (H * (col1 - col0 > kWaveCols ? 2 : 1));
         lanes.push_back(Lane{request, member_off, ncols, tok0, tok_end, hb * H, H, col0, col1, S,
                              ceil_div(nblk, S), 0, 0});
       }
@@ -455,10 +470,9 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
     rq.deepest = deepest_c[i];
     rq.sfx_lane = -1;
     rq.sfx_H = 1;
-    if (sfx_tokens[i] > 0) {
-      int chunks;
-      rq.sfx_lane = add_lanes(all, P->req3[3 * i] * bs, lens[i], i, -1, r, &rq.sfx_H, &chunks);
-    }
+    rq.sfx_chunks = 1;
+    if (sfx_tokens[i] > 0)
+      rq.sfx_lane = add_lanes(all, P->req3[3 * i] * bs, lens[i], i, -1, r, &rq.sfx_H, &rq.sfx_chunks);
   }
   if (P->desc.flags & FCA_PLAN_SEPARATE_PASSES) {
     cut(0, n_glanes);
@@ -718,7 +732,8 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
     if (k < (int)P->launches.size()) {
       const Launch& ln = P->launches[k];
       gp.bins = reinterpret_cast<const BinHead*>(P->sched + S.heads) + ln.bin0;
-      FCA_TRY(launch_attention(gp, ln.n_bins, s), "attention launch");
+      FCA_TRY(P->kind == kMla ? launch_mla(gp, ln.n_bins, s) : launch_attention(gp, ln.n_bins, s),
+              "attention launch");
     }
     FCA_TRY(mark(2 + 2 * k), "event record");
   }
@@ -733,6 +748,7 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   mp.Hkv = P->desc.num_kv_heads;
   mp.r = P->r;
   mp.Dv = P->desc.head_dim_v;
+  mp.item_cols = P->item_cols;
   mp.part = part;
   mp.out = out_dev;
   mp.lse = lse_dev;

@@ -35,10 +35,12 @@ static_assert(sizeof(WorkItem) == sizeof(fca_work_item), "work item layout");
 
 // Per-request data the merge reads.
 struct ReqMeta {
-  int32_t pos;       // position in the depth-first member order
-  int32_t deepest;   // canonical index of the deepest group, -1 if none
-  int32_t sfx_lane;  // first lane of the suffix (-1: no suffix tokens)
-  int32_t sfx_H;     // KV heads per suffix lane
+  int32_t pos;         // position in the depth-first member order
+  int32_t deepest;     // canonical index of the deepest group, -1 if none
+  int32_t sfx_lane;    // first lane of the suffix (-1: no suffix tokens); the
+  int32_t sfx_H;       //   lane of (kv head h, query row n) is
+  int32_t sfx_chunks;  //   sfx_lane + (h / sfx_H) * sfx_chunks + n / item_cols
+  int32_t pad0, pad1, pad2;
 };
 
 // Per-group data the merge reads (canonical order).
@@ -48,7 +50,7 @@ struct GroupMeta {
   int32_t ncols;   // members * (Hq / Hkv)
   int32_t lane0;   // lane of (head block 0, column chunk 0)
   int32_t H;       // KV heads per lane; lane of (kv head h, column n) is
-  int32_t chunks;  //   lane0 + (h / H) * chunks + n / 64
+  int32_t chunks;  //   lane0 + (h / H) * chunks + n / item_cols
   int32_t pad0, pad1;
 };
 
@@ -138,11 +140,16 @@ struct GqaParams {
 // (bins [0, n_bins) of p.bins).
 hipError_t launch_attention(const GqaParams& p, int n_bins, hipStream_t s);
 
+// The same for a latent cache (576-wide keys, values = first 512 dims,
+// 64-token blocks): items of up to 128 query rows of one head.
+hipError_t launch_mla(const GqaParams& p, int n_bins, hipStream_t s);
+
 struct MergeParams {
   const ReqMeta* req;
   const GroupMeta* grp;
   const LaneMeta* lanes;
   int32_t B, Hq, Hkv, r, Dv;
+  int32_t item_cols;  // query rows per column chunk of a lane
   PartialPtrs part;
   void* out;
   float* lse;

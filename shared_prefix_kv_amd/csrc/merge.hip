@@ -71,14 +71,15 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
   auto lane_of = [&](int g, int* col) {
     const GroupMeta gm = P.grp[g];
     *col = (rq.pos - gm.r0) * P.r + rr;
-    return gm.lane0 + (kvh / gm.H) * gm.chunks + *col / 64;
+    return gm.lane0 + (kvh / gm.H) * gm.chunks + *col / P.item_cols;
   };
   int n_src = 0;
   for (int g = rq.deepest; g >= 0; g = P.grp[g].parent) {
     int col;
     n_src += P.lanes[lane_of(g, &col)].splits;
   }
-  if (rq.sfx_lane >= 0) n_src += P.lanes[rq.sfx_lane + kvh / rq.sfx_H].splits;
+  const int sfx_ln = rq.sfx_lane + (kvh / rq.sfx_H) * rq.sfx_chunks + rr / P.item_cols;
+  if (rq.sfx_lane >= 0) n_src += P.lanes[sfx_ln].splits;
 
   float M = -INFINITY, L = 0.f;
   float acc[VPL];
@@ -98,7 +99,7 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
         if (g >= 0) {
           ln = lane_of(g, &col);
         } else {
-          ln = rq.sfx_lane + kvh / rq.sfx_H;
+          ln = sfx_ln;
           col = rr;
         }
         const LaneMeta lm = P.lanes[ln];
