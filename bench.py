@@ -31,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+RIDGE_FLOP_PER_BYTE = 312.0  # 2.5 PFLOP/s bf16 over 8 TB/s
 COPY_BYTES = 1 << 30
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
@@ -265,23 +266,42 @@ def main():
     value = logical / (ms / 1000.0)
     unique_gbps = unique_bytes / (ms / 1000.0) / 1e9
 
+    att_kernel = "fca_mla_kernel" if sh.v_aliases_k else "fca_attention_kernel"
     kernels = {
-        "fca_attention_kernel": ("attention", pb["attention"]),
+        att_kernel: ("attention", pb["attention"]),
         "fca_merge_kernel_d128" if sh.head_dim_v == 128 else "fca_merge_kernel_d512": ("merge", pb["merge"]),
     }
     dom_name, (dom_pass, dom_bytes) = max(kernels.items(), key=lambda kv: per[kv[1][0]])
-    achieved = dom_bytes / (per[dom_pass] / 1000.0) / 1e9
-    roofline = {
-        "kernel": dom_name,
-        "bound": "hbm",
-        "achieved": round(achieved, 1),
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": None,
-        "bytes_per_launch": int(dom_bytes),
-        "avg_launch_ms": round(per[dom_pass], 5),
-    }
+    att_flops = logical * 2 * sh.num_q_heads * (sh.head_dim_qk + sh.head_dim_v)
+    if dom_name == att_kernel and att_flops / dom_bytes > RIDGE_FLOP_PER_BYTE:
+        # The latent cache: every query row costs 2 (Dqk + Dv) flops per
+        # token, above the ridge, so the bound is the bf16 MFMA rate.
+        achieved = att_flops / (per[dom_pass] / 1000.0) / 1e12
+        roofline = {
+            "kernel": dom_name,
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": int(att_flops),
+            "bytes_per_launch": int(dom_bytes),
+            "avg_launch_ms": round(per[dom_pass], 5),
+        }
+    else:
+        achieved = dom_bytes / (per[dom_pass] / 1000.0) / 1e9
+        roofline = {
+            "kernel": dom_name,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": int(dom_bytes),
+            "avg_launch_ms": round(per[dom_pass], 5),
+        }
     # HBM bytes per launch measured with FETCH_SIZE / WRITE_SIZE (calibrated
     # against a copy of known size) in the committed profile summary, used
     # only while the library sources are the ones it was taken with.

@@ -92,6 +92,8 @@ __device__ __forceinline__ WorkItem load_item(cint32* items, int i) {
 
 __device__ __forceinline__ int item_blocks(const WorkItem& it) { return (it.tok_end - it.tok_begin + kBS - 1) / kBS; }
 
+}  // namespace
+
 __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * kTileBytes];
 
@@ -263,8 +265,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
     }
   }
 }
-
-}  // namespace
 
 hipError_t launch_mla(const GqaParams& p, int n_bins, hipStream_t s) {
   if (n_bins <= 0) return hipSuccess;

@@ -32,6 +32,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
 ATTENTION = "fca_attention_kernel"
+MLA = "fca_mla_kernel"
 MERGE = "fca_merge_kernel"
 CALIBRATION = "mul"  # torch.mul elementwise kernel of the calibration copy
 
@@ -56,7 +57,7 @@ def _one(dirpath: str, suffix: str) -> str:
 
 def _short(name: str) -> str:
     """Kernel name without namespaces, template arguments or parameters."""
-    base = name.split("(")[0].replace("void ", "")
+    base = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
     return base.split("::")[-1][:42]
 
 
@@ -111,7 +112,8 @@ def _pick(by: dict[str, list[float]], key: str) -> list[float]:
 
 def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_bytes, cmds, out):
     stats = kernel_stats(stats_dir)
-    att_us = kernel_durations(stats_dir, ATTENTION)
+    kernel = ATTENTION if kernel_durations(stats_dir, ATTENTION) else MLA
+    att_us = kernel_durations(stats_dir, kernel)
     fetch = counters(fetch_dir, "FETCH_SIZE")
     write = counters(write_dir, "WRITE_SIZE")
     cal_f = _pick(fetch, CALIBRATION)
@@ -121,7 +123,7 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
     f_factor = copy_bytes / statistics.median(cal_f)
     w_factor = copy_bytes / statistics.median(cal_w)
     res = {}
-    for key in (ATTENTION, MERGE):
+    for key in (kernel, MERGE):
         fv, wv = _pick(fetch, key), _pick(write, key)
         if fv and wv:
             res[key] = dict(
@@ -131,9 +133,9 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
                 fetch_bytes=statistics.median(fv) * f_factor,
                 write_bytes=statistics.median(wv) * w_factor,
             )
-    att = res.get(ATTENTION)
+    att = res.get(kernel)
     lines = [
-        f"# {ATTENTION} on the {config} workload: kernel times and HBM traffic (rocprofv3)",
+        f"# {kernel} on the {config} workload: kernel times and HBM traffic (rocprofv3)",
         "",
         "Commands (from the repository root on the GPU box):",
     ]
@@ -149,9 +151,7 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
         if "fca" in r["name"]:
             lines.append(f"  {_short(r['name']):42s} {r['calls']:6d} {r['avg_us']:9.2f} {r['min_us']:9.2f} {r['max_us']:9.2f}")
     if att_us:
-        lines.append(
-            f"  {ATTENTION}: median of {len(att_us)} dispatches {statistics.median(att_us):.2f} us"
-        )
+        lines.append(f"  {kernel}: median of {len(att_us)} dispatches {statistics.median(att_us):.2f} us")
     lines += [
         "",
         f"Counter calibration: the copy reads and writes {copy_bytes} bytes per dispatch;",
@@ -174,7 +174,7 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
     payload = dict(
         config=config,
         source_sha256=source_sha256(),
-        kernel=ATTENTION,
+        kernel=kernel,
         avg_launch_us=statistics.median(att_us) if att_us else None,
         fetch_factor=f_factor,
         write_factor=w_factor,
@@ -190,9 +190,11 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
 def load_traffic(config: str):
     """Calibrated traffic per attention dispatch from the committed summary,
     or None if there is none or the sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"{ATTENTION}.{config}.txt")
-    if not os.path.exists(path):
+    paths = [os.path.join(ROOT, "profiles", f"{k}.{config}.txt") for k in (ATTENTION, MLA)]
+    paths = [p for p in paths if os.path.exists(p)]
+    if not paths:
         return None
+    path = paths[0]
     with open(path) as fh:
         for line in fh:
             if line.startswith("json: "):
