@@ -66,6 +66,7 @@ Tuning tuning() {
   return t;
 }
 
+constexpr int kXcds = 8;  // accelerator dies per device; workgroup b is dispatched to die b mod 8
 constexpr int kItemColsGqa = 64;   // query rows of one GQA work item at most
 constexpr int kItemColsMla = 64;   // query rows of one latent-cache work item at most
 constexpr int kItemWaves = kAttnWaves;  // waves per work item: heads x column groups x block stripes
@@ -451,6 +452,126 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
     }
   };
 
+  // Latent cache: one persistent workgroup per compute unit, and the column
+  // chunks of one large unit are cut at the same token boundaries and placed
+  // on bins of one die (bin b runs on die b mod kXcds), so the chunks that
+  // read the same key tiles at the same time share that die's L2: the
+  // grouped pass then fetches each prefix block from HBM about once instead
+  // of once per chunk.  Large units (several chunks, at least half the mean
+  // bin load) go first, largest first, in pieces of about the mean bin load
+  // on the least loaded bins; the other lanes are then poured in order into
+  // the bins up to a common makespan.  Bins left empty are dropped.
+  auto place = [&](size_t l0, size_t l1) {
+    int64_t W = 0;
+    for (size_t k = l0; k < l1; ++k) W += all[k].stages;
+    if (W == 0) return;
+    const int nb = (int)std::min<int64_t>(W, n_cu_);
+    const double T = (double)W / nb;
+    struct Unit {
+      size_t l0, l1;
+    };
+    std::vector<Unit> units;
+    for (size_t k = l0; k < l1;) {
+      size_t e = k + 1;
+      while (e < l1 && all[e].request == all[k].request && all[e].member_off == all[k].member_off &&
+             all[e].tok0 == all[k].tok0 && all[e].tok_end == all[k].tok_end)
+        ++e;
+      units.push_back(Unit{k, e});
+      k = e;
+    }
+    auto large = [&](const Unit& u) { return u.l1 - u.l0 >= 2 && 2.0 * all[u.l0].stages >= T; };
+    std::stable_partition(units.begin(), units.end(), large);
+    const size_t n_large = std::count_if(units.begin(), units.end(), large);
+    std::stable_sort(units.begin(), units.begin() + n_large, [&](const Unit& a, const Unit& b) {
+      return all[a.l0].stages * (int64_t)(a.l1 - a.l0) > all[b.l0].stages * (int64_t)(b.l1 - b.l0);
+    });
+    std::vector<std::vector<std::pair<int, std::pair<int64_t, int64_t>>>> bin(nb);  // (lane, stages)
+    std::vector<int64_t> load(nb, 0);
+    const int per_die = (nb + kXcds - 1) / kXcds;
+    std::vector<int> cand;
+    for (size_t ui = 0; ui < n_large; ++ui) {
+      const Unit& u = units[ui];
+      const int64_t n = all[u.l0].stages;
+      const int64_t pieces = std::max<int64_t>(1, std::min<int64_t>(n, std::llround(n / T)));
+      const int C = (int)(u.l1 - u.l0);
+      for (int64_t p = 0; p < pieces; ++p) {
+        const int64_t s0 = p * n / pieces, s1 = (p + 1) * n / pieces;
+        for (int c0 = 0; c0 < C; c0 += per_die) {
+          const int cn = std::min(per_die, C - c0);
+          // The die whose cn least loaded bins carry the least work.
+          int best_x = 0;
+          int64_t best = INT64_MAX;
+          for (int x = 0; x < kXcds && x < nb; ++x) {
+            cand.clear();
+            for (int b = x; b < nb; b += kXcds) cand.push_back(b);
+            if ((int)cand.size() < cn) continue;
+            std::partial_sort(cand.begin(), cand.begin() + cn, cand.end(),
+                              [&](int a, int b) { return load[a] < load[b]; });
+            int64_t sum = 0;
+            for (int j = 0; j < cn; ++j) sum += load[cand[j]];
+            if (sum < best) {
+              best = sum;
+              best_x = x;
+            }
+          }
+          cand.clear();
+          for (int b = best_x; b < nb; b += kXcds) cand.push_back(b);
+          const int take = std::min<int>(cn, (int)cand.size());
+          std::partial_sort(cand.begin(), cand.begin() + take, cand.end(),
+                            [&](int a, int b) { return load[a] < load[b]; });
+          for (int j = 0; j < cn; ++j) {
+            const int b = cand[j % take];
+            bin[b].push_back({(int)(u.l0 + c0 + j), {s0, s1}});
+            load[b] += s1 - s0;
+          }
+        }
+      }
+    }
+    // Pour the other lanes, in order, into the room left under the makespan.
+    int64_t M = (W + nb - 1) / nb;
+    for (int b = 0; b < nb; ++b) M = std::max(M, load[b]);
+    int fb = 0;
+    for (size_t ui = n_large; ui < units.size(); ++ui)
+      for (size_t k = units[ui].l0; k < units[ui].l1; ++k) {
+        int64_t s0 = 0;
+        const int64_t n = all[k].stages;
+        while (s0 < n) {
+          while (fb < nb && load[fb] >= M) ++fb;  // the room under M covers what is left
+          if (fb == nb) throw std::logic_error("placement overflow");
+          const int64_t take = std::min(n - s0, M - load[fb]);
+          bin[fb].push_back({(int)k, {s0, s0 + take}});
+          load[fb] += take;
+          s0 += take;
+        }
+      }
+    const int first = (int)P->bins.size() - 1;
+    int used = 0;
+    for (int b = 0; b < nb; ++b) {
+      if (bin[b].empty()) continue;
+      for (const auto& e : bin[b]) {
+        Lane& L = all[e.first];
+        const int64_t stok = (int64_t)L.S * bs;
+        WorkItem it{};
+        it.request = L.request;
+        it.tok_begin = (int)(L.tok0 + e.second.first * stok);
+        it.tok_end = (int)std::min<int64_t>(L.tok0 + e.second.second * stok, L.tok_end);
+        it.kv_head = L.kv0;
+        it.kv_heads = L.H;
+        it.member_off = L.member_off;
+        it.ncols = L.ncols;
+        it.col0 = L.col0;
+        it.col1 = L.col1;
+        it.part_base = L.splits++;
+        it.stripes = L.S;
+        P->items.push_back(it);
+        item_lane.push_back(e.first);
+      }
+      P->bins.push_back((int32_t)P->items.size());
+      ++used;
+    }
+    if (used) P->launches.push_back(Launch{first, used});
+  };
+
   int64_t row = 0;
   for (int c = 0; c < G; ++c) {
     const fca_group_record& gr = P->groups[c];
@@ -474,11 +595,17 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
     if (sfx_tokens[i] > 0)
       rq.sfx_lane = add_lanes(all, P->req3[3 * i] * bs, lens[i], i, -1, r, &rq.sfx_H, &rq.sfx_chunks);
   }
+  auto schedule = [&](size_t l0, size_t l1) {
+    if (mla)
+      place(l0, l1);
+    else
+      cut(l0, l1);
+  };
   if (P->desc.flags & FCA_PLAN_SEPARATE_PASSES) {
-    cut(0, n_glanes);
-    cut(n_glanes, all.size());
+    schedule(0, n_glanes);
+    schedule(n_glanes, all.size());
   } else {
-    cut(0, all.size());
+    schedule(0, all.size());
   }
   for (Lane& L : all) {
     L.splits *= L.S;  // stripe splits of every piece

@@ -3,28 +3,29 @@
 // values = its first 512 columns (read once, as part of the key tile).
 //
 // Same method as the GQA kernel ("Core Mechanism" of the ZoRRo Inference &
-// Forest Cascade Attention page, step 2), but every query row now costs
+// Forest Cascade Attention page, step 2), but every query row costs
 // 2 x (576 + 512) flops per token and a request alone has Hq/Hkv = 128 query
 // rows, so both passes are matrix products and the grouped pass is bound by
-// the MFMA rate, not by HBM.  A workgroup of 4 waves (one per SIMD, up to
-// 512 registers each) owns an item of up to 64 query rows (one 16-row tile
-// per wave: the wave's Q operand and its 512-dim output stay in registers
-// for the whole item) and one 64-token block at a time; the block's 72 KiB
-// key tile is copied once into LDS (global_load_lds_dwordx4, a two-slot ring,
-// one block ahead) and read by all four waves.
+// the MFMA rate and by LDS, not by HBM.
 //
-// Per 64-token block and wave:
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: 4 token tiles x 18 d-steps,
-//     the key A operand read straight from the chunked layout (1 KiB per
-//     instruction), the Q B operand held in registers for the whole item;
-//   * online softmax per query row in the log2 domain (4 lane groups reduced
-//     with permlane swaps, lazy rescale on a wave-uniform test);
-//   * O^T += V^T P^T with v_mfma_f32_16x16x16_bf16: the scores are already in
-//     the P^T operand layout; the V^T operand (16 value dims x 4 tokens per
-//     lane) is read from the same chunked key tile with ds_read_b64_tr_b16,
-//     whose 16-lane transpose turns the token-major rows into dim-major
-//     operands: lane (g, c) supplies the 8 bytes of token 4g + c/4, dims
-//     4(c%4)..4(c%4)+3 of the tile and receives dim c of tokens 4g..4g+3.
+// A workgroup of 8 waves (two per SIMD) owns an item of up to 64 query rows
+// and walks its token range in 32-token stages (half a cache block, 36 KiB):
+//   * a 4-slot LDS ring, filled two stages ahead by buffer_load_dwordx4 ... lds
+//     issued by the score waves, one barrier per stage (s_barrier after the
+//     own copies and LDS writes are done: no memory fence, which would wait
+//     for the copies still in flight);
+//   * score waves 0-3, 16 query rows each (the Q operand stays in registers
+//     for the whole item): S^T = K Q^T with v_mfma_f32_16x16x32_bf16, online
+//     softmax per row in the log2 domain with a lazy running max (raised
+//     only when a score exceeds it by more than 2^8, so rescales are rare),
+//     then P (bf16) and the rescale factors go to LDS;
+//   * value waves 4-7, one stage behind, each owning 128 of the 512 value
+//     dims of all 64 rows: O^T += V^T P^T with v_mfma_f32_16x16x32_bf16, the
+//     V^T operand read from the key tile with ds_read_b64_tr_b16 (two 16-token
+//     tiles per operand) and the P^T operand as written by the score waves.
+// Splitting the value dims keeps every wave under 256 registers, so each
+// SIMD runs a score wave and a value wave side by side, and the value tile
+// is read from LDS once per workgroup instead of once per 16 rows.
 // Tokens at or past the end of the range are masked (-inf scores, zeroed
 // values: the tail of a block may hold NaN).
 
@@ -36,22 +37,35 @@ namespace fca {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(4))) const int32_t cint32;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kDq = 576;                   // key (and query) dims
-constexpr int kDv = 512;                   // value dims: the first kDv key dims
-constexpr int kBS = 64;                    // tokens per cache block
-constexpr int kKs = kDq / 32;              // d-steps of the score product
-constexpr int kDt = kDv / 16;              // 16-dim value tiles
-constexpr int kTileBytes = kBS * kDq * 2;  // one (block, head) tile: 72 KiB
-constexpr int kWaves = 4;
-constexpr int kWaveCols = 16;              // query rows per wave
-constexpr int kChunkStride = kBS * 16;     // bytes between 8-dim chunks of a tile
+constexpr int kDq = 576;                         // key (and query) dims
+constexpr int kDv = 512;                         // value dims: the first kDv key dims
+constexpr int kBS = 64;                          // tokens per cache block
+constexpr int kStage = 32;                       // tokens per pipeline stage
+constexpr int kStageBytes = kStage * kDq * 2;    // 36 KiB
+constexpr int kChunk = kStage * 16;              // one 8-dim chunk of a stage in LDS
+constexpr int kSlots = 4;                        // LDS ring
+constexpr int kKs = kDq / 32;                    // d-steps of the score product
+constexpr int kQkWaves = 4;                      // score waves, 16 rows each
+constexpr int kPvWaves = 4;                      // value waves
+constexpr int kWaves = kQkWaves + kPvWaves;
+constexpr int kPvDims = kDv / kPvWaves;          // value dims per value wave
+constexpr int kPvTiles = kPvDims / 16;
+constexpr int kDma = kStageBytes / 1024 / kQkWaves;  // 1 KiB copies per stage and score wave
+static_assert(kDma * kQkWaves * 1024 == kStageBytes, "stage copy split");
+constexpr float kTau = 8.f;                      // lazy-max threshold (log2 units)
+constexpr int kBufferWord3 = 0x00020000;         // raw buffer resource, gfx9 family
+
+constexpr int kOffP = kSlots * kStageBytes;      // P^T operands [2][4 col tiles][64 lanes] x 16 B
+constexpr int kPBytes = kQkWaves * 64 * 16;
+constexpr int kOffA = kOffP + 2 * kPBytes;       // rescale factors [2][16 lanes][4 col tiles]
+constexpr int kLdsBytes = kOffA + 2 * 256;
 
 __device__ __forceinline__ float xmax16(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -70,198 +84,317 @@ __device__ __forceinline__ float xsum32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// s_waitcnt until no vector-memory operation of this wave is outstanding.
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+// s_waitcnt until at most N vector-memory operations of this wave are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
-__device__ __forceinline__ WorkItem load_item(cint32* items, int i) {
+// Workgroup barrier for LDS hand-offs: this wave's LDS operations are done,
+// then s_barrier.  The empty asm statements keep the compiler from moving
+// memory accesses across it.  Copies into LDS are waited for separately.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15 << 0) | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct Item {
+  int request, tok_begin, tok_end, kv_head, member_off, col0, col1, part_base;
+};
+
+__device__ __forceinline__ Item load_item(cint32* items, int i) {
   cint32* p = items + 12 * i;
-  WorkItem w;
+  Item w;
   w.request = p[0];
   w.tok_begin = p[1];
   w.tok_end = p[2];
   w.kv_head = p[3];
   w.member_off = p[4];
-  w.ncols = p[5];
   w.col0 = p[6];
   w.col1 = p[7];
   w.part_base = p[8];
-  w.kv_heads = p[9];
-  w.stripes = w.pad2 = 0;
   return w;
 }
 
-__device__ __forceinline__ int item_blocks(const WorkItem& it) { return (it.tok_end - it.tok_begin + kBS - 1) / kBS; }
+__device__ __forceinline__ int item_stages(const Item& it) { return (it.tok_end - it.tok_begin + kStage - 1) / kStage; }
+
+// Copy cursor: the stages of the bin's items in order, two ahead of the
+// score waves.  Each wave copies instructions [d0, d0 + N) of a stage:
+// instruction i moves chunks 2i and 2i + 1 (32 tokens x 16 B each) of the
+// cache tile into LDS bytes [1024 i, 1024 i + 1024) of the slot.
+template <int N>
+struct Copier {
+  cint32* items;
+  int di, ds, dns, i_end;
+  Item it;
+  __device__ __forceinline__ void next() {
+    if (++ds == dns) {
+      ds = 0;
+      if (++di < i_end) {
+        it = load_item(items, di);
+        dns = item_stages(it);
+      }
+    }
+  }
+  __device__ __forceinline__ void issue(const GqaParams& P, cint32* bt, char* slot, int d0, int lane) {
+    const int t0 = it.tok_begin + ds * kStage;
+    const int id = bt[(int64_t)it.request * P.W + t0 / kBS];
+    const char* tile = static_cast<const char*>(P.k) +
+                       ((int64_t)id * P.k_stride_block + (int64_t)it.kv_head * P.k_stride_head) * 2;
+    // Raw buffer over the tile (MUBUF loads to LDS: counted by vmcnt alone).
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile), (short)0, kBS * kDq * 2, kBufferWord3);
+    const int voff = (lane >> 5) * (kBS * 16) + (lane & 31) * 16;
+    const int half = ((t0 / kStage) & 1) * kChunk;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (d0 + i) * 1024), 16, voff,
+                                               half + (d0 + i) * 2 * (kBS * 16), 0, 0);
+    next();
+  }
+};
 
 }  // namespace
 
 __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int c16 = lane & 15;
   const float NEG_INF = -INFINITY;
-  const float sc = P.scale_log2;
 
   cint32* head = (cint32*)(P.bins + blockIdx.x);
   cint32* items = (cint32*)(P.items);
-  cint32* bt = (cint32*)(P.bt);
-  cint32* perm = (cint32*)(P.perm);
   const int i_begin = head[0];
   const int i_end = head[1];
-  const char* kpool = static_cast<const char*>(P.k);
-  const __bf16* qbase = static_cast<const __bf16*>(P.q);
+  int N = 0;  // stages of the bin
+  for (int i = i_begin; i < i_end; ++i) {
+    cint32* p = items + 12 * i;
+    N += (p[2] - p[1] + kStage - 1) / kStage;
+  }
+  if (N == 0) return;
 
-  // ---- copy cursor: item di, block db ----
-  int di = i_begin, db = 0;
-  WorkItem dit = load_item(items, di);
-  int dnb = item_blocks(dit);
-  // Copy block db of item di into a slot: 72 instructions of 1 KiB, 18 per
-  // wave (wave w copies chunks 18w .. 18w + 17 of the 72 8-dim chunks).
-  auto issue = [&](int slot) {
-    const int id = bt[(int64_t)dit.request * P.W + dit.tok_begin / kBS + db];
-    const char* src =
-        kpool + ((int64_t)id * P.k_stride_block + (int64_t)dit.kv_head * P.k_stride_head) * 2 + lane * 16;
-    char* dst = lds + slot * kTileBytes;
-#pragma unroll
-    for (int i = 0; i < kTileBytes / 1024 / kWaves; ++i) {
-      const int off = (wave * (kTileBytes / 1024 / kWaves) + i) * 1024;
-      __builtin_amdgcn_global_load_lds(src + off, (lds_void*)(dst + off), 16, 0, 0);
-    }
-    if (++db == dnb) {
-      db = 0;
-      if (++di < i_end) {
-        dit = load_item(items, di);
-        dnb = item_blocks(dit);
-      }
-    }
-  };
+  if (wave < kQkWaves) {
+    // ---------------- score wave: rows 16 w .. 16 w + 15 of the item ----------------
+    const int w = wave;
+    cint32* bt = (cint32*)(P.bt);
+    Copier<kDma> cp{items, i_begin, 0, 0, i_end, load_item(items, i_begin)};
+    cp.dns = item_stages(cp.it);
+    const int d0 = w * kDma;
+    cp.issue(P, bt, lds, d0, lane);
+    if (N > 1) cp.issue(P, bt, lds + kStageBytes, d0, lane);
 
-  // ---- compute cursor ----
-  WorkItem cit = load_item(items, i_begin);
-  int ci = i_begin, cb = 0, cnb = item_blocks(cit);
-  int c_lo = 0, ncol = 0;  // this wave's columns of the item, relative to col0
-  bf16x8 qb[kKs];
-  f32x4 o[kDt];
-  float mrow = NEG_INF, lsum = 0.f;
+    const __bf16* qbase = static_cast<const __bf16*>(P.q);
+    cint32* perm = (cint32*)(P.perm);
+    const float sc = P.scale_log2;
+    Item it = load_item(items, i_begin);
+    int ci = i_begin, cs = 0, cns = item_stages(it);
+    bf16x8 qb[kKs];
+    float mrow = NEG_INF, lsum = 0.f;
+    bool active = false;
 
-  // Q^T operand of the wave's 16 columns (d-chunk 32 ks + 8 g of column
-  // c16) and fresh accumulators.  Columns past the item read its first row
-  // and are zeroed.
-  auto begin_item = [&]() {
-    const int ccols = cit.col1 - cit.col0;
-    c_lo = wave * kWaveCols;
-    ncol = min(kWaveCols, ccols - c_lo);
-    const bool use = c16 < ncol;
-    const int col = cit.col0 + (use ? c_lo + c16 : 0);
-    const int member = cit.member_off >= 0 ? perm[cit.member_off + col / P.r] : cit.request;
-    const int qh = cit.kv_head * P.r + col % P.r;
-    const __bf16* qp = qbase + ((int64_t)member * P.Hq + qh) * kDq + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
-      qb[ks] = use ? v : bf16x8{};
-    }
-    mrow = NEG_INF;
-    lsum = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < kDt; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  };
+    for (int t = 0; t <= N; ++t) {
+      // Stage t has landed (this wave's copies; the barrier covers the rest).
+      if (t + 1 < N)
+        wait_vm<kDma>();
+      else
+        wait_vm<0>();
+      lds_barrier();
+      if (t == N) break;
 
-  auto compute_block = [&](const char* kt, int t0) {
-    // Scores of the 4 token tiles.
-    f32x4 s[4];
+      const int ccols = it.col1 - it.col0;
+      if (cs == 0) {
+        // Q^T operand of the wave's 16 rows (d-chunk 32 ks + 8 g of row c16);
+        // rows past the item read its first row.
+        active = 16 * w < ccols;
+        const int col = it.col0 + (16 * w + c16 < ccols ? 16 * w + c16 : 0);
+        const int member = it.member_off >= 0 ? perm[it.member_off + col / P.r] : it.request;
+        const int qh = it.kv_head * P.r + col % P.r;
+        const __bf16* qp = qbase + ((int64_t)member * P.Hq + qh) * kDq + 8 * g;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < kKs; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
+        wait_vm<0>();
+        mrow = NEG_INF;
+        lsum = 0.f;
+      }
+      // The copy of stage t + 2 goes into the slot of stage t - 2, which
+      // every wave finished before this stage's barrier.
+      if (t + 2 < N) cp.issue(P, bt, lds + ((t + 2) % kSlots) * kStageBytes, d0, lane);
+      const int buf = t & 1;
+      if (active) {
+        // S^T = K Q^T over 18 d-steps; the key operands are read from LDS
+        // in 6 batches of 3 d-steps, one batch ahead of the products.
+        const char* kt = lds + (t % kSlots) * kStageBytes + g * kChunk + c16 * 16;
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+        constexpr int kB = 3;
+        bf16x8 ka[2][2 * kB];
 #pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
+        for (int i = 0; i < kB; ++i) {
+          ka[0][2 * i] = *reinterpret_cast<const bf16x8*>(kt + 4 * i * kChunk);
+          ka[0][2 * i + 1] = *reinterpret_cast<const bf16x8*>(kt + 4 * i * kChunk + 16 * 16);
+        }
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + (4 * ks + g) * kChunkStride + (16 * tt + c16) * 16);
-        s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], s[tt], 0, 0, 0);
+        for (int b = 0; b < kKs / kB; ++b) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (b + 1 < kKs / kB) {
+#pragma unroll
+            for (int i = 0; i < kB; ++i) {
+              const int ks = (b + 1) * kB + i;
+              ka[(b + 1) & 1][2 * i] = *reinterpret_cast<const bf16x8*>(kt + 4 * ks * kChunk);
+              ka[(b + 1) & 1][2 * i + 1] = *reinterpret_cast<const bf16x8*>(kt + 4 * ks * kChunk + 16 * 16);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < kB; ++i) {
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[b & 1][2 * i], qb[b * kB + i], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[b & 1][2 * i + 1], qb[b * kB + i], s1, 0, 0, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int nvalid = it.tok_end - (it.tok_begin + cs * kStage);
+        if (nvalid < kStage) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            s0[j] = 4 * g + j < nvalid ? s0[j] : NEG_INF;
+            s1[j] = 16 + 4 * g + j < nvalid ? s1[j] : NEG_INF;
+          }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                         fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+        mx = xmax32(xmax16(mx)) * sc;
+        float alpha = 1.f;
+        if (__builtin_amdgcn_ballot_w64(mx > mrow + kTau)) {
+          const float mnew = mx > mrow + kTau ? mx : mrow;
+          alpha = exp2f(mrow - mnew);
+          lsum *= alpha;
+          mrow = mnew;
+        }
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = exp2f(fmaf(s0[j], sc, -mrow));
+          const float p1 = exp2f(fmaf(s1[j], sc, -mrow));
+          lsum += p0 + p1;
+          pb[j] = (__bf16)p0;
+          pb[4 + j] = (__bf16)p1;
+        }
+        *reinterpret_cast<bf16x8*>(lds + kOffP + buf * kPBytes + (w * 64 + lane) * 16) = pb;
+        if (g == 0) reinterpret_cast<float*>(lds + kOffA + buf * 256)[c16 * 4 + w] = alpha;
+      }
+      if (++cs == cns) {
+        if (active) {
+          const float l = xsum32(xsum16(lsum));
+          if (g == 0 && 16 * w + c16 < ccols) {
+            const int64_t row = (int64_t)it.part_base + 16 * w + c16;
+            P.part.m[row] = mrow;
+            P.part.l[row] = l;
+          }
+        }
+        cs = 0;
+        if (++ci < i_end) {
+          it = load_item(items, ci);
+          cns = item_stages(it);
+        }
       }
     }
-    const bool partial = t0 + kBS > cit.tok_end;
-    if (partial) {
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int nvalid = cit.tok_end - t0 - 16 * tt - 4 * g;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s[tt][j] = j < nvalid ? s[tt][j] : NEG_INF;
-      }
-    }
-    float mx = NEG_INF;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) mx = fmaxf(mx, fmaxf(fmaxf(s[tt][0], s[tt][1]), fmaxf(s[tt][2], s[tt][3])));
-    mx = xmax32(xmax16(mx));
-    const float mnew = fmaxf(mrow, mx * sc);
-    if (__builtin_amdgcn_ballot_w64(mnew > mrow)) {  // some column's max grew
-      const float alpha = exp2f(mrow - mnew);
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < kDt; ++dt) o[dt] *= alpha;
-      mrow = mnew;
-    }
-    bf16x4 pb[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = exp2f(fmaf(s[tt][j], sc, -mrow));
-        pb[tt][j] = (__bf16)p;
-        lsum += p;
-      }
-    // Values: the V^T operand of (value tile dt, token tile tt) through the
-    // transposing LDS read; tokens past the range are zeroed.
-    const int tr_off = ((c16 & 3) / 2) * kChunkStride + (4 * g + c16 / 4) * 16 + (c16 & 1) * 8;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      u32x2 keep = {0xffffffffu, 0xffffffffu};
-      if (partial) {
-        const int nvalid = cit.tok_end - t0 - 16 * tt - 4 * g;
-        keep = u32x2{(nvalid > 0 ? 0xffffu : 0u) | (nvalid > 1 ? 0xffff0000u : 0u),
-                     (nvalid > 2 ? 0xffffu : 0u) | (nvalid > 3 ? 0xffff0000u : 0u)};
-      }
-#pragma unroll
-      for (int dt = 0; dt < kDt; ++dt) {
-        const char* src = kt + 2 * dt * kChunkStride + 16 * tt * 16 + tr_off;
-        const i16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)src);
-        const bf16x4 a = __builtin_bit_cast(bf16x4, __builtin_bit_cast(u32x2, raw) & keep);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb[tt], o[dt], 0, 0, 0);
-      }
-    }
-  };
+  } else {
+    // ---------------- value wave: dims 128 v .. 128 v + 127 of all rows ----------------
+    // Issues no copies, so its LDS reads never wait for copies in flight.
+    const int v = wave - kQkWaves;
+    Item it = load_item(items, i_begin);
+    int ci = i_begin, cs = 0, cns = item_stages(it);
+    f32x4 o[4][kPvTiles];
+    // ds_read_b64_tr_b16 source of lane (g, c16) in a 16 x 16 (token, dim)
+    // tile: token 4 g + c16 / 4, dims 4 (c16 % 4) .. + 3; it receives dim
+    // c16 of tokens 4 g .. 4 g + 3.
+    const int tr_off = ((c16 & 3) >> 1) * kChunk + (4 * g + (c16 >> 2)) * 16 + (c16 & 1) * 8;
 
-  auto finish_item = [&]() {
-    const float l = xsum32(xsum16(lsum));
-    if (c16 < ncol) {
-      const int64_t row = (int64_t)cit.part_base + c_lo + c16;
-      float* dst = P.part.o + row * kDv + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < kDt; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt];
-      if (g == 0) {
-        P.part.m[row] = mrow;
-        P.part.l[row] = l;
-      }
-    }
-  };
+    for (int t = 0; t <= N; ++t) {
+      lds_barrier();
+      if (t == 0) continue;
 
-  issue(0);
-  for (int it = 0;; ++it) {
-    // Block `it` has landed for every wave, and every wave is done with
-    // block it - 1, whose slot the next copy reuses.
-    wait_vm_all();
-    __syncthreads();
-    if (cb == 0) begin_item();
-    if (di < i_end) issue((it + 1) & 1);
-    if (ncol > 0) compute_block(lds + (it & 1) * kTileBytes, cit.tok_begin + cb * kBS);
-    if (++cb == cnb) {
-      if (ncol > 0) finish_item();
-      if (++ci == i_end) break;
-      cit = load_item(items, ci);
-      cnb = item_blocks(cit);
-      cb = 0;
+      // Stage t - 1.
+      const int buf = (t - 1) & 1;
+      const int ccols = it.col1 - it.col0;
+      const int nct = (ccols + 15) >> 4;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        pb[ct] = *reinterpret_cast<const bf16x8*>(lds + kOffP + buf * kPBytes + (ct * 64 + lane) * 16);
+      const char* kt = lds + ((t - 1) % kSlots) * kStageBytes + (2 * v * kPvTiles) * kChunk + tr_off;
+      u32x2 vr[kPvTiles][2];
+#pragma unroll
+      for (int dt = 0; dt < kPvTiles; ++dt)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          vr[dt][tt] = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                         (__attribute__((address_space(3))) i16x4*)(kt + 2 * dt * kChunk + tt * 16 * 16)));
+      __builtin_amdgcn_sched_barrier(0);
+      const int nvalid = it.tok_end - (it.tok_begin + cs * kStage);
+      u32x4 keep = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+      if (nvalid < kStage) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int nv = nvalid - 16 * tt - 4 * g;
+          keep[2 * tt] = (nv > 0 ? 0xffffu : 0u) | (nv > 1 ? 0xffff0000u : 0u);
+          keep[2 * tt + 1] = (nv > 2 ? 0xffffu : 0u) | (nv > 3 ? 0xffff0000u : 0u);
+        }
+      }
+      if (cs == 0) {
+        // First stage of the item: fresh accumulators.
+#pragma unroll
+        for (int dt = 0; dt < kPvTiles; ++dt) {
+          const bf16x8 a =
+              __builtin_bit_cast(bf16x8, u32x4{vr[dt][0][0], vr[dt][0][1], vr[dt][1][0], vr[dt][1][1]} & keep);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ct], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        }
+      } else {
+        const f32x4 al = *reinterpret_cast<const f32x4*>(lds + kOffA + buf * 256 + c16 * 16);
+        bool scale = false;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) scale |= ct < nct && al[ct] != 1.f;
+        if (__builtin_amdgcn_ballot_w64(scale)) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const float f = ct < nct ? al[ct] : 1.f;
+#pragma unroll
+            for (int dt = 0; dt < kPvTiles; ++dt) o[ct][dt] *= f;
+          }
+        }
+#pragma unroll
+        for (int dt = 0; dt < kPvTiles; ++dt) {
+          const bf16x8 a =
+              __builtin_bit_cast(bf16x8, u32x4{vr[dt][0][0], vr[dt][0][1], vr[dt][1][0], vr[dt][1][1]} & keep);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ct], o[ct][dt], 0, 0, 0);
+        }
+      }
+      if (++cs == cns) {
+        // Partial rows hold the unnormalised sums (the merge divides).
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          if (16 * ct + c16 < ccols) {
+            float* dst = P.part.o + ((int64_t)it.part_base + 16 * ct + c16) * kDv + v * kPvDims + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < kPvTiles; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[ct][dt];
+          }
+        }
+        cs = 0;
+        if (++ci < i_end) {
+          it = load_item(items, ci);
+          cns = item_stages(it);
+        }
+      }
     }
   }
 }
