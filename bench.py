@@ -52,6 +52,11 @@ def parse():
     ap.add_argument("--no-noncascade", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="few steps, no baselines (for rocprofv3)")
     ap.add_argument(
+        "--group-sweep",
+        action="store_true",
+        help="also time cascade vs non-cascade over group sizes 1..64 (64 requests, Llama-3 layer shape)",
+    )
+    ap.add_argument(
         "--copy-calibration",
         action="store_true",
         help="also run a plain elementwise copy of known size (scale of the HBM byte counters)",
@@ -152,6 +157,61 @@ def cpu_baseline(batch, vals, budget_s, threads):
         sample=f"first {done} of {batch.batch} requests ({tokens} logical tokens), fp64 numpy oracle, "
         f"{threads} BLAS thread(s), {elapsed:.1f} s",
     )
+
+
+def group_sweep(torch, fca, steps, warmup):
+    """Cascade vs non-cascade over the group size: 64 requests of the
+    Llama-3-8B layer shape, prefix 4096, suffix U{256..1024}, as 64 / s
+    prompts x s samples for s = 1 .. 64.  Two KV pools are cycled."""
+    from workloads import build_batch
+    from workloads.forest import GQA_LLAMA, Config, Node
+    from workloads.values import fill_values_torch
+
+    rows = []
+    for s in (1, 2, 4, 8, 16, 32, 64):
+        if s == 1:  # no sharing: 64 unshared requests of the same lengths
+            cfg = Config(name="sweep_s1", shape=GQA_LLAMA, trees=[], singletons=64,
+                         singleton_len=(4096 + 256, 4096 + 1024), seed=101)
+        else:
+            cfg = Config(
+                name=f"sweep_s{s}",
+                shape=GQA_LLAMA,
+                trees=[Node(4096, samples=s, suffix=(256, 1024)) for _ in range(64 // s)],
+                seed=100 + s,
+            )
+        batch = build_batch(cfg)
+        sh = batch.shape
+        pools, qs = [], []
+        for layer in range(2):
+            v = fill_values_torch(batch, "cuda", seed=cfg.seed * 1000 + layer, poison=False)
+            pools.append((v["k"], v["v"]))
+            qs.append(v["q"])
+        bt = torch.from_numpy(batch.block_tables).cuda()
+        sl = torch.from_numpy(batch.seq_lens).cuda()
+        out = torch.empty((batch.batch, sh.num_q_heads, sh.head_dim_v), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((batch.batch, sh.num_q_heads), dtype=torch.float32, device="cuda")
+        res = {}
+        for cascade in (True, False):
+            plan = fca.fca_plan(bt, sl, fca.desc_from_shape(sh, batch.num_blocks, cascade=cascade))
+            plan.decode_workspace(out.device)
+            time_steps(plan, qs, pools, out, lse, warmup, torch, fca)
+            ms, _ = time_steps(plan, qs, pools, out, lse, steps, torch, fca)
+            res[cascade] = (ms, plan.info)
+        ms_c, info = res[True]
+        ms_n, _ = res[False]
+        row = {
+            "samples_per_prompt": s,
+            "groups": int(info.num_groups),
+            "byte_ratio_R": round(int(info.logical_tokens) / max(int(info.unique_tokens), 1), 3),
+            "cascade_us": round(ms_c * 1000, 2),
+            "non_cascade_us": round(ms_n * 1000, 2),
+            "speedup": round(ms_n / ms_c, 3),
+        }
+        log("group sweep:", row)
+        rows.append(row)
+        del pools, qs
+        torch.cuda.empty_cache()
+    return rows
 
 
 def main():
@@ -381,6 +441,9 @@ def main():
             "byte_ratio_R": round(logical / max(int(info.unique_tokens), 1), 3),
         }
         del plan_nc
+
+    if args.group_sweep and not args.profile_only:
+        result["group_sweep"] = group_sweep(torch, fca, steps, warmup)
 
     if not args.no_cpu_baseline and not args.profile_only:
         ncpu = len(os.sched_getaffinity(0))
