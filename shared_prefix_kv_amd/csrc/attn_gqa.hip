@@ -363,7 +363,7 @@ __device__ __forceinline__ void stream_body(const CopyArgs& ca, const GqaParams&
             mx = xmax32(xmax16(mx));
             const float mnew = fmaxf(mrow[ct], mx * sc);
             if (__builtin_amdgcn_ballot_w64(mnew > mrow[ct])) {  // some column's max grew
-              const float alpha = exp2f(mrow[ct] - mnew);        // 0 on the first block
+              const float alpha = __builtin_amdgcn_exp2f(mrow[ct] - mnew);        // 0 on the first block
               lsum[ct] *= alpha;
 #pragma unroll
               for (int dt = 0; dt < 8; ++dt) o[ct][dt] *= alpha;
@@ -371,7 +371,7 @@ __device__ __forceinline__ void stream_body(const CopyArgs& ca, const GqaParams&
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float p = exp2f(fmaf(s[ct][j], sc, -mrow[ct]));
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[ct][j], sc, -mrow[ct]));
               pb[ct][j] = (__bf16)p;
               lsum[ct] += p;
             }

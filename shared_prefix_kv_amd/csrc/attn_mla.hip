@@ -11,9 +11,10 @@
 // A workgroup of 8 waves (two per SIMD) owns an item of up to 64 query rows
 // and walks its token range in 32-token stages (half a cache block, 36 KiB):
 //   * a 4-slot LDS ring, filled two stages ahead by buffer_load_dwordx4 ... lds
-//     issued by the score waves, one barrier per stage (s_barrier after the
-//     own copies and LDS writes are done: no memory fence, which would wait
-//     for the copies still in flight);
+//     (mostly issued by the value waves, which otherwise wait for the score
+//     waves at the barrier), one barrier per stage (s_barrier after the own
+//     copies and LDS writes are done: no memory fence, which would wait for
+//     the copies still in flight);
 //   * score waves 0-3, 16 query rows each (the Q operand stays in registers
 //     for the whole item): S^T = K Q^T with v_mfma_f32_16x16x32_bf16, online
 //     softmax per row in the log2 domain with a lazy running max (raised
@@ -57,8 +58,9 @@ constexpr int kPvWaves = 4;                      // value waves
 constexpr int kWaves = kQkWaves + kPvWaves;
 constexpr int kPvDims = kDv / kPvWaves;          // value dims per value wave
 constexpr int kPvTiles = kPvDims / 16;
-constexpr int kDma = kStageBytes / 1024 / kQkWaves;  // 1 KiB copies per stage and score wave
-static_assert(kDma * kQkWaves * 1024 == kStageBytes, "stage copy split");
+constexpr int kDmaQ = 2;                                     // 1 KiB copies per stage and score wave
+constexpr int kDmaP = (kStageBytes / 1024 - kQkWaves * kDmaQ) / kPvWaves;  // ... and value wave
+static_assert((kQkWaves * kDmaQ + kPvWaves * kDmaP) * 1024 == kStageBytes, "stage copy split");
 constexpr float kTau = 8.f;                      // lazy-max threshold (log2 units)
 constexpr int kBufferWord3 = 0x00020000;         // raw buffer resource, gfx9 family
 
@@ -90,6 +92,38 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+
+// The 16 V^T operands of a value wave's stage: ds_read_b64_tr_b16 at
+// kt + 1024 dt + 256 tt for dt < 8, tt < 2, in one block that waits for its
+// own results (the compiler would otherwise wait for every LDS copy in
+// flight before each transposing read, as it cannot tell them apart).
+__device__ __forceinline__ void read_vt(const char* kt, u32x2 (&r)[8][2]) {
+  const uint32_t a = (uint32_t)(uintptr_t)kt;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:0\n"
+      "ds_read_b64_tr_b16 %1, %16 offset:256\n"
+      "ds_read_b64_tr_b16 %2, %16 offset:1024\n"
+      "ds_read_b64_tr_b16 %3, %16 offset:1280\n"
+      "ds_read_b64_tr_b16 %4, %16 offset:2048\n"
+      "ds_read_b64_tr_b16 %5, %16 offset:2304\n"
+      "ds_read_b64_tr_b16 %6, %16 offset:3072\n"
+      "ds_read_b64_tr_b16 %7, %16 offset:3328\n"
+      "ds_read_b64_tr_b16 %8, %16 offset:4096\n"
+      "ds_read_b64_tr_b16 %9, %16 offset:4352\n"
+      "ds_read_b64_tr_b16 %10, %16 offset:5120\n"
+      "ds_read_b64_tr_b16 %11, %16 offset:5376\n"
+      "ds_read_b64_tr_b16 %12, %16 offset:6144\n"
+      "ds_read_b64_tr_b16 %13, %16 offset:6400\n"
+      "ds_read_b64_tr_b16 %14, %16 offset:7168\n"
+      "ds_read_b64_tr_b16 %15, %16 offset:7424\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[2][0]), "=&v"(r[2][1]),
+        "=&v"(r[3][0]), "=&v"(r[3][1]), "=&v"(r[4][0]), "=&v"(r[4][1]), "=&v"(r[5][0]), "=&v"(r[5][1]),
+        "=&v"(r[6][0]), "=&v"(r[6][1]), "=&v"(r[7][0]), "=&v"(r[7][1])
+      : "v"(a)
+      : "memory");
+}
+static_assert(2 * kChunk == 1024 && 16 * 16 == 256 && kPvTiles == 8, "read_vt offsets");
 
 // Workgroup barrier for LDS hand-offs: this wave's LDS operations are done,
 // then s_barrier.  The empty asm statements keep the compiler from moving
@@ -183,11 +217,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
     // ---------------- score wave: rows 16 w .. 16 w + 15 of the item ----------------
     const int w = wave;
     cint32* bt = (cint32*)(P.bt);
-    Copier<kDma> cp{items, i_begin, 0, 0, i_end, load_item(items, i_begin)};
+    Copier<kDmaQ> cp{items, i_begin, 0, 0, i_end, load_item(items, i_begin)};
     cp.dns = item_stages(cp.it);
-    const int d0 = w * kDma;
-    cp.issue(P, bt, lds, d0, lane);
-    if (N > 1) cp.issue(P, bt, lds + kStageBytes, d0, lane);
+    const int d0 = w * kDmaQ;
+    if (kDmaQ > 0) {
+      cp.issue(P, bt, lds, d0, lane);
+      if (N > 1) cp.issue(P, bt, lds + kStageBytes, d0, lane);
+    }
 
     const __bf16* qbase = static_cast<const __bf16*>(P.q);
     cint32* perm = (cint32*)(P.perm);
@@ -201,7 +237,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
     for (int t = 0; t <= N; ++t) {
       // Stage t has landed (this wave's copies; the barrier covers the rest).
       if (t + 1 < N)
-        wait_vm<kDma>();
+        wait_vm<kDmaQ>();
       else
         wait_vm<0>();
       lds_barrier();
@@ -224,7 +260,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
       }
       // The copy of stage t + 2 goes into the slot of stage t - 2, which
       // every wave finished before this stage's barrier.
-      if (t + 2 < N) cp.issue(P, bt, lds + ((t + 2) % kSlots) * kStageBytes, d0, lane);
+      if (kDmaQ > 0 && t + 2 < N) cp.issue(P, bt, lds + ((t + 2) % kSlots) * kStageBytes, d0, lane);
       const int buf = t & 1;
       if (active) {
         // S^T = K Q^T over 18 d-steps; the key operands are read from LDS
@@ -232,6 +268,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
         const char* kt = lds + (t % kSlots) * kStageBytes + g * kChunk + c16 * 16;
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
         constexpr int kB = 3;
+        __builtin_amdgcn_s_setprio(1);  // the score products go first on the shared MFMA pipe
         bf16x8 ka[2][2 * kB];
 #pragma unroll
         for (int i = 0; i < kB; ++i) {
@@ -257,6 +294,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         const int nvalid = it.tok_end - (it.tok_begin + cs * kStage);
         if (nvalid < kStage) {
 #pragma unroll
@@ -271,15 +309,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
         float alpha = 1.f;
         if (__builtin_amdgcn_ballot_w64(mx > mrow + kTau)) {
           const float mnew = mx > mrow + kTau ? mx : mrow;
-          alpha = exp2f(mrow - mnew);
+          alpha = __builtin_amdgcn_exp2f(mrow - mnew);
           lsum *= alpha;
           mrow = mnew;
         }
         bf16x8 pb;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = exp2f(fmaf(s0[j], sc, -mrow));
-          const float p1 = exp2f(fmaf(s1[j], sc, -mrow));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[j], sc, -mrow));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[j], sc, -mrow));
           lsum += p0 + p1;
           pb[j] = (__bf16)p0;
           pb[4 + j] = (__bf16)p1;
@@ -305,8 +343,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
     }
   } else {
     // ---------------- value wave: dims 128 v .. 128 v + 127 of all rows ----------------
-    // Issues no copies, so its LDS reads never wait for copies in flight.
     const int v = wave - kQkWaves;
+    cint32* bt = (cint32*)(P.bt);
+    Copier<kDmaP> cp{items, i_begin, 0, 0, i_end, load_item(items, i_begin)};
+    cp.dns = item_stages(cp.it);
+    const int d0 = kQkWaves * kDmaQ + v * kDmaP;
+    cp.issue(P, bt, lds, d0, lane);
+    if (N > 1) cp.issue(P, bt, lds + kStageBytes, d0, lane);
     Item it = load_item(items, i_begin);
     int ci = i_begin, cs = 0, cns = item_stages(it);
     f32x4 o[4][kPvTiles];
@@ -316,7 +359,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
     const int tr_off = ((c16 & 3) >> 1) * kChunk + (4 * g + (c16 >> 2)) * 16 + (c16 & 1) * 8;
 
     for (int t = 0; t <= N; ++t) {
+      if (t + 1 < N)
+        wait_vm<kDmaP>();
+      else
+        wait_vm<0>();
       lds_barrier();
+      // The copy of stage t + 2 goes into the slot of stage t - 2, which
+      // every wave finished before this barrier.
+      if (t + 2 < N) cp.issue(P, bt, lds + ((t + 2) % kSlots) * kStageBytes, d0, lane);
       if (t == 0) continue;
 
       // Stage t - 1.
@@ -329,14 +379,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
         pb[ct] = *reinterpret_cast<const bf16x8*>(lds + kOffP + buf * kPBytes + (ct * 64 + lane) * 16);
       const char* kt = lds + ((t - 1) % kSlots) * kStageBytes + (2 * v * kPvTiles) * kChunk + tr_off;
       u32x2 vr[kPvTiles][2];
-#pragma unroll
-      for (int dt = 0; dt < kPvTiles; ++dt)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          vr[dt][tt] = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                         (__attribute__((address_space(3))) i16x4*)(kt + 2 * dt * kChunk + tt * 16 * 16)));
-      __builtin_amdgcn_sched_barrier(0);
+      read_vt(kt, vr);
       const int nvalid = it.tok_end - (it.tok_begin + cs * kStage);
       u32x4 keep = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
       if (nvalid < kStage) {
