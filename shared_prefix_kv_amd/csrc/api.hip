@@ -136,7 +136,7 @@ Layout make_layout(int B, int W) {
 
 // Plan-owned device buffer holding the schedule.
 struct SchedLayout {
-  size_t items, heads, perm, req, grp, lanes, total;
+  size_t items, heads, perm, src_off, src_row, total;
 };
 
 // One launch of the attention kernel: bins [bin0, bin0 + n_bins) of the
@@ -183,6 +183,7 @@ struct fca_plan_s {
   std::vector<ReqMeta> req;
   std::vector<GroupMeta> grp;
   std::vector<LaneMeta> lanes;  // grouped lanes, then suffix lanes
+  std::vector<int32_t> src_off, src_row;  // merge sources per (request, query head), CSR
   int item_cols = kItemColsGqa;  // query rows per column chunk
   fca_plan_info info;
   // plan-owned device copy of the schedule
@@ -625,10 +626,17 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   for (const Lane& L : all)
     P->lanes.push_back(LaneMeta{(int32_t)L.base, L.splits, L.kv0, L.H, L.col0, L.col1 - L.col0, 0, 0});
 
-  // Merge sources: one per (request, query head, token split on its path).
-  int64_t sources = 0;
+  // Merge sources: one per (request, query head, token split on its path),
+  // as a flat table of partial-row indices the merge reads directly.
+  P->src_off.assign((size_t)B * hq + 1, 0);
+  P->src_row.clear();
   for (int i = 0; i < B; ++i)
-    for (int h = 0; h < hq; ++h) sources += count_sources(*P, i, h);
+    for (int h = 0; h < hq; ++h) {
+      for_each_source(*P, i, h, [&](int64_t rw) { P->src_row.push_back((int32_t)rw); });
+      if (P->src_row.size() > (size_t)INT32_MAX) return fail(FCA_ERR_UNSUPPORTED, "too many merge sources");
+      P->src_off[(size_t)i * hq + h + 1] = (int32_t)P->src_row.size();
+    }
+  const int64_t sources = (int64_t)P->src_row.size();
 
   fca_plan_info& info = P->info;
   info.batch = B;
@@ -732,9 +740,8 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
     S.items = place(P->items.size() * sizeof(WorkItem));
     S.heads = place(heads.size() * sizeof(BinHead));
     S.perm = place(P->perm.size() * 4);
-    S.req = place(P->req.size() * sizeof(ReqMeta));
-    S.grp = place(P->grp.size() * sizeof(GroupMeta));
-    S.lanes = place(P->lanes.size() * sizeof(LaneMeta));
+    S.src_off = place(P->src_off.size() * 4);
+    S.src_row = place(P->src_row.size() * 4);
     S.total = off;
     e = hipMalloc(&P->sched, S.total);
     if (e != hipSuccess) {
@@ -749,9 +756,8 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
         {P->items.data(), S.items, P->items.size() * sizeof(WorkItem)},
         {heads.data(), S.heads, heads.size() * sizeof(BinHead)},
         {P->perm.data(), S.perm, P->perm.size() * 4},
-        {P->req.data(), S.req, P->req.size() * sizeof(ReqMeta)},
-        {P->grp.data(), S.grp, P->grp.size() * sizeof(GroupMeta)},
-        {P->lanes.data(), S.lanes, P->lanes.size() * sizeof(LaneMeta)},
+        {P->src_off.data(), S.src_off, P->src_off.size() * 4},
+        {P->src_row.data(), S.src_row, P->src_row.size() * 4},
     };
     for (const Up& u : ups) {
       if (!u.bytes) continue;
@@ -867,15 +873,11 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   FCA_TRY(mark(5), "event record");
 
   MergeParams mp;
-  mp.req = reinterpret_cast<const ReqMeta*>(P->sched + S.req);
-  mp.grp = reinterpret_cast<const GroupMeta*>(P->sched + S.grp);
-  mp.lanes = reinterpret_cast<const LaneMeta*>(P->sched + S.lanes);
+  mp.src_off = reinterpret_cast<const int32_t*>(P->sched + S.src_off);
+  mp.src_row = reinterpret_cast<const int32_t*>(P->sched + S.src_row);
   mp.B = P->B;
   mp.Hq = P->desc.num_q_heads;
-  mp.Hkv = P->desc.num_kv_heads;
-  mp.r = P->r;
   mp.Dv = P->desc.head_dim_v;
-  mp.item_cols = P->item_cols;
   mp.part = part;
   mp.out = out_dev;
   mp.lse = lse_dev;

@@ -145,11 +145,12 @@ hipError_t launch_attention(const GqaParams& p, int n_bins, hipStream_t s);
 hipError_t launch_mla(const GqaParams& p, int n_bins, hipStream_t s);
 
 struct MergeParams {
-  const ReqMeta* req;
-  const GroupMeta* grp;
-  const LaneMeta* lanes;
-  int32_t B, Hq, Hkv, r, Dv;
-  int32_t item_cols;  // query rows per column chunk of a lane
+  // Partial rows of (request i, query head h), in merge order (deepest
+  // group's splits, then its ancestors', then the suffix's):
+  // src_row[src_off[i * Hq + h] .. src_off[i * Hq + h + 1]).
+  const int32_t* src_off;
+  const int32_t* src_row;
+  int32_t B, Hq, Dv;
   PartialPtrs part;
   void* out;
   float* lse;

@@ -46,8 +46,9 @@ __device__ __forceinline__ float xsum32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One wave per (request, head).  Lane j resolves the j-th partial row of the
-// request's path so that all (m, l) loads are issued at once; the value rows
+// One wave per (request, head).  Lane j reads the j-th partial row index of
+// the pair from the plan's source table, so that all (m, l) loads are issued
+// at once after two dependent loads; the value rows
 // are then accumulated two at a time (lanes 0-31 take even sources, lanes
 // 32-63 odd ones, each lane DV/32 value dims), eight rows in flight per
 // wave, and the two halves are added at the end.
@@ -60,26 +61,8 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
   const int hl = lane & 31;
   const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= (int64_t)P.B * P.Hq) return;
-  const int i = (int)(pair / P.Hq);
-  const int h = (int)(pair % P.Hq);
-  const int kvh = h / P.r;
-  const int rr = h % P.r;
-  const ReqMeta rq = P.req[i];
-
-  // Lanes on the request's path for this head: deepest group first, then
-  // its ancestors, then the suffix.
-  auto lane_of = [&](int g, int* col) {
-    const GroupMeta gm = P.grp[g];
-    *col = (rq.pos - gm.r0) * P.r + rr;
-    return gm.lane0 + (kvh / gm.H) * gm.chunks + *col / P.item_cols;
-  };
-  int n_src = 0;
-  for (int g = rq.deepest; g >= 0; g = P.grp[g].parent) {
-    int col;
-    n_src += P.lanes[lane_of(g, &col)].splits;
-  }
-  const int sfx_ln = rq.sfx_lane + (kvh / rq.sfx_H) * rq.sfx_chunks + rr / P.item_cols;
-  if (rq.sfx_lane >= 0) n_src += P.lanes[sfx_ln].splits;
+  const int off0 = P.src_off[pair];
+  const int n_src = P.src_off[pair + 1] - off0;
 
   float M = -INFINITY, L = 0.f;
   float acc[VPL];
@@ -87,30 +70,8 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
   for (int v = 0; v < VPL; ++v) acc[v] = 0.f;
 
   for (int base = 0; base < n_src; base += 64) {
-    // Row of source j: splits of the deepest group's lane first, then its
-    // ancestors', then the suffix lane's.
     const int j = base + lane;
-    int row = -1;
-    if (j < n_src) {
-      int rem = j;
-      int g = rq.deepest;
-      for (;;) {
-        int ln, col;
-        if (g >= 0) {
-          ln = lane_of(g, &col);
-        } else {
-          ln = sfx_ln;
-          col = rr;
-        }
-        const LaneMeta lm = P.lanes[ln];
-        if (rem < lm.splits || g < 0) {
-          row = lm.base + rem * lm.H * lm.ccols + (kvh - lm.kv0) * lm.ccols + (col - lm.col0);
-          break;
-        }
-        rem -= lm.splits;
-        g = P.grp[g].parent;
-      }
-    }
+    const int row = j < n_src ? P.src_row[off0 + j] : -1;
     float m = -INFINITY, l = 0.f;
     if (row >= 0) {
       l = P.part.l[row];
