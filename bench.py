@@ -97,6 +97,7 @@ def pass_bytes(batch, plan, sched):
         suffix_tokens=suffix_tokens,
         tok_bytes=tok_bytes,
         grouped_flops=flops_g,
+        suffix_flops=suffix_tokens * sh.num_q_heads * 2 * (sh.head_dim_qk + sh.head_dim_v),
     )
 
 
@@ -113,6 +114,20 @@ def time_steps(plan, q, pools, out, lse, steps, torch, fca):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1000.0 / steps
     return start.elapsed_time(stop) / steps, wall
+
+
+def warm(plan, q, pools, out, lse, steps, torch, fca, min_s=0.2):
+    """At least `steps` untimed decodes and at least `min_s` seconds of them,
+    so that every timed loop starts with the GPU at its working clocks."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < steps or time.perf_counter() - t0 < min_s:
+        k, v = pools[n % len(pools)]
+        fca.fca_decode(q[n % len(q)], k, v, plan, out=out, lse=lse)
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(batch, vals, budget_s, threads):
@@ -194,7 +209,7 @@ def group_sweep(torch, fca, steps, warmup):
         for cascade in (True, False):
             plan = fca.fca_plan(bt, sl, fca.desc_from_shape(sh, batch.num_blocks, cascade=cascade))
             plan.decode_workspace(out.device)
-            time_steps(plan, qs, pools, out, lse, warmup, torch, fca)
+            warm(plan, qs, pools, out, lse, warmup, torch, fca)
             ms, _ = time_steps(plan, qs, pools, out, lse, steps, torch, fca)
             res[cascade] = (ms, plan.info)
         ms_c, info = res[True]
@@ -277,12 +292,12 @@ def main():
     plan_sep.decode_workspace(out.device)
     steps, warmup = args.steps, args.warmup
     if args.profile_only:
-        # Only the event-profiled loop: the kernel trace then holds exactly
-        # the launches the roofline figures come from.
-        steps, warmup = min(steps, 10), min(warmup, 2)
+        # Only the launch-timing loops: the kernel trace then holds the timed
+        # plan's launches only, the ones the roofline figures come from.
+        steps, warmup = min(steps, 32), min(warmup, 2)
         ms = wall_ms = float("nan")
     else:
-        time_steps(plan, qs, pools, out, lse, warmup, torch, fca)
+        warm(plan, qs, pools, out, lse, warmup, torch, fca)
         ms, wall_ms = time_steps(plan, qs, pools, out, lse, steps, torch, fca)
         log(f"fca decode: {ms * 1000:.1f} us/step (events), {wall_ms * 1000:.1f} us/step (wall)")
 
@@ -297,26 +312,29 @@ def main():
         log(f"calibration copy: {COPY_BYTES} bytes read and written per launch")
         del src, dst
 
-    # Kernel times: HIP events recorded around each launch on the kernels'
-    # stream (separate loops, so the events do not touch `value`): the
-    # attention launch and the merge of the timed plan, then the two passes
-    # launched on their own.
-    def profiled(pl):
-        time_steps(pl, qs, pools, out, lse, warmup, torch, fca)
-        pl.profile(True)
-        time_steps(pl, qs, pools, out, lse, steps, torch, fca)
-        pr = pl.read_profile()
-        pl.profile(False)
-        n = max(pr["calls"], 1)
-        return {k: pr[f"{k}_ms"] / n for k in ("attention", "grouped", "suffix", "merge", "decode")}
+    # Kernel times: each launch kind of a decode issued back to back between
+    # two HIP events on the kernels' stream (fca_time_launches), cycling over
+    # the KV pools like the timed loop (separate loops, so the events do not
+    # touch `value`).  Latent caches launch the grouped and the per-request
+    # pass one after the other in every plan, so the timed plan gives each
+    # pass's time; otherwise the separate-pass plan does.
+    reps = max(1, steps // len(pools))
 
-    per = profiled(plan)
-    if args.profile_only:
+    def launch_times(pl):
+        warm(pl, qs, pools, out, lse, warmup, torch, fca)
+        return pl.time_launches(qs[0], pools, reps, out, lse)
+
+    per = launch_times(plan)
+    two_launches = per["grouped_ms"] > 0 or per["suffix_ms"] > 0
+    per = {k: per[f"{k}_ms"] for k in ("attention", "grouped", "suffix", "merge", "decode")}
+    if two_launches:
+        pass
+    elif args.profile_only:
         # only the timed plan's launches, so that counter runs see one kind
         per["grouped"] = per["suffix"] = float("nan")
     else:
-        per_sep = profiled(plan_sep)
-        per["grouped"], per["suffix"] = per_sep["grouped"], per_sep["suffix"]
+        per_sep = launch_times(plan_sep)
+        per["grouped"], per["suffix"] = per_sep["grouped_ms"], per_sep["suffix_ms"]
     log("per launch (ms):", {k: round(v, 4) for k, v in per.items()})
     if args.profile_only:
         ms = per["decode"]
@@ -326,26 +344,34 @@ def main():
     value = logical / (ms / 1000.0)
     unique_gbps = unique_bytes / (ms / 1000.0) / 1e9
 
-    att_kernel = "fca_mla_kernel" if sh.v_aliases_k else "fca_attention_kernel"
-    kernels = {
-        att_kernel: ("attention", pb["attention"]),
-        "fca_merge_kernel_d128" if sh.head_dim_v == 128 else "fca_merge_kernel_d512": ("merge", pb["merge"]),
-    }
-    dom_name, (dom_pass, dom_bytes) = max(kernels.items(), key=lambda kv: per[kv[1][0]])
-    att_flops = logical * 2 * sh.num_q_heads * (sh.head_dim_qk + sh.head_dim_v)
-    if dom_name == att_kernel and att_flops / dom_bytes > RIDGE_FLOP_PER_BYTE:
+    merge_kernel = "fca_merge_kernel_d128" if sh.head_dim_v == 128 else "fca_merge_kernel_d512"
+    # Launches of one decode: (kernel, launch, algorithmic bytes, flops).  The
+    # roofline is taken on the longest one.
+    launches = [(merge_kernel, "merge", pb["merge"], 0)]
+    if two_launches:
+        # the latent-cache kernel, one entry name per pass
+        g_name, s_name = ("fca_mla_grouped_kernel", "fca_mla_suffix_kernel") if sh.v_aliases_k else ("fca_attention_kernel",) * 2
+        launches += [
+            (g_name, "grouped", pb["grouped"], pb["grouped_flops"]),
+            (s_name, "suffix", pb["suffix"], pb["suffix_flops"]),
+        ]
+    else:
+        launches.append(("fca_attention_kernel", "attention", pb["attention"], pb["grouped_flops"] + pb["suffix_flops"]))
+    dom_name, dom_pass, dom_bytes, dom_flops = max(launches, key=lambda x: per[x[1]])
+    if dom_flops / dom_bytes > RIDGE_FLOP_PER_BYTE:
         # The latent cache: every query row costs 2 (Dqk + Dv) flops per
         # token, above the ridge, so the bound is the bf16 MFMA rate.
-        achieved = att_flops / (per[dom_pass] / 1000.0) / 1e12
+        achieved = dom_flops / (per[dom_pass] / 1000.0) / 1e12
         roofline = {
             "kernel": dom_name,
+            "launch": dom_pass,
             "bound": "mfma",
             "achieved": round(achieved, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": None,
-            "flops_per_launch": int(att_flops),
+            "flops_per_launch": int(dom_flops),
             "bytes_per_launch": int(dom_bytes),
             "avg_launch_ms": round(per[dom_pass], 5),
         }
@@ -353,6 +379,7 @@ def main():
         achieved = dom_bytes / (per[dom_pass] / 1000.0) / 1e9
         roofline = {
             "kernel": dom_name,
+            "launch": dom_pass,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -422,7 +449,7 @@ def main():
     }
 
     if not args.profile_only:
-        time_steps(plan_sep, qs, pools, out, lse, warmup, torch, fca)
+        warm(plan_sep, qs, pools, out, lse, warmup, torch, fca)
         ms_sep, _ = time_steps(plan_sep, qs, pools, out, lse, steps, torch, fca)
         log(f"fca decode, separate pass launches: {ms_sep * 1000:.1f} us/step")
         result["separate_passes_ms_per_step"] = round(ms_sep, 5)
@@ -431,7 +458,7 @@ def main():
         desc_nc = fca.desc_from_shape(sh, batch.num_blocks, cascade=False)
         plan_nc = fca.fca_plan(bt, sl, desc_nc)
         plan_nc.decode_workspace(out.device)
-        time_steps(plan_nc, qs, pools, out, lse, warmup, torch, fca)
+        warm(plan_nc, qs, pools, out, lse, warmup, torch, fca)
         ms_nc, _ = time_steps(plan_nc, qs, pools, out, lse, steps, torch, fca)
         log(f"non-cascade: {ms_nc * 1000:.1f} us/step")
         result["non_cascade"] = {
@@ -441,6 +468,40 @@ def main():
             "byte_ratio_R": round(logical / max(int(info.unique_tokens), 1), 3),
         }
         del plan_nc
+
+    if not args.profile_only:
+        # The same steps from a HIP graph: one capture of one decode per KV
+        # pool (one plan shared by the layers), replayed; shows the launch
+        # overhead a graph removes.
+        ws = plan.decode_workspace(out.device)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for li, (k, v) in enumerate(pools):
+                fca.fca_decode(qs[li], k, v, plan, out=out, lse=lse)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for li, (k, v) in enumerate(pools):
+                fca.fca_decode(qs[li], k, v, plan, out=out, lse=lse)
+        torch.cuda.synchronize()
+        reps = max(1, steps // len(pools))
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < 0.2:
+            graph.replay()
+            torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(reps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_graph = g0.elapsed_time(g1) / (reps * len(pools))
+        log(f"fca decode from a HIP graph ({len(pools)} layers per replay): {ms_graph * 1000:.1f} us/step")
+        result["graph_ms_per_step"] = round(ms_graph, 5)
+        del graph, ws
 
     if args.group_sweep and not args.profile_only:
         result["group_sweep"] = group_sweep(torch, fca, steps, warmup)

@@ -55,7 +55,8 @@ typedef enum fca_status {
                                        per-request pass one after the other
                                        (for per-pass timing).  By default one
                                        launch of persistent workgroups runs
-                                       the work items of both passes. */
+                                       the work items of both passes (GQA);
+                                       latent caches always use two. */
 
 /*
  * Shape and cache layout of one attention layer.
@@ -226,9 +227,10 @@ fca_status fca_plan_export_schedule(fca_plan plan, fca_work_item* grouped, fca_w
 
 /* Summed GPU time of the launches of profiled fca_decode calls. */
 typedef struct fca_profile {
-  double attention_ms; /* grouped and per-request passes */
-  double grouped_ms;   /* grouped pass alone (FCA_PLAN_SEPARATE_PASSES, else 0) */
-  double suffix_ms;    /* per-request pass alone (FCA_PLAN_SEPARATE_PASSES, else 0) */
+  double attention_ms; /* all attention launches (grouped and per-request passes) */
+  double grouped_ms;   /* the launch of the grouped pass alone, when the plan
+                          launches the passes separately (else 0) */
+  double suffix_ms;    /* the launch of the per-request pass alone, likewise */
   double merge_ms;     /* log-sum-exp merge */
   double decode_ms;    /* whole call, first launch to last */
   int64_t calls;
@@ -243,6 +245,35 @@ typedef struct fca_profile {
  */
 fca_status fca_profile_enable(fca_plan plan, int32_t enable);
 fca_status fca_profile_read(fca_plan plan, fca_profile* out);
+
+/*
+ * Measurement hook: average GPU time of each launch of a decode, free of the
+ * per-launch event overhead of fca_profile_enable.  Each launch kind of the
+ * plan (the attention launch, or the grouped then the per-request launch,
+ * then the merge) is issued repeats * n_caches times back to back between two
+ * HIP events on `stream`, cycling over the caches (so that one cache does not
+ * stay in the last-level cache between launches).
+ *
+ *   k_caches, v_caches  host arrays of n_caches device pointers, layout as for
+ *                       fca_decode (v_caches ignored, may be NULL, when
+ *                       v_aliases_k).
+ *   q_dev, out_dev, lse_dev, workspace_dev  as for fca_decode; out / lse end
+ *                       up holding the decode of the last cache.
+ *   result              per-launch averages in ms (attention_ms sums the
+ *                       plan's attention launches; grouped_ms / suffix_ms are
+ *                       set when the plan launches the passes separately, as
+ *                       on latent caches;
+ *                       decode_ms = attention_ms + merge_ms); calls =
+ *                       repeats * n_caches.
+ *
+ * Blocks the host until the launches finish.  FCA_ERR_INVALID_ARG for NULL
+ * arguments or n_caches / repeats < 1, FCA_ERR_WORKSPACE as fca_decode,
+ * FCA_ERR_HIP if a launch or event call fails.
+ */
+fca_status fca_time_launches(fca_plan plan, const void* q_dev, const void* const* k_caches,
+                             const void* const* v_caches, int32_t n_caches, int32_t repeats, void* out_dev,
+                             float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream,
+                             fca_profile* result);
 
 /* Frees the host-side plan.  The workspace stays the caller's.  NULL is ok. */
 void fca_plan_destroy(fca_plan plan);

@@ -39,6 +39,7 @@ EXPORTED = [
     "fca_plan_export_schedule",
     "fca_profile_enable",
     "fca_profile_read",
+    "fca_time_launches",
     "fca_plan_destroy",
     "fca_last_error",
     "fca_version",
@@ -145,6 +146,7 @@ def lib():
         L.fca_plan_export_schedule.argtypes = [vp, vp, vp, vp, vp]
         L.fca_profile_enable.argtypes = [vp, i32]
         L.fca_profile_read.argtypes = [vp, ctypes.POINTER(Profile)]
+        L.fca_time_launches.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp, ctypes.POINTER(Profile)]
         L.fca_plan_destroy.argtypes = [vp]
         L.fca_plan_destroy.restype = None
         L.fca_last_error.restype = ctypes.c_char_p
@@ -314,6 +316,43 @@ class Plan:
     def read_profile(self) -> dict:
         p = Profile()
         _check(lib().fca_profile_read(self._h, ctypes.byref(p)))
+        return {f: getattr(p, f) for f, _ in Profile._fields_}
+
+    def time_launches(self, q, caches, repeats, out, lse=None, workspace=None, stream=None) -> dict:
+        """Average GPU time (ms) of each launch kind of a decode, each issued
+        repeats * len(caches) times back to back between two HIP events
+        (fca_time_launches).  `caches` is a list of (k_cache, v_cache); out /
+        lse end up holding the decode of the last one."""
+        import torch
+
+        d = self.desc
+        assert q.dtype == torch.bfloat16 and q.is_contiguous()
+        assert tuple(q.shape) == (self.batch, d.num_q_heads, d.head_dim_qk)
+        assert out.dtype == torch.bfloat16 and out.is_contiguous()
+        assert tuple(out.shape) == (self.batch, d.num_q_heads, d.head_dim_v)
+        if lse is not None:
+            assert lse.dtype == torch.float32 and lse.is_contiguous()
+        n = len(caches)
+        ks = (ctypes.c_void_p * max(n, 1))(*[k.data_ptr() for k, _ in caches])
+        vs = (ctypes.c_void_p * max(n, 1))(*[(v.data_ptr() if v is not None else 0) for _, v in caches])
+        ws = workspace if workspace is not None else self.decode_workspace(q.device)
+        p = Profile()
+        _check(
+            lib().fca_time_launches(
+                self._h,
+                _ptr(q),
+                ks,
+                vs,
+                n,
+                int(repeats),
+                _ptr(out),
+                _ptr(lse),
+                _ptr(ws),
+                ws.numel() * ws.element_size(),
+                _stream_ptr(stream),
+                ctypes.byref(p),
+            )
+        )
         return {f: getattr(p, f) for f, _ in Profile._fields_}
 
     def export(self):

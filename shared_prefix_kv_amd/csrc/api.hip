@@ -140,9 +140,11 @@ struct SchedLayout {
 };
 
 // One launch of the attention kernel: bins [bin0, bin0 + n_bins) of the
-// plan's bins.
+// plan's bins, holding the work items of both passes or of one.
+enum PassSet { kBothPasses = 0, kGroupedPass = 1, kSuffixPass = 2 };
 struct Launch {
   int bin0, n_bins;
+  PassSet passes;
 };
 
 DiscoveryPtrs discovery_ptrs(char* ws, const Layout& L, int B) {
@@ -411,14 +413,14 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   P->items.clear();
   P->bins.assign(1, 0);
   P->launches.clear();
-  auto cut = [&](size_t l0, size_t l1) {
+  auto cut = [&](size_t l0, size_t l1, PassSet passes) {
     int64_t W = 0;
     for (size_t k = l0; k < l1; ++k) {
       W += all[k].stages;
     }
     const int64_t nb = std::min<int64_t>(W, (int64_t)n_cu_ * t.bins_per_cu);
     if (nb == 0) return;
-    P->launches.push_back(Launch{(int)P->bins.size() - 1, (int)nb});
+    P->launches.push_back(Launch{(int)P->bins.size() - 1, (int)nb, passes});
     size_t li = l0;
     int64_t lpos = 0, pos = 0;
     for (int64_t b = 0; b < nb; ++b) {
@@ -462,7 +464,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   // bin load) go first, largest first, in pieces of about the mean bin load
   // on the least loaded bins; the other lanes are then poured in order into
   // the bins up to a common makespan.  Bins left empty are dropped.
-  auto place = [&](size_t l0, size_t l1) {
+  auto place = [&](size_t l0, size_t l1, PassSet passes) {
     int64_t W = 0;
     for (size_t k = l0; k < l1; ++k) W += all[k].stages;
     if (W == 0) return;
@@ -570,7 +572,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
       P->bins.push_back((int32_t)P->items.size());
       ++used;
     }
-    if (used) P->launches.push_back(Launch{first, used});
+    if (used) P->launches.push_back(Launch{first, used, passes});
   };
 
   int64_t row = 0;
@@ -596,17 +598,20 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
     if (sfx_tokens[i] > 0)
       rq.sfx_lane = add_lanes(all, P->req3[3 * i] * bs, lens[i], i, -1, r, &rq.sfx_H, &rq.sfx_chunks);
   }
-  auto schedule = [&](size_t l0, size_t l1) {
+  auto schedule = [&](size_t l0, size_t l1, PassSet passes) {
     if (mla)
-      place(l0, l1);
+      place(l0, l1, passes);
     else
-      cut(l0, l1);
+      cut(l0, l1, passes);
   };
-  if (P->desc.flags & FCA_PLAN_SEPARATE_PASSES) {
-    schedule(0, n_glanes);
-    schedule(n_glanes, all.size());
+  // Latent caches always launch the two passes one after the other: the
+  // grouped pass then runs its die-aligned pieces alone, and the suffix
+  // pieces are not left to the tails of the grouped bins (measured faster).
+  if ((P->desc.flags & FCA_PLAN_SEPARATE_PASSES) || mla) {
+    schedule(0, n_glanes, kGroupedPass);
+    schedule(n_glanes, all.size(), kSuffixPass);
   } else {
-    schedule(0, all.size());
+    schedule(0, all.size(), kBothPasses);
   }
   for (Lane& L : all) {
     L.splits *= L.S;  // stripe splits of every piece
@@ -793,11 +798,15 @@ fca_status fca_plan_get_info(fca_plan plan, fca_plan_info* info) {
   return FCA_OK;
 }
 
-fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
-                      void* out_dev, float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream) {
-  if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
-  const fca_plan_s* P = plan;
-  if (P->B == 0) return FCA_OK;
+}  // extern "C"
+
+namespace {
+
+// Kernel arguments of one decode call: the attention launches' and the
+// merge's.  Checks the caller's pointers and workspace.
+fca_status decode_params(const fca_plan_s* P, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                         void* out_dev, float* lse_dev, void* workspace_dev, size_t workspace_bytes, GqaParams* gp,
+                         MergeParams* mp) {
   if (!q_dev || !k_cache_dev || !out_dev || (!P->desc.v_aliases_k && !v_cache_dev))
     return fail(FCA_ERR_INVALID_ARG, "q / k_cache / v_cache / out is NULL");
   if (P->info.num_partial_rows > 0) {
@@ -808,7 +817,6 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
       return fail(FCA_ERR_WORKSPACE, "decode workspace has %zu bytes, needs %zu", workspace_bytes,
                   P->info.decode_workspace_bytes);
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rows = P->info.num_partial_rows;
   const size_t dv = (size_t)P->desc.head_dim_v;
   char* w = static_cast<char*>(workspace_dev);
@@ -819,21 +827,68 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
 
   const Layout& L = P->L;
   const SchedLayout& S = P->SL;
+  gp->perm = reinterpret_cast<const int32_t*>(P->sched + S.perm);
+  gp->bt = reinterpret_cast<const int32_t*>(P->ws + L.bt);
+  gp->W = P->W;
+  gp->Hq = P->desc.num_q_heads;
+  gp->r = P->r;
+  gp->scale_log2 = P->desc.scale * 1.4426950408889634f;
+  gp->q = q_dev;
+  gp->k = k_cache_dev;
+  gp->v = v_cache_dev;
+  gp->k_stride_block = P->desc.k_stride_block;
+  gp->k_stride_head = P->desc.k_stride_head;
+  gp->v_stride_block = P->desc.v_stride_block;
+  gp->v_stride_head = P->desc.v_stride_head;
+  gp->part = part;
+  gp->items = reinterpret_cast<const WorkItem*>(P->sched + S.items);
+  gp->bins = nullptr;
+
+  mp->src_off = reinterpret_cast<const int32_t*>(P->sched + S.src_off);
+  mp->src_row = reinterpret_cast<const int32_t*>(P->sched + S.src_row);
+  mp->B = P->B;
+  mp->Hq = P->desc.num_q_heads;
+  mp->Dv = P->desc.head_dim_v;
+  mp->part = part;
+  mp->out = out_dev;
+  mp->lse = lse_dev;
+  return FCA_OK;
+}
+
+// Attention launch `k` of the plan.
+hipError_t launch_pass(const fca_plan_s* P, GqaParams gp, int k, hipStream_t s) {
+  const Launch& ln = P->launches[k];
+  gp.bins = reinterpret_cast<const BinHead*>(P->sched + P->SL.heads) + ln.bin0;
+  return P->kind == kMla ? launch_mla(gp, ln.n_bins, ln.passes == kGroupedPass, s)
+                         : launch_attention(gp, ln.n_bins, s);
+}
+
+// Adds the time of attention launch `k` to the profile's per-pass sums.
+void add_pass_time(const fca_plan_s* P, int k, double ms, fca_profile* acc) {
+  acc->attention_ms += ms;
+  if (P->launches[k].passes == kGroupedPass) acc->grouped_ms += ms;
+  if (P->launches[k].passes == kSuffixPass) acc->suffix_ms += ms;
+}
+
+// Timing-only events: no system-scope fence when they complete, which keeps
+// them from adding cache write-back to the launches they bracket.
+hipError_t timing_event(hipEvent_t* ev) { return hipEventCreateWithFlags(ev, hipEventDisableSystemFence); }
+
+}  // namespace
+
+extern "C" {
+
+fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                      void* out_dev, float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
+  const fca_plan_s* P = plan;
+  if (P->B == 0) return FCA_OK;
   GqaParams gp;
-  gp.perm = reinterpret_cast<const int32_t*>(P->sched + S.perm);
-  gp.bt = reinterpret_cast<const int32_t*>(P->ws + L.bt);
-  gp.W = P->W;
-  gp.Hq = P->desc.num_q_heads;
-  gp.r = P->r;
-  gp.scale_log2 = P->desc.scale * 1.4426950408889634f;
-  gp.q = q_dev;
-  gp.k = k_cache_dev;
-  gp.v = v_cache_dev;
-  gp.k_stride_block = P->desc.k_stride_block;
-  gp.k_stride_head = P->desc.k_stride_head;
-  gp.v_stride_block = P->desc.v_stride_block;
-  gp.v_stride_head = P->desc.v_stride_head;
-  gp.part = part;
+  MergeParams mp;
+  fca_status st = decode_params(P, q_dev, k_cache_dev, v_cache_dev, out_dev, lse_dev, workspace_dev, workspace_bytes,
+                                &gp, &mp);
+  if (st != FCA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   fca_plan_s* M = plan;
   // Profiling events: start, then begin/end of each attention launch (up to
@@ -843,7 +898,7 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   if (P->profiling) {
     for (int j = 0; j < kProf; ++j) {
       if (M->event_pool.empty()) {
-        e = hipEventCreate(&ev[j]);
+        e = timing_event(&ev[j]);
         if (e != hipSuccess) return hip_fail(e, "profiling event");
       } else {
         ev[j] = M->event_pool.back();
@@ -859,31 +914,69 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
     if (e != hipSuccess) return hip_fail(e, what); \
   } while (0)
   FCA_TRY(mark(0), "event record");
-  gp.items = reinterpret_cast<const WorkItem*>(P->sched + S.items);
   for (int k = 0; k < 2; ++k) {
     FCA_TRY(mark(1 + 2 * k), "event record");
-    if (k < (int)P->launches.size()) {
-      const Launch& ln = P->launches[k];
-      gp.bins = reinterpret_cast<const BinHead*>(P->sched + S.heads) + ln.bin0;
-      FCA_TRY(P->kind == kMla ? launch_mla(gp, ln.n_bins, s) : launch_attention(gp, ln.n_bins, s),
-              "attention launch");
-    }
+    if (k < (int)P->launches.size()) FCA_TRY(launch_pass(P, gp, k, s), "attention launch");
     FCA_TRY(mark(2 + 2 * k), "event record");
   }
   FCA_TRY(mark(5), "event record");
-
-  MergeParams mp;
-  mp.src_off = reinterpret_cast<const int32_t*>(P->sched + S.src_off);
-  mp.src_row = reinterpret_cast<const int32_t*>(P->sched + S.src_row);
-  mp.B = P->B;
-  mp.Hq = P->desc.num_q_heads;
-  mp.Dv = P->desc.head_dim_v;
-  mp.part = part;
-  mp.out = out_dev;
-  mp.lse = lse_dev;
   FCA_TRY(launch_merge(mp, s), "merge launch");
   FCA_TRY(mark(6), "event record");
 #undef FCA_TRY
+  return FCA_OK;
+}
+
+fca_status fca_time_launches(fca_plan plan, const void* q_dev, const void* const* k_caches,
+                             const void* const* v_caches, int32_t n_caches, int32_t repeats, void* out_dev,
+                             float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream,
+                             fca_profile* result) {
+  if (!plan || !result) return fail(FCA_ERR_INVALID_ARG, "plan / result is NULL");
+  if (!k_caches || (!plan->desc.v_aliases_k && !v_caches)) return fail(FCA_ERR_INVALID_ARG, "cache list is NULL");
+  if (n_caches < 1 || repeats < 1) return fail(FCA_ERR_INVALID_ARG, "n_caches and repeats must be >= 1");
+  const fca_plan_s* P = plan;
+  fca_profile acc{};
+  if (P->B == 0) {
+    *result = acc;
+    return FCA_OK;
+  }
+  const int n_launch = (int)P->launches.size();
+  std::vector<GqaParams> gps(n_caches);
+  MergeParams mp;
+  for (int c = 0; c < n_caches; ++c) {
+    fca_status st = decode_params(P, q_dev, k_caches[c], P->desc.v_aliases_k ? nullptr : v_caches[c], out_dev,
+                                  lse_dev, workspace_dev, workspace_bytes, &gps[c], &mp);
+    if (st != FCA_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // events: begin/end of each attention launch's run, then of the merge's
+  hipEvent_t ev[6] = {};
+  hipError_t e = hipSuccess;
+  const int n_ev = 2 * n_launch + 2;
+  for (int j = 0; j < n_ev && e == hipSuccess; ++j) e = timing_event(&ev[j]);
+  float t[3] = {0, 0, 0};
+  if (e == hipSuccess) {
+    // Each run issues one launch kind repeats x n_caches times back to back,
+    // cycling the caches; the last attention launch is on the last cache, so
+    // out / lse end up as the decode of that cache.
+    for (int k = 0; k <= n_launch && e == hipSuccess; ++k) {
+      e = hipEventRecord(ev[2 * k], s);
+      for (int r = 0; r < repeats && e == hipSuccess; ++r)
+        for (int c = 0; c < n_caches && e == hipSuccess; ++c)
+          e = k < n_launch ? launch_pass(P, gps[c], k, s) : launch_merge(mp, s);
+      if (e == hipSuccess) e = hipEventRecord(ev[2 * k + 1], s);
+    }
+  }
+  if (e == hipSuccess) e = hipEventSynchronize(ev[n_ev - 1]);
+  for (int k = 0; k <= n_launch && e == hipSuccess; ++k) e = hipEventElapsedTime(&t[k], ev[2 * k], ev[2 * k + 1]);
+  for (int j = 0; j < n_ev; ++j)
+    if (ev[j]) hipEventDestroy(ev[j]);
+  if (e != hipSuccess) return hip_fail(e, "timed launches");
+  const double n = (double)repeats * n_caches;
+  for (int k = 0; k < n_launch; ++k) add_pass_time(P, k, t[k] / n, &acc);
+  acc.merge_ms = t[n_launch] / n;
+  acc.decode_ms = acc.attention_ms + acc.merge_ms;
+  acc.calls = (int64_t)n;
+  *result = acc;
   return FCA_OK;
 }
 
@@ -898,21 +991,16 @@ fca_status fca_profile_read(fca_plan plan, fca_profile* out) {
   fca_profile acc{};
   hipError_t err = hipSuccess;
   // events per call: start, launch 1 begin/end, launch 2 begin/end, merge begin/end
-  const bool separate = plan->launches.size() == 2;
+  const int n_launch = (int)plan->launches.size();
   for (size_t c = 0; c + 7 <= plan->pending.size(); c += 7) {
     hipEvent_t* ev = plan->pending.data() + c;
-    float t[5] = {0, 0, 0, 0, 0};
+    float t[4] = {0, 0, 0, 0};
     if (err == hipSuccess) err = hipEventSynchronize(ev[6]);
     if (err == hipSuccess) err = hipEventElapsedTime(&t[0], ev[1], ev[2]);
     if (err == hipSuccess) err = hipEventElapsedTime(&t[1], ev[3], ev[4]);
     if (err == hipSuccess) err = hipEventElapsedTime(&t[2], ev[5], ev[6]);
     if (err == hipSuccess) err = hipEventElapsedTime(&t[3], ev[0], ev[6]);
-    if (err == hipSuccess) err = hipEventElapsedTime(&t[4], ev[1], ev[4]);
-    acc.attention_ms += t[4];
-    if (separate) {
-      acc.grouped_ms += t[0];
-      acc.suffix_ms += t[1];
-    }
+    for (int k = 0; k < n_launch && k < 2; ++k) add_pass_time(plan, k, t[k], &acc);
     acc.merge_ms += t[2];
     acc.decode_ms += t[3];
     acc.calls += 1;

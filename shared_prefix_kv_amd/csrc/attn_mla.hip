@@ -193,7 +193,7 @@ struct Copier {
 
 }  // namespace
 
-__global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
+__device__ __forceinline__ void mla_body(GqaParams P) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -442,9 +442,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_kernel(GqaParams P) {
   }
 }
 
-hipError_t launch_mla(const GqaParams& p, int n_bins, hipStream_t s) {
+// One entry per pass, so that kernel traces tell the two launches of a decode
+// apart; both run the same code.
+__global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_grouped_kernel(GqaParams P) { mla_body(P); }
+__global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_suffix_kernel(GqaParams P) { mla_body(P); }
+
+hipError_t launch_mla(const GqaParams& p, int n_bins, bool grouped_pass, hipStream_t s) {
   if (n_bins <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fca_mla_kernel, dim3(n_bins), dim3(kWaves * 64), 0, s, p);
+  if (grouped_pass)
+    hipLaunchKernelGGL(fca_mla_grouped_kernel, dim3(n_bins), dim3(kWaves * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL(fca_mla_suffix_kernel, dim3(n_bins), dim3(kWaves * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -141,8 +141,9 @@ struct GqaParams {
 hipError_t launch_attention(const GqaParams& p, int n_bins, hipStream_t s);
 
 // The same for a latent cache (576-wide keys, values = first 512 dims,
-// 64-token blocks): items of up to 128 query rows of one head.
-hipError_t launch_mla(const GqaParams& p, int n_bins, hipStream_t s);
+// 64-token blocks): items of up to 128 query rows of one head.  `grouped_pass`
+// picks the kernel entry the launch is traced under (same code).
+hipError_t launch_mla(const GqaParams& p, int n_bins, bool grouped_pass, hipStream_t s);
 
 struct MergeParams {
   // Partial rows of (request i, query head h), in merge order (deepest

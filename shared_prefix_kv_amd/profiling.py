@@ -31,8 +31,9 @@ import statistics
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
-ATTENTION = "fca_attention_kernel"
-MLA = "fca_mla_kernel"
+ATTENTION = "fca_attention_kernel"  # both passes in one launch
+MLA_GROUPED = "fca_mla_grouped_kernel"  # latent cache: grouped-pass launch
+MLA_SUFFIX = "fca_mla_suffix_kernel"  # latent cache: per-request-pass launch
 MERGE = "fca_merge_kernel"
 CALIBRATION = "mul"  # torch.mul elementwise kernel of the calibration copy
 
@@ -79,24 +80,26 @@ def kernel_stats(dirpath: str) -> list[dict]:
 
 
 def kernel_durations(dirpath: str, key: str) -> list[float]:
-    """Per-dispatch durations (us) of kernels whose name contains `key`."""
-    out = []
+    """Per-dispatch durations (us) of kernels whose name contains `key`, in
+    dispatch order."""
+    rows = []
     with open(_one(dirpath, "kernel_trace.csv")) as fh:
         for r in csv.DictReader(fh):
             if key in r["Kernel_Name"]:
-                out.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    return out
+                rows.append((int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    return [d for _, d in sorted(rows)]
 
 
 def counters(dirpath: str, counter: str) -> dict[str, list[float]]:
-    """Counter values (bytes) per dispatch, grouped by kernel name."""
+    """Counter values (bytes) per dispatch in dispatch order, grouped by kernel
+    name."""
     by = {}
     with open(_one(dirpath, "counter_collection.csv")) as fh:
         for r in csv.DictReader(fh):
             if r["Counter_Name"] != counter:
                 continue
-            by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
-    return by
+            by.setdefault(r["Kernel_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"]) * 1024.0))
+    return {k: [v for _, v in sorted(vals)] for k, vals in by.items()}
 
 
 def _pick(by: dict[str, list[float]], key: str) -> list[float]:
@@ -112,8 +115,12 @@ def _pick(by: dict[str, list[float]], key: str) -> list[float]:
 
 def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_bytes, cmds, out):
     stats = kernel_stats(stats_dir)
-    kernel = ATTENTION if kernel_durations(stats_dir, ATTENTION) else MLA
-    att_us = kernel_durations(stats_dir, kernel)
+    att_kernels = [k for k in (ATTENTION, MLA_GROUPED, MLA_SUFFIX) if kernel_durations(stats_dir, k)]
+    if not att_kernels:
+        raise RuntimeError("no attention kernel in the kernel trace")
+    durations = {k: kernel_durations(stats_dir, k) for k in att_kernels + [MERGE]}
+    # the launch the roofline is taken on: the longest attention launch
+    kernel = max(att_kernels, key=lambda k: statistics.median(durations[k]))
     fetch = counters(fetch_dir, "FETCH_SIZE")
     write = counters(write_dir, "WRITE_SIZE")
     cal_f = _pick(fetch, CALIBRATION)
@@ -123,7 +130,7 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
     f_factor = copy_bytes / statistics.median(cal_f)
     w_factor = copy_bytes / statistics.median(cal_w)
     res = {}
-    for key in (kernel, MERGE):
+    for key in att_kernels + [MERGE]:
         fv, wv = _pick(fetch, key), _pick(write, key)
         if fv and wv:
             res[key] = dict(
@@ -150,8 +157,9 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
     for r in stats:
         if "fca" in r["name"]:
             lines.append(f"  {_short(r['name']):42s} {r['calls']:6d} {r['avg_us']:9.2f} {r['min_us']:9.2f} {r['max_us']:9.2f}")
-    if att_us:
-        lines.append(f"  {kernel}: median of {len(att_us)} dispatches {statistics.median(att_us):.2f} us")
+    for k, d in durations.items():
+        if d:
+            lines.append(f"  {k}: median of {len(d)} dispatches {statistics.median(d):.2f} us, mean {statistics.fmean(d):.2f} us")
     lines += [
         "",
         f"Counter calibration: the copy reads and writes {copy_bytes} bytes per dispatch;",
@@ -168,14 +176,14 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
         )
     if att and algorithmic_bytes:
         lines.append(
-            f"  algorithmic bytes per attention dispatch {algorithmic_bytes / 1e6:.2f} MB;"
+            f"  algorithmic bytes per {kernel} launch {algorithmic_bytes / 1e6:.2f} MB;"
             f" measured / algorithmic = {(att['fetch_bytes'] + att['write_bytes']) / algorithmic_bytes:.3f}"
         )
     payload = dict(
         config=config,
         source_sha256=source_sha256(),
         kernel=kernel,
-        avg_launch_us=statistics.median(att_us) if att_us else None,
+        avg_launch_us=statistics.median(durations[kernel]),
         fetch_factor=f_factor,
         write_factor=w_factor,
         traffic=res,
@@ -190,7 +198,7 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
 def load_traffic(config: str):
     """Calibrated traffic per attention dispatch from the committed summary,
     or None if there is none or the sources changed since it was taken."""
-    paths = [os.path.join(ROOT, "profiles", f"{k}.{config}.txt") for k in (ATTENTION, MLA)]
+    paths = [os.path.join(ROOT, "profiles", f"{k}.{config}.txt") for k in (ATTENTION, MLA_GROUPED, MLA_SUFFIX)]
     paths = [p for p in paths if os.path.exists(p)]
     if not paths:
         return None

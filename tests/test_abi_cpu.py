@@ -113,6 +113,8 @@ def test_decode_and_info_reject_null_plan():
     assert L.fca_plan_export_schedule(None, None, None, None, None) == 1
     assert L.fca_profile_enable(None, 1) == 1
     assert L.fca_profile_read(None, None) == 1
+    prof = fca.Profile()
+    assert L.fca_time_launches(None, None, None, None, 1, 1, None, None, None, 0, None, ctypes.byref(prof)) == 1
     L.fca_plan_destroy(None)  # no-op
 
 

@@ -485,3 +485,119 @@ def test_decode_mla_full_size_sampled():
     say("mla", rep, "groups", p.info.num_groups, "items", p.info.num_grouped_items, p.info.num_suffix_items)
     del vals
     torch.cuda.empty_cache()
+
+
+def test_decode_hip_graph_replay():
+    """The decode step (both launches) captured once into a HIP graph and
+    replayed: each replay, with new query values copied into the captured
+    buffer and eager decodes of the same plan in between, equals the eager
+    result bit for bit (the plan is built once and reused, as by the layers
+    of a model)."""
+    b = build_batch(CONFIGS["tiny"])
+    vn = fill_values_numpy(b, poison=True)
+    vals = upload(vn)
+    bt, sl = dev_tables(b)
+    p = fca.fca_plan(bt, sl, fca.desc_from_shape(b.shape, b.num_blocks))
+    sh = b.shape
+    q_static = vals["q"].clone()
+    out_g = torch.empty((b.batch, sh.num_q_heads, sh.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    lse_g = torch.empty((b.batch, sh.num_q_heads), dtype=torch.float32, device="cuda")
+    out_e = torch.empty_like(out_g)
+    lse_e = torch.empty_like(lse_g)
+    ws = p.decode_workspace(q_static.device)
+    # warm up on the capture stream, then capture
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        p.decode(q_static, vals["k"], vals["v"], out=out_g, lse=lse_g, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        p.decode(q_static, vals["k"], vals["v"], out=out_g, lse=lse_g, workspace=ws)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    for rep in range(4):
+        q_new = torch.randn(q_static.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        q_static.copy_(q_new)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ws_e = torch.empty_like(ws)
+        p.decode(q_new, vals["k"], vals["v"], out=out_e, lse=lse_e, workspace=ws_e)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), f"replay {rep}: output differs from eager"
+        assert torch.equal(lse_g, lse_e), f"replay {rep}: lse differs from eager"
+    # and the replayed output is the attention of the last queries (oracle)
+    ref, _ = A.attend(to_bits_np(q_static), vn["k"], vn["v"], b.block_tables, b.seq_lens, sh)
+    assert_close(bf16_tensor_to_f64(out_g), ref, "graph replay")
+    say("graph replay: 4 replays equal to eager")
+
+
+def to_bits_np(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def mla_small_config(seed=52):
+    return Config(
+        name="mla_small_timing",
+        shape=MLA,
+        trees=[Node(256, samples=3, suffix=(1, 150)), Node(192, samples=2, suffix=(60, 200))],
+        singletons=1,
+        singleton_len=(1, 130),
+        seed=seed,
+    )
+
+
+@pytest.mark.parametrize("kind", ["gqa", "mla"])
+def test_time_launches_and_profile(kind):
+    """The measurement entry points: fca_time_launches leaves out / lse equal
+    to a plain decode of the last cache it cycled over, bit for bit, and
+    returns positive per-launch times (per pass on the latent cache, whose
+    plans launch the passes separately); fca_profile_enable / read sum the
+    launch times of profiled decodes."""
+    b = build_batch(CONFIGS["tiny"] if kind == "gqa" else mla_small_config())
+    caches = []
+    for _ in range(2):
+        vn = fill_values_numpy(b, poison=True)  # the batch's rng moves on: new values each time
+        caches.append(upload(vn))
+    q = caches[0]["q"]
+    sh = b.shape
+    bt, sl = dev_tables(b)
+    p = fca.fca_plan(bt, sl, fca.desc_from_shape(sh, b.num_blocks))
+    out_t = torch.empty((b.batch, sh.num_q_heads, sh.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    lse_t = torch.empty((b.batch, sh.num_q_heads), dtype=torch.float32, device="cuda")
+    say("time launches", kind)
+    t = p.time_launches(q, [(c["k"], c["v"]) for c in caches], 3, out_t, lse_t)
+    torch.cuda.synchronize()
+    assert t["calls"] == 6
+    assert t["attention_ms"] > 0 and t["merge_ms"] > 0
+    assert t["decode_ms"] == pytest.approx(t["attention_ms"] + t["merge_ms"])
+    if kind == "mla":
+        assert t["grouped_ms"] > 0 and t["suffix_ms"] > 0
+        assert t["attention_ms"] == pytest.approx(t["grouped_ms"] + t["suffix_ms"])
+    else:
+        assert t["grouped_ms"] == 0 and t["suffix_ms"] == 0
+    out_d = torch.empty_like(out_t)
+    lse_d = torch.empty_like(lse_t)
+    ws = torch.empty_like(p.decode_workspace(q.device))
+    p.decode(q, caches[1]["k"], caches[1]["v"], out=out_d, lse=lse_d, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_t.view(torch.int16), out_d.view(torch.int16))
+    assert torch.equal(lse_t, lse_d)
+    with pytest.raises(fca.FcaError):
+        p.time_launches(q, [], 1, out_t, lse_t)
+    with pytest.raises(fca.FcaError):
+        p.time_launches(q, [(caches[0]["k"], caches[0]["v"])], 0, out_t, lse_t)
+
+    p.profile(True)
+    for c in caches:
+        p.decode(q, c["k"], c["v"], out=out_d, lse=lse_d)
+    pr = p.read_profile()
+    p.profile(False)
+    assert pr["calls"] == 2
+    assert pr["attention_ms"] > 0 and pr["merge_ms"] > 0 and pr["decode_ms"] >= pr["attention_ms"]
+    if kind == "mla":
+        assert pr["grouped_ms"] > 0 and pr["suffix_ms"] > 0
+    assert torch.equal(out_d.view(torch.int16), out_t.view(torch.int16))
+    say("time launches", kind, {k: round(v, 4) for k, v in t.items()})
