@@ -363,10 +363,10 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   // ---- Work items ----
   // A lane is one (unit, head block, column chunk) stream of stages: a unit
   // is a group's prefix range or a request's suffix, a head block H KV heads,
-  // a column chunk up to 64 query rows.  The 8 waves of a workgroup take an
+  // a column chunk up to 64 query rows.  The 4 waves of a workgroup take an
   // item's H heads x C column groups (C = 2 for chunks wider than 32 rows) x
-  // S = 8 / (H C) block stripes, so one stage is S blocks of each head.  H is
-  // the largest power of two that divides Hkv with H x C <= 8 for the unit's
+  // S = 4 / (H C) block stripes, so one stage is S blocks of each head.  H is
+  // the largest power of two that divides Hkv with H x C <= 4 for the unit's
   // widest chunk.  The lanes are laid end to end and the stream is cut into
   // one equal run of stages per persistent workgroup; a lane cut k times
   // yields k + 1 items (token pieces), and every piece has S stripe splits,

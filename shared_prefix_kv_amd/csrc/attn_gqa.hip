@@ -11,11 +11,14 @@
 // all read the same KV tiles, so QK^T and PV are real matrix products and run
 // on bf16 MFMA; a per-request item has the Hq/Hkv <= 16 rows of each head.
 //
-// Persistent workgroups of 8 independent waves, two per SIMD: the planner
-// cuts the work items of both passes into one equal run of work per
-// workgroup (its bin).  In an item the 8 waves are H heads x C column groups
-// (up to 32 rows each; C = 2 only for items wider than 32 rows) x S = 8/(H C)
-// block stripes; the wave of stripe t reads blocks t, t + S, ... of the range.
+// Persistent workgroups of 4 independent waves, two workgroups per CU (two
+// waves per SIMD): the planner cuts the work items of both passes into one
+// equal run of work per workgroup (its bin).  In an item the 4 waves are H
+// heads x C column groups (up to 32 rows each; C = 2 only for items wider
+// than 32 rows) x S = 4/(H C) block stripes; the wave of stripe t reads
+// blocks t, t + S, ... of the range.  With the usual pool layout (the heads
+// of a block side by side) the H heads of one block are one contiguous read
+// per workgroup, which measured faster than S stripes over scattered blocks.
 // Each (stripe, head) writes its own partial triples (the merge folds stripes
 // like token splits), so waves never wait for one another: no barrier.
 //
