@@ -11,10 +11,11 @@
 // A workgroup of 8 waves (two per SIMD) owns an item of up to 64 query rows
 // and walks its token range in 32-token stages (half a cache block, 36 KiB):
 //   * a 4-slot LDS ring, filled two stages ahead by buffer_load_dwordx4 ... lds
-//     (mostly issued by the value waves, which otherwise wait for the score
-//     waves at the barrier), one barrier per stage (s_barrier after the own
-//     copies and LDS writes are done: no memory fence, which would wait for
-//     the copies still in flight);
+//     issued by the value waves (which otherwise wait for the score waves at
+//     the barrier; copies issued by the score waves stall their products),
+//     one barrier per stage (s_barrier after the own copies and LDS writes
+//     are done: no memory fence, which would wait for the copies still in
+//     flight);
 //   * score waves 0-3, 16 query rows each (the Q operand stays in registers
 //     for the whole item): S^T = K Q^T with v_mfma_f32_16x16x32_bf16, online
 //     softmax per row in the log2 domain with a lazy running max (raised
@@ -58,9 +59,8 @@ constexpr int kPvWaves = 4;                      // value waves
 constexpr int kWaves = kQkWaves + kPvWaves;
 constexpr int kPvDims = kDv / kPvWaves;          // value dims per value wave
 constexpr int kPvTiles = kPvDims / 16;
-constexpr int kDmaQ = 2;                                     // 1 KiB copies per stage and score wave
-constexpr int kDmaP = (kStageBytes / 1024 - kQkWaves * kDmaQ) / kPvWaves;  // ... and value wave
-static_assert((kQkWaves * kDmaQ + kPvWaves * kDmaP) * 1024 == kStageBytes, "stage copy split");
+constexpr int kDmaP = kStageBytes / 1024 / kPvWaves;  // 1 KiB copies per stage and value wave
+static_assert(kPvWaves * kDmaP * 1024 == kStageBytes, "stage copy split");
 constexpr float kTau = 8.f;                      // lazy-max threshold (log2 units)
 constexpr int kBufferWord3 = 0x00020000;         // raw buffer resource, gfx9 family
 
@@ -216,14 +216,6 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
   if (wave < kQkWaves) {
     // ---------------- score wave: rows 16 w .. 16 w + 15 of the item ----------------
     const int w = wave;
-    cint32* bt = (cint32*)(P.bt);
-    Copier<kDmaQ> cp{items, i_begin, 0, 0, i_end, load_item(items, i_begin)};
-    cp.dns = item_stages(cp.it);
-    const int d0 = w * kDmaQ;
-    if (kDmaQ > 0) {
-      cp.issue(P, bt, lds, d0, lane);
-      if (N > 1) cp.issue(P, bt, lds + kStageBytes, d0, lane);
-    }
 
     const __bf16* qbase = static_cast<const __bf16*>(P.q);
     cint32* perm = (cint32*)(P.perm);
@@ -235,11 +227,7 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
     bool active = false;
 
     for (int t = 0; t <= N; ++t) {
-      // Stage t has landed (this wave's copies; the barrier covers the rest).
-      if (t + 1 < N)
-        wait_vm<kDmaQ>();
-      else
-        wait_vm<0>();
+      // Stage t has landed once the value waves that copy it pass the barrier.
       lds_barrier();
       if (t == N) break;
 
@@ -258,9 +246,6 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
         mrow = NEG_INF;
         lsum = 0.f;
       }
-      // The copy of stage t + 2 goes into the slot of stage t - 2, which
-      // every wave finished before this stage's barrier.
-      if (kDmaQ > 0 && t + 2 < N) cp.issue(P, bt, lds + ((t + 2) % kSlots) * kStageBytes, d0, lane);
       const int buf = t & 1;
       if (active) {
         // S^T = K Q^T over 18 d-steps; the key operands are read from LDS
@@ -347,7 +332,7 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
     cint32* bt = (cint32*)(P.bt);
     Copier<kDmaP> cp{items, i_begin, 0, 0, i_end, load_item(items, i_begin)};
     cp.dns = item_stages(cp.it);
-    const int d0 = kQkWaves * kDmaQ + v * kDmaP;
+    const int d0 = v * kDmaP;
     cp.issue(P, bt, lds, d0, lane);
     if (N > 1) cp.issue(P, bt, lds + kStageBytes, d0, lane);
     Item it = load_item(items, i_begin);
