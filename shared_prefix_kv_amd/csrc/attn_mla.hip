@@ -366,21 +366,24 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
       u32x2 vr[kPvTiles][2];
       read_vt(kt, vr);
       const int nvalid = it.tok_end - (it.tok_begin + cs * kStage);
-      u32x4 keep = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
       if (nvalid < kStage) {
+        // Tokens past the range: zero their values (the operands are masked
+        // here, before the products, so that the product sequence reads them
+        // straight from the registers the transposing reads filled).
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const int nv = nvalid - 16 * tt - 4 * g;
-          keep[2 * tt] = (nv > 0 ? 0xffffu : 0u) | (nv > 1 ? 0xffff0000u : 0u);
-          keep[2 * tt + 1] = (nv > 2 ? 0xffffu : 0u) | (nv > 3 ? 0xffff0000u : 0u);
+          const u32x2 keep = {(nv > 0 ? 0xffffu : 0u) | (nv > 1 ? 0xffff0000u : 0u),
+                              (nv > 2 ? 0xffffu : 0u) | (nv > 3 ? 0xffff0000u : 0u)};
+#pragma unroll
+          for (int dt = 0; dt < kPvTiles; ++dt) vr[dt][tt] &= keep;
         }
       }
       if (cs == 0) {
         // First stage of the item: fresh accumulators.
 #pragma unroll
         for (int dt = 0; dt < kPvTiles; ++dt) {
-          const bf16x8 a =
-              __builtin_bit_cast(bf16x8, u32x4{vr[dt][0][0], vr[dt][0][1], vr[dt][1][0], vr[dt][1][1]} & keep);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{vr[dt][0][0], vr[dt][0][1], vr[dt][1][0], vr[dt][1][1]});
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct)
             o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ct], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -400,8 +403,7 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
         }
 #pragma unroll
         for (int dt = 0; dt < kPvTiles; ++dt) {
-          const bf16x8 a =
-              __builtin_bit_cast(bf16x8, u32x4{vr[dt][0][0], vr[dt][0][1], vr[dt][1][0], vr[dt][1][1]} & keep);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{vr[dt][0][0], vr[dt][0][1], vr[dt][1][0], vr[dt][1][1]});
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct)
             o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ct], o[ct][dt], 0, 0, 0);
