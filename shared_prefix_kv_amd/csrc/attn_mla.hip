@@ -379,6 +379,9 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
           for (int dt = 0; dt < kPvTiles; ++dt) vr[dt][tt] &= keep;
         }
       }
+      // The value products go first on the shared MFMA pipe (the score wave
+      // of this SIMD is in its softmax or at the barrier by now).
+      __builtin_amdgcn_s_setprio(2);
       if (cs == 0) {
         // First stage of the item: fresh accumulators.
 #pragma unroll
@@ -409,6 +412,7 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
             o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ct], o[ct][dt], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (++cs == cns) {
         // Partial rows hold the unnormalised sums (the merge divides).
 #pragma unroll
