@@ -141,10 +141,14 @@ fca_status fca_plan_workspace_size(int32_t batch, int32_t max_blocks, const fca_
  *                     owned by the caller, must outlive the plan.
  *
  * Enqueues the discovery kernels on `stream`, then waits once for a small
- * read-back (group records, counts and the device error flag).  The plan
- * copies the tables and lengths it needs into the workspace: the caller may
- * change or free block_tables_dev / seq_lens_dev once this returns.
- * batch == 0 gives a valid, empty plan.  *out is set only on FCA_OK.
+ * read-back (group records, counts and the device error flag), then enqueues
+ * the upload of the schedule (one copy and one small kernel) on `stream`:
+ * decodes on another stream must be ordered after this point of `stream`.
+ * The plan copies the tables and lengths it needs into the workspace: the
+ * caller may change or free block_tables_dev / seq_lens_dev once this
+ * returns.  `stream` must outlive the plan (fca_plan_destroy records an
+ * event on it).  batch == 0 gives a valid, empty plan.  *out is set only on
+ * FCA_OK.
  */
 fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_stride, const int32_t* seq_lens_dev,
                            int32_t batch, int32_t max_blocks, const fca_attn_desc* desc, void* workspace_dev,
@@ -275,7 +279,14 @@ fca_status fca_time_launches(fca_plan plan, const void* q_dev, const void* const
                              float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream,
                              fca_profile* result);
 
-/* Frees the host-side plan.  The workspace stays the caller's.  NULL is ok. */
+/*
+ * Frees the plan without waiting for the device.  Its device schedule is
+ * kept by the library (a few buffers per process) and reused by a later plan
+ * once the stream the plan was created with has passed the point of this
+ * call: decodes of the plan queued on other streams must be complete, or
+ * ordered before that point, when it is called.  The workspace stays the
+ * caller's.  NULL is ok.
+ */
 void fca_plan_destroy(fca_plan plan);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */

@@ -263,11 +263,15 @@ class Plan:
         _check(lib().fca_plan_get_info(self._h, ctypes.byref(info)))
         self.info = info
         self._decode_ws = None
+        # kept here: at interpreter exit the module's globals may be gone
+        # before the plan is collected
+        self._destroy = lib().fca_plan_destroy
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            lib().fca_plan_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            destroy(h)
             self._h = None
 
     @property

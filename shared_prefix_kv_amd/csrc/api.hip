@@ -167,6 +167,61 @@ int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
 
 }  // namespace
 
+namespace {
+
+// Schedule buffers of destroyed plans, kept for later plans of the same
+// device: hipFree waits for the whole device and a fresh hipMalloc is slow,
+// once per decode step each.  A buffer carries an event recorded on its
+// plan's stream when the plan was destroyed; it is reused once that event
+// has completed (every decode of the plan is ordered before it).
+struct SchedBuf {
+  char* ptr;
+  size_t cap;
+  int dev;
+  hipEvent_t done;
+};
+std::mutex g_sched_mu;
+std::vector<SchedBuf> g_sched_free;
+constexpr size_t kSchedKeep = 8;  // buffers kept at most
+
+// A kept buffer of at least `bytes` on `dev` whose plan's work is done, or
+// none (ptr == nullptr).
+SchedBuf sched_take(int dev, size_t bytes) {
+  std::lock_guard<std::mutex> lock(g_sched_mu);
+  int best = -1;
+  for (int i = 0; i < (int)g_sched_free.size(); ++i) {
+    const SchedBuf& b = g_sched_free[i];
+    if (b.dev != dev || b.cap < bytes || (best >= 0 && b.cap >= g_sched_free[best].cap)) continue;
+    if (hipEventQuery(b.done) != hipSuccess) {
+      (void)hipGetLastError();  // not ready: no error for later calls to see
+      continue;
+    }
+    best = i;
+  }
+  if (best < 0) return SchedBuf{nullptr, 0, dev, nullptr};
+  const SchedBuf b = g_sched_free[best];
+  g_sched_free.erase(g_sched_free.begin() + best);
+  return b;
+}
+
+void sched_give(SchedBuf b) {
+  SchedBuf drop{nullptr, 0, 0, nullptr};
+  {
+    std::lock_guard<std::mutex> lock(g_sched_mu);
+    g_sched_free.push_back(b);
+    if (g_sched_free.size() > kSchedKeep) {
+      drop = g_sched_free.front();
+      g_sched_free.erase(g_sched_free.begin());
+    }
+  }
+  if (drop.ptr) {
+    (void)hipFree(drop.ptr);
+    (void)hipEventDestroy(drop.done);
+  }
+}
+
+}  // namespace
+
 struct fca_plan_s {
   fca_attn_desc desc;
   Kind kind;
@@ -188,19 +243,91 @@ struct fca_plan_s {
   std::vector<int32_t> src_off, src_row;  // merge sources per (request, query head), CSR
   int item_cols = kItemColsGqa;  // query rows per column chunk
   fca_plan_info info;
-  // plan-owned device copy of the schedule
+  // plan-owned device copy of the schedule (a buffer of sched_cap bytes on
+  // device `dev`, created with `stream`), handed to later plans when this one
+  // is destroyed
   char* sched = nullptr;
+  size_t sched_cap = 0;
+  int dev = 0;
+  hipStream_t stream = nullptr;
+  hipEvent_t sched_done = nullptr;
   SchedLayout SL{};
   // measurement hook
   bool profiling = false;
   std::vector<hipEvent_t> event_pool;
   std::vector<hipEvent_t> pending;  // kProfEvents per profiled call
   ~fca_plan_s() {
-    if (sched) (void)hipFree(sched);
+    if (sched) {
+      hipEvent_t ev = sched_done;
+      hipError_t e = ev ? hipSuccess : hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventRecord(ev, stream);
+      if (e == hipSuccess) {
+        sched_give(SchedBuf{sched, sched_cap, dev, ev});
+      } else {
+        (void)hipGetLastError();
+        if (ev) (void)hipEventDestroy(ev);
+        (void)hipFree(sched);
+      }
+    } else if (sched_done) {
+      (void)hipEventDestroy(sched_done);
+    }
     for (hipEvent_t e : pending) (void)hipEventDestroy(e);
     for (hipEvent_t e : event_pool) (void)hipEventDestroy(e);
   }
 };
+
+namespace {
+
+// Pinned host staging for a plan's read-back and schedule upload, one buffer
+// per host thread, grown on demand and kept until the process ends.  An
+// upload from it may still be in flight when the thread's next plan needs it;
+// `busy` (recorded after that upload) orders the reuse.
+struct Staging {
+  char* ptr = nullptr;
+  size_t cap = 0;
+  hipEvent_t busy = nullptr;
+  bool pending = false;
+};
+thread_local Staging t_stage;
+
+hipError_t stage_acquire(size_t bytes, char** out) {
+  Staging& st = t_stage;
+  hipError_t e = hipSuccess;
+  if (st.pending) {
+    e = hipEventSynchronize(st.busy);
+    if (e != hipSuccess) return e;
+    st.pending = false;
+  }
+  if (st.cap < bytes) {
+    if (st.ptr) {
+      e = hipHostFree(st.ptr);
+      st.ptr = nullptr;
+      st.cap = 0;
+      if (e != hipSuccess) return e;
+    }
+    const size_t cap = std::max<size_t>(bytes + bytes / 2, (size_t)64 << 10);
+    e = hipHostMalloc(reinterpret_cast<void**>(&st.ptr), cap, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      st.ptr = nullptr;
+      return e;
+    }
+    st.cap = cap;
+  }
+  *out = st.ptr;
+  return hipSuccess;
+}
+
+// The staging buffer is read by work queued on `s`.
+hipError_t stage_in_use(hipStream_t s) {
+  Staging& st = t_stage;
+  hipError_t e = hipSuccess;
+  if (!st.busy) e = hipEventCreateWithFlags(&st.busy, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(st.busy, s);
+  if (e == hipSuccess) st.pending = true;
+  return e;
+}
+
+}  // namespace
 
 // Partial rows request i merges for query head h, in the merge's order:
 // every split of the deepest group's lane, then of its ancestors' lanes, then
@@ -699,12 +826,15 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
       return hip_fail(e, "discovery launch");
     }
     std::vector<int32_t> rb(L.readback_bytes / 4);
-    e = hipMemcpyAsync(rb.data(), P->ws + L.header, L.readback_bytes, hipMemcpyDeviceToHost, s);
+    char* stage = nullptr;
+    e = stage_acquire(L.readback_bytes, &stage);
+    if (e == hipSuccess) e = hipMemcpyAsync(stage, P->ws + L.header, L.readback_bytes, hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
       delete P;
       return hip_fail(e, "discovery read-back");
     }
+    std::memcpy(rb.data(), stage, L.readback_bytes);
     if (rb[kHdrErr]) {
       const int bad = rb[kHdrBadReq];
       const int err = rb[kHdrErr];
@@ -725,8 +855,8 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
       delete P;
       return st;
     }
-    // Plan-owned device copy of the schedule (pageable copies: the runtime
-    // stages them before returning).
+    // Plan-owned device copy of the schedule, packed in the pinned staging
+    // buffer and uploaded with one copy.
     SchedLayout& S = P->SL;
     size_t off = 0;
     auto place = [&](size_t bytes) {
@@ -734,45 +864,53 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
       off = align_up(off + std::max<size_t>(bytes, 1));
       return at;
     };
-    std::vector<BinHead> heads(P->bins.size() - 1);
-    for (size_t b = 0; b + 1 < P->bins.size(); ++b) {
-      BinHead& h = heads[b];
-      h = BinHead{};
-      h.i_begin = P->bins[b];
-      h.i_end = P->bins[b + 1];
-      h.first = P->items[h.i_begin];
-    }
+    const size_t n_heads = P->bins.size() - 1;
     S.items = place(P->items.size() * sizeof(WorkItem));
-    S.heads = place(heads.size() * sizeof(BinHead));
+    S.heads = place(n_heads * sizeof(BinHead));
     S.perm = place(P->perm.size() * 4);
     S.src_off = place(P->src_off.size() * 4);
     S.src_row = place(P->src_row.size() * 4);
     S.total = off;
-    e = hipMalloc(&P->sched, S.total);
-    if (e != hipSuccess) {
-      P->sched = nullptr;
-      delete P;
-      return hip_fail(e, "schedule buffer");
-    }
-    struct Up {
-      const void* src;
-      size_t off, bytes;
-    } ups[] = {
-        {P->items.data(), S.items, P->items.size() * sizeof(WorkItem)},
-        {heads.data(), S.heads, heads.size() * sizeof(BinHead)},
-        {P->perm.data(), S.perm, P->perm.size() * 4},
-        {P->src_off.data(), S.src_off, P->src_off.size() * 4},
-        {P->src_row.data(), S.src_row, P->src_row.size() * 4},
-    };
-    for (const Up& u : ups) {
-      if (!u.bytes) continue;
-      e = hipMemcpyAsync(P->sched + u.off, u.src, u.bytes, hipMemcpyHostToDevice, s);
+    P->dev = dev;
+    P->stream = s;
+    const SchedBuf kept = sched_take(dev, S.total);
+    if (kept.ptr) {
+      P->sched = kept.ptr;
+      P->sched_cap = kept.cap;
+      P->sched_done = kept.done;
+    } else {
+      const size_t cap = align_up(S.total + S.total / 4);
+      e = hipMalloc(&P->sched, cap);
       if (e != hipSuccess) {
+        P->sched = nullptr;
         delete P;
-        return hip_fail(e, "schedule upload");
+        return hip_fail(e, "schedule buffer");
       }
+      P->sched_cap = cap;
     }
-    e = launch_bin_heads(reinterpret_cast<BinHead*>(P->sched + S.heads), (int)heads.size(),
+    e = stage_acquire(S.total, &stage);
+    if (e != hipSuccess) {
+      delete P;
+      return hip_fail(e, "schedule staging");
+    }
+    std::memset(stage, 0, S.total);
+    std::memcpy(stage + S.items, P->items.data(), P->items.size() * sizeof(WorkItem));
+    BinHead* heads = reinterpret_cast<BinHead*>(stage + S.heads);
+    for (size_t b = 0; b < n_heads; ++b) {
+      heads[b].i_begin = P->bins[b];
+      heads[b].i_end = P->bins[b + 1];
+      heads[b].first = P->items[P->bins[b]];
+    }
+    std::memcpy(stage + S.perm, P->perm.data(), P->perm.size() * 4);
+    std::memcpy(stage + S.src_off, P->src_off.data(), P->src_off.size() * 4);
+    std::memcpy(stage + S.src_row, P->src_row.data(), P->src_row.size() * 4);
+    e = hipMemcpyAsync(P->sched, stage, S.total, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = stage_in_use(s);
+    if (e != hipSuccess) {
+      delete P;
+      return hip_fail(e, "schedule upload");
+    }
+    e = launch_bin_heads(reinterpret_cast<BinHead*>(P->sched + S.heads), (int)n_heads,
                          reinterpret_cast<const int32_t*>(P->ws + P->L.bt), P->W, P->desc.block_size, s);
     if (e != hipSuccess) {
       delete P;

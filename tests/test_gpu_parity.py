@@ -601,3 +601,38 @@ def test_time_launches_and_profile(kind):
         assert pr["grouped_ms"] > 0 and pr["suffix_ms"] > 0
     assert torch.equal(out_d.view(torch.int16), out_t.view(torch.int16))
     say("time launches", kind, {k: round(v, 4) for k, v in t.items()})
+
+
+def test_plan_schedule_memory_reuse():
+    """Plans created and destroyed in turn (their schedules recycled through
+    the library's stream-ordered pool) decode correctly, and a plan kept
+    alive meanwhile still decodes bit for bit as it did at first."""
+    import gc
+
+    keep_b = build_batch(CONFIGS["tiny"])
+    keep_vn = fill_values_numpy(keep_b, poison=True)
+    keep_vals = upload(keep_vn)
+    keep_p, keep_out, keep_lse = run_decode(keep_b, keep_vals)
+    first = keep_out.clone()
+    rng = np.random.default_rng(5)
+    shape = AttnShape(8, 2, 128, 128, 16, 1 / math.sqrt(128))
+    W, bs, nb = 16, 16, 512
+    for it in range(6):
+        B = int(rng.integers(2, 12))
+        tables = rng.permutation(nb)[: B * W].reshape(B, W).astype(np.int32)
+        lens = rng.integers(0, W * bs + 1, size=B).astype(np.int32)
+        for i in range(1, B):
+            # share whole blocks that are full in both rows (no poisoned tails shared)
+            base = int(rng.integers(0, i))
+            cut = int(rng.integers(0, min(lens[i], lens[base]) // bs + 1))
+            tables[i, :cut] = tables[base, :cut]
+        case = small_case(shape, tables, lens, nb, seed=it)
+        ref, _ = A.attend(case["q"], case["k"], case["v"], tables, lens, shape)
+        p, out, _ = run_decode(_B(shape, tables, lens, nb), upload(case))
+        assert_close(bf16_tensor_to_f64(out), ref, f"reuse round {it}")
+        del p, out
+        gc.collect()
+    out2 = torch.empty_like(keep_out)
+    fca.fca_decode(keep_vals["q"], keep_vals["k"], keep_vals["v"], keep_p, out=out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), first.view(torch.int16))
