@@ -57,6 +57,10 @@ typedef enum fca_status {
                                        launch of persistent workgroups runs
                                        the work items of both passes (GQA);
                                        latent caches always use two. */
+#define FCA_PLAN_OUT_F32 4u         /* fca_decode writes `out` as float32
+                                       (an attention state that
+                                       fca_merge_states can combine without
+                                       a bf16 rounding in between) */
 
 /*
  * Shape and cache layout of one attention layer.
@@ -163,8 +167,9 @@ fca_status fca_plan_get_info(fca_plan plan, fca_plan_info* info);
  *   q_dev        bf16 [batch, num_q_heads, head_dim_qk], contiguous.
  *   k_cache_dev  bf16 pool, layout above.  v_cache_dev likewise (ignored
  *                when v_aliases_k).
- *   out_dev      bf16 [batch, num_q_heads, head_dim_v], contiguous; row i is
- *                request i.  A request with seq_len 0 gets zeros.
+ *   out_dev      bf16 [batch, num_q_heads, head_dim_v], contiguous (float32
+ *                with FCA_PLAN_OUT_F32); row i is request i.  A request with
+ *                seq_len 0 gets zeros.
  *   lse_dev      float [batch, num_q_heads] natural-log sum of exp(scores),
  *                or NULL.  -inf for seq_len 0.
  *   workspace_dev >= info.decode_workspace_bytes, 256-byte aligned: holds the
@@ -278,6 +283,38 @@ fca_status fca_time_launches(fca_plan plan, const void* q_dev, const void* const
                              const void* const* v_caches, int32_t n_caches, int32_t repeats, void* out_dev,
                              float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream,
                              fca_profile* result);
+
+/*
+ * Exact combination of attention states over disjoint key sets: state j of
+ * (request i, head h) is a normalised output o_j (float32) and its natural
+ * log-sum-exp lse_j, as fca_decode writes them with FCA_PLAN_OUT_F32 and an
+ * lse buffer.  The result is
+ *   w_j = exp(lse_j - max_j lse_j),  out = sum_j w_j o_j / sum_j w_j,
+ *   lse = max_j lse_j + ln sum_j w_j,
+ * attention over the union of the key sets.  This is the merge half of
+ * routing the query to the holder of a part of the cache ("Move the Query,
+ * Not the Cache", Metodologia: partial attention computed where the blocks
+ * live, combined by the online-softmax merge) and the same weighting as the
+ * exact reduction of "Core Mechanism", step 3.  States with lse = -inf (no
+ * keys) carry no weight; if all do, out = 0 and lse = -inf.
+ *
+ *   outs      host array of n_states device pointers, float32
+ *             [batch, num_heads, head_dim], contiguous.
+ *   lses      host array of n_states device pointers, float32
+ *             [batch, num_heads].
+ *   out_dev   [batch, num_heads, head_dim]: bf16, or float32 with
+ *             FCA_MERGE_OUT_F32 in `flags`; may alias outs[0] when float32.
+ *   lse_dev   float32 [batch, num_heads], or NULL; may alias lses[0].
+ *
+ * n_states in [1, 16], head_dim in {128, 512}, batch * num_heads in
+ * [0, 2^31).  Asynchronous on `stream`; no allocation.
+ * FCA_ERR_INVALID_ARG for NULL pointers or sizes out of range,
+ * FCA_ERR_UNSUPPORTED for another head_dim, FCA_ERR_HIP if the launch fails.
+ */
+#define FCA_MERGE_OUT_F32 1u
+fca_status fca_merge_states(int32_t n_states, const float* const* outs, const float* const* lses, int32_t batch,
+                            int32_t num_heads, int32_t head_dim, void* out_dev, float* lse_dev, uint32_t flags,
+                            void* stream);
 
 /*
  * Frees the plan without waiting for the device.  Its device schedule is

@@ -142,3 +142,22 @@ def merge(parts):
     out[ok] = num[ok] / den[ok, None]
     lse[ok] = M[ok] + np.log(den[ok])
     return out, lse
+
+
+def merge_states(outs, lses):
+    """Combine attention states over disjoint key sets -> (out, lse).
+
+    States are [n, Dv] outputs and [n] lses.  A state (o, lse) is the triple
+    (o, m = lse, l = 1), or the empty triple (o = 0, l = 0) when lse = -inf,
+    whatever its o holds, so this is ``merge`` over those triples (the
+    online-softmax merge of partial attention routed to the holder of the
+    keys, "Move the Query, Not the Cache" page, Metodologia).
+    """
+    parts = []
+    for o, lse in zip(outs, lses):
+        lse = np.asarray(lse, dtype=np.float64)
+        live = np.isfinite(lse)
+        o = np.where(live[:, None], np.asarray(o, dtype=np.float64), 0.0)  # no keys: output undefined
+        parts.append((o, np.where(live, lse, -np.inf), live.astype(np.float64)))
+    return merge(parts)
+

@@ -29,6 +29,8 @@ STATUS_NAMES = {
 }
 FCA_PLAN_DISABLE_CASCADE = 1
 FCA_PLAN_SEPARATE_PASSES = 2
+FCA_PLAN_OUT_F32 = 4
+FCA_MERGE_OUT_F32 = 1
 
 EXPORTED = [
     "fca_plan_workspace_size",
@@ -40,6 +42,7 @@ EXPORTED = [
     "fca_profile_enable",
     "fca_profile_read",
     "fca_time_launches",
+    "fca_merge_states",
     "fca_plan_destroy",
     "fca_last_error",
     "fca_version",
@@ -147,6 +150,7 @@ def lib():
         L.fca_profile_enable.argtypes = [vp, i32]
         L.fca_profile_read.argtypes = [vp, ctypes.POINTER(Profile)]
         L.fca_time_launches.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp, ctypes.POINTER(Profile)]
+        L.fca_merge_states.argtypes = [i32, vp, vp, i32, i32, i32, vp, vp, ctypes.c_uint32, vp]
         L.fca_plan_destroy.argtypes = [vp]
         L.fca_plan_destroy.restype = None
         L.fca_last_error.restype = ctypes.c_char_p
@@ -176,6 +180,7 @@ def make_desc(
     k_strides=None,
     v_strides=None,
     separate_passes=False,
+    out_f32=False,
 ) -> AttnDesc:
     """Descriptor for the documented cache layout (default: dense pools)."""
     d = AttnDesc()
@@ -191,12 +196,16 @@ def make_desc(
         d.v_stride_block, d.v_stride_head = v_strides if v_strides else (num_kv_heads * vsh, vsh)
     d.v_aliases_k = int(bool(v_aliases_k))
     d.scale = float(scale)
-    d.flags = (0 if cascade else FCA_PLAN_DISABLE_CASCADE) | (FCA_PLAN_SEPARATE_PASSES if separate_passes else 0)
+    d.flags = (
+        (0 if cascade else FCA_PLAN_DISABLE_CASCADE)
+        | (FCA_PLAN_SEPARATE_PASSES if separate_passes else 0)
+        | (FCA_PLAN_OUT_F32 if out_f32 else 0)
+    )
     d.reserved = 0
     return d
 
 
-def desc_from_shape(shape, num_blocks, cascade=True, separate_passes=False) -> AttnDesc:
+def desc_from_shape(shape, num_blocks, cascade=True, separate_passes=False, out_f32=False) -> AttnDesc:
     return make_desc(
         shape.num_q_heads,
         shape.num_kv_heads,
@@ -208,6 +217,7 @@ def desc_from_shape(shape, num_blocks, cascade=True, separate_passes=False) -> A
         v_aliases_k=shape.v_aliases_k,
         cascade=cascade,
         separate_passes=separate_passes,
+        out_f32=out_f32,
     )
 
 
@@ -292,11 +302,14 @@ class Plan:
         d = self.desc
         assert q.dtype == torch.bfloat16 and q.is_contiguous()
         assert tuple(q.shape) == (self.batch, d.num_q_heads, d.head_dim_qk)
+        out_dtype = torch.float32 if d.flags & FCA_PLAN_OUT_F32 else torch.bfloat16
         if out is None:
-            out = torch.empty((self.batch, d.num_q_heads, d.head_dim_v), dtype=torch.bfloat16, device=q.device)
-        assert out.dtype == torch.bfloat16 and out.is_contiguous()
+            out = torch.empty((self.batch, d.num_q_heads, d.head_dim_v), dtype=out_dtype, device=q.device)
+        assert out.dtype == out_dtype and out.is_contiguous()
+        assert tuple(out.shape) == (self.batch, d.num_q_heads, d.head_dim_v)
         if lse is not None:
             assert lse.dtype == torch.float32 and lse.is_contiguous()
+            assert tuple(lse.shape) == (self.batch, d.num_q_heads)
         ws = workspace if workspace is not None else self.decode_workspace(q.device)
         _check(
             lib().fca_decode(
@@ -414,6 +427,35 @@ def fca_plan(block_tables, seq_lens, desc: AttnDesc, workspace=None, stream=None
 def fca_decode(q, k_cache, v_cache, plan: Plan, out=None, lse=None, stream=None):
     """Forest Cascade Attention decode for a planned batch; returns `out`."""
     return plan.decode(q, k_cache, v_cache, out=out, lse=lse, stream=stream)
+
+
+def merge_states(outs, lses, out=None, lse=None, out_f32=False, stream=None):
+    """Exact combination of attention states over disjoint key sets
+    (fca_merge_states): ``outs`` float32 [B, H, D] normalised outputs, ``lses``
+    float32 [B, H] natural log-sum-exps, as fca_decode writes them with
+    ``out_f32``.  Returns ``out`` (bf16, or float32 with ``out_f32``)."""
+    import torch
+
+    n = len(outs)
+    assert n == len(lses) and n >= 1
+    B, H, D = outs[0].shape
+    for o, l in zip(outs, lses):
+        assert o.dtype == torch.float32 and o.is_contiguous() and tuple(o.shape) == (B, H, D)
+        assert l.dtype == torch.float32 and l.is_contiguous() and tuple(l.shape) == (B, H)
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((B, H, D), dtype=dt, device=outs[0].device)
+    assert out.dtype == dt and out.is_contiguous() and tuple(out.shape) == (B, H, D)
+    if lse is not None:
+        assert lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == (B, H)
+    po = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    pl = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lses])
+    _check(
+        lib().fca_merge_states(
+            n, po, pl, B, H, D, _ptr(out), _ptr(lse), FCA_MERGE_OUT_F32 if out_f32 else 0, _stream_ptr(stream)
+        )
+    )
+    return out
 
 
 def version() -> str:

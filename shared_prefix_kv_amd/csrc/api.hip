@@ -82,7 +82,7 @@ fca_status check_desc(const fca_attn_desc* d, Kind* kind) {
                 d->num_q_heads, d->num_kv_heads);
   if (d->num_blocks <= 0) return fail(FCA_ERR_INVALID_ARG, "num_blocks must be positive");
   if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return fail(FCA_ERR_INVALID_ARG, "scale must be finite and > 0");
-  if (d->flags & ~(FCA_PLAN_DISABLE_CASCADE | FCA_PLAN_SEPARATE_PASSES))
+  if (d->flags & ~(FCA_PLAN_DISABLE_CASCADE | FCA_PLAN_SEPARATE_PASSES | FCA_PLAN_OUT_F32))
     return fail(FCA_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
   const int r = d->num_q_heads / d->num_kv_heads;
   if (d->head_dim_qk == 128 && d->head_dim_v == 128 && d->block_size == 16 && !d->v_aliases_k) {
@@ -990,6 +990,7 @@ fca_status decode_params(const fca_plan_s* P, const void* q_dev, const void* k_c
   mp->part = part;
   mp->out = out_dev;
   mp->lse = lse_dev;
+  mp->out_f32 = (P->desc.flags & FCA_PLAN_OUT_F32) ? 1 : 0;
   return FCA_OK;
 }
 
@@ -1115,6 +1116,35 @@ fca_status fca_time_launches(fca_plan plan, const void* q_dev, const void* const
   acc.decode_ms = acc.attention_ms + acc.merge_ms;
   acc.calls = (int64_t)n;
   *result = acc;
+  return FCA_OK;
+}
+
+fca_status fca_merge_states(int32_t n_states, const float* const* outs, const float* const* lses, int32_t batch,
+                            int32_t num_heads, int32_t head_dim, void* out_dev, float* lse_dev, uint32_t flags,
+                            void* stream) {
+  if (n_states < 1 || n_states > kMaxStates)
+    return fail(FCA_ERR_INVALID_ARG, "n_states %d outside [1, %d]", n_states, kMaxStates);
+  if (batch < 0 || num_heads < 0) return fail(FCA_ERR_INVALID_ARG, "negative batch or num_heads");
+  if ((int64_t)batch * num_heads >= ((int64_t)1 << 31)) return fail(FCA_ERR_INVALID_ARG, "batch * num_heads too large");
+  if (head_dim != 128 && head_dim != 512) return fail(FCA_ERR_UNSUPPORTED, "head_dim %d is not built", head_dim);
+  if (flags & ~FCA_MERGE_OUT_F32) return fail(FCA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  StatesParams sp;
+  std::memset(&sp, 0, sizeof(sp));
+  sp.n = n_states;
+  sp.pairs = batch * num_heads;
+  sp.D = head_dim;
+  sp.out = out_dev;
+  sp.lse = lse_dev;
+  sp.out_f32 = (flags & FCA_MERGE_OUT_F32) ? 1 : 0;
+  if (sp.pairs == 0) return FCA_OK;
+  if (!outs || !lses || !out_dev) return fail(FCA_ERR_INVALID_ARG, "outs / lses / out is NULL");
+  for (int j = 0; j < n_states; ++j) {
+    if (!outs[j] || !lses[j]) return fail(FCA_ERR_INVALID_ARG, "state %d is NULL", j);
+    sp.outs[j] = outs[j];
+    sp.lses[j] = lses[j];
+  }
+  const hipError_t e = launch_merge_states(sp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
   return FCA_OK;
 }
 

@@ -155,8 +155,23 @@ struct MergeParams {
   PartialPtrs part;
   void* out;
   float* lse;
+  int32_t out_f32;  // out is float32 (else bf16)
 };
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+
+// Combination of attention states (normalised float32 outputs and their
+// natural log-sum-exp) over disjoint key sets.
+constexpr int kMaxStates = 16;
+struct StatesParams {
+  const float* outs[kMaxStates];
+  const float* lses[kMaxStates];
+  int32_t n, pairs, D;
+  void* out;
+  float* lse;
+  int32_t out_f32;
+};
+
+hipError_t launch_merge_states(const StatesParams& p, hipStream_t s);
 
 }  // namespace fca

@@ -46,6 +46,26 @@ __device__ __forceinline__ float xsum32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Row values acc[0..N) * inv at element offset `at` of `out`, bf16 or float32.
+template <int N>
+__device__ __forceinline__ void store_row(void* out, int32_t out_f32, int64_t at, const float* acc, float inv) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  if (out_f32) {
+    float* dst = static_cast<float*>(out) + at;
+#pragma unroll
+    for (int v = 0; v < N; v += 4)
+      *reinterpret_cast<float4*>(dst + v) = float4{acc[v] * inv, acc[v + 1] * inv, acc[v + 2] * inv, acc[v + 3] * inv};
+  } else {
+    __bf16* dst = static_cast<__bf16*>(out) + at;
+#pragma unroll
+    for (int v = 0; v < N; v += 4) {
+      const bf16x4 ob = {(__bf16)(acc[v] * inv), (__bf16)(acc[v + 1] * inv), (__bf16)(acc[v + 2] * inv),
+                         (__bf16)(acc[v + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(dst + v) = ob;
+    }
+  }
+}
+
 // One wave per (request, head).  Lane j reads the j-th partial row index of
 // the pair from the plan's source table, so that all (m, l) loads are issued
 // at once after two dependent loads; the value rows
@@ -123,20 +143,80 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
 #pragma unroll
   for (int v = 0; v < VPL; ++v) acc[v] = xsum32(acc[v]);
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  if (half == 0) {
-    __bf16* dst = static_cast<__bf16*>(P.out) + pair * DV + hl * VPL;
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int v = 0; v < VPL; v += 4) {
-      const bf16x4 ob = {(__bf16)(acc[v] * inv), (__bf16)(acc[v + 1] * inv), (__bf16)(acc[v + 2] * inv),
-                         (__bf16)(acc[v + 3] * inv)};
-      *reinterpret_cast<bf16x4*>(dst + v) = ob;
-    }
-  }
+  if (half == 0) store_row<VPL>(P.out, P.out_f32, pair * DV + hl * VPL, acc, inv);
   if (P.lse && lane == 0) P.lse[pair] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
+// Attention states: one wave per (request, head); lane j < n holds lse_j,
+// then every lane accumulates its D / 64 dims over the states in order
+// (fixed order: bit-reproducible).
+template <int D>
+__device__ __forceinline__ void states_body(const StatesParams& P) {
+  constexpr int VPL = D / 64;  // floats per lane
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= P.pairs) return;
+  float x = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kMaxStates; ++j)
+    if (j < P.n && lane == j) x = P.lses[j][pair];
+  // a state with no keys (lse = -inf, or NaN from an empty decode) weighs nothing
+  if (!(x > -INFINITY)) x = -INFINITY;
+  const float M = wave_max(x);
+  const float w = (x == -INFINITY) ? 0.f : exp2f((x - M) * kLog2e);
+  const float L = wave_sum(w);
+  float acc[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxStates; ++j) {
+    if (j >= P.n) break;
+    const float wj = lane_f(w, j);
+    if (wj > 0.f) {  // wave-uniform; skipping also keeps NaN rows of empty states out
+      const float* src = P.outs[j] + pair * D + lane * VPL;
+#pragma unroll
+      for (int v = 0; v < VPL; v += 2) {
+        const float2 t = *reinterpret_cast<const float2*>(src + v);
+        acc[v] = fmaf(wj, t.x, acc[v]);
+        acc[v + 1] = fmaf(wj, t.y, acc[v + 1]);
+      }
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if constexpr (VPL % 4 == 0) {
+    store_row<VPL>(P.out, P.out_f32, pair * D + lane * VPL, acc, inv);
+  } else {
+    if (P.out_f32) {
+      float* dst = static_cast<float*>(P.out) + pair * D + lane * VPL;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) dst[v] = acc[v] * inv;
+    } else {
+      __bf16* dst = static_cast<__bf16*>(P.out) + pair * D + lane * VPL;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) dst[v] = (__bf16)(acc[v] * inv);
+    }
+  }
+  if (P.lse && lane == 0) P.lse[pair] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
 }  // namespace
+
+__global__ __launch_bounds__(256) void fca_merge_states_d128(StatesParams P) { states_body<128>(P); }
+__global__ __launch_bounds__(256) void fca_merge_states_d512(StatesParams P) { states_body<512>(P); }
+
+hipError_t launch_merge_states(const StatesParams& p, hipStream_t s) {
+  if (p.pairs == 0) return hipSuccess;
+  const dim3 grid((unsigned)((p.pairs + 3) / 4));
+  if (p.D == 128) {
+    hipLaunchKernelGGL(fca_merge_states_d128, grid, dim3(256), 0, s, p);
+  } else if (p.D == 512) {
+    hipLaunchKernelGGL(fca_merge_states_d512, grid, dim3(256), 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 __global__ __launch_bounds__(256) void fca_merge_kernel_d128(MergeParams P) { merge_body<128>(P); }
 __global__ __launch_bounds__(256) void fca_merge_kernel_d512(MergeParams P) { merge_body<512>(P); }

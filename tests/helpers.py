@@ -56,7 +56,8 @@ def assert_close(out, ref, what=""):
 
 def assert_lse_close(lse, ref, what=""):
     both_inf = np.isneginf(lse) & np.isneginf(ref)
-    diff = np.where(both_inf, 0.0, np.abs(lse - ref))
+    with np.errstate(invalid="ignore"):
+        diff = np.where(both_inf, 0.0, np.abs(lse - ref))
     assert (diff <= LSE_ATOL).all(), f"{what}: lse max diff {np.nanmax(diff)}"
 
 

@@ -115,6 +115,17 @@ def test_decode_and_info_reject_null_plan():
     assert L.fca_profile_read(None, None) == 1
     prof = fca.Profile()
     assert L.fca_time_launches(None, None, None, None, 1, 1, None, None, None, 0, None, ctypes.byref(prof)) == 1
+
+
+def test_merge_states_validation_before_device():
+    """fca_merge_states rejects bad arguments without touching the device."""
+    L = fca.lib()
+    assert L.fca_merge_states(0, None, None, 4, 4, 128, None, None, 0, None) == 1  # no states
+    assert L.fca_merge_states(17, None, None, 4, 4, 128, None, None, 0, None) == 1  # too many
+    assert L.fca_merge_states(2, None, None, 4, 4, 64, None, None, 0, None) == 2  # head_dim not built
+    assert L.fca_merge_states(2, None, None, 4, 4, 128, None, None, 8, None) == 1  # unknown flag
+    assert L.fca_merge_states(2, None, None, 4, 4, 128, None, None, 0, None) == 1  # NULL arrays
+    assert L.fca_merge_states(2, None, None, 0, 4, 128, None, None, 0, None) == 0  # empty batch: nothing to do
     L.fca_plan_destroy(None)  # no-op
 
 

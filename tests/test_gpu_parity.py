@@ -636,3 +636,99 @@ def test_plan_schedule_memory_reuse():
     fca.fca_decode(keep_vals["q"], keep_vals["k"], keep_vals["v"], keep_p, out=out2)
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), first.view(torch.int16))
+
+
+# ------------------------------------------------- route-the-query merge ----
+
+
+def split_tables(b, frac):
+    """Each request's blocks cut in two at a block boundary: (tables, lens)
+    of the first part and of the rest (empty parts allowed)."""
+    bs = b.shape.block_size
+    lens = b.seq_lens.astype(np.int64)
+    nb = -(-lens // bs)
+    na = np.minimum((nb * frac).astype(np.int64), lens // bs)
+    ta = b.block_tables.copy()
+    tb = np.zeros_like(b.block_tables)
+    for i in range(b.batch):
+        rest = b.block_tables[i, na[i] : nb[i]]
+        tb[i, : len(rest)] = rest
+    la = (na * bs).astype(np.int32)
+    lb = (lens - na * bs).astype(np.int32)
+    return (ta, la), (tb, lb)
+
+
+@pytest.mark.parametrize("name,frac", [("tiny", 0.5), ("tiny", 0.0), ("llama3_8b", 0.7)])
+def test_route_the_query_split_merge(name, frac):
+    """The cache of every request cut in two (as if half of it lived on
+    another GPU): each part decoded to a float32 state with its lse, the two
+    states combined by fca_merge_states, against the oracle's attention over
+    the whole cache (and the float32 decode of the whole cache)."""
+    b = build_batch(CONFIGS[name])
+    sh = b.shape
+    if name == "tiny":
+        vn = fill_values_numpy(b, poison=True)
+        vals = upload(vn)
+        ref, ref_lse = A.attend(vn["q"], vn["k"], vn["v"], b.block_tables, b.seq_lens, sh)
+        pick = list(range(b.batch))
+    else:
+        vals = fill_values_torch(b, "cuda", seed=CONFIGS[name].seed, poison=True)
+        pick = [0, 9, 33, 63]
+        ref, ref_lse = oracle_requests_from_device(b, vals, pick)
+    states = []
+    for tables, lens in split_tables(b, frac):
+        bt = torch.from_numpy(tables).cuda()
+        sl = torch.from_numpy(lens).cuda()
+        p = fca.fca_plan(bt, sl, fca.desc_from_shape(sh, b.num_blocks, out_f32=True))
+        o = torch.empty((b.batch, sh.num_q_heads, sh.head_dim_v), dtype=torch.float32, device="cuda")
+        l = torch.empty((b.batch, sh.num_q_heads), dtype=torch.float32, device="cuda")
+        fca.fca_decode(vals["q"], vals["k"], vals["v"], p, out=o, lse=l)
+        states.append((o, l))
+    lse = torch.empty((b.batch, sh.num_q_heads), dtype=torch.float32, device="cuda")
+    out = fca.merge_states([s[0] for s in states], [s[1] for s in states], lse=lse)
+    torch.cuda.synchronize()
+    rep = assert_close(bf16_tensor_to_f64(out[pick]), ref, f"{name} split {frac}")
+    assert_lse_close(lse[pick].cpu().numpy(), ref_lse, f"{name} split {frac}")
+    # float32 state of the whole cache, merged with nothing, is the whole decode
+    p = fca.fca_plan(torch.from_numpy(b.block_tables).cuda(), torch.from_numpy(b.seq_lens).cuda(),
+                     fca.desc_from_shape(sh, b.num_blocks, out_f32=True))
+    of = torch.empty_like(states[0][0])
+    lf = torch.empty_like(states[0][1])
+    fca.fca_decode(vals["q"], vals["k"], vals["v"], p, out=of, lse=lf)
+    out1 = fca.merge_states([of], [lf], out_f32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, of)
+    assert (out.float() - of).abs().max().item() < 8e-3
+    say("route-the-query", name, frac, rep)
+
+
+@pytest.mark.parametrize("D", [128, 512])
+def test_merge_states_against_oracle(D):
+    """Random states (including states without keys, whose outputs hold
+    garbage, and pairs where every state is empty) merged on the device
+    against the oracle's merge_states, in bf16 and float32 output, with the
+    output aliasing the first state."""
+    rng = np.random.default_rng(D)
+    B, H, n = 7, 5, 5
+    outs = [rng.standard_normal((B, H, D)).astype(np.float32) for _ in range(n)]
+    lses = [(3.0 * rng.standard_normal((B, H))).astype(np.float32) for _ in range(n)]
+    for j in range(n):
+        dead = rng.random((B, H)) < 0.3
+        lses[j][dead] = -np.inf
+        outs[j][dead] = np.nan  # an empty state's output must not leak in
+    lses[0][2, 3] = lses[1][2, 3] = lses[2][2, 3] = lses[3][2, 3] = lses[4][2, 3] = -np.inf
+    ref, ref_lse = A.merge_states([o.reshape(B * H, D) for o in outs], [l.reshape(B * H) for l in lses])
+    ref, ref_lse = ref.reshape(B, H, D), ref_lse.reshape(B, H)
+    d_outs = [torch.from_numpy(o).cuda() for o in outs]
+    d_lses = [torch.from_numpy(l).cuda() for l in lses]
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    out = fca.merge_states(d_outs, d_lses, lse=lse)
+    torch.cuda.synchronize()
+    assert_close(bf16_tensor_to_f64(out), ref, f"merge states D={D}")
+    assert_lse_close(lse.cpu().numpy(), ref_lse, f"merge states D={D}")
+    assert (bf16_tensor_to_f64(out)[2, 3] == 0).all() and np.isneginf(lse[2, 3].item())
+    # float32, written over the first state
+    out32 = fca.merge_states(d_outs, d_lses, out=d_outs[0], out_f32=True)
+    torch.cuda.synchronize()
+    o32 = out32.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(o32, ref, rtol=1e-5, atol=1e-6)

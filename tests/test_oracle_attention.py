@@ -213,6 +213,44 @@ def test_split_merge_equals_full(seed):
     np.testing.assert_allclose(out2, full, rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_merge_states_of_split_is_full(seed):
+    """States (normalised output, natural lse) of disjoint key sets, merged,
+    are attention over their union, checked against the direct definition;
+    a state without keys (lse = -inf, its output arbitrary) weighs nothing."""
+    rng = np.random.default_rng(10 + seed)
+    L, D, Dv, n = int(rng.integers(2, 150)), 8, 6, 4
+    q = rng.standard_normal((n, D))
+    K = 3.0 * rng.standard_normal((L, D))
+    V = rng.standard_normal((L, Dv))
+    s = 0.5 * q @ K.T
+    w = np.exp(s - s.max(1, keepdims=True))
+    ref = (w @ V) / w.sum(1, keepdims=True)
+    ref_lse = s.max(1) + np.log(w.sum(1))
+    cuts = np.sort(rng.integers(0, L + 1, size=2))
+    outs, lses = [], []
+    for a, b in [(0, cuts[0]), (cuts[0], cuts[1]), (cuts[1], L)]:
+        if a == b:
+            outs.append(np.full((n, Dv), 7.0))  # no keys: must not leak in
+            lses.append(np.full(n, -np.inf))
+            continue
+        sa = 0.5 * q @ K[a:b].T
+        wa = np.exp(sa - sa.max(1, keepdims=True))
+        outs.append((wa @ V[a:b]) / wa.sum(1, keepdims=True))
+        lses.append(sa.max(1) + np.log(wa.sum(1)))
+    outs.append(np.full((n, Dv), 3.0))
+    lses.append(np.full(n, -np.inf))
+    out, lse = A.merge_states(outs, lses)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12)
+    # one state is itself; only empty states give zeros and -inf
+    o1, l1 = A.merge_states([ref], [ref_lse])
+    np.testing.assert_allclose(o1, ref, rtol=1e-14)
+    np.testing.assert_allclose(l1, ref_lse, rtol=1e-14)
+    o0, l0 = A.merge_states([outs[-1]], [lses[-1]])
+    assert (o0 == 0).all() and np.isneginf(l0).all()
+
+
 def test_all_empty_merge():
     e = A.partial(np.ones((2, 4)), np.zeros((0, 4)), np.zeros((0, 3)), 1.0)
     out, lse = A.merge([e, e])
