@@ -509,6 +509,46 @@ def main():
         result["graph_ms_per_step"] = round(ms_graph, 5)
         del graph, ws
 
+    if not args.profile_only:
+        # The route-the-query merge (fca_merge_states) of two float32 states
+        # of this batch's shape: bytes = both states and lses read, the bf16
+        # output and the lse written.
+        Bq, Hq_, Dv = batch.batch, sh.num_q_heads, sh.head_dim_v
+        st_o = [torch.randn((Bq, Hq_, Dv), device="cuda") for _ in range(2)]
+        st_l = [torch.randn((Bq, Hq_), device="cuda") for _ in range(2)]
+        mo = torch.empty((Bq, Hq_, Dv), dtype=torch.bfloat16, device="cuda")
+        ml = torch.empty((Bq, Hq_), dtype=torch.float32, device="cuda")
+        # 20 launches captured in a HIP graph, so that the timing is the
+        # device's and not the Python call rate
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fca.merge_states(st_o, st_l, out=mo, lse=ml)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        per_graph = 20
+        mg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(mg):
+            for _ in range(per_graph):
+                fca.merge_states(st_o, st_l, out=mo, lse=ml)
+        for _ in range(3):
+            mg.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            mg.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_m = e0.elapsed_time(e1) / (reps * per_graph)
+        del mg
+        mbytes = 2 * Bq * Hq_ * (Dv * 4 + 4) + Bq * Hq_ * (Dv * 2 + 4)
+        result["merge_states"] = {"states": 2, "us": round(ms_m * 1000, 2), "GBps": gbps(mbytes, ms_m), "bytes": mbytes}
+        log(f"merge of two float32 states: {ms_m * 1000:.1f} us ({gbps(mbytes, ms_m)} GB/s)")
+        del st_o, st_l, mo, ml
+
     if args.group_sweep and not args.profile_only:
         result["group_sweep"] = group_sweep(torch, fca, steps, warmup)
 
