@@ -113,7 +113,40 @@ def _pick(by: dict[str, list[float]], key: str) -> list[float]:
     return vals
 
 
-def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_bytes, cmds, out):
+UTIL_COUNTERS = ("MfmaUtil", "LdsUtil", "LDSBankConflict", "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+
+
+def utilisation(dirpath: str, kernels, durations) -> dict:
+    """Median per dispatch of the matrix-core and LDS counters of a
+    ``--pmc MfmaUtil LdsUtil LDSBankConflict SQ_INSTS_VALU_MFMA_MOPS_BF16``
+    run, per kernel, plus the bf16 matrix rate from the operation count
+    (512 per unit) over the kernel's median duration."""
+    res = {}
+    for key in kernels:
+        row = {}
+        for c in UTIL_COUNTERS:
+            vals = _pick({k: v for k, v in _raw_counters(dirpath, c).items()}, key)
+            if vals:
+                row[c] = statistics.median(vals)
+        if row:
+            d = durations.get(key)
+            if d and "SQ_INSTS_VALU_MFMA_MOPS_BF16" in row:
+                row["bf16_TFLOPs"] = row["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / (statistics.median(d) * 1e-6) / 1e12
+            res[key] = row
+    return res
+
+
+def _raw_counters(dirpath: str, counter: str) -> dict[str, list[float]]:
+    """Counter values per dispatch (as written, no scaling), by kernel name."""
+    by = {}
+    with open(_one(dirpath, "counter_collection.csv")) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                by.setdefault(r["Kernel_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return {k: [v for _, v in sorted(vals)] for k, vals in by.items()}
+
+
+def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_bytes, cmds, out, util_dir=None):
     stats = kernel_stats(stats_dir)
     att_kernels = [k for k in (ATTENTION, MLA_GROUPED, MLA_SUFFIX) if kernel_durations(stats_dir, k)]
     if not att_kernels:
@@ -179,6 +212,20 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
             f"  algorithmic bytes per {kernel} launch {algorithmic_bytes / 1e6:.2f} MB;"
             f" measured / algorithmic = {(att['fetch_bytes'] + att['write_bytes']) / algorithmic_bytes:.3f}"
         )
+    util = {}
+    if util_dir:
+        util = utilisation(util_dir, att_kernels + [MERGE], durations)
+        lines += [
+            "",
+            "Matrix cores and LDS per dispatch (median; rocprofv3 derived counters MfmaUtil, LdsUtil,",
+            "LDSBankConflict in percent of GPU-active time, and the bf16 MFMA operation count):",
+        ]
+        for key, v in util.items():
+            lines.append(
+                f"  {key:24s} MFMA busy {v.get('MfmaUtil', float('nan')):6.1f} %  LDS active {v.get('LdsUtil', float('nan')):6.1f} %"
+                f"  LDS bank conflicts {v.get('LDSBankConflict', float('nan')):5.1f} %"
+                + (f"  bf16 MFMA {v['bf16_TFLOPs']:7.1f} TFLOP/s" if "bf16_TFLOPs" in v else "")
+            )
     payload = dict(
         config=config,
         source_sha256=source_sha256(),
@@ -187,6 +234,7 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
         fetch_factor=f_factor,
         write_factor=w_factor,
         traffic=res,
+        util=util,
     )
     lines += ["", "json: " + json.dumps(payload)]
     text = "\n".join(lines) + "\n"
@@ -224,9 +272,10 @@ def main():
     s.add_argument("--copy-bytes", type=int, required=True)
     s.add_argument("--algorithmic-bytes", type=int, default=0)
     s.add_argument("--cmd", action="append", default=[])
+    s.add_argument("--util", default=None, help="rocprofv3 folder of the matrix-core / LDS counter run")
     s.add_argument("--out", required=True)
     a = ap.parse_args()
-    print(summarize(a.stats, a.fetch, a.write, a.config, a.copy_bytes, a.algorithmic_bytes, a.cmd, a.out), end="")
+    print(summarize(a.stats, a.fetch, a.write, a.config, a.copy_bytes, a.algorithmic_bytes, a.cmd, a.out, a.util), end="")
 
 
 if __name__ == "__main__":
