@@ -409,6 +409,15 @@ def main():
             "write_bytes": int(t["write_bytes"]),
             "counter_scale": {"fetch": round(tr["fetch_factor"], 4), "write": round(tr["write_factor"], 4)},
         }
+        u = tr.get("util", {}).get(dom_name)
+        if u:
+            # matrix-core and LDS use of the same kernel (derived rocprofv3 counters)
+            roofline["counters"] = {
+                "mfma_busy_pct": round(u.get("MfmaUtil", float("nan")), 1),
+                "lds_active_pct": round(u.get("LdsUtil", float("nan")), 1),
+                "lds_bank_conflict_pct": round(u.get("LDSBankConflict", float("nan")), 1),
+                "bf16_mfma_TFLOPs_counted": round(u.get("bf16_TFLOPs", float("nan")), 1),
+            }
     def gbps(nbytes, ms_):
         return round(nbytes / (ms_ / 1000.0) / 1e9, 1) if ms_ > 0 else None  # None for nan / 0
 
