@@ -469,6 +469,18 @@ def main():
         log(f"fca decode, separate pass launches: {ms_sep * 1000:.1f} us/step")
         result["separate_passes_ms_per_step"] = round(ms_sep, 5)
 
+    if not args.profile_only and not sh.v_aliases_k:
+        # The activation heuristic (FCA_PLAN_AUTO_FOLD): groups that cannot pay
+        # for their partial rows are read per request.
+        plan_af = fca.fca_plan(bt, sl, fca.desc_from_shape(sh, batch.num_blocks, auto_fold=True))
+        n_f = int(plan_af.info.num_folded_groups)
+        plan_af.decode_workspace(out.device)
+        warm(plan_af, qs, pools, out, lse, warmup, torch, fca)
+        ms_af, _ = time_steps(plan_af, qs, pools, out, lse, steps, torch, fca)
+        log(f"fca decode with the activation heuristic: {ms_af * 1000:.1f} us/step ({n_f} of {info.num_groups} groups folded)")
+        result["auto_fold"] = {"ms_per_step": round(ms_af, 5), "folded_groups": n_f, "groups": int(info.num_groups)}
+        del plan_af
+
     if not args.no_noncascade and not args.profile_only:
         desc_nc = fca.desc_from_shape(sh, batch.num_blocks, cascade=False)
         plan_nc = fca.fca_plan(bt, sl, desc_nc)

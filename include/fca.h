@@ -57,6 +57,17 @@ typedef enum fca_status {
                                        launch of persistent workgroups runs
                                        the work items of both passes (GQA);
                                        latent caches always use two. */
+#define FCA_PLAN_AUTO_FOLD 8u       /* activation heuristic (GQA caches):
+                                       a group whose shared blocks would
+                                       save fewer bytes than its partial
+                                       rows cost to write and merge is
+                                       read per request instead (folded
+                                       into its members' suffixes); groups
+                                       are folded from the leaves up.
+                                       Latent caches keep every group (their
+                                       passes are bound by the matrix
+                                       products, which a fold leaves
+                                       unchanged). */
 #define FCA_PLAN_OUT_F32 4u         /* fca_decode writes `out` as float32
                                        (an attention state that
                                        fca_merge_states can combine without
@@ -119,6 +130,7 @@ typedef struct fca_plan_info {
   int64_t logical_tokens;    /* sum of seq_lens */
   int64_t unique_tokens;     /* group ranges once + every suffix */
   size_t decode_workspace_bytes; /* bytes fca_decode needs */
+  int32_t num_folded_groups; /* groups read per request (FCA_PLAN_AUTO_FOLD) */
 } fca_plan_info;
 
 /*
@@ -198,10 +210,18 @@ typedef struct fca_group_record {
  *   groups   [num_groups]
  *   members  [sum of member_count]  request indices
  *   requests [batch * 3]  per request: suffix_block_begin, suffix_tokens,
- *                         deepest group (canonical index) or -1
+ *                         deepest group (canonical index) or -1, as read by
+ *                         the per-request pass (with FCA_PLAN_AUTO_FOLD a
+ *                         folded group's range belongs to its members'
+ *                         suffixes and the deepest group is the nearest
+ *                         one kept)
  * Any pointer may be NULL to skip that part.
  */
 fca_status fca_plan_export(fca_plan plan, fca_group_record* groups, int32_t* members, int32_t* requests);
+
+/* folded [num_groups]: 1 for a group read per request (FCA_PLAN_AUTO_FOLD),
+ * else 0, in canonical order (host copy). */
+fca_status fca_plan_export_folded(fca_plan plan, int32_t* folded);
 
 /* One unit of work of the grouped or per-request pass (host copy). */
 typedef struct fca_work_item {

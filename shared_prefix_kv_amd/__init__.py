@@ -30,6 +30,7 @@ STATUS_NAMES = {
 FCA_PLAN_DISABLE_CASCADE = 1
 FCA_PLAN_SEPARATE_PASSES = 2
 FCA_PLAN_OUT_F32 = 4
+FCA_PLAN_AUTO_FOLD = 8
 FCA_MERGE_OUT_F32 = 1
 
 EXPORTED = [
@@ -39,6 +40,7 @@ EXPORTED = [
     "fca_decode",
     "fca_plan_export",
     "fca_plan_export_schedule",
+    "fca_plan_export_folded",
     "fca_profile_enable",
     "fca_profile_read",
     "fca_time_launches",
@@ -86,6 +88,7 @@ class PlanInfo(ctypes.Structure):
         ("logical_tokens", ctypes.c_int64),
         ("unique_tokens", ctypes.c_int64),
         ("decode_workspace_bytes", ctypes.c_size_t),
+        ("num_folded_groups", ctypes.c_int32),
     ]
 
 
@@ -147,6 +150,7 @@ def lib():
         L.fca_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fca_plan_export.argtypes = [vp, vp, vp, vp]
         L.fca_plan_export_schedule.argtypes = [vp, vp, vp, vp, vp]
+        L.fca_plan_export_folded.argtypes = [vp, vp]
         L.fca_profile_enable.argtypes = [vp, i32]
         L.fca_profile_read.argtypes = [vp, ctypes.POINTER(Profile)]
         L.fca_time_launches.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp, ctypes.POINTER(Profile)]
@@ -181,6 +185,7 @@ def make_desc(
     v_strides=None,
     separate_passes=False,
     out_f32=False,
+    auto_fold=False,
 ) -> AttnDesc:
     """Descriptor for the documented cache layout (default: dense pools)."""
     d = AttnDesc()
@@ -200,12 +205,13 @@ def make_desc(
         (0 if cascade else FCA_PLAN_DISABLE_CASCADE)
         | (FCA_PLAN_SEPARATE_PASSES if separate_passes else 0)
         | (FCA_PLAN_OUT_F32 if out_f32 else 0)
+        | (FCA_PLAN_AUTO_FOLD if auto_fold else 0)
     )
     d.reserved = 0
     return d
 
 
-def desc_from_shape(shape, num_blocks, cascade=True, separate_passes=False, out_f32=False) -> AttnDesc:
+def desc_from_shape(shape, num_blocks, cascade=True, separate_passes=False, out_f32=False, auto_fold=False) -> AttnDesc:
     return make_desc(
         shape.num_q_heads,
         shape.num_kv_heads,
@@ -218,6 +224,7 @@ def desc_from_shape(shape, num_blocks, cascade=True, separate_passes=False, out_
         cascade=cascade,
         separate_passes=separate_passes,
         out_f32=out_f32,
+        auto_fold=auto_fold,
     )
 
 
@@ -398,7 +405,9 @@ class Plan:
                 )
             )
         requests = [(reqs[3 * i], reqs[3 * i + 1], reqs[3 * i + 2]) for i in range(B)]
-        return dict(groups=out, requests=requests)
+        folded = (ctypes.c_int32 * max(G, 1))()
+        _check(lib().fca_plan_export_folded(self._h, folded))
+        return dict(groups=out, requests=requests, folded=[int(folded[g]) for g in range(G)])
 
     def export_schedule(self):
         """Work items of both passes and the merge sources: ``sources[i][h]``

@@ -82,7 +82,7 @@ fca_status check_desc(const fca_attn_desc* d, Kind* kind) {
                 d->num_q_heads, d->num_kv_heads);
   if (d->num_blocks <= 0) return fail(FCA_ERR_INVALID_ARG, "num_blocks must be positive");
   if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return fail(FCA_ERR_INVALID_ARG, "scale must be finite and > 0");
-  if (d->flags & ~(FCA_PLAN_DISABLE_CASCADE | FCA_PLAN_SEPARATE_PASSES | FCA_PLAN_OUT_F32))
+  if (d->flags & ~(FCA_PLAN_DISABLE_CASCADE | FCA_PLAN_SEPARATE_PASSES | FCA_PLAN_OUT_F32 | FCA_PLAN_AUTO_FOLD))
     return fail(FCA_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
   const int r = d->num_q_heads / d->num_kv_heads;
   if (d->head_dim_qk == 128 && d->head_dim_v == 128 && d->block_size == 16 && !d->v_aliases_k) {
@@ -231,6 +231,7 @@ struct fca_plan_s {
   // host copies
   std::vector<fca_group_record> groups;
   std::vector<int32_t> members;   // ascending per group
+  std::vector<int32_t> folded;    // per group: read per request (FCA_PLAN_AUTO_FOLD)
   std::vector<int32_t> req3;      // per request: suffix_block_begin, suffix_tokens, deepest
   std::vector<WorkItem> items_g, items_s;  // host copies of each pass's items, in bin order
   std::vector<WorkItem> items;             // what the device runs: all launches' items
@@ -473,15 +474,56 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
     P->members.insert(P->members.end(), m.begin(), m.end());
   }
 
+  // Activation (FCA_PLAN_AUTO_FOLD, GQA caches): a group is read once for
+  // all members only if that saves more bytes than its partial rows cost.
+  // Reading a group of n members over T tokens once instead of n times
+  // saves (n - 1) T t bytes (t: KV bytes per token); in exchange, each of
+  // its token pieces writes n Hq partial rows that the merge reads back, and
+  // a written byte costs about three read bytes here, so 4 (4 Dv + 8) bytes
+  // per row.  The pieces are estimated as the group's bytes over one
+  // workgroup's share of all unique bytes.  Leaves first: a group is folded
+  // only when all its children are.
+  P->folded.assign(G, 0);
+  int n_folded = 0;
+  std::vector<int> eff_deep(deepest_c);
+  std::vector<int> eff_sb(sfxb, sfxb + B);
+  if ((P->desc.flags & FCA_PLAN_AUTO_FOLD) && P->kind == kGqa && G > 0) {
+    const Tuning tf = tuning();
+    const double tok_bytes = (double)hkv * (P->desc.head_dim_qk + P->desc.head_dim_v) * 2;
+    double unique_tok = 0;
+    for (int i = 0; i < B; ++i) unique_tok += lens[i] - bs * sfxb[i];
+    for (int c = 0; c < G; ++c) unique_tok += (double)(P->groups[c].block_end - P->groups[c].block_begin) * bs;
+    const double share = std::max(unique_tok * tok_bytes / ((double)n_cu_ * tf.bins_per_cu), 1.0);
+    const double row_cost = 4.0 * (4.0 * P->desc.head_dim_v + 8.0);
+    for (int c = G - 1; c >= 0; --c) {  // children come after their parents
+      bool leaves_folded = true;
+      for (int ch : children[c]) leaves_folded = leaves_folded && P->folded[ch];
+      if (!leaves_folded) continue;
+      const double T = (double)(P->groups[c].block_end - P->groups[c].block_begin) * bs;
+      const double saved = (count[c] - 1) * T * tok_bytes;
+      const double pieces = std::max(1.0, std::ceil(T * tok_bytes / share));
+      const double cost = pieces * count[c] * hq * row_cost;
+      if (saved < cost) {
+        P->folded[c] = 1;
+        ++n_folded;
+      }
+    }
+    for (int i = 0; i < B; ++i)
+      while (eff_deep[i] >= 0 && P->folded[eff_deep[i]]) {
+        eff_sb[i] = P->groups[eff_deep[i]].block_begin;
+        eff_deep[i] = P->groups[eff_deep[i]].parent;
+      }
+  }
+
   P->req3.assign((size_t)B * 3, 0);
   int64_t logical = 0, unique = 0;
   std::vector<int> sfx_tokens(B);
   for (int i = 0; i < B; ++i) {
-    const int sb = sfxb[i];
+    const int sb = eff_sb[i];
     sfx_tokens[i] = lens[i] - bs * sb;
     P->req3[3 * i + 0] = sb;
     P->req3[3 * i + 1] = sfx_tokens[i];
-    P->req3[3 * i + 2] = deepest_c[i];
+    P->req3[3 * i + 2] = eff_deep[i];
     logical += lens[i];
     unique += sfx_tokens[i];
     if (sfx_tokens[i] < 0) return fail(FCA_ERR_HIP, "inconsistent discovery output (suffix of request %d)", i);
@@ -709,6 +751,10 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
     gm.parent = gr.parent;
     gm.r0 = r0[c];
     gm.ncols = count[c] * r;
+    gm.lane0 = -1;
+    gm.H = 1;
+    gm.chunks = 0;
+    if (P->folded[c]) continue;  // read per request: no grouped work, on no merge path
     gm.lane0 = add_lanes(all, gr.block_begin * bs, gr.block_end * bs, P->perm[r0[c]], r0[c], count[c] * r,
                          &gm.H, &gm.chunks);
     unique += (int64_t)(gr.block_end - gr.block_begin) * bs;
@@ -718,7 +764,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   for (int i = 0; i < B; ++i) {
     ReqMeta& rq = P->req[i];
     rq.pos = pos[i];
-    rq.deepest = deepest_c[i];
+    rq.deepest = eff_deep[i];
     rq.sfx_lane = -1;
     rq.sfx_H = 1;
     rq.sfx_chunks = 1;
@@ -780,6 +826,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   info.num_partial_rows = row;
   info.logical_tokens = logical;
   info.unique_tokens = unique;
+  info.num_folded_groups = n_folded;
   const size_t dv = (size_t)P->desc.head_dim_v;
   info.decode_workspace_bytes = align_up((size_t)row * dv * 4) + 2 * align_up((size_t)row * 4) + kAlign;
   return FCA_OK;
@@ -1185,6 +1232,12 @@ fca_status fca_plan_export(fca_plan plan, fca_group_record* groups, int32_t* mem
   if (groups) std::copy(plan->groups.begin(), plan->groups.end(), groups);
   if (members) std::copy(plan->members.begin(), plan->members.end(), members);
   if (requests) std::copy(plan->req3.begin(), plan->req3.end(), requests);
+  return FCA_OK;
+}
+
+fca_status fca_plan_export_folded(fca_plan plan, int32_t* folded) {
+  if (!plan || !folded) return fail(FCA_ERR_INVALID_ARG, "plan / folded is NULL");
+  std::copy(plan->folded.begin(), plan->folded.end(), folded);
   return FCA_OK;
 }
 

@@ -72,7 +72,7 @@ def test_workspace_size_and_validation():
     with pytest.raises(fca.FcaError):
         fca.plan_workspace_size(4, 4, d)
     d = gqa_desc()
-    d.flags = 8
+    d.flags = 1 << 10
     with pytest.raises(fca.FcaError):
         fca.plan_workspace_size(4, 4, d)
     d = gqa_desc()

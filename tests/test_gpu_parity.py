@@ -168,7 +168,10 @@ def test_schedule_covers_each_token_once(name):
     h of request i merges exactly the rows of its path's units for its own KV
     head and column, each row read by one (request, head)."""
     b = build_batch(CONFIGS[name])
-    p = plan_for(b)
+    check_schedule(b, plan_for(b))
+
+
+def check_schedule(b, p):
     sh = b.shape
     r = sh.gqa_ratio
     hkv = sh.num_kv_heads
@@ -210,6 +213,7 @@ def test_schedule_covers_each_token_once(name):
         for h in range(it["kv_head"], it["kv_head"] + it["kv_heads"]):
             for c in range(it["col0"], it["col1"]):
                 spans_g.setdefault(key, {}).setdefault((h, c), []).append((it["tok_begin"], it["tok_end"]))
+    kept = [k for k in range(len(ex["groups"])) if not ex["folded"][k]]
     group_key = {}
     for key, arr in spans_g.items():
         assert len(arr) == hkv * key[2]
@@ -219,12 +223,13 @@ def test_schedule_covers_each_token_once(name):
             v = sorted(v)
             assert v[0][0] == lo and v[-1][1] == hi
             assert all(x1 == y0 for (_, x1), (y0, _) in zip(v, v[1:]))
-        match = [k for k, g in enumerate(ex["groups"])
-                 if (g["block_begin"] * bs, g["block_end"] * bs, len(g["members"]) * r) == (lo, hi, key[2])
-                 and first_req[key] in g["members"]]
+        match = [k for k in kept
+                 if (ex["groups"][k]["block_begin"] * bs, ex["groups"][k]["block_end"] * bs,
+                     len(ex["groups"][k]["members"]) * r) == (lo, hi, key[2])
+                 and first_req[key] in ex["groups"][k]["members"]]
         assert len(match) == 1
         group_key[match[0]] = key
-    assert len(group_key) == len(ex["groups"])
+    assert len(group_key) == len(kept)  # folded groups have no grouped work
 
     # suffix items: each request's suffix tokens once per (head, column)
     spans_s = {}
@@ -732,3 +737,90 @@ def test_merge_states_against_oracle(D):
     torch.cuda.synchronize()
     o32 = out32.cpu().numpy().astype(np.float64)
     np.testing.assert_allclose(o32, ref, rtol=1e-5, atol=1e-6)
+
+
+# ------------------------------------------------------ activation (fold) ----
+
+
+def fold_case():
+    """64 requests of the Llama-3-8B layer shape: 16 pairs sharing one block,
+    8 pairs sharing 48 blocks, and a root shared by 16 requests over 2
+    blocks whose children are 8 pairs sharing 40 more blocks each."""
+    shape = AttnShape(32, 8, 128, 128, 16, 1 / math.sqrt(128))
+    rng = np.random.default_rng(77)
+    W, bs = 112, 16
+    B = 64
+    nb = B * W + 64
+    perm = rng.permutation(nb)
+    tables = perm[: B * W].reshape(B, W).astype(np.int32)
+    lens = np.zeros(B, np.int32)
+    for k in range(16):  # pairs over one shared block
+        i = 2 * k
+        tables[i + 1, :1] = tables[i, :1]
+        lens[i], lens[i + 1] = rng.integers(40, 120, size=2) * bs // 2
+    for k in range(8):  # pairs over 48 shared blocks
+        i = 32 + 2 * k
+        tables[i + 1, :48] = tables[i, :48]
+        lens[i], lens[i + 1] = (48 + rng.integers(2, 40, size=2)) * bs - 3
+    for k in range(8):  # root of 16 over 2 blocks, then pairs over 40 more
+        i = 48 + 2 * k
+        tables[i, :2] = tables[48, :2]
+        tables[i + 1, :42] = tables[i, :42]
+        lens[i], lens[i + 1] = (42 + rng.integers(2, 30, size=2)) * bs - 5
+    return shape, tables, lens, nb
+
+
+@pytest.mark.parametrize("case", ["fold", "tiny", "llama3_8b"])
+def test_auto_fold_plan_schedule_and_decode(case):
+    """FCA_PLAN_AUTO_FOLD: discovered groups are those of the oracle; groups
+    that cannot pay for their partial rows are folded into their members'
+    suffixes (leaves first), the schedule still covers every token once,
+    and the decode matches the oracle."""
+    if case == "fold":
+        shape, tables, lens, nb = fold_case()
+        b = _B(shape, tables, lens, nb)
+        vn = small_case(shape, tables, lens, nb, seed=3)
+    else:
+        b = build_batch(CONFIGS[case])
+        shape, tables, lens, nb = b.shape, b.block_tables, b.seq_lens, b.num_blocks
+        vn = fill_values_numpy(b, poison=True) if case == "tiny" else None
+    bt, sl = dev_tables(b)
+    p = fca.fca_plan(bt, sl, fca.desc_from_shape(shape, nb, auto_fold=True))
+    ex = p.export()
+    ref_plan = group(tables, lens, shape.block_size)
+    assert with_block_ids(ex, tables)["groups"] == ref_plan["groups"]
+    folded = ex["folded"]
+    assert p.info.num_folded_groups == sum(folded)
+    # leaves first: a kept group's parent is kept
+    for k, g in enumerate(ex["groups"]):
+        if not folded[k] and g["parent"] >= 0:
+            assert not folded[g["parent"]]
+    # a request's range as read: its suffix starts where its nearest kept group ends
+    for i, (sb, st, deep) in enumerate(ex["requests"]):
+        ref_sb, _, ref_deep = ref_plan["requests"][i]
+        d = ref_deep
+        while d >= 0 and folded[d]:
+            d = ex["groups"][d]["parent"]
+        assert deep == d
+        assert sb == (ex["groups"][d]["block_end"] if d >= 0 else 0)
+        assert st == lens[i] - sb * shape.block_size
+    if case == "fold":
+        # the one-block pairs fold, the 48-block pairs stay, the 2-block root
+        # stays because its children (40 more blocks each) stay
+        by_len = {(g["block_begin"], g["block_end"]): folded[k] for k, g in enumerate(ex["groups"])}
+        assert by_len[(0, 1)] == 1 and by_len[(0, 48)] == 0 and by_len[(0, 2)] == 0 and by_len[(2, 42)] == 0
+    if case == "tiny":
+        assert folded == [1]
+    if case == "llama3_8b":
+        assert sum(folded) == 0
+    check_schedule(b, p)
+    if vn is not None:
+        ref, ref_lse = A.attend(vn["q"], vn["k"], vn["v"], tables, lens, shape)
+        vals = upload(vn)
+        out = torch.empty((len(lens), shape.num_q_heads, shape.head_dim_v), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((len(lens), shape.num_q_heads), dtype=torch.float32, device="cuda")
+        fca.fca_decode(vals["q"], vals["k"], vals["v"], p, out=out, lse=lse)
+        torch.cuda.synchronize()
+        rep = assert_close(bf16_tensor_to_f64(out), ref, f"auto fold {case}")
+        assert_lse_close(lse.cpu().numpy(), ref_lse, f"auto fold {case}")
+        say("auto fold", case, "folded", sum(folded), "of", len(folded), rep)
