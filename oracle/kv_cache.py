@@ -14,10 +14,14 @@ module states that step on host arrays in the documented cache layout:
 
 For request i with L = seq_lens[i] cached tokens the new token is token L:
 block table entry j = L // block_size, slot t = L % block_size.  If
-cow_dst[i] >= 0, block table[i, j] is first copied whole (every head, keys
-and values) to block cow_dst[i] and the table entry is set to it; the token
-is then written into the (possibly new) block.  The lengths are not changed
-here (the caller's next plan uses L + 1).
+cow_dst[i] >= 0 (and differs from table[i, j]), the request's tokens in block
+table[i, j] (slots 0 .. t-1, every head, keys and values) are first copied
+to block cow_dst[i] and the table entry is set to it; the token is then
+written at slot t of the (possibly new) block.  Slots after t of the copy are
+left as they were: the pages say the shared block is copied when a request
+diverges, and the slots after t hold no token of this request (they may
+hold other sharers' tokens), so only the request's own tokens are copied.
+The lengths are not changed here (the caller's next plan uses L + 1).
 """
 
 from __future__ import annotations
@@ -34,11 +38,11 @@ def append(k_pool, v_pool, tables, seq_lens, k_new, v_new, block_size, cow_dst=N
     bt = tables.copy()
     for i, L in enumerate(seq_lens):
         j, t = int(L) // block_size, int(L) % block_size
-        if cow_dst is not None and cow_dst[i] >= 0:
+        if cow_dst is not None and cow_dst[i] >= 0 and int(cow_dst[i]) != int(bt[i, j]):
             src, dst = int(bt[i, j]), int(cow_dst[i])
-            k[dst] = k[src]
+            k[dst, :, :, :t, :] = k[src, :, :, :t, :]
             if v is not None:
-                v[dst] = v[src]
+                v[dst, :, :, :t] = v[src, :, :, :t]
             bt[i, j] = dst
         blk = int(bt[i, j])
         dq = k_new.shape[2]

@@ -57,6 +57,39 @@ def test_copy_on_write_leaves_the_sharer_unchanged():
     np.testing.assert_array_equal(K1[6], A.widen_bf16(kn[0]))
     Kb, _ = A.gather_kv(k2, v2, t2[1], 6, bs, dv, False)
     np.testing.assert_array_equal(Kb, K0)
+    # slots after the new token in the copy keep what the target held
+    np.testing.assert_array_equal(k2[9, :, :, 3:, :], k[9, :, :, 3:, :])
+    np.testing.assert_array_equal(v2[9, :, :, 3:], v[9, :, :, 3:])
+    # and blocks no request writes are untouched
+    for blk in set(range(nb)) - {9}:
+        np.testing.assert_array_equal(k2[blk], k[blk])
+        np.testing.assert_array_equal(v2[blk], v[blk])
+
+
+def test_copy_on_write_for_a_shorter_sharer():
+    """A request that shares the first 5 tokens of a block holding 6 (a fork
+    at an earlier position) copies only its 5 tokens, and the longer sharer
+    appending in place at slot 6 in the same call leaves the copy intact."""
+    rng = np.random.default_rng(3)
+    bs, hkv, dq, dv, nb = 8, 2, 16, 8, 10
+    k, v = _pools(rng, nb, hkv, dq, dv, bs)
+    tables = np.array([[1, 2], [1, 2]], np.int32)
+    lens = np.array([14, 13], np.int32)  # block 2: slots 0..5 (req 0), 0..4 (req 1)
+    kn = rng.integers(0, 2**16, size=(2, hkv, dq), dtype=np.uint16)
+    vn = rng.integers(0, 2**16, size=(2, hkv, dv), dtype=np.uint16)
+    cow = np.array([-1, 7], np.int32)
+    k2, v2, t2 = KV.append(k, v, tables, lens, kn, vn, bs, cow)
+    assert t2.tolist() == [[1, 2], [1, 7]]
+    K0, V0 = A.gather_kv(k, v, tables[0], 14, bs, dv, False)
+    Ka, Va = A.gather_kv(k2, v2, t2[0], 15, bs, dv, False)
+    Kb, Vb = A.gather_kv(k2, v2, t2[1], 14, bs, dv, False)
+    np.testing.assert_array_equal(Ka[:14], K0)
+    np.testing.assert_array_equal(Ka[14], A.widen_bf16(kn[0]))
+    np.testing.assert_array_equal(Kb[:13], K0[:13])
+    np.testing.assert_array_equal(Vb[:13], V0[:13])
+    np.testing.assert_array_equal(Kb[13], A.widen_bf16(kn[1]))
+    np.testing.assert_array_equal(Vb[13], A.widen_bf16(vn[1]))
+    np.testing.assert_array_equal(k2[7, :, :, 6:, :], k[7, :, :, 6:, :])
 
 
 def test_latent_cache_append_writes_the_whole_row():
