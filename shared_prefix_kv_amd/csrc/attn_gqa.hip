@@ -36,9 +36,14 @@
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: lane (g, c) reads d-chunk
 //     4*ks + g of token c (the chunked key layout makes this 1 KiB contiguous);
 //   * S^T lands with token 4*g + j in lane group g, register j, column c --
-//     exactly the B operand (P^T) of v_mfma_f32_16x16x16_bf16 once rounded;
-//   * O^T += V^T P^T: lane (g, c) reads tokens 4g..4g+3 at value dim
-//     16*dt + c, 8 contiguous bytes of the transposed value tile;
+//     the tokens of lane group g in the P^T operand;
+//   * O^T += V^T P^T with v_mfma_f32_16x16x32_bf16: lane (g, c) reads tokens
+//     4g..4g+3 at value dim 16*dt + c, 8 contiguous bytes of the transposed
+//     value tile, and feeds them twice, against the bf16 rounding of each
+//     probability and against the bf16 rounding of its remainder (p - hi).
+//     The 32-deep product thus applies p to about 16 bits at the issue cost
+//     of the 16-deep one it replaces, so the probabilities add no error of
+//     their own beyond that of fp32 accumulation;
 //   * online softmax per column in the log2 domain; the column max is reduced
 //     across the four lane groups with permlane swaps; accumulators are
 //     rescaled only when some column's max grew (a wave-uniform test).
@@ -358,7 +363,7 @@ __device__ __forceinline__ void stream_body(const CopyArgs& ca, const GqaParams&
 #pragma unroll
               for (int j = 0; j < 4; ++j) s[ct][j] = j < nvalid ? s[ct][j] : NEG_INF;
           }
-          bf16x4 pb[NCT];
+          bf16x8 pb[NCT];  // [bf16(p) of tokens 4g..4g+3, bf16(p - bf16(p)) of the same]
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
             if (ct == 1 && !two) break;
@@ -375,7 +380,9 @@ __device__ __forceinline__ void stream_body(const CopyArgs& ca, const GqaParams&
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float p = __builtin_amdgcn_exp2f(fmaf(s[ct][j], sc, -mrow[ct]));
-              pb[ct][j] = (__bf16)p;
+              const __bf16 hi = (__bf16)p;
+              pb[ct][j] = hi;
+              pb[ct][4 + j] = (__bf16)(p - (float)hi);
               lsum[ct] += p;
             }
           }
@@ -390,8 +397,10 @@ __device__ __forceinline__ void stream_body(const CopyArgs& ca, const GqaParams&
           for (int ct = 0; ct < NCT; ++ct) {
             if (ct == 1 && !two) break;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-              o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb[ct], o[ct][dt], 0, 0, 0);
+            for (int dt = 0; dt < 8; ++dt) {
+              const bf16x8 a = __builtin_shufflevector(va[dt], va[dt], 0, 1, 2, 3, 0, 1, 2, 3);
+              o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ct], o[ct][dt], 0, 0, 0);
+            }
           }
         }
       }

@@ -20,11 +20,16 @@
 //     for the whole item): S^T = K Q^T with v_mfma_f32_16x16x32_bf16, online
 //     softmax per row in the log2 domain with a lazy running max (raised
 //     only when a score exceeds it by more than 2^8, so rescales are rare),
-//     then P (bf16) and the rescale factors go to LDS;
+//     then P goes to LDS as two bf16 tiles, the rounding of each probability
+//     and the rounding of its remainder (p - hi), with the row's rescale
+//     factor carried in the low 4 mantissa bits of the remainders (8 of
+//     them per lane hold its 32 bits; the remainder keeps 3 bits, enough for
+//     p to about 12 bits where bf16 alone gives 8);
 //   * value waves 4-7, one stage behind, each owning 128 of the 512 value
 //     dims of all 64 rows: O^T += V^T P^T with v_mfma_f32_16x16x32_bf16, the
 //     V^T operand read from the key tile with ds_read_b64_tr_b16 (two 16-token
-//     tiles per operand) and the P^T operand as written by the score waves.
+//     tiles per operand) and the P^T operand as written by the score waves,
+//     once against each P tile.
 // Splitting the value dims keeps every wave under 256 registers, so each
 // SIMD runs a score wave and a value wave side by side, and the value tile
 // is read from LDS once per workgroup instead of once per 16 rows.
@@ -64,10 +69,10 @@ static_assert(kPvWaves * kDmaP * 1024 == kStageBytes, "stage copy split");
 constexpr float kTau = 8.f;                      // lazy-max threshold (log2 units)
 constexpr int kBufferWord3 = 0x00020000;         // raw buffer resource, gfx9 family
 
-constexpr int kOffP = kSlots * kStageBytes;      // P^T operands [2][4 col tiles][64 lanes] x 16 B
-constexpr int kPBytes = kQkWaves * 64 * 16;
-constexpr int kOffA = kOffP + 2 * kPBytes;       // rescale factors [2][16 lanes][4 col tiles]
-constexpr int kLdsBytes = kOffA + 2 * 256;
+constexpr int kOffP = kSlots * kStageBytes;      // P^T operands [2][hi, lo][4 col tiles][64 lanes] x 16 B
+constexpr int kPTile = kQkWaves * 64 * 16;
+constexpr int kPBytes = 2 * kPTile;
+constexpr int kLdsBytes = kOffP + 2 * kPBytes;   // 160 KiB, all of it
 
 __device__ __forceinline__ float xmax16(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -298,17 +303,27 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
           lsum *= alpha;
           mrow = mnew;
         }
-        bf16x8 pb;
+        bf16x8 pb, pl;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[j], sc, -mrow));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[j], sc, -mrow));
           lsum += p0 + p1;
-          pb[j] = (__bf16)p0;
-          pb[4 + j] = (__bf16)p1;
+          const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+          pb[j] = h0;
+          pb[4 + j] = h1;
+          pl[j] = (__bf16)(p0 - (float)h0);
+          pl[4 + j] = (__bf16)(p1 - (float)h1);
         }
-        *reinterpret_cast<bf16x8*>(lds + kOffP + buf * kPBytes + (w * 64 + lane) * 16) = pb;
-        if (g == 0) reinterpret_cast<float*>(lds + kOffA + buf * 256)[c16 * 4 + w] = alpha;
+        // The rescale factor of row c16 rides in the low mantissa nibbles
+        // of the remainders: bits 4i..4i+3 and 16+4i..16+4i+3 in word i.
+        u32x4 lw = __builtin_bit_cast(u32x4, pl);
+        const uint32_t ab = __float_as_uint(alpha);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lw[i] = (lw[i] & 0xFFF0FFF0u) | ((ab >> (4 * i)) & 0x000F000Fu);
+        char* pt = lds + kOffP + buf * kPBytes + (w * 64 + lane) * 16;
+        *reinterpret_cast<bf16x8*>(pt) = pb;
+        *reinterpret_cast<u32x4*>(pt + kPTile) = lw;
       }
       if (++cs == cns) {
         if (active) {
@@ -358,10 +373,13 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
       const int buf = (t - 1) & 1;
       const int ccols = it.col1 - it.col0;
       const int nct = (ccols + 15) >> 4;
-      bf16x8 pb[4];
+      bf16x8 pb[4], pl[4];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        pb[ct] = *reinterpret_cast<const bf16x8*>(lds + kOffP + buf * kPBytes + (ct * 64 + lane) * 16);
+      for (int ct = 0; ct < 4; ++ct) {
+        const char* pt = lds + kOffP + buf * kPBytes + (ct * 64 + lane) * 16;
+        pb[ct] = *reinterpret_cast<const bf16x8*>(pt);
+        pl[ct] = *reinterpret_cast<const bf16x8*>(pt + kPTile);
+      }
       const char* kt = lds + ((t - 1) % kSlots) * kStageBytes + (2 * v * kPvTiles) * kChunk + tr_off;
       u32x2 vr[kPvTiles][2];
       read_vt(kt, vr);
@@ -388,11 +406,21 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
         for (int dt = 0; dt < kPvTiles; ++dt) {
           const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{vr[dt][0][0], vr[dt][0][1], vr[dt][1][0], vr[dt][1][1]});
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
+          for (int ct = 0; ct < 4; ++ct) {
             o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ct], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[ct], o[ct][dt], 0, 0, 0);
+          }
         }
       } else {
-        const f32x4 al = *reinterpret_cast<const f32x4*>(lds + kOffA + buf * 256 + c16 * 16);
+        f32x4 al;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const u32x4 lw = __builtin_bit_cast(u32x4, pl[ct]);
+          uint32_t ab = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ab |= (lw[i] & 0x000F000Fu) << (4 * i);
+          al[ct] = __uint_as_float(ab);
+        }
         bool scale = false;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) scale |= ct < nct && al[ct] != 1.f;
@@ -408,8 +436,10 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
         for (int dt = 0; dt < kPvTiles; ++dt) {
           const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{vr[dt][0][0], vr[dt][0][1], vr[dt][1][0], vr[dt][1][1]});
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
+          for (int ct = 0; ct < 4; ++ct) {
             o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ct], o[ct][dt], 0, 0, 0);
+            o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[ct], o[ct][dt], 0, 0, 0);
+          }
         }
       }
       __builtin_amdgcn_s_setprio(0);

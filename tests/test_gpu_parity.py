@@ -403,6 +403,34 @@ def test_decode_edge_lengths_and_ratios(hq, hkv):
     say("edge", hq, hkv, "groups", p.info.num_groups)
 
 
+@pytest.mark.parametrize("kind", ["gqa", "mla"])
+def test_decode_short_requests_precision(kind):
+    """Requests of 2 to 9 tokens: the output is a weighted mean of a few
+    value rows, so rounding the probabilities alone (bf16 keeps 8 bits)
+    would leave errors above the tolerance wherever the rows cancel; the
+    kernels apply each probability to about 16 bits (12 in the latent
+    kernel) and must stay within it on every element."""
+    if kind == "gqa":
+        shape = AttnShape(32, 8, 128, 128, 16, 1 / math.sqrt(128))
+    else:
+        shape = AttnShape(16, 1, 576, 512, 64, 1 / math.sqrt(576), v_aliases_k=True)
+    B, W, nb = 96, 1, 128
+    rng = np.random.default_rng(77)
+    lens = rng.integers(2, 10, size=B).astype(np.int32)
+    tables = rng.permutation(nb)[:B].reshape(B, W).astype(np.int32)
+    tables[1::4] = tables[0::4]  # pairs that share their only (partial) block
+    lens[1::4] = lens[0::4]
+    case = small_case(shape, tables, lens, nb, seed=78)
+    ref, ref_lse = A.attend(case["q"], case["k"], case["v"], tables, lens, shape)
+    vals = upload(case)
+    for cascade in (True, False):
+        say("short requests", kind, "cascade", cascade)
+        _, out, lse = run_decode(_B(shape, tables, lens, nb), vals, cascade=cascade)
+        rep = assert_close(bf16_tensor_to_f64(out), ref, f"short requests {kind} cascade={cascade}")
+        assert_lse_close(lse.cpu().numpy(), ref_lse, "short requests")
+        say("short", kind, rep)
+
+
 def test_decode_empty_batch_and_all_empty():
     shape = AttnShape(8, 2, 128, 128, 16, 0.1)
     desc = fca.desc_from_shape(shape, 8)
