@@ -337,6 +337,69 @@ fca_status fca_merge_states(int32_t n_states, const float* const* outs, const fl
                             void* stream);
 
 /*
+ * Append one decode token per request to the paged cache, copying a shared
+ * block first when asked (copy-on-write).  A paged cache grows by filling
+ * fixed-size blocks that the block table lists; requests forked from one
+ * prompt reference the same physical blocks, and the one that writes into a
+ * shared block is given its own copy so the others keep the old contents
+ * (PagedAttention vs. RadixAttention page, "How PagedAttention Works",
+ * steps 3 and 4).  Run before fca_plan_create / fca_decode of the step that
+ * reads the new token; then the plan keeps the invariant it relies on, that
+ * a block two requests share holds the same tokens for both.
+ *
+ * For request i with L = seq_lens_dev[i] cached tokens, let
+ * j = L / block_size and t = L % block_size:
+ *   - if cow_dst_dev is not NULL and c = cow_dst_dev[i] >= 0 (and c differs
+ *     from block_tables_dev[i][j]), the request's tokens of block
+ *     block_tables_dev[i][j] (slots 0 .. t-1, every KV head, keys and
+ *     values) are copied to block c and block_tables_dev[i][j] is set to c;
+ *     slots after t of block c keep what they held (in the source they may
+ *     be a longer sharer's tokens);
+ *   - the new key (and value) is written at slot t of block
+ *     block_tables_dev[i][j], in the cache layout fca_decode reads
+ *     (desc's strides).
+ * seq_lens are not changed: the caller's next plan uses L + 1.  The caller
+ * fills block_tables_dev[i][j] with a fresh block when L is a multiple of
+ * block_size (a new block starts).
+ *
+ *   desc          as for fca_plan_create (shape, strides, num_blocks; flags
+ *                 are checked but unused).
+ *   k_new_dev     bf16 [batch][num_kv_heads][head_dim_qk], contiguous.
+ *   v_new_dev     bf16 [batch][num_kv_heads][head_dim_v]; ignored (may be
+ *                 NULL) when desc->v_aliases_k.
+ *   k_cache_dev, v_cache_dev  the pools (v ignored when v_aliases_k); 16-byte
+ *                 aligned.
+ *   block_tables_dev int32, row i at block_tables_dev + i * bt_row_stride,
+ *                 max_blocks entries used; entry j of a copied request is
+ *                 rewritten.
+ *   seq_lens_dev  int32 [batch].
+ *   cow_dst_dev   int32 [batch] or NULL; negative = no copy.
+ *   status_dev    int32 or NULL.  A request whose L is outside
+ *                 [0, max_blocks * block_size), whose block entry is outside
+ *                 [0, num_blocks), or whose cow target is >= num_blocks is
+ *                 skipped and ORs FCA_APPEND_BAD_LEN / _BAD_BLOCK / _BAD_COW
+ *                 into *status_dev; the caller zeroes it beforehand and reads
+ *                 it when it wants to know.
+ *
+ * A request may write in place only into a slot no other request holds a
+ * token in: of the requests sharing a partly filled last block, at most one
+ * of those with the most tokens in it goes without a cow target.  Cow
+ * targets must differ from each other and from every block a request of the
+ * call reads; overlapping calls race.  Returns
+ * FCA_ERR_INVALID_ARG for NULL or misaligned pointers, batch outside
+ * [0, 8192], max_blocks outside [1, 2^20] or bt_row_stride < max_blocks;
+ * FCA_ERR_UNSUPPORTED as fca_plan_create; FCA_ERR_HIP if the launch fails.
+ * Asynchronous on `stream`.
+ */
+#define FCA_APPEND_BAD_LEN 1
+#define FCA_APPEND_BAD_BLOCK 2
+#define FCA_APPEND_BAD_COW 4
+fca_status fca_kv_append(const fca_attn_desc* desc, const void* k_new_dev, const void* v_new_dev, void* k_cache_dev,
+                         void* v_cache_dev, int32_t* block_tables_dev, int64_t bt_row_stride, int32_t max_blocks,
+                         const int32_t* seq_lens_dev, const int32_t* cow_dst_dev, int32_t* status_dev, int32_t batch,
+                         void* stream);
+
+/*
  * Frees the plan without waiting for the device.  Its device schedule is
  * kept by the library (a few buffers per process) and reused by a later plan
  * once the stream the plan was created with has passed the point of this

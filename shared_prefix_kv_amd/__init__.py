@@ -32,6 +32,9 @@ FCA_PLAN_SEPARATE_PASSES = 2
 FCA_PLAN_OUT_F32 = 4
 FCA_PLAN_AUTO_FOLD = 8
 FCA_MERGE_OUT_F32 = 1
+FCA_APPEND_BAD_LEN = 1
+FCA_APPEND_BAD_BLOCK = 2
+FCA_APPEND_BAD_COW = 4
 
 EXPORTED = [
     "fca_plan_workspace_size",
@@ -45,6 +48,7 @@ EXPORTED = [
     "fca_profile_read",
     "fca_time_launches",
     "fca_merge_states",
+    "fca_kv_append",
     "fca_plan_destroy",
     "fca_last_error",
     "fca_version",
@@ -155,6 +159,7 @@ def lib():
         L.fca_profile_read.argtypes = [vp, ctypes.POINTER(Profile)]
         L.fca_time_launches.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp, ctypes.POINTER(Profile)]
         L.fca_merge_states.argtypes = [i32, vp, vp, i32, i32, i32, vp, vp, ctypes.c_uint32, vp]
+        L.fca_kv_append.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, i64, i32, vp, vp, vp, i32, vp]
         L.fca_plan_destroy.argtypes = [vp]
         L.fca_plan_destroy.restype = None
         L.fca_last_error.restype = ctypes.c_char_p
@@ -465,6 +470,48 @@ def merge_states(outs, lses, out=None, lse=None, out_f32=False, stream=None):
         )
     )
     return out
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, block_tables, seq_lens, desc: AttnDesc, cow_dst=None, status=None,
+              stream=None):
+    """Write one decode token per request into the paged cache, copying a
+    shared last block first where ``cow_dst[i] >= 0`` (fca_kv_append).
+    ``k_new`` bf16 [B, Hkv, Dqk], ``v_new`` bf16 [B, Hkv, Dv] (None for a
+    latent cache), ``block_tables`` int32 [B, W] (updated in place for copied
+    requests), ``seq_lens`` int32 [B] (the position of the new token),
+    ``cow_dst`` int32 [B] or None, ``status`` int32 [1] or None (bits
+    FCA_APPEND_BAD_*, ORed in)."""
+    import torch
+
+    assert block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.stride(1) == 1
+    B, W = block_tables.shape
+    assert seq_lens.dtype == torch.int32 and seq_lens.is_contiguous() and tuple(seq_lens.shape) == (B,)
+    assert k_new.dtype == torch.bfloat16 and k_new.is_contiguous()
+    assert tuple(k_new.shape) == (B, desc.num_kv_heads, desc.head_dim_qk)
+    if not desc.v_aliases_k:
+        assert v_new.dtype == torch.bfloat16 and v_new.is_contiguous()
+        assert tuple(v_new.shape) == (B, desc.num_kv_heads, desc.head_dim_v)
+    if cow_dst is not None:
+        assert cow_dst.dtype == torch.int32 and cow_dst.is_contiguous() and tuple(cow_dst.shape) == (B,)
+    if status is not None:
+        assert status.dtype == torch.int32 and status.numel() >= 1
+    _check(
+        lib().fca_kv_append(
+            ctypes.byref(desc),
+            _ptr(k_new),
+            _ptr(None if desc.v_aliases_k else v_new),
+            _ptr(k_cache),
+            _ptr(None if desc.v_aliases_k else v_cache),
+            _ptr(block_tables),
+            block_tables.stride(0),
+            W,
+            _ptr(seq_lens),
+            _ptr(cow_dst),
+            _ptr(status),
+            B,
+            _stream_ptr(stream),
+        )
+    )
 
 
 def version() -> str:

@@ -1195,6 +1195,47 @@ fca_status fca_merge_states(int32_t n_states, const float* const* outs, const fl
   return FCA_OK;
 }
 
+fca_status fca_kv_append(const fca_attn_desc* desc, const void* k_new_dev, const void* v_new_dev, void* k_cache_dev,
+                         void* v_cache_dev, int32_t* block_tables_dev, int64_t bt_row_stride, int32_t max_blocks,
+                         const int32_t* seq_lens_dev, const int32_t* cow_dst_dev, int32_t* status_dev, int32_t batch,
+                         void* stream) {
+  Kind kind;
+  fca_status st = check_desc(desc, &kind);
+  if (st != FCA_OK) return st;
+  if (batch < 0 || batch > kMaxBatch) return fail(FCA_ERR_INVALID_ARG, "batch %d outside [0, %d]", batch, kMaxBatch);
+  if (max_blocks < 1 || max_blocks > kMaxTableWidth)
+    return fail(FCA_ERR_INVALID_ARG, "max_blocks %d outside [1, %d]", max_blocks, kMaxTableWidth);
+  if (bt_row_stride < max_blocks) return fail(FCA_ERR_INVALID_ARG, "bt_row_stride < max_blocks");
+  if (batch == 0) return FCA_OK;
+  const bool alias = desc->v_aliases_k != 0;
+  if (!k_new_dev || !k_cache_dev || !block_tables_dev || !seq_lens_dev || (!alias && (!v_new_dev || !v_cache_dev)))
+    return fail(FCA_ERR_INVALID_ARG, "k_new / v_new / caches / block_tables / seq_lens is NULL");
+  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
+  if (misaligned(k_new_dev) || misaligned(k_cache_dev) || (!alias && (misaligned(v_new_dev) || misaligned(v_cache_dev))))
+    return fail(FCA_ERR_INVALID_ARG, "new rows and caches must be 16-byte aligned");
+  AppendParams p;
+  p.k_new = static_cast<const uint16_t*>(k_new_dev);
+  p.v_new = alias ? nullptr : static_cast<const uint16_t*>(v_new_dev);
+  p.k_cache = static_cast<uint16_t*>(k_cache_dev);
+  p.v_cache = alias ? nullptr : static_cast<uint16_t*>(v_cache_dev);
+  p.block_tables = block_tables_dev;
+  p.bt_row_stride = bt_row_stride;
+  p.seq_lens = seq_lens_dev;
+  p.cow_dst = cow_dst_dev;
+  p.status = status_dev;
+  p.k_stride_block = desc->k_stride_block;
+  p.k_stride_head = desc->k_stride_head;
+  p.v_stride_block = alias ? 0 : desc->v_stride_block;
+  p.v_stride_head = alias ? 0 : desc->v_stride_head;
+  p.batch = batch;
+  p.num_kv_heads = desc->num_kv_heads;
+  p.max_blocks = max_blocks;
+  p.num_blocks = desc->num_blocks;
+  const hipError_t e = launch_append(p, kind == kMla, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return FCA_OK;
+}
+
 fca_status fca_profile_enable(fca_plan plan, int32_t enable) {
   if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
   plan->profiling = enable != 0;

@@ -174,4 +174,21 @@ struct StatesParams {
 
 hipError_t launch_merge_states(const StatesParams& p, hipStream_t s);
 
+// Decode-token append (kv_append.hip).  Element strides as fca_attn_desc.
+struct AppendParams {
+  const uint16_t* k_new;  // [batch][num_kv_heads][head_dim_qk] bf16
+  const uint16_t* v_new;  // [batch][num_kv_heads][head_dim_v] bf16 (unused for latent caches)
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int32_t* block_tables;
+  int64_t bt_row_stride;
+  const int32_t* seq_lens;
+  const int32_t* cow_dst;  // may be null
+  int32_t* status;         // may be null
+  int64_t k_stride_block, k_stride_head, v_stride_block, v_stride_head;
+  int32_t batch, num_kv_heads, max_blocks, num_blocks;
+};
+
+hipError_t launch_append(const AppendParams& p, bool latent, hipStream_t s);
+
 }  // namespace fca

@@ -129,6 +129,30 @@ def test_merge_states_validation_before_device():
     L.fca_plan_destroy(None)  # no-op
 
 
+def test_kv_append_validation_before_device():
+    """fca_kv_append rejects bad arguments without touching the device; an
+    empty batch launches nothing."""
+    L = fca.lib()
+    d = fca.make_desc(32, 8, 128, 128, 16, 64, 0.088)
+    dp = ctypes.byref(d)
+    odd = ctypes.c_void_p(0x1008)  # not 16-byte aligned
+    ok = ctypes.c_void_p(0x1000)
+    assert L.fca_kv_append(None, ok, ok, ok, ok, ok, 4, 4, ok, None, None, 2, None) == 1  # no desc
+    assert L.fca_kv_append(dp, ok, ok, ok, ok, ok, 4, 4, ok, None, None, -1, None) == 1  # negative batch
+    assert L.fca_kv_append(dp, ok, ok, ok, ok, ok, 4, 4, ok, None, None, 8193, None) == 1  # batch too large
+    assert L.fca_kv_append(dp, ok, ok, ok, ok, ok, 4, 0, ok, None, None, 2, None) == 1  # no table width
+    assert L.fca_kv_append(dp, ok, ok, ok, ok, ok, 3, 4, ok, None, None, 2, None) == 1  # rows overlap
+    assert L.fca_kv_append(dp, ok, None, ok, ok, ok, 4, 4, ok, None, None, 2, None) == 1  # no v_new
+    assert L.fca_kv_append(dp, ok, ok, ok, ok, None, 4, 4, ok, None, None, 2, None) == 1  # no table
+    assert L.fca_kv_append(dp, odd, ok, ok, ok, ok, 4, 4, ok, None, None, 2, None) == 1  # misaligned row
+    assert L.fca_kv_append(dp, ok, ok, ok, odd, ok, 4, 4, ok, None, None, 2, None) == 1  # misaligned pool
+    assert L.fca_kv_append(dp, ok, ok, ok, ok, ok, 4, 4, ok, None, None, 0, None) == 0  # nothing to do
+    bad = fca.make_desc(32, 8, 64, 64, 16, 64, 0.088)
+    assert L.fca_kv_append(ctypes.byref(bad), ok, ok, ok, ok, ok, 4, 4, ok, None, None, 2, None) == 2  # shape
+    mla = fca.make_desc(128, 1, 576, 512, 64, 64, 0.07, v_aliases_k=True)
+    assert L.fca_kv_append(ctypes.byref(mla), ok, None, ok, None, ok, 4, 4, ok, None, None, 0, None) == 0
+
+
 def test_struct_layouts_match_header(tmp_path):
     """ctypes mirrors have the sizes and field offsets a C compiler gives the header."""
     import shutil
