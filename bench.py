@@ -180,6 +180,50 @@ def cpu_baseline(batch, vals, budget_s, threads, cache=None):
     )
 
 
+def kv_append_leg(batch, pool, torch, fca):
+    sh = batch.shape
+    B = batch.batch
+    k, v = pool
+    desc = fca.desc_from_shape(sh, batch.num_blocks)
+    bt = torch.from_numpy(batch.block_tables).cuda()
+    pos = torch.from_numpy(np.maximum(batch.seq_lens - 1, 0).astype(np.int32)).cuda()
+    kn = torch.randn((B, sh.num_kv_heads, sh.head_dim_qk), device="cuda").to(torch.bfloat16)
+    vn = None if sh.v_aliases_k else torch.randn((B, sh.num_kv_heads, sh.head_dim_v), device="cuda").to(torch.bfloat16)
+    free = np.nonzero(~batch.used_blocks)[0].astype(np.int32)
+    res = {}
+    legs = [("in_place_us", None)]
+    if len(free) >= 2 * B:
+        legs.append(("copy_on_write_us", (torch.from_numpy(free[:B]).cuda(), torch.from_numpy(free[B : 2 * B]).cuda())))
+    per_graph, reps = 20, 10
+    for name, cows in legs:
+        def call(j):
+            fca.kv_append(kn, vn, k, v, bt, pos, desc, cow_dst=None if cows is None else cows[j % 2])
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(0)
+            call(1)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(per_graph):
+                call(j)
+        for _ in range(3):
+            g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) * 1000 / (reps * per_graph), 2)
+        del g
+    return res
+
+
 def group_sweep(torch, fca, steps, warmup):
     """Cascade vs non-cascade over the group size: 64 requests of the
     Llama-3-8B layer shape, prefix 4096, suffix U{256..1024}, as 64 / s
@@ -569,6 +613,15 @@ def main():
         result["merge_states"] = {"states": 2, "us": round(ms_m * 1000, 2), "GBps": gbps(mbytes, ms_m), "bytes": mbytes}
         log(f"merge of two float32 states: {ms_m * 1000:.1f} us ({gbps(mbytes, ms_m)} GB/s)")
         del st_o, st_l, mo, ml
+
+    if not args.profile_only:
+        # The step before the path: one new token per request appended to the
+        # last KV pool (over each request's last cached token, so the pools
+        # keep their shape), in place and with a copy-on-write of every
+        # request's last block (targets alternating between two sets of
+        # unused blocks, so every call copies).  20 calls per HIP graph.
+        result["kv_append"] = kv_append_leg(batch, pools[-1], torch, fca)
+        log(f"kv append ({batch.batch} requests): {result['kv_append']}")
 
     if args.group_sweep and not args.profile_only:
         result["group_sweep"] = group_sweep(torch, fca, steps, warmup)
