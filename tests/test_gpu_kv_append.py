@@ -203,3 +203,60 @@ def test_append_skips_bad_requests_and_flags_them():
     exp_t[good] = t2
     assert (bt.cpu().numpy() == exp_t).all()
     assert (to_bits(kd) == k2).all() and (to_bits(vd) == v2).all()
+
+
+def test_append_graph_replays_match_eager_and_edge_targets():
+    """Appends captured in a HIP graph (four replays, eager work and
+    synchronisation between them) leave the same pools and tables as eager
+    calls; a copy target equal to the request's own block, and a request
+    whose new token starts a block, are written in place."""
+    shape = GQA
+    bs, W, nb = shape.block_size, 6, 96
+    rng = np.random.default_rng(21)
+    k = f32_to_bf16_bits(rng.standard_normal((nb, 8, 16, bs, 8), dtype=np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((nb, 8, 128, bs), dtype=np.float32))
+    B = 8
+    tables = rng.permutation(B * W).reshape(B, W).astype(np.int32)  # blocks 48.. unused
+    lens = np.array([5, 16, 37, 0, 50, 9, 31, 80], np.int32)
+    cow = np.array([60, -1, 61, -1, tables[4, 50 // bs], 62, -1, 63], np.int32)  # request 4: own block
+    desc = fca.desc_from_shape(shape, nb)
+    kn_all = [new_rows(rng, shape, B) for _ in range(4)]
+
+    def run(graph):
+        kd, vd = to_device_bf16(k), to_device_bf16(v)
+        bt = torch.from_numpy(tables).cuda()
+        knd = to_device_bf16(kn_all[0][0])
+        vnd = to_device_bf16(kn_all[0][1])
+        sl = torch.from_numpy(lens).cuda()
+        cw = torch.from_numpy(cow).cuda()
+        snaps = []
+        if graph:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    fca.kv_append(knd, vnd, kd, vd, bt, sl, desc, cow_dst=cw, stream=side)
+            torch.cuda.current_stream().wait_stream(side)
+        for r in range(4):
+            knd.copy_(to_device_bf16(kn_all[r][0]))
+            vnd.copy_(to_device_bf16(kn_all[r][1]))
+            if graph:
+                g.replay()
+            else:
+                fca.kv_append(knd, vnd, kd, vd, bt, sl, desc, cow_dst=cw)
+            torch.cuda.synchronize()
+            snaps.append((to_bits(kd), to_bits(vd), bt.cpu().numpy().copy()))
+            sl.add_(1)  # eager work between replays: the next token
+        return snaps
+
+    say("append graph vs eager")
+    eager, graphed = run(False), run(True)
+    kk, vv, tt = k, v, tables
+    ln = lens.copy()
+    for r in range(4):
+        kk, vv, tt = KV.append(kk, vv, tt, ln, kn_all[r][0], kn_all[r][1], bs, cow)
+        ln = ln + 1
+        for snap in (eager[r], graphed[r]):
+            assert (snap[0] == kk).all() and (snap[1] == vv).all() and (snap[2] == tt).all(), f"replay {r}"
+    assert tt[4, 50 // bs] == tables[4, 50 // bs]
