@@ -67,7 +67,6 @@ Tuning tuning() {
 }
 
 constexpr int kXcds = 8;  // accelerator dies per device; workgroup b is dispatched to die b mod 8
-constexpr int kItemColsGqa = 64;   // query rows of one GQA work item at most
 constexpr int kItemColsMla = 64;   // query rows of one latent-cache work item at most
 constexpr int kItemWaves = kAttnWaves;  // waves per work item: heads x column groups x block stripes
 constexpr int kWaveCols = 32;  // query rows one wave covers at most

@@ -73,6 +73,7 @@ constexpr int kSlotBytes = 2 * kTileBytes;
 constexpr int kTileOps = 2 * kTileBytes / 1024;  // vector-memory instructions per tile copy
 constexpr int kQRowBytes = kD * 2;
 constexpr int kWaveCols = 32;             // query rows one wave covers at most
+constexpr int kCachePolicyNT = 2;         // cache-policy bits of a load: non-temporal
 
 // x op x' where x' is the value of lane ^ 16 (resp. ^ 32).
 __device__ __forceinline__ float xmax16(float x) {
@@ -263,12 +264,28 @@ __device__ __forceinline__ void stream_body(const CopyArgs& ca, const GqaParams&
       const int hd = dit.kv_head + dr.hh;
       const char* ksrc = ca.k + ((int64_t)cur_id * ca.ksb + (int64_t)hd * ca.ksh) * 2 + lane * 16;
       const char* vsrc = ca.v + ((int64_t)cur_id * ca.vsb + (int64_t)hd * ca.vsh) * 2 + lane * 16;
+      // A tile that exactly one wave reads streams through the caches with
+      // the non-temporal policy: every suffix tile, and the tiles of a group
+      // whose query rows fit one wave.  A group with more rows has two
+      // column-group waves per item loading each tile (and more items when
+      // it has more than one column chunk); the second load should find the
+      // tile in L2, which the non-temporal policy would have given up.
+      if (dit.member_off < 0 || dit.ncols <= kWaveCols) {
 #pragma unroll
-      for (int i = 0; i < kTileBytes / 1024; ++i)
-        __builtin_amdgcn_global_load_lds(ksrc + i * 1024, (lds_void*)(dst + i * 1024), 16, 0, 0);
+        for (int i = 0; i < kTileBytes / 1024; ++i)
+          __builtin_amdgcn_global_load_lds(ksrc + i * 1024, (lds_void*)(dst + i * 1024), 16, 0, kCachePolicyNT);
 #pragma unroll
-      for (int i = 0; i < kTileBytes / 1024; ++i)
-        __builtin_amdgcn_global_load_lds(vsrc + i * 1024, (lds_void*)(dst + kTileBytes + i * 1024), 16, 0, 0);
+        for (int i = 0; i < kTileBytes / 1024; ++i)
+          __builtin_amdgcn_global_load_lds(vsrc + i * 1024, (lds_void*)(dst + kTileBytes + i * 1024), 16, 0,
+                                           kCachePolicyNT);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kTileBytes / 1024; ++i)
+          __builtin_amdgcn_global_load_lds(ksrc + i * 1024, (lds_void*)(dst + i * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kTileBytes / 1024; ++i)
+          __builtin_amdgcn_global_load_lds(vsrc + i * 1024, (lds_void*)(dst + kTileBytes + i * 1024), 16, 0, 0);
+      }
       last_ops = kTileOps;
       if (++dk == dr.nblk)
         copy_next_item();

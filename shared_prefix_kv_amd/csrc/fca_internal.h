@@ -14,6 +14,7 @@ constexpr int kMaxBatch = 8192;
 constexpr int kMaxTableWidth = 1 << 20;
 constexpr int kAttnLgWaves = 2;                 // log2 of the waves of an attention workgroup
 constexpr int kAttnWaves = 1 << kAttnLgWaves;   // waves that share one work item
+constexpr int kItemColsGqa = 64;                // query rows of one GQA work item at most
 
 // A unit of work of the grouped or per-request pass; same layout as the
 // public fca_work_item.
