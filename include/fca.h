@@ -241,7 +241,10 @@ typedef struct fca_work_item {
   int32_t stripes;    /* block stripes S: stripe t takes blocks t, t+S, ... of
                          the range and writes rows part_base + t*kv_heads*
                          (col1 - col0) + (as above) */
-  int32_t reserved;
+  int32_t flags;      /* bit 0: every tile of the item has exactly one reader
+                         (a suffix of a cascade plan, or a group whose query
+                         rows fit one wave), so the GQA kernel loads it with
+                         the non-temporal cache policy */
 } fca_work_item;
 
 /*

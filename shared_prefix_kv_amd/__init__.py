@@ -120,7 +120,7 @@ class WorkItem(ctypes.Structure):
         ("part_base", ctypes.c_int32),
         ("kv_heads", ctypes.c_int32),
         ("stripes", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -426,7 +426,7 @@ class Plan:
         _check(lib().fca_plan_export_schedule(self._h, gi, si, off, src))
 
         def items(arr, n):
-            names = [f[0] for f in WorkItem._fields_ if f[0] != "reserved"]
+            names = [f[0] for f in WorkItem._fields_]
             return [{k: getattr(arr[j], k) for k in names} for j in range(n)]
 
         sources = [[list(src[off[i * hq + h] : off[i * hq + h + 1]]) for h in range(hq)] for i in range(B)]

@@ -546,14 +546,15 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   struct Lane {
     int request, member_off, ncols, tok0, tok_end;
     int kv0, H, col0, col1;
-    int S;  // block stripes
+    int S;       // block stripes
+    int stream;  // kItemStream when every tile of the lane has one reader
     int64_t stages;
     int64_t base;
     int splits;
   };
   // Appends the lanes of one unit; returns the index of its first lane.
   auto add_lanes = [&](std::vector<Lane>& lanes, int tok0, int tok_end, int request, int member_off,
-                       int ncols, int* H_out, int* chunks_out) {
+                       int ncols, bool one_reader, int* H_out, int* chunks_out) {
     const int first = (int)lanes.size();
     const int icols = P->item_cols;
     const int cmax = std::min(ncols, icols) > kWaveCols ? 2 : 1;
@@ -567,7 +568,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
         const int col0 = c * icols, col1 = std::min(ncols, (c + 1) * icols);
         const int S = mla ? 1 : kItemWaves / (H * (col1 - col0 > kWaveCols ? 2 : 1));
         lanes.push_back(Lane{request, member_off, ncols, tok0, tok_end, hb * H, H, col0, col1, S,
-                             ceil_div(nblk, S), 0, 0});
+                             one_reader ? kItemStream : 0, ceil_div(nblk, S), 0, 0});
       }
     *H_out = H;
     *chunks_out = chunks;
@@ -609,6 +610,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
         it.col1 = L.col1;
         it.part_base = L.splits++;
         it.stripes = L.S;
+        it.flags = L.stream;
         P->items.push_back(it);
         item_lane.push_back((int)li);
         pos += take;
@@ -734,6 +736,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
         it.col1 = L.col1;
         it.part_base = L.splits++;
         it.stripes = L.S;
+        it.flags = L.stream;
         P->items.push_back(it);
         item_lane.push_back(e.first);
       }
@@ -754,8 +757,10 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
     gm.H = 1;
     gm.chunks = 0;
     if (P->folded[c]) continue;  // read per request: no grouped work, on no merge path
+    // The group's tiles have one reader when its query rows fit one wave
+    // (one column chunk, one column group).
     gm.lane0 = add_lanes(all, gr.block_begin * bs, gr.block_end * bs, P->perm[r0[c]], r0[c], count[c] * r,
-                         &gm.H, &gm.chunks);
+                         count[c] * r <= kWaveCols, &gm.H, &gm.chunks);
     unique += (int64_t)(gr.block_end - gr.block_begin) * bs;
   }
   const size_t n_glanes = all.size();
@@ -767,8 +772,12 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
     rq.sfx_lane = -1;
     rq.sfx_H = 1;
     rq.sfx_chunks = 1;
+    // A suffix has one reader in a cascade plan unless it took in a folded
+    // group's blocks; without the cascade, shared prefixes are in every
+    // member's suffix.
+    const bool one_reader = !(P->desc.flags & FCA_PLAN_DISABLE_CASCADE) && eff_sb[i] == sfxb[i];
     if (sfx_tokens[i] > 0)
-      rq.sfx_lane = add_lanes(all, P->req3[3 * i] * bs, lens[i], i, -1, r, &rq.sfx_H, &rq.sfx_chunks);
+      rq.sfx_lane = add_lanes(all, P->req3[3 * i] * bs, lens[i], i, -1, r, one_reader, &rq.sfx_H, &rq.sfx_chunks);
   }
   auto schedule = [&](size_t l0, size_t l1, PassSet passes) {
     if (mla)

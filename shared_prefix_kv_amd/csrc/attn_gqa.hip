@@ -129,7 +129,8 @@ __device__ __forceinline__ WorkItem load_item(cint32* items, int i) {
   w.col1 = p[7];
   w.part_base = p[8];
   w.kv_heads = p[9];
-  w.stripes = w.pad2 = 0;
+  w.stripes = 0;
+  w.flags = p[11];
   return w;
 }
 
@@ -264,13 +265,14 @@ __device__ __forceinline__ void stream_body(const CopyArgs& ca, const GqaParams&
       const int hd = dit.kv_head + dr.hh;
       const char* ksrc = ca.k + ((int64_t)cur_id * ca.ksb + (int64_t)hd * ca.ksh) * 2 + lane * 16;
       const char* vsrc = ca.v + ((int64_t)cur_id * ca.vsb + (int64_t)hd * ca.vsh) * 2 + lane * 16;
-      // A tile that exactly one wave reads streams through the caches with
-      // the non-temporal policy: every suffix tile, and the tiles of a group
-      // whose query rows fit one wave.  A group with more rows has two
-      // column-group waves per item loading each tile (and more items when
-      // it has more than one column chunk); the second load should find the
-      // tile in L2, which the non-temporal policy would have given up.
-      if (dit.member_off < 0 || dit.ncols <= kWaveCols) {
+      // A tile that exactly one wave reads (the planner's kItemStream: a
+      // suffix of a cascade plan, or a group whose query rows fit one wave)
+      // streams through the caches with the non-temporal policy.  Other
+      // tiles are loaded by two column-group waves of an item, by several
+      // column chunks, or by several requests (shared blocks in suffixes of
+      // plans without the cascade or with folded groups); their later loads
+      // should find them in L2, which the non-temporal policy gives up.
+      if (dit.flags & kItemStream) {
 #pragma unroll
         for (int i = 0; i < kTileBytes / 1024; ++i)
           __builtin_amdgcn_global_load_lds(ksrc + i * 1024, (lds_void*)(dst + i * 1024), 16, 0, kCachePolicyNT);

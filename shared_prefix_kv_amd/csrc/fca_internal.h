@@ -30,8 +30,9 @@ struct WorkItem {
   int32_t part_base;
   int32_t kv_heads;  // KV heads the item covers: kv_head .. kv_head + kv_heads - 1
   int32_t stripes;   // block stripes (the kernel derives them; exported for tests)
-  int32_t pad2;
+  int32_t flags;     // kItemStream: tiles with one reader (non-temporal loads)
 };
+constexpr int32_t kItemStream = 1;
 static_assert(sizeof(WorkItem) == sizeof(fca_work_item), "work item layout");
 
 // Per-request data the merge reads.

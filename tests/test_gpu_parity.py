@@ -852,3 +852,34 @@ def test_auto_fold_plan_schedule_and_decode(case):
         rep = assert_close(bf16_tensor_to_f64(out), ref, f"auto fold {case}")
         assert_lse_close(lse.cpu().numpy(), ref_lse, f"auto fold {case}")
         say("auto fold", case, "folded", sum(folded), "of", len(folded), rep)
+
+
+@pytest.mark.parametrize("case", ["tiny", "llama3_8b", "long_rl", "fold"])
+def test_streaming_flags_mark_single_reader_tiles(case):
+    """Work items carry kItemStream (non-temporal tile loads) exactly when
+    each of their tiles has one reader: a suffix of a cascade plan of a
+    request in no folded group, or a group whose query rows fit one wave
+    (32).  Plans without the cascade mark nothing (shared prefixes sit in
+    every member's suffix)."""
+    if case == "fold":
+        shape, tables, lens, nb = fold_case()
+    else:
+        b = build_batch(CONFIGS[case])
+        shape, tables, lens, nb = b.shape, b.block_tables, b.seq_lens, b.num_blocks
+    bt, sl = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    for cascade, fold in ((True, False), (True, True), (False, False)):
+        p = fca.fca_plan(bt, sl, fca.desc_from_shape(shape, nb, cascade=cascade, auto_fold=fold))
+        ex, sc = p.export(), p.export_schedule()
+        folded = ex["folded"]
+        n_flagged = 0
+        for it in sc["grouped"] + sc["suffix"]:
+            if it["member_off"] >= 0:
+                want = it["ncols"] <= 32
+            else:
+                in_folded = any(f and it["request"] in g["members"] for f, g in zip(folded, ex["groups"]))
+                want = cascade and not in_folded
+            assert bool(it["flags"] & 1) == want, (case, cascade, fold, it)
+            n_flagged += bool(it["flags"] & 1)
+        say("stream flags", case, "cascade", cascade, "fold", fold, "flagged", n_flagged, "of", len(sc["grouped"]) + len(sc["suffix"]))
+        if not cascade:
+            assert n_flagged == 0
