@@ -92,6 +92,31 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
   for (int base = 0; base < n_src; base += 64) {
     const int j = base + lane;
     const int row = j < n_src ? P.src_row[off0 + j] : -1;
+    const int cnt = min(64, n_src - base);
+    const int row0 = __builtin_amdgcn_readlane(row, 0);  // a valid row for idle slots
+    // Value rows of sources s .. s + 2U - 1 (even ones in the lower half
+    // wave, odd ones in the upper); they depend on the row indices only.
+    float x[U][VPL];
+    auto load_rows = [&](int s) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int se = s + 2 * u;
+        const int re = se < cnt ? __builtin_amdgcn_readlane(row, se) : row0;
+        const int ro = se + 1 < cnt ? __builtin_amdgcn_readlane(row, se + 1) : row0;
+        const float* src = P.part.o + (int64_t)(half ? ro : re) * DV + hl * VPL;
+#pragma unroll
+        for (int v = 0; v < VPL; v += 4) {
+          const float4 t = *reinterpret_cast<const float4*>(src + v);
+          x[u][v] = t.x;
+          x[u][v + 1] = t.y;
+          x[u][v + 2] = t.z;
+          x[u][v + 3] = t.w;
+        }
+      }
+    };
+    // The first batch goes out with the (m, l) loads: one memory round
+    // trip instead of two before the first accumulation.
+    load_rows(0);
     float m = -INFINITY, l = 0.f;
     if (row >= 0) {
       l = P.part.l[row];
@@ -110,28 +135,15 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
     const float w = l > 0.f ? exp2f(m - muse) : 0.f;
     L += wave_sum(w * l);
     M = Mn;
-    const int cnt = min(64, n_src - base);
-    const int row0 = __builtin_amdgcn_readlane(row, 0);  // a valid row for idle slots
     for (int s = 0; s < cnt; s += 2 * U) {
-      float x[U][VPL];
+      if (s > 0) load_rows(s);
       float ws[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int se = s + 2 * u;  // even source; odd one is se + 1 (wave-uniform indices)
         const float we = se < cnt ? lane_f(w, se) : 0.f;
         const float wo = se + 1 < cnt ? lane_f(w, se + 1) : 0.f;
-        const int re = se < cnt ? __builtin_amdgcn_readlane(row, se) : row0;
-        const int ro = se + 1 < cnt ? __builtin_amdgcn_readlane(row, se + 1) : row0;
         ws[u] = half ? wo : we;
-        const float* src = P.part.o + (int64_t)(half ? ro : re) * DV + hl * VPL;
-#pragma unroll
-        for (int v = 0; v < VPL; v += 4) {
-          const float4 t = *reinterpret_cast<const float4*>(src + v);
-          x[u][v] = t.x;
-          x[u][v + 1] = t.y;
-          x[u][v + 2] = t.z;
-          x[u][v + 3] = t.w;
-        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
