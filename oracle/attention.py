@@ -65,6 +65,9 @@ def attend_one(q, K, V, scale, num_kv_heads):
 
     q: [Hq, Dqk] float64;  K: [L, Hkv, Dqk];  V: [L, Hkv, Dv].
     Returns o [Hq, Dv], lse [Hq] (float64).
+
+    The query heads that read one KV head (h // r == kvh) are one matrix
+    product against that head's keys; every row is still its own softmax.
     """
     hq = q.shape[0]
     r = hq // num_kv_heads
@@ -74,14 +77,16 @@ def attend_one(q, K, V, scale, num_kv_heads):
     lse = np.full(hq, -np.inf)
     if L == 0:
         return o, lse
-    for h in range(hq):
-        kvh = h // r
-        s = scale * (K[:, kvh, :] @ q[h])
-        m = s.max()
-        w = np.exp(s - m)
-        l = w.sum()
-        o[h] = (w @ V[:, kvh, :]) / l
-        lse[h] = m + np.log(l)
+    for kvh in range(num_kv_heads):
+        rows = slice(kvh * r, (kvh + 1) * r)
+        Kh = np.ascontiguousarray(K[:, kvh, :])  # [L, Dqk]
+        Vh = np.ascontiguousarray(V[:, kvh, :])  # [L, Dv]
+        s = scale * (q[rows] @ Kh.T)  # [r, L]
+        m = s.max(axis=1)
+        w = np.exp(s - m[:, None])
+        l = w.sum(axis=1)
+        o[rows] = (w @ Vh) / l[:, None]
+        lse[rows] = m + np.log(l)
     return o, lse
 
 

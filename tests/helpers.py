@@ -1,4 +1,4 @@
-"""Shared test helpers: tolerance, device upload, sampled oracle runs."""
+"""Shared test helpers: tolerance, device upload, oracle runs over whole batches."""
 
 from __future__ import annotations
 
@@ -6,10 +6,17 @@ import numpy as np
 
 from oracle import attention as A
 
-# Tolerance on bf16 outputs vs the fp64 oracle: |out - ref| <= ATOL + RTOL*|ref|
-# element-wise (max-abs 2e-3 and relative 1e-2 read as an allclose pair).
+# Tolerance vs the fp64 oracle (max-abs 2e-3, relative 1e-2):
+#  * every output: the row-relative error max_(i,h) ||out - ref||_inf /
+#    ||ref||_inf <= ROW_RTOL (rows whose reference is all zero are held to the
+#    absolute bound alone);
+#  * bf16 outputs: element-wise |out - ref| <= ATOL + RTOL*|ref| (rounding the
+#    output to bf16 alone moves an element by up to 2^-9 |ref|, so a plain
+#    2e-3 absolute bound cannot hold where |ref| exceeds about 1);
+#  * float32 outputs (FCA_PLAN_OUT_F32): max |out - ref| <= ATOL.
 ATOL = 2e-3
 RTOL = 1e-2
+ROW_RTOL = 1e-2
 # log-sum-exp: fp32 scores and a denominator summed from bf16-rounded weights.
 LSE_ATOL = 1e-3
 
@@ -40,7 +47,25 @@ def error_report(out, ref):
     return dict(max_abs=float(err.max()) if err.size else 0.0, row_rel=float(rowrel.max()) if rowrel.size else 0.0)
 
 
+def _check_rows(out, ref, what):
+    err = np.abs(out - ref).max(axis=-1)
+    rowmax = np.abs(ref).max(axis=-1)
+    live = rowmax > 0
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.where(live, err / np.where(live, rowmax, 1.0), 0.0)
+    if (rel > ROW_RTOL).any():
+        idx = np.unravel_index(np.argmax(rel), rel.shape)
+        raise AssertionError(
+            f"{what}: row-relative error {rel[idx]:.3g} > {ROW_RTOL} at row {idx} "
+            f"(max |err| {err[idx]:.3g}, max |ref| {rowmax[idx]:.3g}); {error_report(out, ref)}"
+        )
+    dead = ~live
+    if dead.any() and (err[dead] > ATOL).any():
+        raise AssertionError(f"{what}: rows with an all-zero reference are off by more than {ATOL}")
+
+
 def assert_close(out, ref, what=""):
+    """bf16 outputs: element-wise bound and row-relative bound."""
     assert np.isfinite(out).all(), f"{what}: non-finite output"
     err = np.abs(out - ref)
     bound = ATOL + RTOL * np.abs(ref)
@@ -51,6 +76,18 @@ def assert_close(out, ref, what=""):
             f"{what}: {int(bad.sum())} elements out of tolerance; worst at {idx}: "
             f"out={out[idx]!r} ref={ref[idx]!r}; {error_report(out, ref)}"
         )
+    _check_rows(out, ref, what)
+    return error_report(out, ref)
+
+
+def assert_close_f32(out, ref, what=""):
+    """float32 outputs: max-abs bound and row-relative bound."""
+    assert np.isfinite(out).all(), f"{what}: non-finite output"
+    err = np.abs(out - ref)
+    if err.size and err.max() > ATOL:
+        idx = np.unravel_index(np.argmax(err), err.shape)
+        raise AssertionError(f"{what}: max |err| {err[idx]:.3g} > {ATOL} at {idx}; {error_report(out, ref)}")
+    _check_rows(out, ref, what)
     return error_report(out, ref)
 
 
@@ -61,24 +98,41 @@ def assert_lse_close(lse, ref, what=""):
     assert (diff <= LSE_ATOL).all(), f"{what}: lse max diff {np.nanmax(diff)}"
 
 
-def oracle_requests_from_device(batch, vals, requests):
-    """Oracle output for the listed requests, reading their blocks back from
-    the device pool into a compact pool (blocks relabelled 0..n-1)."""
-    import torch
+def host_values(vals):
+    """Host copies (uint16 bf16 bits) of device q / k / v, taken before any
+    decode runs, so that the oracle sees the inputs and not whatever a
+    kernel might leave in device memory."""
+    return {k: (to_bits(v) if v is not None else None) for k, v in vals.items()}
+
+
+def oracle_all(batch, host, requests=None, threads=None, say=None):
+    """fp64 oracle attention of every request (or the listed ones) of a batch
+    from host copies of its inputs; requests run on a pool of threads (one
+    BLAS thread each).  Returns (out [B, Hq, Dv], lse [B, Hq])."""
+    import os
+    import time
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
 
     sh = batch.shape
-    bs = sh.block_size
-    outs, lses = [], []
-    q_bits = to_bits(vals["q"])
-    for i in requests:
-        L = int(batch.seq_lens[i])
-        nblk = -(-L // bs)
-        blocks = torch.from_numpy(batch.block_tables[i, :nblk].astype(np.int64)).to(vals["k"].device)
-        k = to_bits(vals["k"].index_select(0, blocks))
-        v = None if sh.v_aliases_k else to_bits(vals["v"].index_select(0, blocks))
-        table = np.arange(nblk, dtype=np.int32)
-        K, V = A.gather_kv(k, v, table, L, bs, sh.head_dim_v, sh.v_aliases_k)
-        o, l = A.attend_one(A.widen_bf16(q_bits[i]), K, V, sh.scale, sh.num_kv_heads)
-        outs.append(o)
-        lses.append(l)
-    return np.stack(outs), np.stack(lses)
+    reqs = list(range(batch.batch)) if requests is None else list(requests)
+    out = np.zeros((batch.batch, sh.num_q_heads, sh.head_dim_v))
+    lse = np.full((batch.batch, sh.num_q_heads), -np.inf)
+    n_threads = threads or min(16, len(os.sched_getaffinity(0)))
+    t0 = time.perf_counter()
+    done = [0]
+
+    def one(i):
+        o, l = A.attend(host["q"], host["k"], host["v"], batch.block_tables, batch.seq_lens, sh, requests=[i])
+        out[i], lse[i] = o[i], l[i]
+        done[0] += 1
+        if say is not None and done[0] % 64 == 0:
+            say(f"oracle: {done[0]} of {len(reqs)} requests, {time.perf_counter() - t0:.1f} s")
+
+    with threadpool_limits(limits=1):
+        with ThreadPoolExecutor(n_threads) as ex:
+            list(ex.map(one, reqs))
+    if say is not None:
+        say(f"oracle: {len(reqs)} requests in {time.perf_counter() - t0:.1f} s on {n_threads} threads")
+    return out, lse
