@@ -4,16 +4,19 @@
 One step = one ``fca_decode`` of a whole batch (grouped prefix pass,
 per-request suffix pass, log-sum-exp merge) for one attention layer.  The
 batch is a seeded synthetic shared-prefix rollout batch (default: the
-Llama-3-8B layer shape, 64 requests = 8 prompts x 8 samples, prefix 4096,
-suffix U{256..1024}, GQA 32/8, head dim 128, 16-token blocks).  Steps cycle
+long-context RL rollout, the largest of the five workloads: 256 requests =
+16 prompts x 16 samples, prefix 16384, suffix U{1..4096}, GQA 32/8, head dim
+128, 16-token blocks).  Steps cycle
 through ``--layers`` independent KV pools that share one plan, as the layers
 of a model do, so each step reads KV that is not resident in L2 / MALL.
 
 Printed (one JSON line on stdout): logical-KV tokens/s (the value), unique-KV
 GB/s and its share of the 8 TB/s HBM peak, per-pass times measured with HIP
 events on the kernels' stream, the roofline of the dominant kernel, the
-non-cascade baseline (same kernels, every request read whole) and the CPU
-oracle timed on a bounded sample.  Progress goes to stderr.
+non-cascade baseline (same kernels, every request read whole), the CPU
+oracle timed on a bounded sample, the streaming-read rate a plain kernel
+reaches on the device, and a short record of each of the other workloads
+(cascade vs non-cascade).  Progress goes to stderr.
 """
 
 from __future__ import annotations
@@ -45,7 +48,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="llama3_8b")
+    ap.add_argument("--config", default="long_rl")
+    ap.add_argument(
+        "--others",
+        default="tiny,llama3_8b,forest_mixed,mla",
+        help="workloads given a short cascade / non-cascade record beside the headline one ('' for none)",
+    )
     ap.add_argument("--layers", type=int, default=8, help="independent KV pools cycled by the steps")
     ap.add_argument("--cpu-seconds", type=float, default=24.0, help="budget of the CPU oracle sample (split between the all-threads and one-thread runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -178,6 +186,75 @@ def cpu_baseline(batch, vals, budget_s, threads, cache=None):
         sample=f"{done} request decodes ({passes:.2f} passes over the {batch.batch} requests of the batch, "
         f"{tokens} logical tokens), fp64 numpy oracle, {threads} BLAS thread(s), {elapsed:.1f} s",
     )
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def read_peak(torch, fca):
+    """HBM read rate of a plain streaming kernel (fca_measure_read_bandwidth):
+    two 2 GiB buffers, each far larger than the 256 MB last-level cache, read
+    alternately 4 times each."""
+    bufs = [torch.ones((1 << 31) // 2, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    gbps = fca.measure_read_bandwidth(bufs, repeats=4)
+    del bufs
+    torch.cuda.empty_cache()
+    return gbps
+
+
+def short_record(name, torch, fca, steps, warmup, layers=4):
+    """Cascade vs non-cascade on another workload: decode time per step, the
+    logical-KV rate, unique-KV GB/s, the byte ratio R and the speedup."""
+    from workloads import CONFIGS, build_batch
+    from workloads.values import fill_values_torch
+
+    cfg = CONFIGS[name]
+    batch = build_batch(cfg)
+    sh = batch.shape
+    pools, qs = [], []
+    for layer in range(layers):
+        v = fill_values_torch(batch, "cuda", seed=cfg.seed * 1000 + layer, poison=False)
+        pools.append((v["k"], v["v"]))
+        qs.append(v["q"])
+    bt = torch.from_numpy(batch.block_tables).cuda()
+    sl = torch.from_numpy(batch.seq_lens).cuda()
+    out = torch.empty((batch.batch, sh.num_q_heads, sh.head_dim_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((batch.batch, sh.num_q_heads), dtype=torch.float32, device="cuda")
+    res = {}
+    for key, desc in (
+        ("fca", fca.desc_from_shape(sh, batch.num_blocks)),
+        ("non_cascade", fca.desc_from_shape(sh, batch.num_blocks, cascade=False)),
+    ):
+        plan = fca.fca_plan(bt, sl, desc)
+        plan.decode_workspace(out.device)
+        warm(plan, qs, pools, out, lse, warmup, torch, fca)
+        ms, _ = time_steps(plan, qs, pools, out, lse, steps, torch, fca)
+        res[key] = (ms, plan.info)
+        del plan
+    ms, info = res["fca"]
+    ms_nc, _ = res["non_cascade"]
+    tok_bytes = sh.kv_bytes_per_token()
+    rec = {
+        "workload": f"{cfg.name}: {cfg.description}",
+        "fca_us_per_step": round(ms * 1000, 2),
+        "non_cascade_us_per_step": round(ms_nc * 1000, 2),
+        "logical_kv_tokens_per_s": round(int(info.logical_tokens) / (ms / 1000.0), 1),
+        "unique_kv_GBps": round(int(info.unique_tokens) * tok_bytes / (ms / 1000.0) / 1e9, 1),
+        "byte_ratio_R": round(int(info.logical_tokens) / max(int(info.unique_tokens), 1), 3),
+        "speedup_vs_non_cascade": round(ms_nc / ms, 3),
+    }
+    del pools, qs
+    torch.cuda.empty_cache()
+    return rec
 
 
 def kv_append_leg(batch, pool, torch, fca):
@@ -503,6 +580,7 @@ def main():
         "grouped_mfma_TFLOPs": round(grouped_tflops, 1),
         "grouped_mfma_frac_of_peak": round(grouped_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "plan_ms": round(plan_ms, 3),
+        "plan_ms_per_layer_of_32": round(plan_ms / 32, 4),
         "plan_ms_first_call": round(plan_ms_first, 3),
         "roofline": roofline,
     }
@@ -626,13 +704,34 @@ def main():
     if args.group_sweep and not args.profile_only:
         result["group_sweep"] = group_sweep(torch, fca, steps, warmup)
 
+    if not args.profile_only:
+        rp = read_peak(torch, fca)
+        result["read_peak_GBps"] = round(rp, 1)
+        result["roofline"]["measured_read_peak_GBps"] = round(rp, 1)
+        result["roofline"]["frac_of_measured_read_peak"] = (
+            round(roofline["achieved"] / rp, 4) if roofline["unit"] == "GB/s" and rp > 0 else None
+        )
+        log(f"streaming read, plain kernel: {rp:.0f} GB/s")
+
     if not args.no_cpu_baseline and not args.profile_only:
         ncpu = len(os.sched_getaffinity(0))
         log(f"cpu baseline (oracle), {ncpu} threads then 1 ...")
         blocks = {}
         result["cpu_baseline"] = cpu_baseline(batch, vals0, args.cpu_seconds / 2, ncpu, blocks)
         result["cpu_baseline_1_thread"] = cpu_baseline(batch, vals0, args.cpu_seconds / 2, 1, blocks)
+        for k in ("cpu_baseline", "cpu_baseline_1_thread"):
+            result[k]["cpu_model"] = cpu_model()
         del blocks
+
+    others = [o for o in args.others.split(",") if o and o != cfg.name] if not args.profile_only else []
+    if others:
+        del pools, qs, vals0, vals
+        torch.cuda.empty_cache()
+        result["other_workloads"] = {}
+        for name in others:
+            rec = short_record(name, torch, fca, max(steps // 2, 8), warmup)
+            log(f"{name}: {rec}")
+            result["other_workloads"][name] = rec
 
     print(json.dumps(result), flush=True)
 

@@ -195,6 +195,24 @@ fca_status fca_plan_get_info(fca_plan plan, fca_plan_info* info);
 fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
                       void* out_dev, float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
 
+/*
+ * The decode of several layers that share one batch and so one plan (the
+ * plan is made once for each decode batch and serves every layer: "Core
+ * Mechanism").  Layer l reads q_dev[l], k_caches_dev[l], v_caches_dev[l] and
+ * writes out_dev[l], lse_dev[l], each as for fca_decode; the arrays are host
+ * arrays of n_layers device pointers (v_caches_dev may be NULL when
+ * v_aliases_k; lse_dev may be NULL, or hold NULL entries).  The layers run in
+ * order on `stream` and share one decode workspace (>=
+ * info.decode_workspace_bytes), which is safe because each layer's launches
+ * are queued after the previous layer's.  Every layer's arguments are checked
+ * before anything is launched; an error names the layer.  Asynchronous, no
+ * allocation on the device, no host synchronisation; it can be captured in a
+ * HIP graph.  Profiling (fca_profile_enable) does not record these launches.
+ */
+fca_status fca_decode_layers(fca_plan plan, int32_t n_layers, const void* const* q_dev, const void* const* k_caches_dev,
+                             const void* const* v_caches_dev, void* const* out_dev, float* const* lse_dev,
+                             void* workspace_dev, size_t workspace_bytes, void* stream);
+
 /* One discovered group, canonical order: sorted by (smallest member, depth). */
 typedef struct fca_group_record {
   int32_t depth;        /* number of groups strictly above; roots are 0 */
@@ -308,6 +326,20 @@ fca_status fca_time_launches(fca_plan plan, const void* q_dev, const void* const
                              fca_profile* result);
 
 /*
+ * Measurement hook: the HBM read rate of a plain streaming kernel on this
+ * device, the practical ceiling next to the published peak.  Each of the
+ * n_bufs buffers (device, 16-byte aligned, `bytes` each, a positive multiple
+ * of 16; bytes well above the 256 MB last-level cache) is read once untimed,
+ * then repeats * n_bufs reads cycling over the buffers run back to back
+ * between two HIP events on `stream`; *gbps = bytes read / elapsed time
+ * (1e9 bytes per second).  Nothing is written.  Blocks the host until the
+ * reads finish.  FCA_ERR_INVALID_ARG for NULL or misaligned pointers or bad
+ * sizes, FCA_ERR_HIP if a launch or event call fails.
+ */
+fca_status fca_measure_read_bandwidth(const void* const* bufs_dev, int32_t n_bufs, size_t bytes, int32_t repeats,
+                                      void* stream, double* gbps);
+
+/*
  * Exact combination of attention states over disjoint key sets: state j of
  * (request i, head h) is a normalised output o_j (float32) and its natural
  * log-sum-exp lse_j, as fca_decode writes them with FCA_PLAN_OUT_F32 and an
@@ -393,6 +425,12 @@ fca_status fca_merge_states(int32_t n_states, const float* const* outs, const fl
  * [0, 8192], max_blocks outside [1, 2^20] or bt_row_stride < max_blocks;
  * FCA_ERR_UNSUPPORTED as fca_plan_create; FCA_ERR_HIP if the launch fails.
  * Asynchronous on `stream`.
+ *
+ * This call covers one layer's pool.  When several layers share the block
+ * table (as they share the plan), use fca_kv_append_layers: appending layer
+ * by layer with this call would rewrite a copied request's table entry after
+ * the first layer, and the later layers would then write in place into the
+ * copy without copying their own tokens.
  */
 #define FCA_APPEND_BAD_LEN 1
 #define FCA_APPEND_BAD_BLOCK 2
@@ -401,6 +439,26 @@ fca_status fca_kv_append(const fca_attn_desc* desc, const void* k_new_dev, const
                          void* v_cache_dev, int32_t* block_tables_dev, int64_t bt_row_stride, int32_t max_blocks,
                          const int32_t* seq_lens_dev, const int32_t* cow_dst_dev, int32_t* status_dev, int32_t batch,
                          void* stream);
+
+/*
+ * fca_kv_append for n_layers layers that share one block table (each layer
+ * its own pool with the same block IDs): k_new_dev[l], v_new_dev[l],
+ * k_caches_dev[l], v_caches_dev[l] are host arrays of device pointers, one
+ * entry per layer, each as for fca_kv_append (v arrays may be NULL when
+ * v_aliases_k).  Every layer's copy reads block_tables_dev as the caller
+ * left it; the entries of copied requests are rewritten once, after every
+ * layer's copy (so a copy target receives the request's tokens in every
+ * layer).  Status bits are ORed once per skipped request.  Same contract and
+ * errors as fca_kv_append, plus FCA_ERR_INVALID_ARG for n_layers < 0 or a
+ * NULL / misaligned layer pointer (the error names the layer).  n_layers == 0
+ * or batch == 0 does nothing.  Asynchronous on `stream`: a few launches, no
+ * allocation.
+ */
+fca_status fca_kv_append_layers(const fca_attn_desc* desc, int32_t n_layers, const void* const* k_new_dev,
+                                const void* const* v_new_dev, void* const* k_caches_dev, void* const* v_caches_dev,
+                                int32_t* block_tables_dev, int64_t bt_row_stride, int32_t max_blocks,
+                                const int32_t* seq_lens_dev, const int32_t* cow_dst_dev, int32_t* status_dev,
+                                int32_t batch, void* stream);
 
 /*
  * Frees the plan without waiting for the device.  Its device schedule is

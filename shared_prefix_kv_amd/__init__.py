@@ -41,14 +41,17 @@ EXPORTED = [
     "fca_plan_create",
     "fca_plan_get_info",
     "fca_decode",
+    "fca_decode_layers",
     "fca_plan_export",
     "fca_plan_export_schedule",
     "fca_plan_export_folded",
     "fca_profile_enable",
     "fca_profile_read",
     "fca_time_launches",
+    "fca_measure_read_bandwidth",
     "fca_merge_states",
     "fca_kv_append",
+    "fca_kv_append_layers",
     "fca_plan_destroy",
     "fca_last_error",
     "fca_version",
@@ -152,14 +155,17 @@ def lib():
         L.fca_plan_create.argtypes = [vp, i64, vp, i32, i32, ctypes.POINTER(AttnDesc), vp, sz, vp, ctypes.POINTER(vp)]
         L.fca_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
         L.fca_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.fca_decode_layers.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fca_plan_export.argtypes = [vp, vp, vp, vp]
         L.fca_plan_export_schedule.argtypes = [vp, vp, vp, vp, vp]
         L.fca_plan_export_folded.argtypes = [vp, vp]
         L.fca_profile_enable.argtypes = [vp, i32]
         L.fca_profile_read.argtypes = [vp, ctypes.POINTER(Profile)]
         L.fca_time_launches.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp, ctypes.POINTER(Profile)]
+        L.fca_measure_read_bandwidth.argtypes = [vp, i32, sz, i32, vp, ctypes.POINTER(ctypes.c_double)]
         L.fca_merge_states.argtypes = [i32, vp, vp, i32, i32, i32, vp, vp, ctypes.c_uint32, vp]
         L.fca_kv_append.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, i64, i32, vp, vp, vp, i32, vp]
+        L.fca_kv_append_layers.argtypes = [ctypes.POINTER(AttnDesc), i32, vp, vp, vp, vp, vp, i64, i32, vp, vp, vp, i32, vp]
         L.fca_plan_destroy.argtypes = [vp]
         L.fca_plan_destroy.restype = None
         L.fca_last_error.restype = ctypes.c_char_p
@@ -250,6 +256,34 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _pool_extent(num_blocks, stride_block, stride_head, num_heads, tile):
+    """Elements a pool of `num_blocks` blocks spans: the last tile's end."""
+    return (num_blocks - 1) * stride_block + (num_heads - 1) * stride_head + tile
+
+
+def _span(t):
+    """Elements from the tensor's first element to the end of its storage
+    (what a kernel given its data pointer may read)."""
+    return t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+
+
+def _check_pool(d: AttnDesc, k_cache, v_cache):
+    """The pools a call reads or writes: bf16, 16-byte aligned, and large
+    enough for every block ID the descriptor allows (the C ABI cannot see
+    sizes; a short pool would be read past its end)."""
+    import torch
+
+    assert k_cache is not None and k_cache.dtype == torch.bfloat16, "k_cache must be a bf16 tensor"
+    assert k_cache.data_ptr() % 16 == 0, "k_cache must be 16-byte aligned"
+    need_k = _pool_extent(d.num_blocks, d.k_stride_block, d.k_stride_head, d.num_kv_heads, d.head_dim_qk * d.block_size)
+    assert _span(k_cache) >= need_k, f"k_cache spans {_span(k_cache)} elements, the descriptor needs {need_k}"
+    if not d.v_aliases_k:
+        assert v_cache is not None and v_cache.dtype == torch.bfloat16, "v_cache must be a bf16 tensor"
+        assert v_cache.data_ptr() % 16 == 0, "v_cache must be 16-byte aligned"
+        need_v = _pool_extent(d.num_blocks, d.v_stride_block, d.v_stride_head, d.num_kv_heads, d.head_dim_v * d.block_size)
+        assert _span(v_cache) >= need_v, f"v_cache spans {_span(v_cache)} elements, the descriptor needs {need_v}"
+
+
 class Plan:
     """A planned batch: prefix forest + decode schedule (fca_plan_create)."""
 
@@ -309,6 +343,10 @@ class Plan:
         return self._decode_ws
 
     def decode(self, q, k_cache, v_cache, out=None, lse=None, workspace=None, stream=None):
+        """fca_decode of this plan.  Without ``workspace`` the plan's own
+        decode workspace is used, so calls of one plan on different streams
+        that may overlap must each pass a workspace of their own
+        (``torch.empty_like(plan.decode_workspace(device))``)."""
         import torch
 
         d = self.desc
@@ -322,6 +360,7 @@ class Plan:
         if lse is not None:
             assert lse.dtype == torch.float32 and lse.is_contiguous()
             assert tuple(lse.shape) == (self.batch, d.num_q_heads)
+        _check_pool(d, k_cache, v_cache)
         ws = workspace if workspace is not None else self.decode_workspace(q.device)
         _check(
             lib().fca_decode(
@@ -337,6 +376,45 @@ class Plan:
             )
         )
         return out
+
+    def decode_layers(self, qs, caches, outs, lses=None, workspace=None, stream=None):
+        """One call decoding several layers with this plan
+        (fca_decode_layers): ``qs[l]`` bf16 [B, Hq, Dqk], ``caches[l]`` =
+        (k_cache, v_cache), ``outs[l]`` the outputs, ``lses[l]`` float32
+        [B, Hq] or None."""
+        import torch
+
+        d = self.desc
+        n = len(qs)
+        assert len(caches) == n and len(outs) == n and (lses is None or len(lses) == n)
+        out_dtype = torch.float32 if d.flags & FCA_PLAN_OUT_F32 else torch.bfloat16
+        for l in range(n):
+            q, out = qs[l], outs[l]
+            assert q.dtype == torch.bfloat16 and q.is_contiguous()
+            assert tuple(q.shape) == (self.batch, d.num_q_heads, d.head_dim_qk)
+            assert out.dtype == out_dtype and out.is_contiguous()
+            assert tuple(out.shape) == (self.batch, d.num_q_heads, d.head_dim_v)
+            if lses is not None and lses[l] is not None:
+                assert lses[l].dtype == torch.float32 and lses[l].is_contiguous()
+                assert tuple(lses[l].shape) == (self.batch, d.num_q_heads)
+            _check_pool(d, caches[l][0], caches[l][1])
+        arr = lambda ts: (ctypes.c_void_p * max(n, 1))(*[(t.data_ptr() if t is not None else 0) for t in ts])
+        ws = workspace if workspace is not None else self.decode_workspace(qs[0].device)
+        _check(
+            lib().fca_decode_layers(
+                self._h,
+                n,
+                arr(qs),
+                arr([c[0] for c in caches]),
+                arr([c[1] for c in caches]),
+                arr(outs),
+                arr(lses) if lses is not None else None,
+                _ptr(ws),
+                ws.numel() * ws.element_size(),
+                _stream_ptr(stream),
+            )
+        )
+        return outs
 
     def profile(self, enable: bool):
         """Record per-pass HIP events in later decode calls (measurement)."""
@@ -361,6 +439,8 @@ class Plan:
         assert tuple(out.shape) == (self.batch, d.num_q_heads, d.head_dim_v)
         if lse is not None:
             assert lse.dtype == torch.float32 and lse.is_contiguous()
+        for k, v in caches:
+            _check_pool(d, k, v)
         n = len(caches)
         ks = (ctypes.c_void_p * max(n, 1))(*[k.data_ptr() for k, _ in caches])
         vs = (ctypes.c_void_p * max(n, 1))(*[(v.data_ptr() if v is not None else 0) for _, v in caches])
@@ -495,6 +575,7 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_tables, seq_lens, desc: Attn
         assert cow_dst.dtype == torch.int32 and cow_dst.is_contiguous() and tuple(cow_dst.shape) == (B,)
     if status is not None:
         assert status.dtype == torch.int32 and status.numel() >= 1
+    _check_pool(desc, k_cache, None if desc.v_aliases_k else v_cache)
     _check(
         lib().fca_kv_append(
             ctypes.byref(desc),
@@ -512,6 +593,66 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_tables, seq_lens, desc: Attn
             _stream_ptr(stream),
         )
     )
+
+
+def kv_append_layers(k_news, v_news, caches, block_tables, seq_lens, desc: AttnDesc, cow_dst=None, status=None,
+                     stream=None):
+    """fca_kv_append_layers: one decode token per request appended to every
+    layer's pool (``caches[l]`` = (k_cache, v_cache), ``k_news[l]`` /
+    ``v_news[l]`` that layer's new rows), the table entries of copied requests
+    rewritten once after all layers."""
+    import torch
+
+    assert block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.stride(1) == 1
+    B, W = block_tables.shape
+    n = len(caches)
+    assert len(k_news) == n and (desc.v_aliases_k or len(v_news) == n)
+    assert seq_lens.dtype == torch.int32 and seq_lens.is_contiguous() and tuple(seq_lens.shape) == (B,)
+    for l in range(n):
+        assert k_news[l].dtype == torch.bfloat16 and k_news[l].is_contiguous()
+        assert tuple(k_news[l].shape) == (B, desc.num_kv_heads, desc.head_dim_qk)
+        if not desc.v_aliases_k:
+            assert v_news[l].dtype == torch.bfloat16 and v_news[l].is_contiguous()
+            assert tuple(v_news[l].shape) == (B, desc.num_kv_heads, desc.head_dim_v)
+        _check_pool(desc, caches[l][0], None if desc.v_aliases_k else caches[l][1])
+    if cow_dst is not None:
+        assert cow_dst.dtype == torch.int32 and cow_dst.is_contiguous() and tuple(cow_dst.shape) == (B,)
+    if status is not None:
+        assert status.dtype == torch.int32 and status.numel() >= 1
+    arr = lambda ts: (ctypes.c_void_p * max(n, 1))(*[(t.data_ptr() if t is not None else 0) for t in ts])
+    alias = bool(desc.v_aliases_k)
+    _check(
+        lib().fca_kv_append_layers(
+            ctypes.byref(desc),
+            n,
+            arr(k_news),
+            None if alias else arr(v_news),
+            arr([c[0] for c in caches]),
+            None if alias else arr([c[1] for c in caches]),
+            _ptr(block_tables),
+            block_tables.stride(0),
+            W,
+            _ptr(seq_lens),
+            _ptr(cow_dst),
+            _ptr(status),
+            B,
+            _stream_ptr(stream),
+        )
+    )
+
+
+def measure_read_bandwidth(buffers, repeats=4, stream=None) -> float:
+    """HBM read rate (GB/s, 1e9 B/s) of a plain streaming kernel over the
+    given device tensors (equal sizes, multiple of 16 bytes), cycled
+    ``repeats`` times (fca_measure_read_bandwidth)."""
+    n = len(buffers)
+    nbytes = buffers[0].numel() * buffers[0].element_size()
+    for b in buffers:
+        assert b.is_contiguous() and b.numel() * b.element_size() == nbytes
+    arr = (ctypes.c_void_p * n)(*[b.data_ptr() for b in buffers])
+    g = ctypes.c_double()
+    _check(lib().fca_measure_read_bandwidth(arr, n, nbytes, int(repeats), _stream_ptr(stream), ctypes.byref(g)))
+    return g.value
 
 
 def version() -> str:

@@ -1120,6 +1120,44 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   return FCA_OK;
 }
 
+fca_status fca_decode_layers(fca_plan plan, int32_t n_layers, const void* const* q_dev, const void* const* k_caches_dev,
+                             const void* const* v_caches_dev, void* const* out_dev, float* const* lse_dev,
+                             void* workspace_dev, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
+  if (n_layers < 0) return fail(FCA_ERR_INVALID_ARG, "n_layers %d < 0", n_layers);
+  const fca_plan_s* P = plan;
+  if (P->B == 0 || n_layers == 0) return FCA_OK;
+  if (!q_dev || !k_caches_dev || !out_dev || (!P->desc.v_aliases_k && !v_caches_dev))
+    return fail(FCA_ERR_INVALID_ARG, "q / k_caches / v_caches / out array is NULL");
+  try {
+    // Every layer's arguments are checked before the first launch.
+    std::vector<GqaParams> gps(n_layers);
+    std::vector<MergeParams> mps(n_layers);
+    for (int l = 0; l < n_layers; ++l) {
+      fca_status st = decode_params(P, q_dev[l], k_caches_dev[l], P->desc.v_aliases_k ? nullptr : v_caches_dev[l],
+                                    out_dev[l], lse_dev ? lse_dev[l] : nullptr, workspace_dev, workspace_bytes,
+                                    &gps[l], &mps[l]);
+      if (st != FCA_OK) {
+        char buf[600];
+        snprintf(buf, sizeof(buf), "layer %d: %s", l, g_last_error.c_str());
+        return fail(st, "%s", buf);
+      }
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int l = 0; l < n_layers; ++l) {
+      for (int k = 0; k < (int)P->launches.size(); ++k) {
+        const hipError_t e = launch_pass(P, gps[l], k, s);
+        if (e != hipSuccess) return hip_fail(e, "attention launch");
+      }
+      const hipError_t e = launch_merge(mps[l], s);
+      if (e != hipSuccess) return hip_fail(e, "merge launch");
+    }
+    return FCA_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(FCA_ERR_HOST_ALLOC, "host allocation failed");
+  }
+}
+
 fca_status fca_time_launches(fca_plan plan, const void* q_dev, const void* const* k_caches,
                              const void* const* v_caches, int32_t n_caches, int32_t repeats, void* out_dev,
                              float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream,
@@ -1163,7 +1201,7 @@ fca_status fca_time_launches(fca_plan plan, const void* q_dev, const void* const
   if (e == hipSuccess) e = hipEventSynchronize(ev[n_ev - 1]);
   for (int k = 0; k <= n_launch && e == hipSuccess; ++k) e = hipEventElapsedTime(&t[k], ev[2 * k], ev[2 * k + 1]);
   for (int j = 0; j < n_ev; ++j)
-    if (ev[j]) hipEventDestroy(ev[j]);
+    if (ev[j]) (void)hipEventDestroy(ev[j]);
   if (e != hipSuccess) return hip_fail(e, "timed launches");
   const double n = (double)repeats * n_caches;
   for (int k = 0; k < n_launch; ++k) add_pass_time(P, k, t[k] / n, &acc);
@@ -1203,34 +1241,37 @@ fca_status fca_merge_states(int32_t n_states, const float* const* outs, const fl
   return FCA_OK;
 }
 
-fca_status fca_kv_append(const fca_attn_desc* desc, const void* k_new_dev, const void* v_new_dev, void* k_cache_dev,
-                         void* v_cache_dev, int32_t* block_tables_dev, int64_t bt_row_stride, int32_t max_blocks,
-                         const int32_t* seq_lens_dev, const int32_t* cow_dst_dev, int32_t* status_dev, int32_t batch,
-                         void* stream) {
+fca_status fca_kv_append_layers(const fca_attn_desc* desc, int32_t n_layers, const void* const* k_new_dev,
+                                const void* const* v_new_dev, void* const* k_caches_dev, void* const* v_caches_dev,
+                                int32_t* block_tables_dev, int64_t bt_row_stride, int32_t max_blocks,
+                                const int32_t* seq_lens_dev, const int32_t* cow_dst_dev, int32_t* status_dev,
+                                int32_t batch, void* stream) {
   Kind kind;
   fca_status st = check_desc(desc, &kind);
   if (st != FCA_OK) return st;
+  if (n_layers < 0) return fail(FCA_ERR_INVALID_ARG, "n_layers %d < 0", n_layers);
   if (batch < 0 || batch > kMaxBatch) return fail(FCA_ERR_INVALID_ARG, "batch %d outside [0, %d]", batch, kMaxBatch);
   if (max_blocks < 1 || max_blocks > kMaxTableWidth)
     return fail(FCA_ERR_INVALID_ARG, "max_blocks %d outside [1, %d]", max_blocks, kMaxTableWidth);
   if (bt_row_stride < max_blocks) return fail(FCA_ERR_INVALID_ARG, "bt_row_stride < max_blocks");
-  if (batch == 0) return FCA_OK;
+  if (batch == 0 || n_layers == 0) return FCA_OK;
   const bool alias = desc->v_aliases_k != 0;
-  if (!k_new_dev || !k_cache_dev || !block_tables_dev || !seq_lens_dev || (!alias && (!v_new_dev || !v_cache_dev)))
+  if (!k_new_dev || !k_caches_dev || !block_tables_dev || !seq_lens_dev || (!alias && (!v_new_dev || !v_caches_dev)))
     return fail(FCA_ERR_INVALID_ARG, "k_new / v_new / caches / block_tables / seq_lens is NULL");
   auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
-  if (misaligned(k_new_dev) || misaligned(k_cache_dev) || (!alias && (misaligned(v_new_dev) || misaligned(v_cache_dev))))
-    return fail(FCA_ERR_INVALID_ARG, "new rows and caches must be 16-byte aligned");
+  for (int l = 0; l < n_layers; ++l) {
+    if (!k_new_dev[l] || !k_caches_dev[l] || (!alias && (!v_new_dev[l] || !v_caches_dev[l])))
+      return fail(FCA_ERR_INVALID_ARG, "layer %d: k_new / v_new / cache is NULL", l);
+    if (misaligned(k_new_dev[l]) || misaligned(k_caches_dev[l]) ||
+        (!alias && (misaligned(v_new_dev[l]) || misaligned(v_caches_dev[l]))))
+      return fail(FCA_ERR_INVALID_ARG, "layer %d: new rows and caches must be 16-byte aligned", l);
+  }
   AppendParams p;
-  p.k_new = static_cast<const uint16_t*>(k_new_dev);
-  p.v_new = alias ? nullptr : static_cast<const uint16_t*>(v_new_dev);
-  p.k_cache = static_cast<uint16_t*>(k_cache_dev);
-  p.v_cache = alias ? nullptr : static_cast<uint16_t*>(v_cache_dev);
+  std::memset(&p, 0, sizeof(p));
   p.block_tables = block_tables_dev;
   p.bt_row_stride = bt_row_stride;
   p.seq_lens = seq_lens_dev;
   p.cow_dst = cow_dst_dev;
-  p.status = status_dev;
   p.k_stride_block = desc->k_stride_block;
   p.k_stride_head = desc->k_stride_head;
   p.v_stride_block = alias ? 0 : desc->v_stride_block;
@@ -1239,8 +1280,66 @@ fca_status fca_kv_append(const fca_attn_desc* desc, const void* k_new_dev, const
   p.num_kv_heads = desc->num_kv_heads;
   p.max_blocks = max_blocks;
   p.num_blocks = desc->num_blocks;
-  const hipError_t e = launch_append(p, kind == kMla, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "append launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Every layer reads the table as the caller left it; the entries of copied
+  // blocks are rewritten once, after the last layer.
+  for (int l0 = 0; l0 < n_layers; l0 += kAppendLayers) {
+    p.n_layers = std::min(kAppendLayers, n_layers - l0);
+    for (int l = 0; l < p.n_layers; ++l) {
+      p.k_new[l] = static_cast<const uint16_t*>(k_new_dev[l0 + l]);
+      p.k_cache[l] = static_cast<uint16_t*>(k_caches_dev[l0 + l]);
+      p.v_new[l] = alias ? nullptr : static_cast<const uint16_t*>(v_new_dev[l0 + l]);
+      p.v_cache[l] = alias ? nullptr : static_cast<uint16_t*>(v_caches_dev[l0 + l]);
+    }
+    const hipError_t e = launch_append(p, kind == kMla, s);
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+  }
+  const hipError_t e = launch_append_commit(block_tables_dev, bt_row_stride, seq_lens_dev, cow_dst_dev, status_dev,
+                                            batch, max_blocks, desc->block_size, desc->num_blocks, s);
+  if (e != hipSuccess) return hip_fail(e, "append commit launch");
+  return FCA_OK;
+}
+
+fca_status fca_kv_append(const fca_attn_desc* desc, const void* k_new_dev, const void* v_new_dev, void* k_cache_dev,
+                         void* v_cache_dev, int32_t* block_tables_dev, int64_t bt_row_stride, int32_t max_blocks,
+                         const int32_t* seq_lens_dev, const int32_t* cow_dst_dev, int32_t* status_dev, int32_t batch,
+                         void* stream) {
+  const void* kn[1] = {k_new_dev};
+  const void* vn[1] = {v_new_dev};
+  void* kc[1] = {k_cache_dev};
+  void* vc[1] = {v_cache_dev};
+  return fca_kv_append_layers(desc, 1, kn, vn, kc, vc, block_tables_dev, bt_row_stride, max_blocks, seq_lens_dev,
+                              cow_dst_dev, status_dev, batch, stream);
+}
+
+fca_status fca_measure_read_bandwidth(const void* const* bufs_dev, int32_t n_bufs, size_t bytes, int32_t repeats,
+                                      void* stream, double* gbps) {
+  if (!bufs_dev || !gbps) return fail(FCA_ERR_INVALID_ARG, "buffers / gbps is NULL");
+  if (n_bufs < 1 || repeats < 1) return fail(FCA_ERR_INVALID_ARG, "n_bufs and repeats must be >= 1");
+  if (bytes < 16 || bytes % 16) return fail(FCA_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  for (int b = 0; b < n_bufs; ++b)
+    if (!bufs_dev[b] || reinterpret_cast<uintptr_t>(bufs_dev[b]) % 16)
+      return fail(FCA_ERR_INVALID_ARG, "buffer %d is NULL or not 16-byte aligned", b);
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "compute-unit count");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  for (int j = 0; j < 2 && e == hipSuccess; ++j) e = timing_event(&ev[j]);
+  // one untimed pass over every buffer, then the timed ones
+  for (int b = 0; b < n_bufs && e == hipSuccess; ++b) e = launch_stream_read(bufs_dev[b], bytes, n_cu, s);
+  if (e == hipSuccess) e = hipEventRecord(ev[0], s);
+  for (int r = 0; r < repeats && e == hipSuccess; ++r)
+    for (int b = 0; b < n_bufs && e == hipSuccess; ++b) e = launch_stream_read(bufs_dev[b], bytes, n_cu, s);
+  if (e == hipSuccess) e = hipEventRecord(ev[1], s);
+  if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+  for (int j = 0; j < 2; ++j)
+    if (ev[j]) (void)hipEventDestroy(ev[j]);
+  if (e != hipSuccess) return hip_fail(e, "read probe");
+  *gbps = ms > 0.f ? (double)bytes * repeats * n_bufs / (ms * 1e-3) / 1e9 : 0.0;
   return FCA_OK;
 }
 

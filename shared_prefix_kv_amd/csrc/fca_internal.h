@@ -177,20 +177,33 @@ struct StatesParams {
 hipError_t launch_merge_states(const StatesParams& p, hipStream_t s);
 
 // Decode-token append (kv_append.hip).  Element strides as fca_attn_desc.
+// One launch handles up to kAppendLayers layers of one block table; the
+// table entries of copied blocks are rewritten by a separate commit launch
+// after every layer's copy has read them.
+constexpr int kAppendLayers = 32;
 struct AppendParams {
-  const uint16_t* k_new;  // [batch][num_kv_heads][head_dim_qk] bf16
-  const uint16_t* v_new;  // [batch][num_kv_heads][head_dim_v] bf16 (unused for latent caches)
-  uint16_t* k_cache;
-  uint16_t* v_cache;
-  int32_t* block_tables;
+  const uint16_t* k_new[kAppendLayers];  // [batch][num_kv_heads][head_dim_qk] bf16 per layer
+  const uint16_t* v_new[kAppendLayers];  // [batch][num_kv_heads][head_dim_v] bf16 (unused for latent caches)
+  uint16_t* k_cache[kAppendLayers];
+  uint16_t* v_cache[kAppendLayers];
+  int32_t n_layers;                      // layers of this launch
+  const int32_t* block_tables;           // read only here
   int64_t bt_row_stride;
   const int32_t* seq_lens;
   const int32_t* cow_dst;  // may be null
-  int32_t* status;         // may be null
   int64_t k_stride_block, k_stride_head, v_stride_block, v_stride_head;
   int32_t batch, num_kv_heads, max_blocks, num_blocks;
 };
 
+// Copies / in-place writes of every layer in p (block tables unchanged).
 hipError_t launch_append(const AppendParams& p, bool latent, hipStream_t s);
+// Points block_tables[i][L / bs] at cow_dst[i] where the append copied, and
+// ORs FCA_APPEND_BAD_* bits into *status for skipped requests.
+hipError_t launch_append_commit(int32_t* block_tables, int64_t bt_row_stride, const int32_t* seq_lens,
+                                const int32_t* cow_dst, int32_t* status, int batch, int max_blocks, int block_size,
+                                int num_blocks, hipStream_t s);
+
+// Streaming-read probe (measure.hip): reads `bytes` (multiple of 16) from src.
+hipError_t launch_stream_read(const void* src, size_t bytes, int n_cu, hipStream_t s);
 
 }  // namespace fca

@@ -17,14 +17,21 @@
 // none of them belongs to this request.  Slots after t of the target keep
 // what they held.
 //
-// One workgroup per request.  Blocks hold every KV head, so the copy moves
+// Several layers share one block table (each layer has its own pool, the
+// same block IDs): the copy of every layer reads the table entry as it was,
+// and one commit launch afterwards points the entry at the copy.  A layer
+// that read the entry after another layer had already rewritten it would
+// find source and target equal and skip its copy.
+//
+// One workgroup per (request, layer).  Blocks hold every KV head, so the copy moves
 // num_kv_heads key and value tiles in 16-byte pieces: a key piece is 8 dims
 // of one token, so slot t's pieces come from the new token and later ones are
 // skipped; a value piece is 8 tokens of one dim, and the one holding slot t
 // is merged from the source (slots before t), the new value (slot t) and the
 // target (slots after t).  Each target byte is written once.  Without a copy
 // only the new token's bytes are written.  Requests whose length or block
-// IDs are out of range are skipped and set a bit of *status.
+// IDs are out of range are skipped; the commit launch sets a bit of *status
+// for them.
 
 #include "fca_internal.h"
 
@@ -37,36 +44,52 @@ __device__ __forceinline__ void raise_status(int32_t* status, int bit) {
   if (status) atomicOr(status, bit);
 }
 
+// What request i does this step: the block of its new slot (cur), the copy
+// target (dst, -1 for none or when it is cur), the slot t; false when the
+// request is skipped (bit set in *why).
+__device__ __forceinline__ bool append_target(const int32_t* bt, int64_t stride, const int32_t* seq_lens,
+                                              const int32_t* cow_dst, int i, int max_blocks, int bs,
+                                              int num_blocks, int* cur, int* dst, int* t, int* why) {
+  const int L = seq_lens[i];
+  *why = 0;
+  if (L < 0 || L >= max_blocks * bs) {
+    *why = FCA_APPEND_BAD_LEN;
+    return false;
+  }
+  const int j = L / bs;
+  *t = L % bs;
+  *cur = bt[(int64_t)i * stride + j];
+  const int c = cow_dst ? cow_dst[i] : -1;
+  if (*cur < 0 || *cur >= num_blocks) {
+    *why = FCA_APPEND_BAD_BLOCK;
+    return false;
+  }
+  if (c >= num_blocks) {
+    *why = FCA_APPEND_BAD_COW;
+    return false;
+  }
+  *dst = (c >= 0 && c != *cur) ? c : -1;
+  return true;
+}
+
 template <int DQK, int DV, int BS, bool ALIAS>
 __device__ __forceinline__ void append_body(const AppendParams& p) {
   static_assert(DQK % 8 == 0 && DV % 8 == 0 && BS % 8 == 0, "16-byte pieces");
   constexpr int kKPieces = DQK / 8 * BS;            // key tile of one head: [DQK/8][BS][8]
   constexpr int kVPieces = ALIAS ? 0 : DV * BS / 8;  // value tile of one head: [DV][BS]
   const int i = blockIdx.x;
+  const int layer = blockIdx.y;
   const int tid = threadIdx.x;
-  const int L = p.seq_lens[i];
-  if (L < 0 || L >= p.max_blocks * BS) {
-    if (tid == 0) raise_status(p.status, FCA_APPEND_BAD_LEN);
+  int cur, dst, t, why;
+  if (!append_target(p.block_tables, p.bt_row_stride, p.seq_lens, p.cow_dst, i, p.max_blocks, BS, p.num_blocks, &cur,
+                     &dst, &t, &why))
     return;
-  }
-  const int j = L / BS, t = L % BS;
-  int32_t* entry = p.block_tables + (int64_t)i * p.bt_row_stride + j;
-  const int cur = *entry;
-  const int dst = p.cow_dst ? p.cow_dst[i] : -1;
-  // Every wave has read the table entry before thread 0 may replace it.
-  __syncthreads();
-  if (cur < 0 || cur >= p.num_blocks) {
-    if (tid == 0) raise_status(p.status, FCA_APPEND_BAD_BLOCK);
-    return;
-  }
-  if (dst >= p.num_blocks) {
-    if (tid == 0) raise_status(p.status, FCA_APPEND_BAD_COW);
-    return;
-  }
-  const uint16_t* kn = p.k_new + (int64_t)i * p.num_kv_heads * DQK;
-  const uint16_t* vn = ALIAS ? nullptr : p.v_new + (int64_t)i * p.num_kv_heads * DV;
+  const uint16_t* kn = p.k_new[layer] + (int64_t)i * p.num_kv_heads * DQK;
+  const uint16_t* vn = ALIAS ? nullptr : p.v_new[layer] + (int64_t)i * p.num_kv_heads * DV;
+  uint16_t* kc = p.k_cache[layer];
+  uint16_t* vc = ALIAS ? nullptr : p.v_cache[layer];
 
-  if (dst >= 0 && dst != cur) {
+  if (dst >= 0) {
     const int per_head = kKPieces + kVPieces;
     const int total = p.num_kv_heads * per_head;
     for (int c = tid; c < total; c += kAppendThreads) {
@@ -80,15 +103,15 @@ __device__ __forceinline__ void append_body(const AppendParams& p) {
         if (tok == t)
           piece = *reinterpret_cast<const uint4*>(kn + h * DQK + dc * 8);
         else
-          piece = *reinterpret_cast<const uint4*>(p.k_cache + (int64_t)cur * p.k_stride_block + off);
-        *reinterpret_cast<uint4*>(p.k_cache + (int64_t)dst * p.k_stride_block + off) = piece;
+          piece = *reinterpret_cast<const uint4*>(kc + (int64_t)cur * p.k_stride_block + off);
+        *reinterpret_cast<uint4*>(kc + (int64_t)dst * p.k_stride_block + off) = piece;
       } else if (!ALIAS) {
         const int rv = r - kKPieces;
         const int d = rv / (BS / 8), tok0 = (rv - d * (BS / 8)) * 8;
         if (tok0 > t) continue;
         const int64_t off = (int64_t)h * p.v_stride_head + (int64_t)rv * 8;
-        uint16_t* to = p.v_cache + (int64_t)dst * p.v_stride_block + off;
-        uint4 piece = *reinterpret_cast<const uint4*>(p.v_cache + (int64_t)cur * p.v_stride_block + off);
+        uint16_t* to = vc + (int64_t)dst * p.v_stride_block + off;
+        uint4 piece = *reinterpret_cast<const uint4*>(vc + (int64_t)cur * p.v_stride_block + off);
         if (t < tok0 + 8) {
           const uint4 old = *reinterpret_cast<const uint4*>(to);
           uint16_t e[8], o[8];
@@ -103,7 +126,6 @@ __device__ __forceinline__ void append_body(const AppendParams& p) {
         *reinterpret_cast<uint4*>(to) = piece;
       }
     }
-    if (tid == 0) *entry = dst;
     return;
   }
 
@@ -112,14 +134,13 @@ __device__ __forceinline__ void append_body(const AppendParams& p) {
   for (int c = tid; c < p.num_kv_heads * (DQK / 8); c += kAppendThreads) {
     const int h = c / (DQK / 8), dc = c - h * (DQK / 8);
     const uint4 piece = *reinterpret_cast<const uint4*>(kn + h * DQK + dc * 8);
-    *reinterpret_cast<uint4*>(p.k_cache + (int64_t)cur * p.k_stride_block + (int64_t)h * p.k_stride_head +
+    *reinterpret_cast<uint4*>(kc + (int64_t)cur * p.k_stride_block + (int64_t)h * p.k_stride_head +
                               ((int64_t)dc * BS + t) * 8) = piece;
   }
   if (!ALIAS) {
     for (int c = tid; c < p.num_kv_heads * DV; c += kAppendThreads) {
       const int h = c / DV, d = c - h * DV;
-      p.v_cache[(int64_t)cur * p.v_stride_block + (int64_t)h * p.v_stride_head + (int64_t)d * BS + t] =
-          vn[h * DV + d];
+      vc[(int64_t)cur * p.v_stride_block + (int64_t)h * p.v_stride_head + (int64_t)d * BS + t] = vn[h * DV + d];
     }
   }
 }
@@ -133,13 +154,37 @@ __global__ __launch_bounds__(kAppendThreads) void fca_kv_append_mla_kernel(Appen
   append_body<576, 512, 64, true>(p);
 }
 
+// One thread per request, after every layer's copy.
+__global__ __launch_bounds__(256) void fca_kv_append_commit_kernel(int32_t* block_tables, int64_t stride,
+                                                                   const int32_t* seq_lens, const int32_t* cow_dst,
+                                                                   int32_t* status, int batch, int max_blocks,
+                                                                   int bs, int num_blocks) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= batch) return;
+  int cur, dst, t, why;
+  if (!append_target(block_tables, stride, seq_lens, cow_dst, i, max_blocks, bs, num_blocks, &cur, &dst, &t, &why)) {
+    raise_status(status, why);
+    return;
+  }
+  if (dst >= 0) block_tables[(int64_t)i * stride + seq_lens[i] / bs] = dst;
+}
+
 hipError_t launch_append(const AppendParams& p, bool latent, hipStream_t s) {
-  if (p.batch == 0) return hipSuccess;
-  const dim3 grid((unsigned)p.batch);
+  if (p.batch == 0 || p.n_layers == 0) return hipSuccess;
+  const dim3 grid((unsigned)p.batch, (unsigned)p.n_layers);
   if (latent)
     hipLaunchKernelGGL(fca_kv_append_mla_kernel, grid, dim3(kAppendThreads), 0, s, p);
   else
     hipLaunchKernelGGL(fca_kv_append_gqa_kernel, grid, dim3(kAppendThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_commit(int32_t* block_tables, int64_t bt_row_stride, const int32_t* seq_lens,
+                                const int32_t* cow_dst, int32_t* status, int batch, int max_blocks, int block_size,
+                                int num_blocks, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(fca_kv_append_commit_kernel, dim3((batch + 255) / 256), dim3(256), 0, s, block_tables,
+                     bt_row_stride, seq_lens, cow_dst, status, batch, max_blocks, block_size, num_blocks);
   return hipGetLastError();
 }
 

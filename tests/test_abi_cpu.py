@@ -183,3 +183,31 @@ def test_struct_layouts_match_header(tmp_path):
         assert int(got[cname]) == ctypes.sizeof(py), cname
         for fname, _ in py._fields_:
             assert int(got[f"{cname}.{fname}"]) == getattr(py, fname).offset, (cname, fname)
+
+
+def test_layers_and_probe_validation_before_device():
+    """fca_decode_layers, fca_kv_append_layers and fca_measure_read_bandwidth
+    reject bad arguments without touching the device; zero layers or an empty
+    batch launch nothing."""
+    L = fca.lib()
+    ok = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1008)
+    assert L.fca_decode_layers(None, 1, None, None, None, None, None, None, 0, None) == 1  # no plan
+    d = fca.make_desc(32, 8, 128, 128, 16, 64, 0.088)
+    dp = ctypes.byref(d)
+    one = lambda p: (ctypes.c_void_p * 1)(p)
+    arr = one(ok)
+    assert L.fca_kv_append_layers(None, 1, arr, arr, arr, arr, ok, 4, 4, ok, None, None, 2, None) == 1  # no desc
+    assert L.fca_kv_append_layers(dp, -1, arr, arr, arr, arr, ok, 4, 4, ok, None, None, 2, None) == 1  # n < 0
+    assert L.fca_kv_append_layers(dp, 0, None, None, None, None, ok, 4, 4, ok, None, None, 2, None) == 0  # no layers
+    assert L.fca_kv_append_layers(dp, 1, None, arr, arr, arr, ok, 4, 4, ok, None, None, 2, None) == 1  # no k_new array
+    assert L.fca_kv_append_layers(dp, 1, one(None), arr, arr, arr, ok, 4, 4, ok, None, None, 2, None) == 1  # NULL entry
+    assert b"layer 0" in L.fca_last_error()
+    assert L.fca_kv_append_layers(dp, 1, arr, arr, one(odd), arr, ok, 4, 4, ok, None, None, 2, None) == 1  # misaligned
+    assert L.fca_kv_append_layers(dp, 1, arr, arr, arr, arr, ok, 4, 4, ok, None, None, 0, None) == 0  # empty batch
+    g = ctypes.c_double()
+    assert L.fca_measure_read_bandwidth(None, 1, 1 << 20, 1, None, ctypes.byref(g)) == 1
+    assert L.fca_measure_read_bandwidth(arr, 0, 1 << 20, 1, None, ctypes.byref(g)) == 1
+    assert L.fca_measure_read_bandwidth(arr, 1, 1000, 1, None, ctypes.byref(g)) == 1  # not a multiple of 16
+    assert L.fca_measure_read_bandwidth(one(odd), 1, 1 << 20, 1, None, ctypes.byref(g)) == 1
+    assert L.fca_measure_read_bandwidth(arr, 1, 1 << 20, 0, None, ctypes.byref(g)) == 1

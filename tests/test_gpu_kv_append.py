@@ -260,3 +260,75 @@ def test_append_graph_replays_match_eager_and_edge_targets():
         for snap in (eager[r], graphed[r]):
             assert (snap[0] == kk).all() and (snap[1] == vv).all() and (snap[2] == tt).all(), f"replay {r}"
     assert tt[4, 50 // bs] == tables[4, 50 // bs]
+
+
+@pytest.mark.parametrize("shape", [GQA, MLA], ids=["gqa", "mla"])
+def test_append_layers_share_one_table(shape):
+    """Three layers with their own pools and one block table (as the layers
+    of a model share the plan): fca_kv_append_layers over three decode steps
+    leaves every layer's pools and the table as the oracle's append of each
+    layer from the same table, and the decode of every layer over the grown
+    caches matches oracle attention.  Appending layer by layer with
+    fca_kv_append would rewrite the table after the first layer and leave
+    the later layers' copies without the request's earlier tokens."""
+    bs = shape.block_size
+    n_layers = 3
+    tables, lens, k0, v0, free = forked_case(shape, seed=31 + shape.head_dim_qk)
+    B = len(lens)
+    rng = np.random.default_rng(17)
+    nan_k = k0 == BF16_NAN
+    nan_v = None if v0 is None else v0 == BF16_NAN
+    ks, vs = [k0], [v0]
+    for _ in range(1, n_layers):  # same poisoned slots, new values
+        k = f32_to_bf16_bits(rng.standard_normal(k0.shape, dtype=np.float32))
+        k[nan_k] = BF16_NAN
+        ks.append(k)
+        if v0 is None:
+            vs.append(None)
+        else:
+            v = f32_to_bf16_bits(rng.standard_normal(v0.shape, dtype=np.float32))
+            v[nan_v] = BF16_NAN
+            vs.append(v)
+    kd = [to_device_bf16(k) for k in ks]
+    vd = [to_device_bf16(v) if v is not None else None for v in vs]
+    desc = fca.desc_from_shape(shape, k0.shape[0])
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for step in range(3):
+        tables, cow = choose_step(tables, lens, bs, free)
+        rows = [new_rows(rng, shape, B) for _ in range(n_layers)]
+        say("append layers", "mla" if shape.v_aliases_k else "gqa", "step", step, "cow", cow.tolist())
+        bt = torch.from_numpy(tables).cuda()
+        fca.kv_append_layers(
+            [to_device_bf16(r[0]) for r in rows],
+            [to_device_bf16(r[1]) if r[1] is not None else None for r in rows],
+            list(zip(kd, vd)),
+            bt,
+            torch.from_numpy(lens).cuda(),
+            desc,
+            cow_dst=torch.from_numpy(cow).cuda(),
+            status=status,
+        )
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        new_tables = None
+        for l in range(n_layers):
+            ks[l], vs[l], t_l = KV.append(ks[l], vs[l], tables, lens, rows[l][0], rows[l][1], bs, cow)
+            new_tables = t_l if new_tables is None else new_tables
+            assert (t_l == new_tables).all()
+            assert (to_bits(kd[l]) == ks[l]).all(), f"step {step} layer {l}: key pool differs"
+            if vs[l] is not None:
+                assert (to_bits(vd[l]) == vs[l]).all(), f"step {step} layer {l}: value pool differs"
+        tables = new_tables
+        assert (bt.cpu().numpy() == tables).all(), f"step {step}: block tables differ"
+        lens = lens + 1
+        p = fca.fca_plan(bt, torch.from_numpy(lens).cuda(), desc)
+        qs = [f32_to_bf16_bits(rng.standard_normal((B, shape.num_q_heads, shape.head_dim_qk), dtype=np.float32))
+              for _ in range(n_layers)]
+        outs = [torch.empty((B, shape.num_q_heads, shape.head_dim_v), dtype=torch.bfloat16, device="cuda")
+                for _ in range(n_layers)]
+        p.decode_layers([to_device_bf16(q) for q in qs], list(zip(kd, vd)), outs)
+        torch.cuda.synchronize()
+        for l in range(n_layers):
+            ref, _ = A.attend(qs[l], ks[l], vs[l], tables, lens, shape)
+            assert_close(bf16_tensor_to_f64(outs[l]), ref, f"step {step} layer {l}")
+        say("append layers step", step, "ok")

@@ -567,6 +567,63 @@ def test_decode_hip_graph_replay():
     say("graph replay: 4 replays equal to eager")
 
 
+@pytest.mark.parametrize("name", ["tiny", "llama3_8b"])
+def test_decode_layers_graph_replay_every_layer(name):
+    """One plan, four layers (their own KV pools and queries) decoded by one
+    fca_decode_layers call captured in a HIP graph: three replays with new
+    queries copied into the captured buffers, eager calls between them; each
+    replay equals the eager call bit for bit, and every layer of the last
+    replay matches the oracle."""
+    b = build_batch(CONFIGS[name])
+    sh = b.shape
+    n_layers = 4
+    say("decode layers", name, "layers", n_layers)
+    layers = [fill_values_torch(b, "cuda", seed=1000 + l, poison=True) for l in range(n_layers)]
+    hosts = [host_values(v) for v in layers]
+    caches = [(v["k"], v["v"]) for v in layers]
+    bt, sl = dev_tables(b)
+    p = fca.fca_plan(bt, sl, fca.desc_from_shape(sh, b.num_blocks))
+    shape_out = (b.batch, sh.num_q_heads, sh.head_dim_v)
+    q_static = [v["q"].clone() for v in layers]
+    outs_g = [torch.empty(shape_out, dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
+    lses_g = [torch.empty((b.batch, sh.num_q_heads), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    outs_e = [torch.empty_like(o) for o in outs_g]
+    lses_e = [torch.empty_like(l) for l in lses_g]
+    ws = p.decode_workspace(q_static[0].device)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        p.decode_layers(q_static, caches, outs_g, lses_g, workspace=ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        p.decode_layers(q_static, caches, outs_g, lses_g, workspace=ws)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    for rep in range(3):
+        q_new = [torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+                 for q in q_static]
+        for qs_, qn in zip(q_static, q_new):
+            qs_.copy_(qn)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ws_e = torch.empty_like(ws)
+        p.decode_layers(q_new, caches, outs_e, lses_e, workspace=ws_e)
+        torch.cuda.synchronize()
+        for l in range(n_layers):
+            assert torch.equal(outs_g[l].view(torch.int16), outs_e[l].view(torch.int16)), f"replay {rep} layer {l}"
+            assert torch.equal(lses_g[l], lses_e[l]), f"replay {rep} layer {l}: lse"
+    for l in range(n_layers):
+        host = dict(hosts[l], q=to_bits_np(q_static[l]))
+        ref, ref_lse = oracle_all(b, host)
+        rep = assert_close(bf16_tensor_to_f64(outs_g[l]), ref, f"{name} layer {l}")
+        assert_lse_close(lses_g[l].cpu().numpy(), ref_lse, f"{name} layer {l}")
+        say("decode layers", name, "layer", l, rep)
+    del graph, layers, caches
+
+
 def to_bits_np(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
