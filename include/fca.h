@@ -196,6 +196,27 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
                       void* out_dev, float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
+ * fca_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the partial (o, max, denominator) rows go to a
+ * scratch array that the library keeps in each device's memory (64 MiB per
+ * device, for the life of the process).  Same arguments, layout, results and
+ * launches as fca_decode, bit for bit.  The call allocates nothing (no
+ * hipMalloc, no host allocation of device memory) and does not record
+ * profiling events; its first call on a device looks up that device's
+ * scratch address once.
+ *
+ * Every call on one device shares that device's scratch and leaves its rows
+ * there: calls that may overlap on one device (other streams, other host
+ * threads) race and must be ordered by the caller.  The plan must have been
+ * made on the current device (FCA_ERR_INVALID_ARG otherwise).  A plan whose
+ * info.decode_workspace_bytes exceeds 64 MiB is rejected with
+ * FCA_ERR_WORKSPACE before anything is launched.
+ */
+fca_status fca_decode_no_alloc(fca_plan plan, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                               void* out_dev, float* lse_dev, void* stream);
+
+/*
  * The decode of several layers that share one batch and so one plan (the
  * plan is made once for each decode batch and serves every layer: "Core
  * Mechanism").  Layer l reads q_dev[l], k_caches_dev[l], v_caches_dev[l] and

@@ -42,6 +42,7 @@ EXPORTED = [
     "fca_plan_get_info",
     "fca_decode",
     "fca_decode_layers",
+    "fca_decode_no_alloc",
     "fca_plan_export",
     "fca_plan_export_schedule",
     "fca_plan_export_folded",
@@ -156,6 +157,7 @@ def lib():
         L.fca_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
         L.fca_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fca_decode_layers.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.fca_decode_no_alloc.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         L.fca_plan_export.argtypes = [vp, vp, vp, vp]
         L.fca_plan_export_schedule.argtypes = [vp, vp, vp, vp, vp]
         L.fca_plan_export_folded.argtypes = [vp, vp]
@@ -373,6 +375,29 @@ class Plan:
                 _ptr(ws),
                 ws.numel() * ws.element_size(),
                 _stream_ptr(stream),
+            )
+        )
+        return out
+
+    def decode_no_alloc(self, q, k_cache, v_cache, out, lse=None, stream=None):
+        """fca_decode_no_alloc: the decode with the partial rows in the
+        library's per-device static scratch (no workspace, no allocation;
+        calls on one device must not overlap).  ``out`` is required."""
+        import torch
+
+        d = self.desc
+        assert q.dtype == torch.bfloat16 and q.is_contiguous()
+        assert tuple(q.shape) == (self.batch, d.num_q_heads, d.head_dim_qk)
+        out_dtype = torch.float32 if d.flags & FCA_PLAN_OUT_F32 else torch.bfloat16
+        assert out.dtype == out_dtype and out.is_contiguous()
+        assert tuple(out.shape) == (self.batch, d.num_q_heads, d.head_dim_v)
+        if lse is not None:
+            assert lse.dtype == torch.float32 and lse.is_contiguous()
+            assert tuple(lse.shape) == (self.batch, d.num_q_heads)
+        _check_pool(d, k_cache, v_cache)
+        _check(
+            lib().fca_decode_no_alloc(
+                self._h, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _stream_ptr(stream)
             )
         )
         return out

@@ -993,6 +993,13 @@ fca_status fca_plan_get_info(fca_plan plan, fca_plan_info* info) {
 
 }  // extern "C"
 
+// Device scratch of fca_decode_no_alloc: the partial (o, max, denominator)
+// rows of one decode, for callers that cannot allocate.  One copy per
+// device, held until the process ends; its device address is looked up once
+// per device (the host-side name is not a device address).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 // Kernel arguments of one decode call: the attention launches' and the
@@ -1068,13 +1075,11 @@ void add_pass_time(const fca_plan_s* P, int k, double ms, fca_profile* acc) {
 // them from adding cache write-back to the launches they bracket.
 hipError_t timing_event(hipEvent_t* ev) { return hipEventCreateWithFlags(ev, hipEventDisableSystemFence); }
 
-}  // namespace
-
-extern "C" {
-
-fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
-                      void* out_dev, float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream) {
-  if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
+// One decode: the plan's attention launches, then the merge.  Profiling
+// events are recorded only when `profile` is set and the plan asks for them.
+fca_status decode_impl(fca_plan plan, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                       void* out_dev, float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream,
+                       bool profile) {
   const fca_plan_s* P = plan;
   if (P->B == 0) return FCA_OK;
   GqaParams gp;
@@ -1089,7 +1094,7 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   // two), then begin/end of the merge.
   constexpr int kProf = 7;
   hipEvent_t ev[kProf] = {};
-  if (P->profiling) {
+  if (profile && P->profiling) {
     for (int j = 0; j < kProf; ++j) {
       if (M->event_pool.empty()) {
         e = timing_event(&ev[j]);
@@ -1118,6 +1123,52 @@ fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev,
   FCA_TRY(mark(6), "event record");
 #undef FCA_TRY
   return FCA_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fca_status scratch_for_device(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(FCA_ERR_UNSUPPORTED, "device %d: scratch kept for %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "scratch address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fca_status fca_decode(fca_plan plan, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                      void* out_dev, float* lse_dev, void* workspace_dev, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
+  return decode_impl(plan, q_dev, k_cache_dev, v_cache_dev, out_dev, lse_dev, workspace_dev, workspace_bytes, stream,
+                     true);
+}
+
+fca_status fca_decode_no_alloc(fca_plan plan, const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                               void* out_dev, float* lse_dev, void* stream) {
+  if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
+  const fca_plan_s* P = plan;
+  if (P->B == 0) return FCA_OK;
+  if (P->info.decode_workspace_bytes > kScratchBytes)
+    return fail(FCA_ERR_WORKSPACE, "decode needs %zu bytes of scratch, the static scratch holds %zu",
+                P->info.decode_workspace_bytes, kScratchBytes);
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "current device");
+  if (dev != P->dev) return fail(FCA_ERR_INVALID_ARG, "plan was made on device %d, device %d is current", P->dev, dev);
+  void* ws = nullptr;
+  const fca_status st = scratch_for_device(dev, &ws);
+  if (st != FCA_OK) return st;
+  return decode_impl(plan, q_dev, k_cache_dev, v_cache_dev, out_dev, lse_dev, ws, kScratchBytes, stream, false);
 }
 
 fca_status fca_decode_layers(fca_plan plan, int32_t n_layers, const void* const* q_dev, const void* const* k_caches_dev,

@@ -107,6 +107,7 @@ def test_create_rejects_bad_args_before_device():
 def test_decode_and_info_reject_null_plan():
     L = fca.lib()
     assert L.fca_decode(None, None, None, None, None, None, None, 0, None) == 1
+    assert L.fca_decode_no_alloc(None, None, None, None, None, None, None) == 1
     info = fca.PlanInfo()
     assert L.fca_plan_get_info(None, ctypes.byref(info)) == 1
     assert L.fca_plan_export(None, None, None, None) == 1
