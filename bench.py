@@ -565,6 +565,7 @@ def main():
             "unique_kv_tokens": int(info.unique_tokens),
             "groups": int(info.num_groups),
             "kv_pools_cycled": args.layers,
+            "folded_groups": int(info.num_folded_groups),
         },
         "unique_kv_GBps": round(unique_gbps, 1),
         "unique_kv_frac_of_hbm_peak": round(unique_gbps / HBM_PEAK_GBPS, 4),
@@ -592,16 +593,21 @@ def main():
         result["separate_passes_ms_per_step"] = round(ms_sep, 5)
 
     if not args.profile_only and not sh.v_aliases_k:
-        # The activation heuristic (FCA_PLAN_AUTO_FOLD): groups that cannot pay
-        # for their partial rows are read per request.
-        plan_af = fca.fca_plan(bt, sl, fca.desc_from_shape(sh, batch.num_blocks, auto_fold=True))
-        n_f = int(plan_af.info.num_folded_groups)
-        plan_af.decode_workspace(out.device)
-        warm(plan_af, qs, pools, out, lse, warmup, torch, fca)
-        ms_af, _ = time_steps(plan_af, qs, pools, out, lse, steps, torch, fca)
-        log(f"fca decode with the activation heuristic: {ms_af * 1000:.1f} us/step ({n_f} of {info.num_groups} groups folded)")
-        result["auto_fold"] = {"ms_per_step": round(ms_af, 5), "folded_groups": n_f, "groups": int(info.num_groups)}
-        del plan_af
+        # Every discovered group kept (FCA_PLAN_KEEP_GROUPS): the timed plan
+        # above runs the library's default activation heuristic, which reads
+        # groups that cannot pay for their partial rows per request.
+        plan_kg = fca.fca_plan(bt, sl, fca.desc_from_shape(sh, batch.num_blocks, auto_fold=False))
+        plan_kg.decode_workspace(out.device)
+        warm(plan_kg, qs, pools, out, lse, warmup, torch, fca)
+        ms_kg, _ = time_steps(plan_kg, qs, pools, out, lse, steps, torch, fca)
+        n_f = int(info.num_folded_groups)
+        log(f"fca decode keeping every group: {ms_kg * 1000:.1f} us/step (default plan: {n_f} of {info.num_groups} groups folded)")
+        result["activation"] = {
+            "folded_groups": n_f,
+            "groups": int(info.num_groups),
+            "keep_groups_ms_per_step": round(ms_kg, 5),
+        }
+        del plan_kg
 
     if not args.no_noncascade and not args.profile_only:
         desc_nc = fca.desc_from_shape(sh, batch.num_blocks, cascade=False)

@@ -57,17 +57,23 @@ typedef enum fca_status {
                                        launch of persistent workgroups runs
                                        the work items of both passes (GQA);
                                        latent caches always use two. */
-#define FCA_PLAN_AUTO_FOLD 8u       /* activation heuristic (GQA caches):
-                                       a group whose shared blocks would
-                                       save fewer bytes than its partial
-                                       rows cost to write and merge is
-                                       read per request instead (folded
-                                       into its members' suffixes); groups
-                                       are folded from the leaves up.
-                                       Latent caches keep every group (their
-                                       passes are bound by the matrix
-                                       products, which a fold leaves
+#define FCA_PLAN_AUTO_FOLD 8u       /* activation heuristic (GQA caches),
+                                       on by default (this bit is accepted
+                                       and changes nothing): a group whose
+                                       shared blocks would save fewer bytes
+                                       than its partial rows cost to write
+                                       and merge is read per request instead
+                                       (folded into its members' suffixes);
+                                       groups are folded from the leaves up.
+                                       When every group folds, the plan is
+                                       the non-cascade one (the cascade is
+                                       bypassed).  Latent caches keep every
+                                       group (their passes are bound by the
+                                       matrix products, which a fold leaves
                                        unchanged). */
+#define FCA_PLAN_KEEP_GROUPS 16u    /* no activation heuristic: every
+                                       discovered group is read once for all
+                                       its members */
 #define FCA_PLAN_OUT_F32 4u         /* fca_decode writes `out` as float32
                                        (an attention state that
                                        fca_merge_states can combine without
@@ -352,8 +358,9 @@ fca_status fca_time_launches(fca_plan plan, const void* q_dev, const void* const
  * n_bufs buffers (device, 16-byte aligned, `bytes` each, a positive multiple
  * of 16; bytes well above the 256 MB last-level cache) is read once untimed,
  * then repeats * n_bufs reads cycling over the buffers run back to back
- * between two HIP events on `stream`; *gbps = bytes read / elapsed time
- * (1e9 bytes per second).  Nothing is written.  Blocks the host until the
+ * between two HIP events on `stream`, for each of two launch shapes of the
+ * kernel; *gbps = bytes read / elapsed time of the faster shape (1e9 bytes
+ * per second).  Nothing is written.  Blocks the host until the
  * reads finish.  FCA_ERR_INVALID_ARG for NULL or misaligned pointers or bad
  * sizes, FCA_ERR_HIP if a launch or event call fails.
  */

@@ -30,7 +30,8 @@ STATUS_NAMES = {
 FCA_PLAN_DISABLE_CASCADE = 1
 FCA_PLAN_SEPARATE_PASSES = 2
 FCA_PLAN_OUT_F32 = 4
-FCA_PLAN_AUTO_FOLD = 8
+FCA_PLAN_AUTO_FOLD = 8  # the default; accepted, no effect
+FCA_PLAN_KEEP_GROUPS = 16
 FCA_MERGE_OUT_F32 = 1
 FCA_APPEND_BAD_LEN = 1
 FCA_APPEND_BAD_BLOCK = 2
@@ -198,9 +199,12 @@ def make_desc(
     v_strides=None,
     separate_passes=False,
     out_f32=False,
-    auto_fold=False,
+    auto_fold=True,
 ) -> AttnDesc:
-    """Descriptor for the documented cache layout (default: dense pools)."""
+    """Descriptor for the documented cache layout (default: dense pools).
+    ``auto_fold=False`` keeps every discovered group (FCA_PLAN_KEEP_GROUPS);
+    by default the library folds groups that cannot pay for their partial
+    rows (GQA caches)."""
     d = AttnDesc()
     d.num_q_heads, d.num_kv_heads = num_q_heads, num_kv_heads
     d.head_dim_qk, d.head_dim_v = head_dim_qk, head_dim_v
@@ -218,13 +222,13 @@ def make_desc(
         (0 if cascade else FCA_PLAN_DISABLE_CASCADE)
         | (FCA_PLAN_SEPARATE_PASSES if separate_passes else 0)
         | (FCA_PLAN_OUT_F32 if out_f32 else 0)
-        | (FCA_PLAN_AUTO_FOLD if auto_fold else 0)
+        | (0 if auto_fold else FCA_PLAN_KEEP_GROUPS)
     )
     d.reserved = 0
     return d
 
 
-def desc_from_shape(shape, num_blocks, cascade=True, separate_passes=False, out_f32=False, auto_fold=False) -> AttnDesc:
+def desc_from_shape(shape, num_blocks, cascade=True, separate_passes=False, out_f32=False, auto_fold=True) -> AttnDesc:
     return make_desc(
         shape.num_q_heads,
         shape.num_kv_heads,

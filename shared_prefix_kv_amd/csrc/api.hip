@@ -81,7 +81,8 @@ fca_status check_desc(const fca_attn_desc* d, Kind* kind) {
                 d->num_q_heads, d->num_kv_heads);
   if (d->num_blocks <= 0) return fail(FCA_ERR_INVALID_ARG, "num_blocks must be positive");
   if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return fail(FCA_ERR_INVALID_ARG, "scale must be finite and > 0");
-  if (d->flags & ~(FCA_PLAN_DISABLE_CASCADE | FCA_PLAN_SEPARATE_PASSES | FCA_PLAN_OUT_F32 | FCA_PLAN_AUTO_FOLD))
+  if (d->flags & ~(FCA_PLAN_DISABLE_CASCADE | FCA_PLAN_SEPARATE_PASSES | FCA_PLAN_OUT_F32 | FCA_PLAN_AUTO_FOLD |
+                   FCA_PLAN_KEEP_GROUPS))
     return fail(FCA_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
   const int r = d->num_q_heads / d->num_kv_heads;
   if (d->head_dim_qk == 128 && d->head_dim_v == 128 && d->block_size == 16 && !d->v_aliases_k) {
@@ -473,8 +474,9 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
     P->members.insert(P->members.end(), m.begin(), m.end());
   }
 
-  // Activation (FCA_PLAN_AUTO_FOLD, GQA caches): a group is read once for
-  // all members only if that saves more bytes than its partial rows cost.
+  // Activation (GQA caches, unless FCA_PLAN_KEEP_GROUPS): a group is read
+  // once for all members only if that saves more bytes than its partial
+  // rows cost.
   // Reading a group of n members over T tokens once instead of n times
   // saves (n - 1) T t bytes (t: KV bytes per token); in exchange, each of
   // its token pieces writes n Hq partial rows that the merge reads back, and
@@ -486,7 +488,7 @@ static fca_status build_plan(fca_plan_s* P, const std::vector<int32_t>& rb, int 
   int n_folded = 0;
   std::vector<int> eff_deep(deepest_c);
   std::vector<int> eff_sb(sfxb, sfxb + B);
-  if ((P->desc.flags & FCA_PLAN_AUTO_FOLD) && P->kind == kGqa && G > 0) {
+  if (!(P->desc.flags & FCA_PLAN_KEEP_GROUPS) && P->kind == kGqa && G > 0) {
     const Tuning tf = tuning();
     const double tok_bytes = (double)hkv * (P->desc.head_dim_qk + P->desc.head_dim_v) * 2;
     double unique_tok = 0;
@@ -1378,15 +1380,20 @@ fca_status fca_measure_read_bandwidth(const void* const* bufs_dev, int32_t n_buf
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t ev[2] = {nullptr, nullptr};
   for (int j = 0; j < 2 && e == hipSuccess; ++j) e = timing_event(&ev[j]);
-  // one untimed pass over every buffer, then the timed ones
-  for (int b = 0; b < n_bufs && e == hipSuccess; ++b) e = launch_stream_read(bufs_dev[b], bytes, n_cu, s);
-  if (e == hipSuccess) e = hipEventRecord(ev[0], s);
-  for (int r = 0; r < repeats && e == hipSuccess; ++r)
-    for (int b = 0; b < n_bufs && e == hipSuccess; ++b) e = launch_stream_read(bufs_dev[b], bytes, n_cu, s);
-  if (e == hipSuccess) e = hipEventRecord(ev[1], s);
-  if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+  // Each launch shape: one untimed pass over every buffer, then the timed
+  // ones; the faster shape is reported.
   float ms = 0.f;
-  if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+  for (int shape = 0; shape < kReadShapes && e == hipSuccess; ++shape) {
+    for (int b = 0; b < n_bufs && e == hipSuccess; ++b) e = launch_stream_read(bufs_dev[b], bytes, n_cu, shape, s);
+    if (e == hipSuccess) e = hipEventRecord(ev[0], s);
+    for (int r = 0; r < repeats && e == hipSuccess; ++r)
+      for (int b = 0; b < n_bufs && e == hipSuccess; ++b) e = launch_stream_read(bufs_dev[b], bytes, n_cu, shape, s);
+    if (e == hipSuccess) e = hipEventRecord(ev[1], s);
+    if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, ev[0], ev[1]);
+    if (e == hipSuccess && t > 0.f && (ms == 0.f || t < ms)) ms = t;
+  }
   for (int j = 0; j < 2; ++j)
     if (ev[j]) (void)hipEventDestroy(ev[j]);
   if (e != hipSuccess) return hip_fail(e, "read probe");

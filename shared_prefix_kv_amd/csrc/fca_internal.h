@@ -203,7 +203,9 @@ hipError_t launch_append_commit(int32_t* block_tables, int64_t bt_row_stride, co
                                 const int32_t* cow_dst, int32_t* status, int batch, int max_blocks, int block_size,
                                 int num_blocks, hipStream_t s);
 
-// Streaming-read probe (measure.hip): reads `bytes` (multiple of 16) from src.
-hipError_t launch_stream_read(const void* src, size_t bytes, int n_cu, hipStream_t s);
+// Streaming-read probe (measure.hip): reads `bytes` (multiple of 16) from src
+// with launch shape 0 (512 threads x 4 loads) or 1 (256 threads x 8 loads).
+constexpr int kReadShapes = 2;
+hipError_t launch_stream_read(const void* src, size_t bytes, int n_cu, int shape, hipStream_t s);
 
 }  // namespace fca

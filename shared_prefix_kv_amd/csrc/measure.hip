@@ -19,18 +19,21 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kReadThreads = 512;
-
-__global__ __launch_bounds__(kReadThreads) void fca_stream_read_kernel(const u32x4* __restrict__ src, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * kReadThreads;
-  int64_t i = (int64_t)blockIdx.x * kReadThreads + threadIdx.x;
+// Each thread keeps U 16-byte loads in flight per iteration.  Measured on
+// MI355X over 2 GiB buffers, one workgroup per compute unit read fastest
+// (6.3-7.2 TB/s) with 512 threads x 4 loads or 256 threads x 8 loads; more
+// workgroups per unit, or plain (temporal) loads, were 5-15 % slower.
+template <int THREADS, int U>
+__global__ __launch_bounds__(THREADS) void fca_stream_read_kernel(const u32x4* __restrict__ src, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * THREADS;
+  int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = __builtin_nontemporal_load(src + i);
-    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += stride) {
     const u32x4 a = __builtin_nontemporal_load(src + i);
@@ -41,12 +44,15 @@ __global__ __launch_bounds__(kReadThreads) void fca_stream_read_kernel(const u32
 
 }  // namespace
 
-hipError_t launch_stream_read(const void* src, size_t bytes, int n_cu, hipStream_t s) {
+hipError_t launch_stream_read(const void* src, size_t bytes, int n_cu, int shape, hipStream_t s) {
   const int64_t n16 = (int64_t)(bytes / 16);
   if (n16 == 0) return hipSuccess;
-  const int grid = std::max(1, n_cu * 4);
-  hipLaunchKernelGGL(fca_stream_read_kernel, dim3(grid), dim3(kReadThreads), 0, s,
-                     static_cast<const u32x4*>(src), n16);
+  const int grid = std::max(1, n_cu);
+  const u32x4* p = static_cast<const u32x4*>(src);
+  if (shape == 0)
+    hipLaunchKernelGGL((fca_stream_read_kernel<512, 4>), dim3(grid), dim3(512), 0, s, p, n16);
+  else
+    hipLaunchKernelGGL((fca_stream_read_kernel<256, 8>), dim3(grid), dim3(256), 0, s, p, n16);
   return hipGetLastError();
 }
 

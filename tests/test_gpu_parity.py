@@ -52,9 +52,11 @@ def dev_tables(batch):
     )
 
 
-def plan_for(batch, cascade=True):
+def plan_for(batch, cascade=True, auto_fold=False):
+    """Plan of a batch; by default every discovered group is kept, so that
+    the export is the discovery itself."""
     bt, sl = dev_tables(batch)
-    desc = fca.desc_from_shape(batch.shape, batch.num_blocks, cascade=cascade)
+    desc = fca.desc_from_shape(batch.shape, batch.num_blocks, cascade=cascade, auto_fold=auto_fold)
     return fca.fca_plan(bt, sl, desc)
 
 
@@ -107,7 +109,7 @@ def test_plan_fuzz_forests():
         for width in [1, 3, 8, 70]:
             for alphabet in [1, 2, 3, 50]:
                 tables, lens = random_forest(rng, B, width, 16, alphabet)
-                desc = fca.desc_from_shape(shape, 64)
+                desc = fca.desc_from_shape(shape, 64, auto_fold=False)
                 p = fca.fca_plan(torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), desc)
                 got = with_block_ids(p.export(), tables)
                 exp = group(tables, lens, 16)
@@ -125,7 +127,7 @@ def test_plan_deep_chain_and_duplicates():
     lens = np.full(B, W * 16, np.int32)
     tables = np.concatenate([t, t[:5]])  # plus exact duplicates
     lens = np.concatenate([lens, lens[:5]])
-    desc = fca.desc_from_shape(AttnShape(4, 4, 128, 128, 16, 0.1), 10**6)
+    desc = fca.desc_from_shape(AttnShape(4, 4, 128, 128, 16, 0.1), 10**6, auto_fold=False)
     p = fca.fca_plan(torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), desc)
     assert with_block_ids(p.export(), tables) == group(tables, lens, 16)
     assert p.info.max_depth > 10
@@ -284,9 +286,10 @@ def check_schedule(b, p):
 # --------------------------------------------------------------- decode ----
 
 
-def run_decode(batch, vals, cascade=True, lse=True, separate=False, out_f32=False):
+def run_decode(batch, vals, cascade=True, lse=True, separate=False, out_f32=False, auto_fold=True):
     bt, sl = dev_tables(batch)
-    desc = fca.desc_from_shape(batch.shape, batch.num_blocks, cascade=cascade, separate_passes=separate, out_f32=out_f32)
+    desc = fca.desc_from_shape(batch.shape, batch.num_blocks, cascade=cascade, separate_passes=separate, out_f32=out_f32,
+                               auto_fold=auto_fold)
     p = fca.fca_plan(bt, sl, desc)
     dt = torch.float32 if out_f32 else torch.bfloat16
     out = torch.empty((batch.batch, batch.shape.num_q_heads, batch.shape.head_dim_v), dtype=dt, device="cuda")
@@ -296,17 +299,22 @@ def run_decode(batch, vals, cascade=True, lse=True, separate=False, out_f32=Fals
     return p, out, l
 
 
+# (cascade, activation heuristic): every group kept, the library's default
+# (groups that cannot pay are read per request), no cascade
+MODES = ((True, False), (True, True), (False, True))
+
+
 def upload(vals_np):
     return {k: (to_device_bf16(v) if v is not None else None) for k, v in vals_np.items()}
 
 
-@pytest.mark.parametrize("cascade", [True, False])
-def test_decode_tiny_full(cascade):
+@pytest.mark.parametrize("cascade,fold", MODES)
+def test_decode_tiny_full(cascade, fold):
     b = build_batch(CONFIGS["tiny"])
     vn = fill_values_numpy(b, poison=True)
-    say("decode tiny cascade", cascade)
+    say("decode tiny cascade", cascade, "fold", fold)
     ref, ref_lse = A.attend(vn["q"], vn["k"], vn["v"], b.block_tables, b.seq_lens, b.shape)
-    _, out, lse = run_decode(b, upload(vn), cascade=cascade)
+    _, out, lse = run_decode(b, upload(vn), cascade=cascade, auto_fold=fold)
     rep = assert_close(bf16_tensor_to_f64(out), ref, f"tiny cascade={cascade}")
     assert_lse_close(lse.cpu().numpy(), ref_lse, "tiny")
     say("tiny", rep)
@@ -410,9 +418,9 @@ def test_decode_edge_lengths_and_ratios(hq, hkv):
     ref, ref_lse = A.attend(case["q"], case["k"], case["v"], tables, lens, shape)
     b = _B(shape, tables, lens, nb)
     vals = upload(case)
-    for cascade in (True, False):
-        p, out, lse = run_decode(b, vals, cascade=cascade)
-        assert_close(bf16_tensor_to_f64(out), ref, f"edge hq={hq} hkv={hkv} cascade={cascade}")
+    for cascade, fold in MODES:
+        p, out, lse = run_decode(b, vals, cascade=cascade, auto_fold=fold)
+        assert_close(bf16_tensor_to_f64(out), ref, f"edge hq={hq} hkv={hkv} cascade={cascade} fold={fold}")
         assert_lse_close(lse.cpu().numpy(), ref_lse, "edge")
         o = bf16_tensor_to_f64(out)
         assert (o[0] == 0).all() and np.isneginf(lse[0].cpu().numpy()).all()
@@ -439,10 +447,10 @@ def test_decode_short_requests_precision(kind):
     case = small_case(shape, tables, lens, nb, seed=78)
     ref, ref_lse = A.attend(case["q"], case["k"], case["v"], tables, lens, shape)
     vals = upload(case)
-    for cascade in (True, False):
-        say("short requests", kind, "cascade", cascade)
-        _, out, lse = run_decode(_B(shape, tables, lens, nb), vals, cascade=cascade)
-        rep = assert_close(bf16_tensor_to_f64(out), ref, f"short requests {kind} cascade={cascade}")
+    for cascade, fold in MODES:
+        say("short requests", kind, "cascade", cascade, "fold", fold)
+        _, out, lse = run_decode(_B(shape, tables, lens, nb), vals, cascade=cascade, auto_fold=fold)
+        rep = assert_close(bf16_tensor_to_f64(out), ref, f"short requests {kind} cascade={cascade} fold={fold}")
         assert_lse_close(lse.cpu().numpy(), ref_lse, "short requests")
         say("short", kind, rep)
 
@@ -514,7 +522,7 @@ def test_decode_mla_small(hq, hkv):
     ref, ref_lse = A.attend(vn["q"], vn["k"], vn["v"], b.block_tables, b.seq_lens, shape)
     vals = upload(vn)
     for cascade in (True, False):
-        p, out, lse = run_decode(b, vals, cascade=cascade)
+        p, out, lse = run_decode(b, vals, cascade=cascade, auto_fold=False)
         rep = assert_close(bf16_tensor_to_f64(out), ref, f"mla small hq={hq} hkv={hkv} cascade={cascade}")
         assert_lse_close(lse.cpu().numpy(), ref_lse, "mla small")
         say("mla small", hq, hkv, "cascade", cascade, rep, "groups", p.info.num_groups)
@@ -530,7 +538,7 @@ def test_decode_hip_graph_replay():
     vn = fill_values_numpy(b, poison=True)
     vals = upload(vn)
     bt, sl = dev_tables(b)
-    p = fca.fca_plan(bt, sl, fca.desc_from_shape(b.shape, b.num_blocks))
+    p = fca.fca_plan(bt, sl, fca.desc_from_shape(b.shape, b.num_blocks, auto_fold=False))
     sh = b.shape
     q_static = vals["q"].clone()
     out_g = torch.empty((b.batch, sh.num_q_heads, sh.head_dim_v), dtype=torch.bfloat16, device="cuda")
@@ -896,6 +904,9 @@ def test_auto_fold_plan_schedule_and_decode(case):
         assert by_len[(0, 1)] == 1 and by_len[(0, 48)] == 0 and by_len[(0, 2)] == 0 and by_len[(2, 42)] == 0
     if case == "tiny":
         assert folded == [1]
+        # every group folded: the schedule is the non-cascade one (bypass)
+        nc = fca.fca_plan(bt, sl, fca.desc_from_shape(shape, nb, cascade=False)).export_schedule()
+        assert p.export_schedule() == nc
     if case == "llama3_8b":
         assert sum(folded) == 0
     check_schedule(b, p)
