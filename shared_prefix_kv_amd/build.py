@@ -2,8 +2,9 @@
 
     python -m shared_prefix_kv_amd.build
 
-Every .hip file under csrc/ is compiled to an object in _build/ and linked
-into shared_prefix_kv_amd/libfca.so.  Packed fp32 instructions are turned
+Every .hip file under csrc/ is compiled (hipcc, gfx950) and every .cpp file
+(host-only code, the planner) is compiled with the host compiler, to
+objects in _build/ that are linked into shared_prefix_kv_amd/libfca.so.  Packed fp32 instructions are turned
 off for device code (``-packed-fp32-ops``); hipcc's host pass warns that it
 does not know that feature, which is harmless.
 """
@@ -40,9 +41,16 @@ FLAGS = [
 ]
 
 
+HOST_CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wno-unused-parameter", "-I" + os.path.join(ROOT, "include")]
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [HOST_CXX, *HOST_FLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(
         line
@@ -50,7 +58,7 @@ def _compile(src: str, verbose: bool) -> str:
         if "packed-fp32-ops" not in line  # host-pass notice about the device-only feature
     )
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{out}")
+        raise RuntimeError(f"{cmd[0]} failed on {src}:\n{out}")
     if verbose and out.strip():
         print(out, file=sys.stderr)
     return obj
@@ -59,7 +67,7 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libfca.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"

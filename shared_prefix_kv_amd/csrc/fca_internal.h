@@ -7,72 +7,9 @@
 #include <cstdint>
 
 #include "fca.h"
+#include "plan_types.h"
 
 namespace fca {
-
-constexpr int kMaxBatch = 8192;
-constexpr int kMaxTableWidth = 1 << 20;
-constexpr int kAttnLgWaves = 2;                 // log2 of the waves of an attention workgroup
-constexpr int kAttnWaves = 1 << kAttnLgWaves;   // waves that share one work item
-constexpr int kItemColsGqa = 64;                // query rows of one GQA work item at most
-
-// A unit of work of the grouped or per-request pass; same layout as the
-// public fca_work_item.
-struct WorkItem {
-  int32_t request;
-  int32_t tok_begin;
-  int32_t tok_end;
-  int32_t kv_head;
-  int32_t member_off;
-  int32_t ncols;
-  int32_t col0;
-  int32_t col1;
-  int32_t part_base;
-  int32_t kv_heads;  // KV heads the item covers: kv_head .. kv_head + kv_heads - 1
-  int32_t stripes;   // block stripes (the kernel derives them; exported for tests)
-  int32_t flags;     // kItemStream: tiles with one reader (non-temporal loads)
-};
-constexpr int32_t kItemStream = 1;
-static_assert(sizeof(WorkItem) == sizeof(fca_work_item), "work item layout");
-
-// Per-request data the merge reads.
-struct ReqMeta {
-  int32_t pos;         // position in the depth-first member order
-  int32_t deepest;     // canonical index of the deepest group, -1 if none
-  int32_t sfx_lane;    // first lane of the suffix (-1: no suffix tokens); the
-  int32_t sfx_H;       //   lane of (kv head h, query row n) is
-  int32_t sfx_chunks;  //   sfx_lane + (h / sfx_H) * sfx_chunks + n / item_cols
-  int32_t pad0, pad1, pad2;
-};
-
-// Per-group data the merge reads (canonical order).
-struct GroupMeta {
-  int32_t parent;  // canonical index or -1
-  int32_t r0;      // first position of the group's members in `perm`
-  int32_t ncols;   // members * (Hq / Hkv)
-  int32_t lane0;   // lane of (head block 0, column chunk 0)
-  int32_t H;       // KV heads per lane; lane of (kv head h, column n) is
-  int32_t chunks;  //   lane0 + (h / H) * chunks + n / item_cols
-  int32_t pad0, pad1;
-};
-
-// One (unit, head block, column chunk) stream of a pass and its partial
-// rows: token split s, KV head h, column n is row
-//   base + s * H * ccols + (h - kv0) * ccols + (n - col0).
-struct LaneMeta {
-  int32_t base;
-  int32_t splits;
-  int32_t kv0;
-  int32_t H;
-  int32_t col0;
-  int32_t ccols;
-  int32_t pad0, pad1;
-};
-
-// Discovery header words.
-enum { kHdrGroups = 0, kHdrErr = 1, kHdrBadReq = 2, kHdrWords = 64 };
-enum { kErrBadBlock = 1, kErrBadLen = 2 };
-constexpr int kRecordInts = 8;  // leader, depth, parent gid, begin, end, count, 0, 0
 
 // Device arrays of the discovery step (all inside the plan workspace).
 struct DiscoveryPtrs {
@@ -105,19 +42,6 @@ struct PartialPtrs {
   float* m;
   float* l;
 };
-
-// What a persistent attention workgroup needs first, in one 128-byte line:
-// its range of items, the first item, and the block IDs of that item's
-// first four blocks (each wave's first tile), so that the first copies go
-// out after a single memory round trip.
-struct BinHead {
-  int32_t i_begin, i_end;  // items of the bin: [i_begin, i_end) of the item array
-  int32_t id[4];           // block IDs of blocks 0..3 of the first item (0 past its end)
-  int32_t pad0, pad1;
-  WorkItem first;          // item i_begin
-  int32_t pad2[12];
-};
-static_assert(sizeof(BinHead) == 128, "bin head layout");
 
 // Fills id[] of every bin head from the block-table copy (plan time).
 hipError_t launch_bin_heads(BinHead* heads, int n_bins, const int32_t* bt, int W, int bs, hipStream_t s);

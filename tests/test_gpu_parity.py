@@ -11,6 +11,8 @@ import pytest
 
 from oracle import attention as A
 from oracle.grouping import group
+from tests.forests import random_forest
+from tests.schedule_check import check_schedule_data
 from tests.helpers import (
     assert_close,
     assert_close_f32,
@@ -81,24 +83,6 @@ def test_plan_matches_oracle(name):
     assert p.info.unique_tokens == sum((g["block_end"] - g["block_begin"]) * b.shape.block_size for g in got["groups"]) + sum(r[1] for r in got["requests"])
     pn = plan_for(b, cascade=False)
     assert with_block_ids(pn.export(), b.block_tables) == group(b.block_tables, b.seq_lens, b.shape.block_size, cascade=False)
-
-
-def random_forest(rng, B, width, bs, alphabet):
-    rows = []
-    for i in range(B):
-        if rows and rng.random() < 0.6:
-            base = rows[int(rng.integers(0, len(rows)))]
-            cut = int(rng.integers(0, width + 1))
-            row = list(base[:cut]) + list(rng.integers(0, alphabet, size=width - cut))
-        else:
-            row = list(rng.integers(0, alphabet, size=width))
-        rows.append(row)
-    tables = np.array(rows, dtype=np.int32).reshape(B, width)
-    lens = rng.integers(0, width * bs + 1, size=B).astype(np.int32)
-    for i in range(B):
-        nb = -(-int(lens[i]) // bs)
-        tables[i, nb:] = rng.integers(-(2**31), 2**31, size=width - nb, dtype=np.int64).astype(np.int32)
-    return tables, lens
 
 
 def test_plan_fuzz_forests():
@@ -176,111 +160,7 @@ def test_schedule_covers_each_token_once(name):
 
 
 def check_schedule(b, p):
-    sh = b.shape
-    r = sh.gqa_ratio
-    hkv = sh.num_kv_heads
-    bs = sh.block_size
-    ex = p.export()
-    sc = p.export_schedule()
-    nrows = p.info.num_partial_rows
-    written = np.zeros(nrows, dtype=np.int64)
-    row_info = {}  # row -> (unit key, kv head, column, tok_begin, tok_end, stripe, stripes)
-
-    def record(it, key):
-        # The item's waves are kv_heads heads x C column groups (2 above 32
-        # rows) x S block stripes; stripe t of head h writes row
-        # part_base + (t * kv_heads + h - kv_head) * w + n - col0.
-        assert it["tok_begin"] < it["tok_end"]
-        assert 0 <= it["col0"] < it["col1"] <= it["ncols"] and it["col1"] - it["col0"] <= 64
-        assert it["kv_heads"] in (1, 2, 4, 8) and it["kv_head"] % it["kv_heads"] == 0
-        w = it["col1"] - it["col0"]
-        S = it["stripes"]
-        assert S >= 1 and S & (S - 1) == 0 and it["kv_heads"] * S <= 8
-        for t in range(S):
-            for h in range(it["kv_head"], it["kv_head"] + it["kv_heads"]):
-                for c in range(it["col0"], it["col1"]):
-                    row = it["part_base"] + (t * it["kv_heads"] + h - it["kv_head"]) * w + (c - it["col0"])
-                    assert 0 <= row < nrows
-                    written[row] += 1
-                    row_info[row] = (key, h, c, it["tok_begin"], it["tok_end"], t, S)
-
-    # grouped items: unit key (member_off, ncols); the group is the one whose
-    # member list holds the item's request and whose range and width match.
-    spans_g = {}
-    first_req = {}
-    for it in sc["grouped"]:
-        assert it["member_off"] >= 0
-        key = ("g", it["member_off"], it["ncols"])
-        first_req.setdefault(key, it["request"])
-        assert first_req[key] == it["request"]
-        record(it, key)
-        for h in range(it["kv_head"], it["kv_head"] + it["kv_heads"]):
-            for c in range(it["col0"], it["col1"]):
-                spans_g.setdefault(key, {}).setdefault((h, c), []).append((it["tok_begin"], it["tok_end"]))
-    kept = [k for k in range(len(ex["groups"])) if not ex["folded"][k]]
-    group_key = {}
-    for key, arr in spans_g.items():
-        assert len(arr) == hkv * key[2]
-        lo = min(s0 for v in arr.values() for s0, _ in v)
-        hi = max(s1 for v in arr.values() for _, s1 in v)
-        for v in arr.values():  # each (head, column) tiles the whole range once
-            v = sorted(v)
-            assert v[0][0] == lo and v[-1][1] == hi
-            assert all(x1 == y0 for (_, x1), (y0, _) in zip(v, v[1:]))
-        match = [k for k in kept
-                 if (ex["groups"][k]["block_begin"] * bs, ex["groups"][k]["block_end"] * bs,
-                     len(ex["groups"][k]["members"]) * r) == (lo, hi, key[2])
-                 and first_req[key] in ex["groups"][k]["members"]]
-        assert len(match) == 1
-        group_key[match[0]] = key
-    assert len(group_key) == len(kept)  # folded groups have no grouped work
-
-    # suffix items: each request's suffix tokens once per (head, column)
-    spans_s = {}
-    for it in sc["suffix"]:
-        assert it["member_off"] == -1 and 0 <= it["col0"] < it["col1"] <= r and it["ncols"] == r
-        key = ("s", it["request"])
-        record(it, key)
-        for h in range(it["kv_head"], it["kv_head"] + it["kv_heads"]):
-            for c in range(it["col0"], it["col1"]):
-                spans_s.setdefault((it["request"], h, c), []).append((it["tok_begin"], it["tok_end"]))
-    for i, (sb, st, _) in enumerate(ex["requests"]):
-        for h, c in ((h, c) for h in range(hkv) for c in range(r)):
-            v = sorted(spans_s.get((i, h, c), []))
-            assert sum(e - s0 for s0, e in v) == st
-            if st:
-                assert v[0][0] == sb * bs and v[-1][1] == int(b.seq_lens[i])
-                assert all(x1 == y0 for (_, x1), (y0, _) in zip(v, v[1:]))
-    assert (written == 1).all()
-
-    # merge sources
-    seen = np.zeros(nrows, dtype=np.int64)
-    for i, (sb, st, deepest) in enumerate(ex["requests"]):
-        path = []
-        g = deepest
-        while g >= 0:
-            path.append(group_key[g])
-            g = ex["groups"][g]["parent"]
-        if st:
-            path.append(("s", i))
-        for h in range(sh.num_q_heads):
-            rows = sc["sources"][i][h]
-            per_unit = {}
-            for row in rows:
-                seen[row] += 1
-                key, kvh, col, t0, t1, t, S = row_info[row]
-                assert kvh == h // r and col % r == h % r
-                per_unit.setdefault(key, []).append((col, t0, t1, t, S))
-            assert list(per_unit) == path  # deepest group first, suffix last
-            for key, v in per_unit.items():
-                assert len({x[0] for x in v}) == 1  # one column per unit
-                pieces = {}
-                for _, t0, t1, t, S in v:
-                    pieces.setdefault((t0, t1, S), set()).add(t)
-                assert all(len(ts) == S for (_, _, S), ts in pieces.items())  # every stripe of every piece
-                spans = sorted((t0, t1) for t0, t1, _ in pieces)
-                assert all(x1 == y0 for (_, x1), (y0, _) in zip(spans, spans[1:]))
-    assert (seen == 1).all()
+    check_schedule_data(b.shape, b.seq_lens, p.info.num_partial_rows, p.export(), p.export_schedule())
 
 
 # --------------------------------------------------------------- decode ----
