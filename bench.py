@@ -60,6 +60,11 @@ def parse():
     ap.add_argument("--no-noncascade", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="few steps, no baselines (for rocprofv3)")
     ap.add_argument(
+        "--no-cascade",
+        action="store_true",
+        help="time the non-cascade plan as the main one (to profile the baseline's launches)",
+    )
+    ap.add_argument(
         "--group-sweep",
         action="store_true",
         help="also time cascade vs non-cascade over group sizes 1..64 (64 requests, Llama-3 layer shape)",
@@ -230,8 +235,16 @@ def short_record(name, torch, fca, steps, warmup, layers=4):
     out = torch.empty((batch.batch, sh.num_q_heads, sh.head_dim_v), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((batch.batch, sh.num_q_heads), dtype=torch.float32, device="cuda")
     res = {}
+    desc = fca.desc_from_shape(sh, batch.num_blocks)
+    fca.fca_plan(bt, sl, desc)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        fca.fca_plan(bt, sl, desc)
+    torch.cuda.synchronize()
+    plan_ms = (time.perf_counter() - t0) * 1000 / 5
     for key, desc in (
-        ("fca", fca.desc_from_shape(sh, batch.num_blocks)),
+        ("fca", desc),
         ("non_cascade", fca.desc_from_shape(sh, batch.num_blocks, cascade=False)),
     ):
         plan = fca.fca_plan(bt, sl, desc)
@@ -251,6 +264,9 @@ def short_record(name, torch, fca, steps, warmup, layers=4):
         "unique_kv_GBps": round(int(info.unique_tokens) * tok_bytes / (ms / 1000.0) / 1e9, 1),
         "byte_ratio_R": round(int(info.logical_tokens) / max(int(info.unique_tokens), 1), 3),
         "speedup_vs_non_cascade": round(ms_nc / ms, 3),
+        "plan_ms": round(plan_ms, 3),
+        "plan_ms_per_layer_of_32": round(plan_ms / 32, 4),
+        "folded_groups": int(info.num_folded_groups),
     }
     del pools, qs
     torch.cuda.empty_cache()
@@ -394,7 +410,7 @@ def main():
 
     bt = torch.from_numpy(batch.block_tables).cuda()
     sl = torch.from_numpy(batch.seq_lens).cuda()
-    desc = fca.desc_from_shape(sh, batch.num_blocks)
+    desc = fca.desc_from_shape(sh, batch.num_blocks, cascade=not args.no_cascade)
     t0 = time.perf_counter()
     plan = fca.fca_plan(bt, sl, desc)
     torch.cuda.synchronize()
@@ -407,7 +423,9 @@ def main():
     info = plan.info
     # The same batch with the grouped and per-request passes launched one
     # after the other, for per-pass kernel times.
-    plan_sep = fca.fca_plan(bt, sl, fca.desc_from_shape(sh, batch.num_blocks, separate_passes=True))
+    plan_sep = fca.fca_plan(
+        bt, sl, fca.desc_from_shape(sh, batch.num_blocks, separate_passes=True, cascade=not args.no_cascade)
+    )
     sched = plan.export_schedule()
     pb = pass_bytes(batch, plan, sched)
     log(f"plan: {info.num_groups} groups, {info.num_grouped_items} grouped + {info.num_suffix_items} suffix items, {plan_ms:.2f} ms")
@@ -521,7 +539,7 @@ def main():
     # only while the library sources are the ones it was taken with.
     from shared_prefix_kv_amd.profiling import load_traffic
 
-    tr = load_traffic(cfg.name)
+    tr = load_traffic(cfg.name + (".non_cascade" if args.no_cascade else ""))
     if tr and dom_name == tr["kernel"] and dom_name in tr["traffic"]:
         t = tr["traffic"][dom_name]
         roofline["traffic"] = int(t["fetch_bytes"] + t["write_bytes"])
@@ -622,6 +640,18 @@ def main():
             "speedup_fca": round(ms_nc / ms, 3),
             "byte_ratio_R": round(logical / max(int(info.unique_tokens), 1), 3),
         }
+        # HBM bytes the non-cascade attention launch moves (committed counter
+        # summary of the same sources), against the logical KV bytes it reads:
+        # below 1 where the last-level cache serves repeated prefix blocks.
+        trn = load_traffic(cfg.name + ".non_cascade")
+        if trn and "fca_attention_kernel" in trn["traffic"]:
+            t = trn["traffic"]["fca_attention_kernel"]
+            logical_bytes = logical * pb["tok_bytes"] + batch.batch * sh.num_q_heads * sh.head_dim_qk * 2
+            result["non_cascade"]["traffic"] = int(t["fetch_bytes"] + t["write_bytes"])
+            result["non_cascade"]["traffic_over_logical_bytes"] = round(
+                (t["fetch_bytes"] + t["write_bytes"]) / logical_bytes, 4
+            )
+            result["non_cascade"]["attention_launch_us_profiled"] = round(trn["avg_launch_us"], 2)
         del plan_nc
 
     if not args.profile_only:

@@ -298,6 +298,10 @@ typedef struct fca_work_item {
  *   src_off [batch * num_q_heads + 1], src [num_merge_sources]
  * Query head h of request i merges the partial rows
  *   src[s], s in [src_off[i * num_q_heads + h], src_off[i * num_q_heads + h + 1]).
+ * src_off and src are copied from the tables the merge reads, which the
+ * plan builds on the device: asking for them waits for the plan's stream.
+ * num_merge_sources equals num_partial_rows (every row is read by exactly
+ * one (request, head)).
  */
 fca_status fca_plan_export_schedule(fca_plan plan, fca_work_item* grouped, fca_work_item* suffix,
                                     int32_t* src_off, int32_t* src);

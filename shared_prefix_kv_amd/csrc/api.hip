@@ -83,12 +83,15 @@ fca_status check_desc(const fca_attn_desc* d, Kind* kind) {
               d->head_dim_qk, d->head_dim_v, d->block_size, d->v_aliases_k);
 }
 
+constexpr int kStateArrays = 9;  // per-request discovery state (DiscoveryPtrs)
+
 // Caller-owned plan workspace: discovery read-back region, table copy and
 // discovery state.  Its size depends only on (batch, max_blocks).
 struct Layout {
   size_t header, lens, deepest, sfx_begin, records, readback_bytes;
   size_t bt, state;
   size_t total;
+  int W4;  // row stride of the table copy: the width rounded up to 4 (16-byte rows)
 };
 
 Layout make_layout(int B, int W) {
@@ -101,17 +104,19 @@ Layout make_layout(int B, int W) {
   L.records = L.sfx_begin + b * 4;
   L.readback_bytes = L.records + b * kRecordInts * 4 - L.header;
   size_t off = align_up(L.header + L.readback_bytes);
+  L.W4 = (W + 3) / 4 * 4;
   L.bt = off;
-  off = align_up(off + b * (size_t)W * 4);
+  off = align_up(off + b * (size_t)L.W4 * 4);
   L.state = off;
-  off = align_up(off + 11 * b * 4);
+  off = align_up(off + kStateArrays * b * 4);
   L.total = off;
   return L;
 }
 
 // Plan-owned device buffer holding the schedule.
 struct SchedLayout {
-  size_t items, heads, perm, src_off, src_row, total;
+  size_t items, heads, perm, req, grp, lanes, counter, upload;  // uploaded from the host: [0, upload)
+  size_t src_span, src_row, total;                              // merge tables, built on the device
 };
 
 
@@ -124,9 +129,8 @@ DiscoveryPtrs discovery_ptrs(char* ws, const Layout& L, int B) {
   p.records = reinterpret_cast<int32_t*>(ws + L.records);
   p.bt = reinterpret_cast<int32_t*>(ws + L.bt);
   int32_t* st = reinterpret_cast<int32_t*>(ws + L.state);
-  int32_t** arr[] = {&p.nfull,  &p.root,   &p.depth_at, &p.node, &p.gdepth, &p.gparent,
-                     &p.active, &p.ndstar, &p.ncount,   &p.ngid, &p.newnode};
-  for (int a = 0; a < 11; ++a) *arr[a] = st + (size_t)a * B;
+  int32_t** arr[] = {&p.nfull, &p.root, &p.depth_at, &p.node, &p.gdepth, &p.gparent, &p.active, &p.lcp0, &p.ngid};
+  for (int a = 0; a < kStateArrays; ++a) *arr[a] = st + (size_t)a * B;
   return p;
 }
 
@@ -333,7 +337,7 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool cascade = !(desc->flags & FCA_PLAN_DISABLE_CASCADE);
     DiscoveryPtrs dp = discovery_ptrs(P->ws, L, batch);
-    hipError_t e = launch_discovery(block_tables_dev, bt_row_stride, seq_lens_dev, batch, max_blocks,
+    hipError_t e = launch_discovery(block_tables_dev, bt_row_stride, seq_lens_dev, batch, max_blocks, L.W4,
                                     desc->block_size, desc->num_blocks, cascade, dp, s);
     if (e != hipSuccess) {
       delete P;
@@ -380,7 +384,8 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
       }
     }
     // Plan-owned device copy of the schedule, packed in the pinned staging
-    // buffer and uploaded with one copy.
+    // buffer and uploaded with one copy; the merge tables are then built on
+    // the device from the uploaded metadata.
     SchedLayout& S = P->SL;
     size_t off = 0;
     auto place = [&](size_t bytes) {
@@ -392,8 +397,13 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
     S.items = place(P->items.size() * sizeof(WorkItem));
     S.heads = place(n_heads * sizeof(BinHead));
     S.perm = place(P->perm.size() * 4);
-    S.src_off = place(P->src_off.size() * 4);
-    S.src_row = place(P->src_row.size() * 4);
+    S.req = place(P->req.size() * sizeof(ReqMeta));
+    S.grp = place(P->grp.size() * sizeof(GroupMeta));
+    S.lanes = place(P->lanes.size() * sizeof(LaneMeta));
+    S.counter = place(4);  // zero in the upload: the merge-table kernel's row counter
+    S.upload = off;
+    S.src_span = place((size_t)P->B * P->desc.num_q_heads * 8);
+    S.src_row = place((size_t)P->info.num_partial_rows * 4);
     S.total = off;
     P->dev = dev;
     P->stream = s;
@@ -412,12 +422,12 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
       }
       P->sched_cap = cap;
     }
-    e = stage_acquire(S.total, &stage);
+    e = stage_acquire(S.upload, &stage);
     if (e != hipSuccess) {
       delete P;
       return hip_fail(e, "schedule staging");
     }
-    std::memset(stage, 0, S.total);
+    std::memset(stage, 0, S.upload);
     std::memcpy(stage + S.items, P->items.data(), P->items.size() * sizeof(WorkItem));
     BinHead* heads = reinterpret_cast<BinHead*>(stage + S.heads);
     for (size_t b = 0; b < n_heads; ++b) {
@@ -426,19 +436,38 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
       heads[b].first = P->items[P->bins[b]];
     }
     std::memcpy(stage + S.perm, P->perm.data(), P->perm.size() * 4);
-    std::memcpy(stage + S.src_off, P->src_off.data(), P->src_off.size() * 4);
-    std::memcpy(stage + S.src_row, P->src_row.data(), P->src_row.size() * 4);
-    e = hipMemcpyAsync(P->sched, stage, S.total, hipMemcpyHostToDevice, s);
+    std::memcpy(stage + S.req, P->req.data(), P->req.size() * sizeof(ReqMeta));
+    std::memcpy(stage + S.grp, P->grp.data(), P->grp.size() * sizeof(GroupMeta));
+    std::memcpy(stage + S.lanes, P->lanes.data(), P->lanes.size() * sizeof(LaneMeta));
+    e = hipMemcpyAsync(P->sched, stage, S.upload, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = stage_in_use(s);
     if (e != hipSuccess) {
       delete P;
       return hip_fail(e, "schedule upload");
     }
     e = launch_bin_heads(reinterpret_cast<BinHead*>(P->sched + S.heads), (int)n_heads,
-                         reinterpret_cast<const int32_t*>(P->ws + P->L.bt), P->W, P->desc.block_size, s);
+                         reinterpret_cast<const int32_t*>(P->ws + P->L.bt), P->L.W4, P->desc.block_size, s);
     if (e != hipSuccess) {
       delete P;
       return hip_fail(e, "bin heads");
+    }
+    {
+      TableParams tp;
+      tp.req = reinterpret_cast<const ReqMeta*>(P->sched + S.req);
+      tp.grp = reinterpret_cast<const GroupMeta*>(P->sched + S.grp);
+      tp.lanes = reinterpret_cast<const LaneMeta*>(P->sched + S.lanes);
+      tp.B = P->B;
+      tp.Hq = P->desc.num_q_heads;
+      tp.r = P->r;
+      tp.item_cols = P->item_cols;
+      tp.src_span = reinterpret_cast<int2*>(P->sched + S.src_span);
+      tp.src_row = reinterpret_cast<int32_t*>(P->sched + S.src_row);
+      tp.total = reinterpret_cast<int32_t*>(P->sched + S.counter);
+      e = launch_merge_tables(tp, s);
+      if (e != hipSuccess) {
+        delete P;
+        return hip_fail(e, "merge tables");
+      }
     }
     *out = P;
     return FCA_OK;
@@ -498,7 +527,7 @@ fca_status decode_params(const fca_plan_s* P, const void* q_dev, const void* k_c
   const SchedLayout& S = P->SL;
   gp->perm = reinterpret_cast<const int32_t*>(P->sched + S.perm);
   gp->bt = reinterpret_cast<const int32_t*>(P->ws + L.bt);
-  gp->W = P->W;
+  gp->W = P->L.W4;
   gp->Hq = P->desc.num_q_heads;
   gp->r = P->r;
   gp->scale_log2 = P->desc.scale * 1.4426950408889634f;
@@ -513,7 +542,7 @@ fca_status decode_params(const fca_plan_s* P, const void* q_dev, const void* k_c
   gp->items = reinterpret_cast<const WorkItem*>(P->sched + S.items);
   gp->bins = nullptr;
 
-  mp->src_off = reinterpret_cast<const int32_t*>(P->sched + S.src_off);
+  mp->src_span = reinterpret_cast<const int2*>(P->sched + S.src_span);
   mp->src_row = reinterpret_cast<const int32_t*>(P->sched + S.src_row);
   mp->B = P->B;
   mp->Hq = P->desc.num_q_heads;
@@ -920,18 +949,28 @@ fca_status fca_plan_export_schedule(fca_plan plan, fca_work_item* grouped, fca_w
   const fca_plan_s* P = plan;
   if (grouped) std::memcpy(grouped, P->items_g.data(), P->items_g.size() * sizeof(WorkItem));
   if (suffix) std::memcpy(suffix, P->items_s.data(), P->items_s.size() * sizeof(WorkItem));
-  if (src_off || src) {
-    const int hq = P->desc.num_q_heads;
+  if ((src_off || src) && P->B > 0) {
+    // the merge tables as the device built them, in (request, head) order
+    const size_t pairs = (size_t)P->B * P->desc.num_q_heads;
+    std::vector<int2> span(pairs);
+    std::vector<int32_t> rows((size_t)P->info.num_partial_rows);
+    hipError_t e = hipMemcpyAsync(span.data(), P->sched + P->SL.src_span, pairs * sizeof(int2), hipMemcpyDeviceToHost,
+                                  P->stream);
+    if (e == hipSuccess && !rows.empty())
+      e = hipMemcpyAsync(rows.data(), P->sched + P->SL.src_row, rows.size() * 4, hipMemcpyDeviceToHost, P->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(P->stream);
+    if (e != hipSuccess) return hip_fail(e, "merge table read-back");
     int64_t n = 0;
-    for (int i = 0; i < P->B; ++i)
-      for (int h = 0; h < hq; ++h) {
-        if (src_off) src_off[(int64_t)i * hq + h] = (int32_t)n;
-        for_each_source(*P, i, h, [&](int64_t row) {
-          if (src) src[n] = (int32_t)row;
-          ++n;
-        });
-      }
-    if (src_off) src_off[(int64_t)P->B * hq] = (int32_t)n;
+    for (size_t q = 0; q < pairs; ++q) {
+      if (span[q].x < 0 || span[q].y < 0 || (size_t)span[q].x + span[q].y > rows.size())
+        return fail(FCA_ERR_HIP, "merge table entry %zu out of range", q);
+      if (src_off) src_off[q] = (int32_t)n;
+      if (src) std::memcpy(src + n, rows.data() + span[q].x, (size_t)span[q].y * 4);
+      n += span[q].y;
+    }
+    if (src_off) src_off[pairs] = (int32_t)n;
+  } else if (src_off) {
+    src_off[0] = 0;
   }
   return FCA_OK;
 }

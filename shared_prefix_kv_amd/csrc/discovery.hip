@@ -10,24 +10,38 @@
 //
 // Kernels:
 //   k_init_header  clears the counters and error flags.
-//   k_prepare      copies the used table entries into the plan workspace,
-//                  checks block IDs and lengths, initialises per-request state.
+//   k_prepare      copies the used table entries into the plan workspace
+//                  (rows padded to 16 bytes), checks block IDs and lengths,
+//                  initialises per-request state.
 //   k_roots        one wave per request: the smallest request index with the
 //                  same first block (the tree a request belongs to).
-//   k_trees        one workgroup per tree.  Refinement rounds: members of a
-//                  trie node are split by the block ID at the node's start;
-//                  each part takes its smallest index as leader; each member's
-//                  longest common prefix with the leader (wave-wide 64-entry
-//                  compares with a ballot) gives the part's common prefix
-//                  d* = min over members; a part with >= 2 members is a group
-//                  covering [start, d*); members with more full blocks carry
-//                  on from d*.  Work is O(sum of compared entries) plus an
-//                  O(n^2) leader search per round inside LDS.
+//   k_lcp0         one wave per request: its common prefix with its tree's
+//                  root (the leader of every tree's first round), for all
+//                  trees at once across the device.
+//   k_trees        one workgroup per tree, refinement rounds over the trie:
+//                  every active member sits at a node (the request that
+//                  leads it) and a depth; the members are sorted in LDS by
+//                  (node, block ID at the depth, request), so each part -- the
+//                  members of one node that continue with the same block -- is
+//                  a contiguous run led by its smallest request; binary
+//                  searches give every member its part's bounds.  For the
+//                  members of parts with two or more requests, the longest
+//                  common prefix with the leader's row is found by 16-lane
+//                  groups comparing 256 entries per round trip (4 rows of 16
+//                  bytes per lane in flight); the part's common prefix d* is
+//                  the minimum.  Such a part is a group covering [depth, d*);
+//                  members with more full blocks carry on from d*, the rest
+//                  end there.  Parts of one request end.  Work per round:
+//                  a sort of the active members (skipped when they form a
+//                  single part, as in every tree's first round, whose common
+//                  prefixes k_lcp0 has found) and the entries the common
+//                  prefixes cover.
 // Group IDs come from an atomic counter, so their numbering varies between
 // runs; the host sorts groups into the canonical (smallest member, depth)
 // order, which is unique.
 
 #include <climits>
+#include <cstdlib>
 
 #include "fca_internal.h"
 
@@ -40,13 +54,13 @@ __global__ void k_init_header(int32_t* header) {
 }
 
 __global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ bt_in, int64_t stride,
-                                                 const int32_t* __restrict__ lens_in, int B, int W, int bs,
+                                                 const int32_t* __restrict__ lens_in, int B, int W, int W4, int bs,
                                                  int num_blocks, DiscoveryPtrs p) {
-  const int64_t total = (int64_t)B * W;
+  const int64_t total = (int64_t)B * W4;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
-    const int i = (int)(idx / W);
-    const int j = (int)(idx - (int64_t)i * W);
+    const int i = (int)(idx / W4);
+    const int j = (int)(idx - (int64_t)i * W4);
     const int L = lens_in[i];
     const bool badlen = L < 0 || (int64_t)L > (int64_t)W * bs;
     const int Lc = badlen ? 0 : L;
@@ -75,16 +89,16 @@ __global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ bt_
   }
 }
 
-__global__ __launch_bounds__(256) void k_roots(int B, int W, DiscoveryPtrs p) {
+__global__ __launch_bounds__(256) void k_roots(int B, int W4, DiscoveryPtrs p) {
   const int i = (int)((blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= B) return;
   if (p.nfull[i] == 0) return;  // root stays -1: nothing to share
-  const int key = p.bt[(int64_t)i * W];
+  const int key = p.bt[(int64_t)i * W4];
   int found = i;
   for (int k0 = 0; k0 <= i; k0 += 64) {
     const int k = k0 + lane;
-    const bool hit = k <= i && p.nfull[k] > 0 && p.bt[(int64_t)k * W] == key;
+    const bool hit = k <= i && p.nfull[k] > 0 && p.bt[(int64_t)k * W4] == key;
     const unsigned long long mask = __ballot(hit);
     if (mask) {
       found = k0 + __ffsll((long long)mask) - 1;
@@ -94,30 +108,111 @@ __global__ __launch_bounds__(256) void k_roots(int B, int W, DiscoveryPtrs p) {
   if (lane == 0) p.root[i] = found;
 }
 
-constexpr int kTreeThreads = 1024;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W, DiscoveryPtrs p) {
+// Entries 1 .. cap of request k's row against its root's (entry 0 is equal
+// by the root's definition): 64 lanes x 4 loads x 4 entries per round trip.
+__global__ __launch_bounds__(256) void k_lcp0(int B, int W4, DiscoveryPtrs p) {
+  const int k = (int)((blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  if (k >= B) return;
+  const int rt = p.root[k];
+  if (rt < 0) return;
+  const int cap = min(p.nfull[k], p.nfull[rt]);
+  const int32_t* rk = p.bt + (int64_t)k * W4;
+  const int32_t* rr = p.bt + (int64_t)rt * W4;
+  int found = cap;
+  if (rt != k) {
+    for (int base = 0; base < cap; base += 1024) {
+      i32x4 va[4], vb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int pos = base + 4 * (64 * u + lane);
+        if (pos < cap) {
+          va[u] = *reinterpret_cast<const i32x4*>(rk + pos);
+          vb[u] = *reinterpret_cast<const i32x4*>(rr + pos);
+        }
+      }
+      int first = INT_MAX;
+#pragma unroll
+      for (int u = 3; u >= 0; --u) {
+        const int pos = base + 4 * (64 * u + lane);
+        if (pos < cap) {
+#pragma unroll
+          for (int e = 3; e >= 0; --e) {
+            const int q = pos + e;
+            if (q >= 1 && q < cap && va[u][e] != vb[u][e]) first = q;
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) first = min(first, __shfl_xor(first, m));
+      if (first != INT_MAX) {
+        found = first;
+        break;
+      }
+    }
+  }
+  if (lane == 0) p.lcp0[k] = found;
+}
+
+constexpr int kTreeThreads = 1024;
+constexpr int kTreeWaves = kTreeThreads / 64;
+constexpr int kIdxBits = 13;  // request index in a sort key (kMaxBatch = 8192)
+static_assert((1 << kIdxBits) >= kMaxBatch, "request index field");
+constexpr uint64_t kIdxMask = (1u << kIdxBits) - 1;
+
+// Sort key of an active member: node (13 bits), block ID at its depth (31
+// bits, validated non-negative), request (13 bits).  Ascending order puts the
+// members of one part together, smallest request first.
+__device__ __forceinline__ uint64_t part_key(int node, int block, int k) {
+  return ((uint64_t)node << (31 + kIdxBits)) | ((uint64_t)(uint32_t)block << kIdxBits) | (uint64_t)k;
+}
+
+// First position in [0, n) whose key's part bits are >= those of `part`
+// (keys sorted ascending).
+__device__ __forceinline__ int lower_part(const uint64_t* key, int n, uint64_t part) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((key[mid] >> kIdxBits) < part)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// LCP_LANES lanes compare one member's row, each with LCP_LOADS 16-byte
+// loads of both rows in flight: LCP_LANES * LCP_LOADS * 4 entries per round
+// trip, 1024 / LCP_LANES members at once.
+template <int LCP_LANES, int LCP_LOADS>
+__global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W4, DiscoveryPtrs p) {
+  constexpr int kLcpGroup = LCP_LANES;
+  constexpr int kGroups = 64 / LCP_LANES;  // members per wave
+  constexpr int kLcpSpan = LCP_LANES * LCP_LOADS * 4;
   const int i = blockIdx.x;
   if (p.root[i] != i) return;  // not a tree root (uniform over the workgroup)
 
-  __shared__ int mem[kMaxBatch];
-  __shared__ int snode[kMaxBatch];
-  __shared__ int skey[kMaxBatch];
-  __shared__ int n_mem;
-  __shared__ int any_active;
+  __shared__ uint64_t skey[kMaxBatch];  // active members; sorted keys during a round
+  __shared__ int16_t sbeg[kMaxBatch];   // part start (position) of each sorted member
+  __shared__ int16_t scnt[kMaxBatch];   // part size
+  __shared__ int32_t sdiff[kMaxBatch];  // common prefix with the part's leader; d* at the leader
+  __shared__ int n_act, n_next;
+  __shared__ unsigned long long kmin, kmax;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, nwaves = kTreeThreads / 64;
-  if (tid == 0) n_mem = 0;
+  const int wave = tid >> 6, lane = tid & 63;
+  if (tid == 0) n_act = 0;
   __syncthreads();
   for (int k = tid; k < B; k += kTreeThreads)
-    if (p.root[k] == i) mem[atomicAdd(&n_mem, 1)] = k;
+    if (p.root[k] == i) skey[atomicAdd(&n_act, 1)] = (uint64_t)k;
   __syncthreads();
-  const int nm = n_mem;
-  if (nm < 2) return;  // a lone request: no group, suffix from block 0
+  int n = n_act;
+  if (n < 2) return;  // a lone request: no group, suffix from block 0
 
-  for (int x = tid; x < nm; x += kTreeThreads) {
-    const int k = mem[x];
+  for (int x = tid; x < n; x += kTreeThreads) {
+    const int k = (int)skey[x];
     p.depth_at[k] = 0;
     p.node[k] = i;
     p.gdepth[k] = 0;
@@ -126,75 +221,150 @@ __global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W, DiscoveryP
   }
   __syncthreads();
 
-  for (;;) {
-    // Node and first block of every active member.
-    for (int x = tid; x < nm; x += kTreeThreads) {
-      const int k = mem[x];
-      if (p.active[k]) {
-        snode[x] = p.node[k];
-        skey[x] = p.bt[(int64_t)k * W + p.depth_at[k]];
-      } else {
-        snode[x] = -1;
+  for (bool first_round = true;; first_round = false) {
+    // Keys of the active members (skey holds their request indices).
+    if (tid == 0) {
+      kmin = ~0ull;
+      kmax = 0ull;
+      n_next = 0;
+    }
+    __syncthreads();
+    {
+      unsigned long long lo = ~0ull, hi = 0ull;
+      for (int x = tid; x < n; x += kTreeThreads) {
+        const int k = (int)(skey[x] & kIdxMask);
+        const uint64_t key = part_key(p.node[k], p.bt[(int64_t)k * W4 + p.depth_at[k]], k);
+        skey[x] = key;
+        lo = min(lo, (unsigned long long)key);
+        hi = max(hi, (unsigned long long)key);
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        lo = min(lo, (unsigned long long)__shfl_xor((long long)lo, m));
+        hi = max(hi, (unsigned long long)__shfl_xor((long long)hi, m));
+      }
+      if (lane == 0) {
+        atomicMin(&kmin, lo);
+        atomicMax(&kmax, hi);
       }
     }
     __syncthreads();
-    // Leader of each (node, first block) part: its smallest request index.
-    for (int x = tid; x < nm; x += kTreeThreads) {
-      const int nd = snode[x];
-      if (nd < 0) continue;
-      const int key = skey[x];
-      int best = INT_MAX;
-      for (int y = 0; y < nm; ++y)
-        if (snode[y] == nd && skey[y] == key) best = min(best, mem[y]);
-      p.newnode[mem[x]] = best;
+    const bool one_part = (kmin >> kIdxBits) == (kmax >> kIdxBits);
+    if (!one_part) {
+      // Bitonic sort of skey[0, N), padded with the largest key.
+      int N = 1;
+      while (N < n) N <<= 1;
+      for (int x = n + tid; x < N; x += kTreeThreads) skey[x] = ~0ull;
+      __syncthreads();
+      for (int size = 2; size <= N; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int t = tid; t < N / 2; t += kTreeThreads) {
+            const int a = 2 * t - (t & (stride - 1));
+            const int b = a + stride;
+            const bool up = (a & size) == 0;
+            const uint64_t ka = skey[a], kb = skey[b];
+            if ((ka > kb) == up) {
+              skey[a] = kb;
+              skey[b] = ka;
+            }
+          }
+          __syncthreads();
+        }
     }
-    __syncthreads();
-    for (int x = tid; x < nm; x += kTreeThreads) {
-      const int k = mem[x];
-      if (!p.active[k]) continue;
-      const int lead = p.newnode[k];
-      p.node[k] = lead;
-      if (lead == k) {
-        p.ndstar[k] = INT_MAX;
-        p.ncount[k] = 0;
-      }
-    }
-    __syncthreads();
-    // Longest common prefix with the leader, one wave per member.
-    for (int x = wave; x < nm; x += nwaves) {
-      const int k = mem[x];
-      if (!p.active[k]) continue;
-      const int lead = p.node[k];
-      const int d0 = p.depth_at[k];
-      int lcp;
-      if (lead == k) {
-        lcp = p.nfull[k];
+    // Part bounds.  One part: its leader is the smallest key (the members are
+    // not sorted then, so the leader is found by its key).
+    for (int x = tid; x < n; x += kTreeThreads) {
+      int b0, cnt;
+      if (one_part) {
+        b0 = -1;
+        cnt = n;
       } else {
-        const int cap = min(p.nfull[k], p.nfull[lead]);
-        const int32_t* rk = p.bt + (int64_t)k * W;
-        const int32_t* rl = p.bt + (int64_t)lead * W;
-        lcp = cap;
-        for (int j0 = d0; j0 < cap; j0 += 64) {
-          const int j = j0 + lane;
-          const bool diff = j < cap && rk[j] != rl[j];
-          const unsigned long long mask = __ballot(diff);
-          if (mask) {
-            lcp = j0 + __ffsll((long long)mask) - 1;
-            break;
+        const uint64_t part = skey[x] >> kIdxBits;
+        b0 = lower_part(skey, x + 1, part);
+        cnt = lower_part(skey, n, part + 1) - b0;
+      }
+      sbeg[x] = (int16_t)b0;
+      scnt[x] = (int16_t)cnt;
+      if (one_part && skey[x] == kmin) n_next = x;  // the leader's position (unique key)
+    }
+    __syncthreads();
+    const int lead_pos = n_next;  // valid when one_part
+    __syncthreads();
+    if (tid == 0) n_next = 0;
+    for (int x = tid; x < n; x += kTreeThreads) {
+      if (one_part) sbeg[x] = (int16_t)lead_pos;
+      const int k = (int)(skey[x] & kIdxMask);
+      const int lead = (int)(skey[one_part ? lead_pos : sbeg[x]] & kIdxMask);
+      // first round: the leader is the root and k_lcp0 has the prefixes
+      sdiff[x] = lead == k ? p.nfull[k] : first_round ? p.lcp0[k] : min(p.nfull[k], p.nfull[lead]);
+    }
+    __syncthreads();
+
+    // Longest common prefix of every member of a part of two or more with the
+    // part's leader, from its depth: groups of kLcpGroup lanes, kGroups
+    // members per wave.
+    if (!first_round) {
+      const int g = lane / kLcpGroup, gl = lane % kLcpGroup;
+      for (int x0 = kGroups * wave; x0 < n; x0 += kGroups * kTreeWaves) {
+        const int x = x0 + g;
+        bool busy = false;
+        int k = 0, lead = 0, d0 = 0, cap = 0, a0 = 0;
+        if (x < n && scnt[x] >= 2 && sbeg[x] != x) {
+          k = (int)(skey[x] & kIdxMask);
+          lead = (int)(skey[sbeg[x]] & kIdxMask);
+          d0 = p.depth_at[k] + 1;  // the block at the depth is the part's key
+          cap = sdiff[x];
+          a0 = d0 & ~3;
+          busy = d0 < cap;
+        }
+        const int32_t* rk = p.bt + (int64_t)k * W4;
+        const int32_t* rl = p.bt + (int64_t)lead * W4;
+        int found = INT_MAX;
+        for (int base = a0; __ballot(busy) != 0; base += kLcpSpan) {
+          if (busy) {
+            i32x4 va[LCP_LOADS], vb[LCP_LOADS];
+#pragma unroll
+            for (int u = 0; u < LCP_LOADS; ++u) {
+              const int pos = base + 4 * (kLcpGroup * u + gl);
+              if (pos < cap) {
+                va[u] = *reinterpret_cast<const i32x4*>(rk + pos);
+                vb[u] = *reinterpret_cast<const i32x4*>(rl + pos);
+              }
+            }
+            int first = INT_MAX;
+#pragma unroll
+            for (int u = LCP_LOADS - 1; u >= 0; --u) {
+              const int pos = base + 4 * (kLcpGroup * u + gl);
+              if (pos < cap) {
+#pragma unroll
+                for (int e = 3; e >= 0; --e) {
+                  const int q = pos + e;
+                  if (q >= d0 && q < cap && va[u][e] != vb[u][e]) first = q;
+                }
+              }
+            }
+            found = min(found, first);
+          }
+          // minimum over the lanes of the group
+#pragma unroll
+          for (int m = kLcpGroup / 2; m >= 1; m >>= 1) found = min(found, __shfl_xor(found, m));
+          if (busy && (found != INT_MAX || base + kLcpSpan >= cap)) {
+            if (gl == 0 && found != INT_MAX) sdiff[x] = found;
+            busy = false;
           }
         }
       }
-      if (lane == 0) {
-        atomicMin(&p.ndstar[lead], lcp);
-        atomicAdd(&p.ncount[lead], 1);
-      }
     }
     __syncthreads();
+    // Part common prefix d* = minimum over its members, kept at the leader.
+    for (int x = tid; x < n; x += kTreeThreads)
+      if (scnt[x] >= 2 && sbeg[x] != x) atomicMin(&sdiff[sbeg[x]], sdiff[x]);
+    __syncthreads();
     // Parts with two or more members become groups.
-    for (int x = tid; x < nm; x += kTreeThreads) {
-      const int k = mem[x];
-      if (!p.active[k] || p.node[k] != k) continue;
-      const int cnt = p.ncount[k];
+    for (int x = tid; x < n; x += kTreeThreads) {
+      if (sbeg[x] != x) continue;
+      const int k = (int)(skey[x] & kIdxMask);
+      const int cnt = scnt[x];
       if (cnt >= 2) {
         const int gid = atomicAdd(&p.header[kHdrGroups], 1);
         int32_t* rec = p.records + (int64_t)gid * kRecordInts;
@@ -202,7 +372,7 @@ __global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W, DiscoveryP
         rec[1] = p.gdepth[k];
         rec[2] = p.gparent[k];
         rec[3] = p.depth_at[k];
-        rec[4] = p.ndstar[k];
+        rec[4] = sdiff[x];
         rec[5] = cnt;
         rec[6] = 0;
         rec[7] = 0;
@@ -212,18 +382,19 @@ __global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W, DiscoveryP
       }
     }
     __syncthreads();
-    // Advance: finish lone members and members whose full blocks end here.
-    for (int x = tid; x < nm; x += kTreeThreads) {
-      const int k = mem[x];
-      if (!p.active[k]) continue;
-      const int lead = p.node[k];
+    // Advance: members of lone parts end at their depth; the others join
+    // their group and end at d* or carry on from it.
+    for (int x = tid; x < n; x += kTreeThreads) {
+      const int k = (int)(skey[x] & kIdxMask);
+      const int b0 = sbeg[x];
+      const int lead = (int)(skey[b0] & kIdxMask);
       const int gid = p.ngid[lead];
       if (gid < 0) {
         p.sfx_begin[k] = p.depth_at[k];
         p.deepest[k] = p.gparent[k];
         p.active[k] = 0;
       } else {
-        const int ds = p.ndstar[lead];
+        const int ds = sdiff[b0];
         p.gparent[k] = gid;
         p.gdepth[k] += 1;
         p.deepest[k] = gid;
@@ -232,15 +403,22 @@ __global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W, DiscoveryP
           p.active[k] = 0;
         } else {
           p.depth_at[k] = ds;
+          p.node[k] = lead;
         }
       }
     }
-    if (tid == 0) any_active = 0;
     __syncthreads();
-    for (int x = tid; x < nm; x += kTreeThreads)
-      if (p.active[mem[x]]) any_active = 1;
+    // The members still active, compacted for the next round (through sdiff,
+    // whose values are no longer needed).
+    for (int x = tid; x < n; x += kTreeThreads) {
+      const int k = (int)(skey[x] & kIdxMask);
+      if (p.active[k]) sdiff[atomicAdd(&n_next, 1)] = k;
+    }
     __syncthreads();
-    if (!any_active) break;
+    n = n_next;
+    for (int x = tid; x < n; x += kTreeThreads) skey[x] = (uint64_t)sdiff[x];
+    __syncthreads();
+    if (n == 0) break;
   }
 }
 
@@ -249,33 +427,46 @@ __global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W, DiscoveryP
 // One thread per bin: the block IDs of the first four blocks of its first
 // item (block IDs are validated by k_prepare).
 __global__ __launch_bounds__(256) void k_bin_heads(BinHead* __restrict__ heads, int n_bins,
-                                                   const int32_t* __restrict__ bt, int W, int bs) {
+                                                   const int32_t* __restrict__ bt, int W4, int bs) {
   const int b = blockIdx.x * 256 + threadIdx.x;
   if (b >= n_bins) return;
   BinHead& h = heads[b];
   const WorkItem& it = h.first;
   const int nblk = (it.tok_end - it.tok_begin + bs - 1) / bs;
   for (int j = 0; j < 4; ++j)
-    h.id[j] = j < nblk ? bt[(int64_t)it.request * W + it.tok_begin / bs + j] : 0;
+    h.id[j] = j < nblk ? bt[(int64_t)it.request * W4 + it.tok_begin / bs + j] : 0;
 }
 
-hipError_t launch_bin_heads(BinHead* heads, int n_bins, const int32_t* bt, int W, int bs, hipStream_t s) {
+hipError_t launch_bin_heads(BinHead* heads, int n_bins, const int32_t* bt, int W4, int bs, hipStream_t s) {
   if (n_bins <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bin_heads, dim3((n_bins + 255) / 256), dim3(256), 0, s, heads, n_bins, bt, W, bs);
+  hipLaunchKernelGGL(k_bin_heads, dim3((n_bins + 255) / 256), dim3(256), 0, s, heads, n_bins, bt, W4, bs);
   return hipGetLastError();
 }
 
-hipError_t launch_discovery(const int32_t* bt_in, int64_t bt_stride, const int32_t* lens_in, int B, int W,
+hipError_t launch_discovery(const int32_t* bt_in, int64_t bt_stride, const int32_t* lens_in, int B, int W, int W4,
                             int block_size, int num_blocks, bool cascade, const DiscoveryPtrs& p, hipStream_t s) {
   hipLaunchKernelGGL(k_init_header, dim3(1), dim3(64), 0, s, p.header);
   if (B == 0) return hipGetLastError();
-  const int64_t total = (int64_t)B * W;
+  const int64_t total = (int64_t)B * W4;
   const int grid = (int)std::min<int64_t>((total + 255) / 256, 4096);
-  hipLaunchKernelGGL(k_prepare, dim3(grid), dim3(256), 0, s, bt_in, bt_stride, lens_in, B, W, block_size,
+  hipLaunchKernelGGL(k_prepare, dim3(grid), dim3(256), 0, s, bt_in, bt_stride, lens_in, B, W, W4, block_size,
                      num_blocks, p);
   if (cascade) {
-    hipLaunchKernelGGL(k_roots, dim3((B + 3) / 4), dim3(256), 0, s, B, W, p);
-    hipLaunchKernelGGL(k_trees, dim3(B), dim3(kTreeThreads), 0, s, B, W, p);
+    hipLaunchKernelGGL(k_roots, dim3((B + 3) / 4), dim3(256), 0, s, B, W4, p);
+    hipLaunchKernelGGL(k_lcp0, dim3((B + 3) / 4), dim3(256), 0, s, B, W4, p);
+    // lanes per compared row (developer tuning knob): 4 (default: most
+    // members in flight; measured fastest on the two-level forest), 8 or 16
+    static const int lcp_lanes = [] {
+      const char* v = getenv("FCA_TUNE_LCP_LANES");
+      const int x = v ? atoi(v) : 4;
+      return (x == 8 || x == 16) ? x : 4;
+    }();
+    if (lcp_lanes == 4)
+      hipLaunchKernelGGL((k_trees<4, 4>), dim3(B), dim3(kTreeThreads), 0, s, B, W4, p);
+    else if (lcp_lanes == 8)
+      hipLaunchKernelGGL((k_trees<8, 4>), dim3(B), dim3(kTreeThreads), 0, s, B, W4, p);
+    else
+      hipLaunchKernelGGL((k_trees<16, 4>), dim3(B), dim3(kTreeThreads), 0, s, B, W4, p);
   }
   return hipGetLastError();
 }

@@ -18,7 +18,7 @@ struct DiscoveryPtrs {
   int32_t* deepest;    // [B] device group id, -1   -- read back
   int32_t* sfx_begin;  // [B] first suffix block    -- read back
   int32_t* records;    // [B * kRecordInts]         -- read back
-  int32_t* bt;         // [B * W] copy of the used table entries (-1 elsewhere)
+  int32_t* bt;         // [B * W4] copy of the used table entries (-1 elsewhere), rows 16-byte aligned
   int32_t* nfull;
   int32_t* root;
   int32_t* depth_at;   // current node's first block
@@ -26,13 +26,13 @@ struct DiscoveryPtrs {
   int32_t* gdepth;
   int32_t* gparent;
   int32_t* active;
-  int32_t* ndstar;
-  int32_t* ncount;
+  int32_t* lcp0;       // common prefix (full blocks) of each request with its tree's root
   int32_t* ngid;
-  int32_t* newnode;
 };
 
-hipError_t launch_discovery(const int32_t* bt_in, int64_t bt_stride, const int32_t* lens_in, int B, int W,
+// W: table width (entries per row the caller's tables use); W4: row stride of
+// the copy in the workspace (W rounded up to a multiple of 4).
+hipError_t launch_discovery(const int32_t* bt_in, int64_t bt_stride, const int32_t* lens_in, int B, int W, int W4,
                             int block_size, int num_blocks, bool cascade, const DiscoveryPtrs& p, hipStream_t s);
 
 // Partial (o, m, l) rows: o unnormalised w.r.t. its own running max m
@@ -51,7 +51,7 @@ struct GqaParams {
   const BinHead* bins;      // one per workgroup
   const int32_t* perm;
   const int32_t* bt;
-  int32_t W;
+  int32_t W;  // row stride of bt (the workspace copy)
   int32_t Hq;
   int32_t r;
   float scale_log2;
@@ -71,11 +71,26 @@ hipError_t launch_attention(const GqaParams& p, int n_bins, hipStream_t s);
 // picks the kernel entry the launch is traced under (same code).
 hipError_t launch_mla(const GqaParams& p, int n_bins, bool grouped_pass, hipStream_t s);
 
+// Merge tables built at plan time (plan_tables.hip) from the planner's
+// metadata: src_span [B * Hq] (start, count) into src_row [total rows];
+// *total (zero before the launch) ends at the number of rows.
+struct TableParams {
+  const ReqMeta* req;
+  const GroupMeta* grp;
+  const LaneMeta* lanes;
+  int32_t B, Hq, r, item_cols;
+  int2* src_span;
+  int32_t* src_row;
+  int32_t* total;
+};
+
+hipError_t launch_merge_tables(const TableParams& p, hipStream_t s);
+
 struct MergeParams {
   // Partial rows of (request i, query head h), in merge order (deepest
   // group's splits, then its ancestors', then the suffix's):
-  // src_row[src_off[i * Hq + h] .. src_off[i * Hq + h + 1]).
-  const int32_t* src_off;
+  // src_row[s.x .. s.x + s.y), s = src_span[i * Hq + h].
+  const int2* src_span;
   const int32_t* src_row;
   int32_t B, Hq, Dv;
   PartialPtrs part;

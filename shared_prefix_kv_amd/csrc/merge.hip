@@ -81,8 +81,9 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
   const int hl = lane & 31;
   const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= (int64_t)P.B * P.Hq) return;
-  const int off0 = P.src_off[pair];
-  const int n_src = P.src_off[pair + 1] - off0;
+  const int2 span = P.src_span[pair];
+  const int off0 = span.x;
+  const int n_src = span.y;
 
   float M = -INFINITY, L = 0.f;
   float acc[VPL];

@@ -1,0 +1,83 @@
+// Merge tables of a plan, built on the device at plan time (gfx950).
+//
+// The exact combination of "Core Mechanism" step 3 (ZoRRo Inference &
+// Forest Cascade Attention page) reads, for request i and query head h, the
+// partial rows of every token split of every group on i's path (deepest
+// group first, then its parents) and of i's own suffix.  The merge kernel
+// takes them from a flat table: (start, count) = src_span[i * Hq + h] gives
+// src_row[start .. start + count).  The host planner lays out the lanes
+// (LaneMeta: base row, splits, head block, column range of one (unit, head
+// block, column chunk) stream) and the per-request and per-group metadata;
+// one kernel turns them into the table -- a thread per (request, head)
+// counts its rows, each wave takes room for its threads' rows with one atomic
+// add on a counter, and every thread writes its rows -- instead of the host
+// walking B x Hq paths at every plan.  Where a pair's rows sit in src_row
+// depends on the order in which waves reach the counter; what they are, and
+// their order, does not.
+
+#include "fca_internal.h"
+
+namespace fca {
+namespace {
+
+constexpr int kTableThreads = 256;
+
+// Calls f(lane, column) for the units on the path of (request i, head h), in
+// merge order.
+template <class F>
+__device__ __forceinline__ void path_units(const TableParams& p, int i, int h, F&& f) {
+  const int kvh = h / p.r, rr = h - kvh * p.r;
+  const ReqMeta rq = p.req[i];
+  for (int g = rq.deepest; g >= 0;) {
+    const GroupMeta gm = p.grp[g];
+    const int col = (rq.pos - gm.r0) * p.r + rr;
+    f(gm.lane0 + (kvh / gm.H) * gm.chunks + col / p.item_cols, col);
+    g = gm.parent;
+  }
+  if (rq.sfx_lane >= 0) f(rq.sfx_lane + (kvh / rq.sfx_H) * rq.sfx_chunks + rr / p.item_cols, rr);
+}
+
+__global__ __launch_bounds__(kTableThreads) void k_merge_table(TableParams p) {
+  const int64_t pair = (int64_t)blockIdx.x * kTableThreads + threadIdx.x;
+  const int64_t n = (int64_t)p.B * p.Hq;
+  const int lane = threadIdx.x & 63;
+  int i = 0, h = 0, cnt = 0;
+  if (pair < n) {
+    i = (int)(pair / p.Hq);
+    h = (int)(pair - (int64_t)i * p.Hq);
+    path_units(p, i, h, [&](int lane_id, int) { cnt += p.lanes[lane_id].splits; });
+  }
+  // inclusive prefix sum of the counts over the wave
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  int base = 0;
+  if (lane == 63) base = atomicAdd(p.total, incl);
+  base = __shfl(base, 63);
+  if (pair >= n) return;
+  const int start = base + incl - cnt;
+  p.src_span[pair] = make_int2(start, cnt);
+  const int kvh = h / p.r;
+  int32_t* out = p.src_row + start;
+  path_units(p, i, h, [&](int lane_id, int col) {
+    const LaneMeta L = p.lanes[lane_id];
+    const int step = L.H * L.ccols;
+    int row = L.base + (kvh - L.kv0) * L.ccols + (col - L.col0);
+    for (int s = 0; s < L.splits; ++s, row += step) *out++ = row;
+  });
+}
+
+}  // namespace
+
+hipError_t launch_merge_tables(const TableParams& p, hipStream_t s) {
+  const int64_t n = (int64_t)p.B * p.Hq;
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n + kTableThreads - 1) / kTableThreads);
+  hipLaunchKernelGGL(k_merge_table, dim3(grid), dim3(kTableThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace fca

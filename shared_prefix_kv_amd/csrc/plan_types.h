@@ -132,7 +132,6 @@ struct PlanHost {
   std::vector<ReqMeta> req;
   std::vector<GroupMeta> grp;
   std::vector<LaneMeta> lanes;  // grouped lanes, then suffix lanes
-  std::vector<int32_t> src_off, src_row;  // merge sources per (request, query head), CSR
   int item_cols = kItemColsGqa;  // query rows per column chunk
   fca_plan_info info{};
 };

@@ -299,6 +299,7 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
   // P->bins / P->items.  An item's part_base holds its piece index until the
   // lane bases are known.
   std::vector<Lane> all;
+  all.reserve((size_t)(G + B) * hkv * 2);
   std::vector<int> item_lane;
   P->items.clear();
   P->bins.assign(1, 0);
@@ -310,6 +311,10 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
     }
     const int64_t nb = std::min<int64_t>(W, (int64_t)n_cu_ * t.bins_per_cu);
     if (nb == 0) return;
+    // every bin boundary cuts at most one lane: items <= lanes + bins
+    P->items.reserve(P->items.size() + (l1 - l0) + (size_t)nb);
+    item_lane.reserve(P->items.capacity());
+    P->bins.reserve(P->bins.size() + (size_t)nb);
     P->launches.push_back(Launch{(int)P->bins.size() - 1, (int)nb, passes});
     size_t li = l0;
     int64_t lpos = 0, pos = 0;
@@ -379,10 +384,20 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
     std::stable_sort(units.begin(), units.begin() + n_large, [&](const Unit& a, const Unit& b) {
       return all[a.l0].stages * (int64_t)(a.l1 - a.l0) > all[b.l0].stages * (int64_t)(b.l1 - b.l0);
     });
-    std::vector<std::vector<std::pair<int, std::pair<int64_t, int64_t>>>> bin(nb);  // (lane, stages)
+    // (bin, lane, stage range) of every piece, in placement order; emitted
+    // bin by bin (stable) at the end
+    struct Piece {
+      int bin, lane;
+      int64_t s0, s1;
+    };
+    std::vector<Piece> placed;
+    placed.reserve((l1 - l0) * 4 + (size_t)nb);
     std::vector<int64_t> load(nb, 0);
     const int per_die = (nb + kXcds - 1) / kXcds;
-    std::vector<int> cand;
+    // The bins of each die, kept sorted by (load, bin).
+    std::vector<std::vector<int>> die(kXcds);
+    for (int b = 0; b < nb; ++b) die[b % kXcds].push_back(b);
+    auto by_load = [&](int a, int b) { return load[a] != load[b] ? load[a] < load[b] : a < b; };
     for (size_t ui = 0; ui < n_large; ++ui) {
       const Unit& u = units[ui];
       const int64_t n = all[u.l0].stages;
@@ -393,31 +408,26 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
         for (int c0 = 0; c0 < C; c0 += per_die) {
           const int cn = std::min(per_die, C - c0);
           // The die whose cn least loaded bins carry the least work.
-          int best_x = 0;
+          int best_x = -1;
           int64_t best = INT64_MAX;
           for (int x = 0; x < kXcds && x < nb; ++x) {
-            cand.clear();
-            for (int b = x; b < nb; b += kXcds) cand.push_back(b);
-            if ((int)cand.size() < cn) continue;
-            std::partial_sort(cand.begin(), cand.begin() + cn, cand.end(),
-                              [&](int a, int b) { return load[a] < load[b]; });
+            if ((int)die[x].size() < cn) continue;
             int64_t sum = 0;
-            for (int j = 0; j < cn; ++j) sum += load[cand[j]];
+            for (int j = 0; j < cn; ++j) sum += load[die[x][j]];
             if (sum < best) {
               best = sum;
               best_x = x;
             }
           }
-          cand.clear();
-          for (int b = best_x; b < nb; b += kXcds) cand.push_back(b);
+          if (best_x < 0) best_x = 0;  // fewer bins per die than chunks: reuse the least loaded ones
+          std::vector<int>& cand = die[best_x];
           const int take = std::min<int>(cn, (int)cand.size());
-          std::partial_sort(cand.begin(), cand.begin() + take, cand.end(),
-                            [&](int a, int b) { return load[a] < load[b]; });
           for (int j = 0; j < cn; ++j) {
             const int b = cand[j % take];
-            bin[b].push_back({(int)(u.l0 + c0 + j), {s0, s1}});
+            placed.push_back(Piece{b, (int)(u.l0 + c0 + j), s0, s1});
             load[b] += s1 - s0;
           }
+          std::sort(cand.begin(), cand.end(), by_load);
         }
       }
     }
@@ -433,22 +443,26 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
           while (fb < nb && load[fb] >= M) ++fb;  // the room under M covers what is left
           if (fb == nb) throw std::logic_error("placement overflow");
           const int64_t take = std::min(n - s0, M - load[fb]);
-          bin[fb].push_back({(int)k, {s0, s0 + take}});
+          placed.push_back(Piece{fb, (int)k, s0, s0 + take});
           load[fb] += take;
           s0 += take;
         }
       }
+    std::stable_sort(placed.begin(), placed.end(), [](const Piece& a, const Piece& b) { return a.bin < b.bin; });
     const int first = (int)P->bins.size() - 1;
     int used = 0;
-    for (int b = 0; b < nb; ++b) {
-      if (bin[b].empty()) continue;
-      for (const auto& e : bin[b]) {
-        Lane& L = all[e.first];
+    P->items.reserve(P->items.size() + placed.size());
+    item_lane.reserve(P->items.capacity());
+    for (size_t q = 0; q < placed.size();) {
+      const int b = placed[q].bin;
+      for (; q < placed.size() && placed[q].bin == b; ++q) {
+        const Piece& e = placed[q];
+        Lane& L = all[e.lane];
         const int64_t stok = (int64_t)L.S * bs;
         WorkItem it{};
         it.request = L.request;
-        it.tok_begin = (int)(L.tok0 + e.second.first * stok);
-        it.tok_end = (int)std::min<int64_t>(L.tok0 + e.second.second * stok, L.tok_end);
+        it.tok_begin = (int)(L.tok0 + e.s0 * stok);
+        it.tok_end = (int)std::min<int64_t>(L.tok0 + e.s1 * stok, L.tok_end);
         it.kv_head = L.kv0;
         it.kv_heads = L.H;
         it.member_off = L.member_off;
@@ -459,7 +473,7 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
         it.stripes = L.S;
         it.flags = L.stream;
         P->items.push_back(it);
-        item_lane.push_back(e.first);
+        item_lane.push_back(e.lane);
       }
       P->bins.push_back((int32_t)P->items.size());
       ++used;
@@ -533,48 +547,11 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
   for (const Lane& L : all)
     P->lanes.push_back(LaneMeta{(int32_t)L.base, L.splits, L.kv0, L.H, L.col0, L.col1 - L.col0, 0, 0});
 
-  // Merge sources: one per (request, query head, token split on its path),
-  // as a flat table of partial-row indices the merge reads directly, in the
-  // order of for_each_source.  Counted first, then written in place.
-  P->src_off.assign((size_t)B * hq + 1, 0);
-  {
-    // The lanes (and the column in them) of request i's path for query head
-    // h: deepest group first, then its ancestors, then the suffix.
-    std::vector<std::pair<int, int>> path;
-    auto path_of = [&](int i, int h) {
-      const int kvh = h / r, rr = h % r;
-      const ReqMeta& rq = P->req[i];
-      path.clear();
-      for (int g = rq.deepest; g >= 0; g = P->grp[g].parent) {
-        const GroupMeta& gm = P->grp[g];
-        const int col = (rq.pos - gm.r0) * r + rr;
-        path.push_back({gm.lane0 + (kvh / gm.H) * gm.chunks + col / P->item_cols, col});
-      }
-      if (rq.sfx_lane >= 0) path.push_back({rq.sfx_lane + (kvh / rq.sfx_H) * rq.sfx_chunks + rr / P->item_cols, rr});
-    };
-    int64_t total = 0;
-    for (int i = 0; i < B; ++i)
-      for (int h = 0; h < hq; ++h) {
-        path_of(i, h);
-        for (const auto& u : path) total += P->lanes[u.first].splits;
-        if (total > (int64_t)INT32_MAX) return pfail(err, FCA_ERR_UNSUPPORTED, "too many merge sources");
-        P->src_off[(size_t)i * hq + h + 1] = (int32_t)total;
-      }
-    P->src_row.resize((size_t)total);
-    int32_t* out = P->src_row.data();
-    for (int i = 0; i < B; ++i)
-      for (int h = 0; h < hq; ++h) {
-        path_of(i, h);
-        const int kvh = h / r;
-        for (const auto& u : path) {
-          const LaneMeta& L = P->lanes[u.first];
-          const int64_t step = (int64_t)L.H * L.ccols;
-          int64_t row = (int64_t)L.base + (int64_t)(kvh - L.kv0) * L.ccols + (u.second - L.col0);
-          for (int sp = 0; sp < L.splits; ++sp, row += step) *out++ = (int32_t)row;
-        }
-      }
-  }
-  const int64_t sources = (int64_t)P->src_row.size();
+  // Merge sources: every partial row is read by exactly one (request, query
+  // head), so there are as many sources as rows.  The table itself (per
+  // (request, head) the rows of its path, for_each_source order) is built on
+  // the device from req / grp / lanes.
+  const int64_t sources = row;
 
   fca_plan_info& info = P->info;
   info.batch = B;

@@ -1,7 +1,13 @@
-"""Summaries of rocprofv3 runs of bench.py (kernel times and HBM traffic).
+"""rocprofv3 runs of bench.py and their summaries (kernel times and HBM traffic).
 
+    python -m shared_prefix_kv_amd.profiling run --config NAME [--out-dir gpurun_out/prof]
     python -m shared_prefix_kv_amd.profiling summarize \\
         --stats DIR --fetch DIR --write DIR --config NAME --out FILE [--cmd "..."]...
+
+``run`` (on a GPU machine) runs the four rocprofv3 passes below one after the
+other as child processes, each under its own time limit, and then writes the
+summary to profiles/<kernel>.<config>.txt; this process itself never touches
+the GPU.
 
 DIR are rocprofv3 output folders (``-f csv``): ``--stats`` from
 ``--kernel-trace --stats``, ``--fetch`` / ``--write`` from ``--pmc FETCH_SIZE``
@@ -261,9 +267,80 @@ def load_traffic(config: str):
     return None
 
 
+PASSES = [
+    ("stats", ["--kernel-trace", "--stats"]),
+    ("fetch", ["--pmc", "FETCH_SIZE"]),
+    ("write", ["--pmc", "WRITE_SIZE"]),
+    ("util", ["--pmc", "MfmaUtil", "LdsUtil", "LDSBankConflict", "SQ_INSTS_VALU_MFMA_MOPS_BF16"]),
+]
+
+
+def run(config: str, out_dir: str, extra: list[str], timeout_s: int = 300) -> str:
+    """The four rocprofv3 passes of ``bench.py --profile-only`` for one
+    workload, then the summary; returns its path."""
+    import subprocess
+    import sys
+
+    out_dir = os.path.abspath(out_dir)
+    config_dir = config + ("_non_cascade" if "--no-cascade" in extra else "")
+    bench = [sys.executable, os.path.join(ROOT, "bench.py"), "--config", config, "--profile-only", "--copy-calibration",
+             "--no-cpu-baseline", *extra]
+    env = dict(os.environ, TMPDIR="/tmp")
+    cmds = ["cd /tmp && export TMPDIR=/tmp"]
+    for name, opts in PASSES:
+        d = os.path.join(out_dir, config_dir, name)
+        cmd = ["timeout", "-k", "10", str(timeout_s), "rocprofv3", *opts, "-f", "csv", "-d", d, "-o", "run", "--", *bench]
+        shown = " ".join(cmd).replace(ROOT, "<repo>").replace(sys.executable, "python3")
+        cmds.append(shown)
+        print("[profile]", shown, flush=True)
+        res = subprocess.run(cmd, cwd="/tmp", env=env)
+        # rocprofv3 may end with a signal after the program finished and its
+        # files are complete; a missing result file is what counts as failure
+        found = glob.glob(os.path.join(d, "**", "*kernel_stats.csv" if name == "stats" else "*counter_collection.csv"),
+                          recursive=True)
+        if not found:
+            raise RuntimeError(f"rocprofv3 pass {name} left no results (exit {res.returncode})")
+    # algorithmic bytes of the dominant launch, as bench.py reports them
+    algo = 0
+    tmp = os.path.join(out_dir, config_dir, "algorithmic.json")
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", config, "--profile-only",
+                          "--no-cpu-baseline", *extra], capture_output=True, text=True, env=env, timeout=timeout_s)
+    if res.returncode == 0 and res.stdout.strip():
+        line = json.loads(res.stdout.strip().splitlines()[-1])
+        algo = int(line["roofline"].get("bytes_per_launch", 0))
+        with open(tmp, "w") as fh:
+            fh.write(json.dumps(line["roofline"]))
+    kernel = _dominant_kernel(os.path.join(out_dir, config_dir, "stats"))
+    label = config + (".non_cascade" if "--no-cascade" in extra else "")
+    out = os.path.join(ROOT, "profiles", f"{kernel}.{label}.txt")
+    summ = [
+        f"python3 -m shared_prefix_kv_amd.profiling summarize --stats {out_dir}/{config_dir}/stats --fetch "
+        f"{out_dir}/{config_dir}/fetch --write {out_dir}/{config_dir}/write --util {out_dir}/{config_dir}/util --config {label} "
+        f"--copy-bytes {COPY_BYTES} --algorithmic-bytes {algo} --out profiles/{kernel}.{label}.txt".replace(ROOT, "<repo>")
+    ]
+    cmds = [f"python3 -m shared_prefix_kv_amd.profiling run --config {config}" + (" " + " ".join(extra) if extra else ""),
+            "which runs:"] + ["  " + c for c in cmds + summ]
+    summarize(os.path.join(out_dir, config_dir, "stats"), os.path.join(out_dir, config_dir, "fetch"),
+              os.path.join(out_dir, config_dir, "write"), label, COPY_BYTES, algo, cmds, out,
+              os.path.join(out_dir, config_dir, "util"))
+    return out
+
+
+COPY_BYTES = 1 << 30  # the calibration copy bench.py launches (--copy-calibration)
+
+
+def _dominant_kernel(stats_dir: str) -> str:
+    ks = [k for k in (ATTENTION, MLA_GROUPED, MLA_SUFFIX) if kernel_durations(stats_dir, k)]
+    return max(ks, key=lambda k: statistics.median(kernel_durations(stats_dir, k)))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--config", required=True)
+    r.add_argument("--out-dir", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    r.add_argument("--bench-arg", action="append", default=[], help="extra bench.py argument (repeatable)")
     s = sub.add_parser("summarize")
     s.add_argument("--stats", required=True)
     s.add_argument("--fetch", required=True)
@@ -275,6 +352,9 @@ def main():
     s.add_argument("--util", default=None, help="rocprofv3 folder of the matrix-core / LDS counter run")
     s.add_argument("--out", required=True)
     a = ap.parse_args()
+    if a.cmd == "run":
+        print(open(run(a.config, a.out_dir, a.bench_arg)).read(), end="")
+        return
     print(summarize(a.stats, a.fetch, a.write, a.config, a.copy_bytes, a.algorithmic_bytes, a.cmd, a.out, a.util), end="")
 
 
