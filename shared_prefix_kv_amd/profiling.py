@@ -320,9 +320,12 @@ def run(config: str, out_dir: str, extra: list[str], timeout_s: int = 300) -> st
     ]
     cmds = [f"python3 -m shared_prefix_kv_amd.profiling run --config {config}" + (" " + " ".join(extra) if extra else ""),
             "which runs:"] + ["  " + c for c in cmds + summ]
-    summarize(os.path.join(out_dir, config_dir, "stats"), os.path.join(out_dir, config_dir, "fetch"),
-              os.path.join(out_dir, config_dir, "write"), label, COPY_BYTES, algo, cmds, out,
-              os.path.join(out_dir, config_dir, "util"))
+    text = summarize(os.path.join(out_dir, config_dir, "stats"), os.path.join(out_dir, config_dir, "fetch"),
+                     os.path.join(out_dir, config_dir, "write"), label, COPY_BYTES, algo, cmds, out,
+                     os.path.join(out_dir, config_dir, "util"))
+    # a copy beside the raw results (the folder that comes back from a GPU machine)
+    with open(os.path.join(out_dir, os.path.basename(out)), "w") as fh:
+        fh.write(text)
     return out
 
 
