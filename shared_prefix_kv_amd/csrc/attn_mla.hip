@@ -20,16 +20,17 @@
 //     for the whole item): S^T = K Q^T with v_mfma_f32_16x16x32_bf16, online
 //     softmax per row in the log2 domain with a lazy running max (raised
 //     only when a score exceeds it by more than 2^8, so rescales are rare),
-//     then P goes to LDS as two bf16 tiles, the rounding of each probability
-//     and the rounding of its remainder (p - hi), with the row's rescale
-//     factor carried in the low 4 mantissa bits of the remainders (8 of
-//     them per lane hold its 32 bits; the remainder keeps 3 bits, enough for
-//     p to about 12 bits where bf16 alone gives 8);
+//     then P goes to LDS as one fp16 tile (11 significant bits; bf16 would
+//     keep 8, which leaves errors above the tolerance on requests of a few
+//     tokens whose value rows cancel) and the row's rescale factor beside it;
 //   * value waves 4-7, one stage behind, each owning 128 of the 512 value
-//     dims of all 64 rows: O^T += V^T P^T with v_mfma_f32_16x16x32_bf16, the
+//     dims of all 64 rows: O^T += V^T P^T with v_mfma_f32_16x16x32_f16, the
 //     V^T operand read from the key tile with ds_read_b64_tr_b16 (two 16-token
-//     tiles per operand) and the P^T operand as written by the score waves,
-//     once against each P tile.
+//     tiles per operand) and converted from bf16 to fp16 in registers (exact:
+//     every bf16 value of magnitude below 65504 is an fp16 value, apart from
+//     the fp16 subnormal range below 2^-14, where the conversion keeps an
+//     absolute error under 2^-24), and the P^T operand as the score waves
+//     wrote it.
 // Splitting the value dims keeps every wave under 256 registers, so each
 // SIMD runs a score wave and a value wave side by side, and the value tile
 // is read from LDS once per workgroup instead of once per 16 rows.
@@ -44,6 +45,7 @@ namespace fca {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -69,10 +71,11 @@ static_assert(kPvWaves * kDmaP * 1024 == kStageBytes, "stage copy split");
 constexpr float kTau = 8.f;                      // lazy-max threshold (log2 units)
 constexpr int kBufferWord3 = 0x00020000;         // raw buffer resource, gfx9 family
 
-constexpr int kOffP = kSlots * kStageBytes;      // P^T operands [2][hi, lo][4 col tiles][64 lanes] x 16 B
+constexpr int kOffP = kSlots * kStageBytes;      // P^T operands (fp16) [2][4 col tiles][64 lanes] x 16 B
 constexpr int kPTile = kQkWaves * 64 * 16;
-constexpr int kPBytes = 2 * kPTile;
-constexpr int kLdsBytes = kOffP + 2 * kPBytes;   // 160 KiB, all of it
+constexpr int kOffA = kOffP + 2 * kPTile;        // rescale factor of each row [2][64] fp32
+constexpr int kLdsBytes = kOffA + 2 * 64 * 4;
+static_assert(kLdsBytes <= 160 * 1024, "LDS");
 
 __device__ __forceinline__ float xmax16(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -303,27 +306,17 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
           lsum *= alpha;
           mrow = mnew;
         }
-        bf16x8 pb, pl;
+        f16x8 ph;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[j], sc, -mrow));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[j], sc, -mrow));
           lsum += p0 + p1;
-          const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
-          pb[j] = h0;
-          pb[4 + j] = h1;
-          pl[j] = (__bf16)(p0 - (float)h0);
-          pl[4 + j] = (__bf16)(p1 - (float)h1);
+          ph[j] = (_Float16)p0;
+          ph[4 + j] = (_Float16)p1;
         }
-        // The rescale factor of row c16 rides in the low mantissa nibbles
-        // of the remainders: bits 4i..4i+3 and 16+4i..16+4i+3 in word i.
-        u32x4 lw = __builtin_bit_cast(u32x4, pl);
-        const uint32_t ab = __float_as_uint(alpha);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lw[i] = (lw[i] & 0xFFF0FFF0u) | ((ab >> (4 * i)) & 0x000F000Fu);
-        char* pt = lds + kOffP + buf * kPBytes + (w * 64 + lane) * 16;
-        *reinterpret_cast<bf16x8*>(pt) = pb;
-        *reinterpret_cast<u32x4*>(pt + kPTile) = lw;
+        *reinterpret_cast<f16x8*>(lds + kOffP + buf * kPTile + (w * 64 + lane) * 16) = ph;
+        if (g == 0) *reinterpret_cast<float*>(lds + kOffA + buf * 256 + (16 * w + c16) * 4) = alpha;
       }
       if (++cs == cns) {
         if (active) {
@@ -373,13 +366,10 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
       const int buf = (t - 1) & 1;
       const int ccols = it.col1 - it.col0;
       const int nct = (ccols + 15) >> 4;
-      bf16x8 pb[4], pl[4];
+      f16x8 ph[4];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const char* pt = lds + kOffP + buf * kPBytes + (ct * 64 + lane) * 16;
-        pb[ct] = *reinterpret_cast<const bf16x8*>(pt);
-        pl[ct] = *reinterpret_cast<const bf16x8*>(pt + kPTile);
-      }
+      for (int ct = 0; ct < 4; ++ct)
+        ph[ct] = *reinterpret_cast<const f16x8*>(lds + kOffP + buf * kPTile + (ct * 64 + lane) * 16);
       const char* kt = lds + ((t - 1) % kSlots) * kStageBytes + (2 * v * kPvTiles) * kChunk + tr_off;
       u32x2 vr[kPvTiles][2];
       read_vt(kt, vr);
@@ -397,6 +387,19 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
           for (int dt = 0; dt < kPvTiles; ++dt) vr[dt][tt] &= keep;
         }
       }
+      // bf16 pair (low, high half of a word) -> fp16 pair: the bf16 bits are
+      // the top half of the fp32 value, which converts exactly.
+      auto to_f16 = [](const u32x2 (&w)[2]) {
+        f16x8 a;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t x = w[i >> 1][i & 1];
+          const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u));
+          a[2 * i] = h[0];
+          a[2 * i + 1] = h[1];
+        }
+        return a;
+      };
       // The value products go first on the shared MFMA pipe (the score wave
       // of this SIMD is in its softmax or at the barrier by now).
       __builtin_amdgcn_s_setprio(2);
@@ -404,23 +407,15 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
         // First stage of the item: fresh accumulators.
 #pragma unroll
         for (int dt = 0; dt < kPvTiles; ++dt) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{vr[dt][0][0], vr[dt][0][1], vr[dt][1][0], vr[dt][1][1]});
+          const f16x8 a = to_f16(vr[dt]);
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ct], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[ct], o[ct][dt], 0, 0, 0);
-          }
+          for (int ct = 0; ct < 4; ++ct)
+            o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ph[ct], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         }
       } else {
-        f32x4 al;
+        float al[4];
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const u32x4 lw = __builtin_bit_cast(u32x4, pl[ct]);
-          uint32_t ab = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ab |= (lw[i] & 0x000F000Fu) << (4 * i);
-          al[ct] = __uint_as_float(ab);
-        }
+        for (int ct = 0; ct < 4; ++ct) al[ct] = *reinterpret_cast<const float*>(lds + kOffA + buf * 256 + (16 * ct + c16) * 4);
         bool scale = false;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) scale |= ct < nct && al[ct] != 1.f;
@@ -434,12 +429,10 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
         }
 #pragma unroll
         for (int dt = 0; dt < kPvTiles; ++dt) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{vr[dt][0][0], vr[dt][0][1], vr[dt][1][0], vr[dt][1][1]});
+          const f16x8 a = to_f16(vr[dt]);
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[ct], o[ct][dt], 0, 0, 0);
-            o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[ct], o[ct][dt], 0, 0, 0);
-          }
+          for (int ct = 0; ct < 4; ++ct)
+            o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ph[ct], o[ct][dt], 0, 0, 0);
         }
       }
       __builtin_amdgcn_s_setprio(0);
