@@ -99,7 +99,10 @@ typedef enum fca_status {
  *   - GQA:  head_dim_qk = head_dim_v = 128, block_size = 16,
  *           num_q_heads / num_kv_heads in [1, 16], v_aliases_k = 0.
  *   - MLA:  head_dim_qk = 576, head_dim_v = 512, block_size = 64,
- *           num_kv_heads = 1, v_aliases_k = 1.
+ *           num_kv_heads = 1, v_aliases_k = 1.  The value products run in
+ *           fp16 (probabilities to 11 bits), so the value columns (the first
+ *           512 dims) must stay below 65504 in magnitude; larger values are
+ *           not representable there and give wrong results.
  *
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  * `scale` multiplies q.k before the softmax.
