@@ -235,6 +235,7 @@ def short_record(name, torch, fca, steps, warmup, layers=4):
     out = torch.empty((batch.batch, sh.num_q_heads, sh.head_dim_v), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((batch.batch, sh.num_q_heads), dtype=torch.float32, device="cuda")
     res = {}
+    latent = None
     desc = fca.desc_from_shape(sh, batch.num_blocks)
     fca.fca_plan(bt, sl, desc)
     torch.cuda.synchronize()
@@ -252,6 +253,18 @@ def short_record(name, torch, fca, steps, warmup, layers=4):
         warm(plan, qs, pools, out, lse, warmup, torch, fca)
         ms, _ = time_steps(plan, qs, pools, out, lse, steps, torch, fca)
         res[key] = (ms, plan.info)
+        if key == "fca" and sh.v_aliases_k:
+            # Latent cache: the two passes are separate launches; time each.
+            t = plan.time_launches(qs[0], pools, 10, out, lse)
+            pb = pass_bytes(batch, plan, None)
+            launch = {k[:-3]: round(v, 5) for k, v in t.items() if k.endswith("_ms") and v > 0}
+            g_tf = pb["grouped_flops"] / (t["grouped_ms"] / 1000.0) / 1e12 if t["grouped_ms"] > 0 else 0.0
+            latent = {
+                "per_launch_ms": launch,
+                "grouped_mfma_TFLOPs": round(g_tf, 1),
+                "grouped_mfma_frac_of_peak": round(g_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                "suffix_GBps": round(pb["suffix"] / (t["suffix_ms"] / 1000.0) / 1e9, 1) if t["suffix_ms"] > 0 else None,
+            }
         del plan
     ms, info = res["fca"]
     ms_nc, _ = res["non_cascade"]
@@ -268,6 +281,8 @@ def short_record(name, torch, fca, steps, warmup, layers=4):
         "plan_ms_per_layer_of_32": round(plan_ms / 32, 4),
         "folded_groups": int(info.num_folded_groups),
     }
+    if latent:
+        rec["latent"] = latent
     del pools, qs
     torch.cuda.empty_cache()
     return rec
@@ -748,6 +763,13 @@ def main():
             round(roofline["achieved"] / rp, 4) if roofline["unit"] == "GB/s" and rp > 0 else None
         )
         log(f"streaming read, plain kernel: {rp:.0f} GB/s")
+        # Matrix-core counterpart: a loop of independent 16x16x32 products.
+        mf = {d: round(fca.measure_mfma_rate(d, iters=4000), 1) for d in ("bf16", "f16")}
+        result["mfma_peak_TFLOPs"] = mf
+        if roofline["unit"] == "TFLOP/s":
+            result["roofline"]["measured_mfma_peak_TFLOPs"] = mf["bf16"]
+            result["roofline"]["frac_of_measured_mfma_peak"] = round(roofline["achieved"] / mf["bf16"], 4)
+        log(f"dense MFMA loop, plain kernel: {mf} TFLOP/s")
 
     if not args.no_cpu_baseline and not args.profile_only:
         ncpu = len(os.sched_getaffinity(0))
@@ -766,6 +788,9 @@ def main():
         result["other_workloads"] = {}
         for name in others:
             rec = short_record(name, torch, fca, max(steps // 2, 8), warmup)
+            if "latent" in rec and "mfma_peak_TFLOPs" in result:
+                peak = result["mfma_peak_TFLOPs"]["bf16"]
+                rec["latent"]["grouped_frac_of_measured_mfma_peak"] = round(rec["latent"]["grouped_mfma_TFLOPs"] / peak, 4)
             log(f"{name}: {rec}")
             result["other_workloads"][name] = rec
 

@@ -374,6 +374,26 @@ fca_status fca_time_launches(fca_plan plan, const void* q_dev, const void* const
 fca_status fca_measure_read_bandwidth(const void* const* bufs_dev, int32_t n_bufs, size_t bytes, int32_t repeats,
                                       void* stream, double* gbps);
 
+/* Operand types of fca_measure_mfma_rate. */
+#define FCA_MFMA_BF16 0
+#define FCA_MFMA_F16 1
+
+/*
+ * Measurement hook: the matrix-core rate a plain loop of independent dense
+ * products reaches on this device, the practical ceiling next to the
+ * published dense peak (2.5 PFLOP/s bf16 and fp16 on MI355X) that the
+ * latent-cache kernels' roofline fractions are quoted against.  One
+ * workgroup of 8 waves per compute unit; each wave issues iters x 32
+ * v_mfma_f32_16x16x32 products (dtype FCA_MFMA_BF16 or FCA_MFMA_F16) into
+ * 32 independent accumulators, the operand shape of the value products.
+ * One untimed launch, then one timed between two HIP events on `stream`;
+ * *tflops = 2 x 16 x 16 x 32 flops per product / elapsed time (1e12 per
+ * second).  Nothing is read or written in device memory.  Blocks the host
+ * until the launch ends.  FCA_ERR_INVALID_ARG for NULL tflops, another dtype
+ * or iters outside [1, 2^20], FCA_ERR_HIP if a launch or event call fails.
+ */
+fca_status fca_measure_mfma_rate(int32_t dtype, int32_t iters, void* stream, double* tflops);
+
 /*
  * Exact combination of attention states over disjoint key sets: state j of
  * (request i, head h) is a normalised output o_j (float32) and its natural

@@ -51,6 +51,7 @@ EXPORTED = [
     "fca_profile_read",
     "fca_time_launches",
     "fca_measure_read_bandwidth",
+    "fca_measure_mfma_rate",
     "fca_merge_states",
     "fca_kv_append",
     "fca_kv_append_layers",
@@ -166,6 +167,7 @@ def lib():
         L.fca_profile_read.argtypes = [vp, ctypes.POINTER(Profile)]
         L.fca_time_launches.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp, ctypes.POINTER(Profile)]
         L.fca_measure_read_bandwidth.argtypes = [vp, i32, sz, i32, vp, ctypes.POINTER(ctypes.c_double)]
+        L.fca_measure_mfma_rate.argtypes = [i32, i32, vp, ctypes.POINTER(ctypes.c_double)]
         L.fca_merge_states.argtypes = [i32, vp, vp, i32, i32, i32, vp, vp, ctypes.c_uint32, vp]
         L.fca_kv_append.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, i64, i32, vp, vp, vp, i32, vp]
         L.fca_kv_append_layers.argtypes = [ctypes.POINTER(AttnDesc), i32, vp, vp, vp, vp, vp, i64, i32, vp, vp, vp, i32, vp]
@@ -682,6 +684,20 @@ def measure_read_bandwidth(buffers, repeats=4, stream=None) -> float:
     g = ctypes.c_double()
     _check(lib().fca_measure_read_bandwidth(arr, n, nbytes, int(repeats), _stream_ptr(stream), ctypes.byref(g)))
     return g.value
+
+
+
+FCA_MFMA_BF16 = 0
+FCA_MFMA_F16 = 1
+
+
+def measure_mfma_rate(dtype="bf16", iters=4000, stream=None) -> float:
+    """Dense matrix-core rate (TFLOP/s) of a loop of independent 16x16x32
+    products, bf16 or fp16 operands (fca_measure_mfma_rate)."""
+    code = {"bf16": FCA_MFMA_BF16, "f16": FCA_MFMA_F16}[dtype]
+    t = ctypes.c_double()
+    _check(lib().fca_measure_mfma_rate(code, int(iters), _stream_ptr(stream), ctypes.byref(t)))
+    return t.value
 
 
 def version() -> str:

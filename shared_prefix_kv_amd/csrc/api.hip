@@ -897,6 +897,34 @@ fca_status fca_measure_read_bandwidth(const void* const* bufs_dev, int32_t n_buf
   return FCA_OK;
 }
 
+fca_status fca_measure_mfma_rate(int32_t dtype, int32_t iters, void* stream, double* tflops) {
+  if (!tflops) return fail(FCA_ERR_INVALID_ARG, "tflops is NULL");
+  if (dtype != FCA_MFMA_BF16 && dtype != FCA_MFMA_F16) return fail(FCA_ERR_INVALID_ARG, "dtype must be FCA_MFMA_BF16 or FCA_MFMA_F16");
+  if (iters < 1 || iters > (1 << 20)) return fail(FCA_ERR_INVALID_ARG, "iters must be in [1, 2^20]");
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "compute-unit count");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == FCA_MFMA_BF16;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  for (int j = 0; j < 2 && e == hipSuccess; ++j) e = timing_event(&ev[j]);
+  // One untimed launch, then the timed one.
+  if (e == hipSuccess) e = launch_mfma_rate(bf16, iters, n_cu, s);
+  if (e == hipSuccess) e = hipEventRecord(ev[0], s);
+  if (e == hipSuccess) e = launch_mfma_rate(bf16, iters, n_cu, s);
+  if (e == hipSuccess) e = hipEventRecord(ev[1], s);
+  if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+  for (int j = 0; j < 2; ++j)
+    if (ev[j]) (void)hipEventDestroy(ev[j]);
+  if (e != hipSuccess) return hip_fail(e, "MFMA-rate probe");
+  const double flops = (double)std::max(1, n_cu) * (kMfmaThreads / 64) * (double)iters * kMfmaPerIter * (2.0 * 16 * 16 * 32);
+  *tflops = ms > 0.f ? flops / (ms * 1e-3) / 1e12 : 0.0;
+  return FCA_OK;
+}
+
 fca_status fca_profile_enable(fca_plan plan, int32_t enable) {
   if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
   plan->profiling = enable != 0;

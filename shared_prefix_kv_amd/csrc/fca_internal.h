@@ -146,5 +146,10 @@ hipError_t launch_append_commit(int32_t* block_tables, int64_t bt_row_stride, co
 // with launch shape 0 (512 threads x 4 loads) or 1 (256 threads x 8 loads).
 constexpr int kReadShapes = 2;
 hipError_t launch_stream_read(const void* src, size_t bytes, int n_cu, int shape, hipStream_t s);
+// MFMA-rate probe: one workgroup of kMfmaThreads per compute unit, each wave
+// issuing 32 x iters 16x16x32 products (bf16, else fp16).
+constexpr int kMfmaThreads = 512;
+constexpr int kMfmaPerIter = 32;
+hipError_t launch_mfma_rate(bool bf16, int iters, int n_cu, hipStream_t s);
 
 }  // namespace fca

@@ -1,23 +1,31 @@
 // Streaming-read probe (gfx950): the HBM read rate a plain kernel reaches on
 // this device, measured next to the 8 TB/s published peak that the decode
-// kernels' roofline fractions are quoted against.
+// kernels' roofline fractions are quoted against.  And its matrix-core
+// counterpart: the rate of a loop of independent 16x16x32 MFMAs, next to the
+// 2.5 PFLOP/s dense bf16 / fp16 figure.
 //
 // Each thread reads 16-byte pieces in a grid-stride loop, four loads in
 // flight per iteration, and folds them into a running XOR; the XOR is stored
 // only if it equals a value no input produces in practice, so the loads
 // cannot be dropped and nothing is written.
 
+#include <type_traits>
+
 #include "fca_internal.h"
 
 namespace fca {
 
-// Externally visible, so that the store that keeps the loads alive is not
-// dropped as dead code.
+// Externally visible, so that the stores that keep the loads and products
+// alive are not dropped as dead code.
 __device__ uint32_t g_read_sink;
+__device__ float g_mfma_sink;
 
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Each thread keeps U 16-byte loads in flight per iteration.  Measured on
 // MI355X over 2 GiB buffers, one workgroup per compute unit read fastest
@@ -42,7 +50,59 @@ __global__ __launch_bounds__(THREADS) void fca_stream_read_kernel(const u32x4* _
   if (acc == 0x9e3779b9u) g_read_sink = acc;
 }
 
+// Two waves per SIMD (8 per workgroup, one workgroup per compute unit), each
+// issuing 32 independent 16x16x32 products per iteration: 8 A operands x 4
+// B operands into 32 accumulators, the operand shape of the decode kernels'
+// value products.  Operands are small multiples of 1/64, so the sums stay
+// finite; the accumulators are kept alive by a store no input triggers.
+template <bool BF16>
+__global__ __launch_bounds__(kMfmaThreads) void fca_mfma_rate_kernel(int iters) {
+  const int lane = threadIdx.x & 63;
+  typedef typename std::conditional<BF16, bf16x8, f16x8>::type op8;
+  typedef typename std::conditional<BF16, __bf16, _Float16>::type elem;
+  op8 a[8], b[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[i][j] = (elem)((float)((lane + 3 * i + j) & 7) * 0.015625f);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[i][j] = (elem)((float)((5 * lane + i + j) & 7) * 0.015625f);
+  f32x4 o[4][8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[c][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (BF16)
+          o[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[d], b[c], o[c][d], 0, 0, 0);
+        else
+          o[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[d], b[c], o[c][d], 0, 0, 0);
+      }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) sum += o[c][d][0] + o[c][d][1] + o[c][d][2] + o[c][d][3];
+  if (sum == -1.f) g_mfma_sink = sum;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_rate(bool bf16, int iters, int n_cu, hipStream_t s) {
+  const int grid = std::max(1, n_cu);
+  if (bf16)
+    hipLaunchKernelGGL(fca_mfma_rate_kernel<true>, dim3(grid), dim3(kMfmaThreads), 0, s, iters);
+  else
+    hipLaunchKernelGGL(fca_mfma_rate_kernel<false>, dim3(grid), dim3(kMfmaThreads), 0, s, iters);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* src, size_t bytes, int n_cu, int shape, hipStream_t s) {
   const int64_t n16 = (int64_t)(bytes / 16);

@@ -187,7 +187,7 @@ def test_struct_layouts_match_header(tmp_path):
 
 
 def test_layers_and_probe_validation_before_device():
-    """fca_decode_layers, fca_kv_append_layers and fca_measure_read_bandwidth
+    """fca_decode_layers, fca_kv_append_layers and the two measurement probes
     reject bad arguments without touching the device; zero layers or an empty
     batch launch nothing."""
     L = fca.lib()
@@ -212,3 +212,7 @@ def test_layers_and_probe_validation_before_device():
     assert L.fca_measure_read_bandwidth(arr, 1, 1000, 1, None, ctypes.byref(g)) == 1  # not a multiple of 16
     assert L.fca_measure_read_bandwidth(one(odd), 1, 1 << 20, 1, None, ctypes.byref(g)) == 1
     assert L.fca_measure_read_bandwidth(arr, 1, 1 << 20, 0, None, ctypes.byref(g)) == 1
+    assert L.fca_measure_mfma_rate(fca.FCA_MFMA_BF16, 16, None, None) == 1  # no result pointer
+    assert L.fca_measure_mfma_rate(7, 16, None, ctypes.byref(g)) == 1  # unknown operand type
+    assert L.fca_measure_mfma_rate(fca.FCA_MFMA_F16, 0, None, ctypes.byref(g)) == 1
+    assert L.fca_measure_mfma_rate(fca.FCA_MFMA_F16, (1 << 20) + 1, None, ctypes.byref(g)) == 1
