@@ -42,7 +42,7 @@ FLAGS = [
 
 
 HOST_CXX = os.environ.get("CXX", "g++")
-HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wno-unused-parameter", "-I" + os.path.join(ROOT, "include")]
+HOST_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wno-unused-parameter", "-I" + os.path.join(ROOT, "include")]
 
 
 def _compile(src: str, verbose: bool) -> str:

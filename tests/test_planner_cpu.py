@@ -60,9 +60,10 @@ def harness(tmp_path_factory):
 
 @pytest.fixture(scope="module")
 def harness_fast(tmp_path_factory):
-    """Optimised build without sanitizers, for the planner's host time."""
+    """Optimised build without sanitizers (the library's host flags), for the
+    planner's host time."""
     tmp = str(tmp_path_factory.mktemp("planner_fast"))
-    return _build(tmp, "planner_o2", ["-O2"])
+    return _build(tmp, "planner_o3", ["-O3"])
 
 
 def readback_from_oracle(tables, lens, bs, cascade=True, seed=0):
