@@ -1,13 +1,13 @@
 """rocprofv3 runs of bench.py and their summaries (kernel times and HBM traffic).
 
-    python -m shared_prefix_kv_amd.profiling run --config NAME [--out-dir gpurun_out/prof]
+    python -m shared_prefix_kv_amd.profiling run --config NAME [--out-dir DIR] [--bench-arg=ARG]...
     python -m shared_prefix_kv_amd.profiling summarize \\
         --stats DIR --fetch DIR --write DIR --config NAME --out FILE [--cmd "..."]...
 
-``run`` (on a GPU machine) runs the four rocprofv3 passes below one after the
+``run`` (on the MI355X) runs the four rocprofv3 passes below one after the
 other as child processes, each under its own time limit, and then writes the
-summary to profiles/<kernel>.<config>.txt; this process itself never touches
-the GPU.
+summary to profiles/<kernel>.<config>.txt and a copy of it into the output
+folder; this process itself never touches the GPU.
 
 DIR are rocprofv3 output folders (``-f csv``): ``--stats`` from
 ``--kernel-trace --stats``, ``--fetch`` / ``--write`` from ``--pmc FETCH_SIZE``
@@ -183,7 +183,7 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
     lines = [
         f"# {kernel} on the {config} workload: kernel times and HBM traffic (rocprofv3)",
         "",
-        "Commands (from the repository root on the GPU box):",
+        "Commands (from the repository root, on the MI355X):",
     ]
     lines += [f"  {c}" for c in cmds]
     lines += [
@@ -290,7 +290,7 @@ def run(config: str, out_dir: str, extra: list[str], timeout_s: int = 300) -> st
     for name, opts in PASSES:
         d = os.path.join(out_dir, config_dir, name)
         cmd = ["timeout", "-k", "10", str(timeout_s), "rocprofv3", *opts, "-f", "csv", "-d", d, "-o", "run", "--", *bench]
-        shown = " ".join(cmd).replace(ROOT, "<repo>").replace(sys.executable, "python3")
+        shown = " ".join(cmd).replace(out_dir, "<out>").replace(ROOT, "<repo>").replace(sys.executable, "python3")
         cmds.append(shown)
         print("[profile]", shown, flush=True)
         res = subprocess.run(cmd, cwd="/tmp", env=env)
@@ -316,14 +316,15 @@ def run(config: str, out_dir: str, extra: list[str], timeout_s: int = 300) -> st
     summ = [
         f"python3 -m shared_prefix_kv_amd.profiling summarize --stats {out_dir}/{config_dir}/stats --fetch "
         f"{out_dir}/{config_dir}/fetch --write {out_dir}/{config_dir}/write --util {out_dir}/{config_dir}/util --config {label} "
-        f"--copy-bytes {COPY_BYTES} --algorithmic-bytes {algo} --out profiles/{kernel}.{label}.txt".replace(ROOT, "<repo>")
+        f"--copy-bytes {COPY_BYTES} --algorithmic-bytes {algo} --out profiles/{kernel}.{label}.txt".replace(out_dir, "<out>").replace(ROOT, "<repo>")
     ]
-    cmds = [f"python3 -m shared_prefix_kv_amd.profiling run --config {config}" + (" " + " ".join(extra) if extra else ""),
+    cmds = [f"python3 -m shared_prefix_kv_amd.profiling run --config {config} --out-dir <out>"
+            + "".join(f" --bench-arg={a}" for a in extra),
             "which runs:"] + ["  " + c for c in cmds + summ]
     text = summarize(os.path.join(out_dir, config_dir, "stats"), os.path.join(out_dir, config_dir, "fetch"),
                      os.path.join(out_dir, config_dir, "write"), label, COPY_BYTES, algo, cmds, out,
                      os.path.join(out_dir, config_dir, "util"))
-    # a copy beside the raw results (the folder that comes back from a GPU machine)
+    # a copy beside the raw rocprofv3 results
     with open(os.path.join(out_dir, os.path.basename(out)), "w") as fh:
         fh.write(text)
     return out
@@ -342,7 +343,7 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
     r.add_argument("--config", required=True)
-    r.add_argument("--out-dir", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    r.add_argument("--out-dir", default=os.path.join(ROOT, "_build", "prof"))
     r.add_argument("--bench-arg", action="append", default=[], help="extra bench.py argument (repeatable)")
     s = sub.add_parser("summarize")
     s.add_argument("--stats", required=True)
