@@ -4,7 +4,7 @@
     python -m shared_prefix_kv_amd.profiling summarize \\
         --stats DIR --fetch DIR --write DIR --config NAME --out FILE [--cmd "..."]...
 
-``run`` (on the MI355X) runs the four rocprofv3 passes below one after the
+``run`` (on the MI355X) runs the five rocprofv3 passes below one after the
 other as child processes, each under its own time limit, and then writes the
 summary to profiles/<kernel>.<config>.txt and a copy of it into the output
 folder; this process itself never touches the GPU.
@@ -120,24 +120,31 @@ def _pick(by: dict[str, list[float]], key: str) -> list[float]:
 
 
 UTIL_COUNTERS = ("MfmaUtil", "LdsUtil", "LDSBankConflict", "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+MOPS_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16",)
 
 
-def utilisation(dirpath: str, kernels, durations) -> dict:
+def utilisation(dirpath: str, kernels, durations, mops_dir: str | None = None) -> dict:
     """Median per dispatch of the matrix-core and LDS counters of a
     ``--pmc MfmaUtil LdsUtil LDSBankConflict SQ_INSTS_VALU_MFMA_MOPS_BF16``
     run, per kernel, plus the bf16 matrix rate from the operation count
-    (512 per unit) over the kernel's median duration."""
+    (512 per unit) over the kernel's median duration; with ``mops_dir`` (a
+    ``--pmc SQ_INSTS_VALU_MFMA_MOPS_F16`` run) the fp16 rate as well."""
     res = {}
+    sources = [(dirpath, UTIL_COUNTERS)]
+    if mops_dir and glob.glob(os.path.join(mops_dir, "**", "*counter_collection.csv"), recursive=True):
+        sources.append((mops_dir, MOPS_COUNTERS))
     for key in kernels:
         row = {}
-        for c in UTIL_COUNTERS:
-            vals = _pick({k: v for k, v in _raw_counters(dirpath, c).items()}, key)
-            if vals:
-                row[c] = statistics.median(vals)
+        for d_, counters in sources:
+            for c in counters:
+                vals = _pick({k: v for k, v in _raw_counters(d_, c).items()}, key)
+                if vals:
+                    row[c] = statistics.median(vals)
         if row:
             d = durations.get(key)
-            if d and "SQ_INSTS_VALU_MFMA_MOPS_BF16" in row:
-                row["bf16_TFLOPs"] = row["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / (statistics.median(d) * 1e-6) / 1e12
+            for c, name in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", "bf16_TFLOPs"), ("SQ_INSTS_VALU_MFMA_MOPS_F16", "f16_TFLOPs")):
+                if d and c in row:
+                    row[name] = row[c] * 512 / (statistics.median(d) * 1e-6) / 1e12
             res[key] = row
     return res
 
@@ -152,7 +159,8 @@ def _raw_counters(dirpath: str, counter: str) -> dict[str, list[float]]:
     return {k: [v for _, v in sorted(vals)] for k, vals in by.items()}
 
 
-def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_bytes, cmds, out, util_dir=None):
+def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_bytes, cmds, out, util_dir=None,
+              mops_dir=None):
     stats = kernel_stats(stats_dir)
     att_kernels = [k for k in (ATTENTION, MLA_GROUPED, MLA_SUFFIX) if kernel_durations(stats_dir, k)]
     if not att_kernels:
@@ -220,17 +228,18 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
         )
     util = {}
     if util_dir:
-        util = utilisation(util_dir, att_kernels + [MERGE], durations)
+        util = utilisation(util_dir, att_kernels + [MERGE], durations, mops_dir)
         lines += [
             "",
             "Matrix cores and LDS per dispatch (median; rocprofv3 derived counters MfmaUtil, LdsUtil,",
-            "LDSBankConflict in percent of GPU-active time, and the bf16 MFMA operation count):",
+            "LDSBankConflict in percent of GPU-active time, and the bf16 / fp16 MFMA operation counts):",
         ]
         for key, v in util.items():
             lines.append(
                 f"  {key:24s} MFMA busy {v.get('MfmaUtil', float('nan')):6.1f} %  LDS active {v.get('LdsUtil', float('nan')):6.1f} %"
                 f"  LDS bank conflicts {v.get('LDSBankConflict', float('nan')):5.1f} %"
                 + (f"  bf16 MFMA {v['bf16_TFLOPs']:7.1f} TFLOP/s" if "bf16_TFLOPs" in v else "")
+                + (f"  fp16 MFMA {v['f16_TFLOPs']:7.1f} TFLOP/s" if "f16_TFLOPs" in v else "")
             )
     payload = dict(
         config=config,
@@ -272,11 +281,13 @@ PASSES = [
     ("fetch", ["--pmc", "FETCH_SIZE"]),
     ("write", ["--pmc", "WRITE_SIZE"]),
     ("util", ["--pmc", "MfmaUtil", "LdsUtil", "LDSBankConflict", "SQ_INSTS_VALU_MFMA_MOPS_BF16"]),
+    ("mops", ["--pmc", "SQ_INSTS_VALU_MFMA_MOPS_F16"]),
 ]
+OPTIONAL_PASSES = ("mops",)
 
 
 def run(config: str, out_dir: str, extra: list[str], timeout_s: int = 300) -> str:
-    """The four rocprofv3 passes of ``bench.py --profile-only`` for one
+    """The rocprofv3 passes of ``bench.py --profile-only`` for one
     workload, then the summary; returns its path."""
     import subprocess
     import sys
@@ -298,7 +309,7 @@ def run(config: str, out_dir: str, extra: list[str], timeout_s: int = 300) -> st
         # files are complete; a missing result file is what counts as failure
         found = glob.glob(os.path.join(d, "**", "*kernel_stats.csv" if name == "stats" else "*counter_collection.csv"),
                           recursive=True)
-        if not found:
+        if not found and name not in OPTIONAL_PASSES:
             raise RuntimeError(f"rocprofv3 pass {name} left no results (exit {res.returncode})")
     # algorithmic bytes of the dominant launch, as bench.py reports them
     algo = 0
@@ -315,7 +326,7 @@ def run(config: str, out_dir: str, extra: list[str], timeout_s: int = 300) -> st
     out = os.path.join(ROOT, "profiles", f"{kernel}.{label}.txt")
     summ = [
         f"python3 -m shared_prefix_kv_amd.profiling summarize --stats {out_dir}/{config_dir}/stats --fetch "
-        f"{out_dir}/{config_dir}/fetch --write {out_dir}/{config_dir}/write --util {out_dir}/{config_dir}/util --config {label} "
+        f"{out_dir}/{config_dir}/fetch --write {out_dir}/{config_dir}/write --util {out_dir}/{config_dir}/util --mops {out_dir}/{config_dir}/mops --config {label} "
         f"--copy-bytes {COPY_BYTES} --algorithmic-bytes {algo} --out profiles/{kernel}.{label}.txt".replace(out_dir, "<out>").replace(ROOT, "<repo>")
     ]
     cmds = [f"python3 -m shared_prefix_kv_amd.profiling run --config {config} --out-dir <out>"
@@ -323,7 +334,7 @@ def run(config: str, out_dir: str, extra: list[str], timeout_s: int = 300) -> st
             "which runs:"] + ["  " + c for c in cmds + summ]
     text = summarize(os.path.join(out_dir, config_dir, "stats"), os.path.join(out_dir, config_dir, "fetch"),
                      os.path.join(out_dir, config_dir, "write"), label, COPY_BYTES, algo, cmds, out,
-                     os.path.join(out_dir, config_dir, "util"))
+                     os.path.join(out_dir, config_dir, "util"), os.path.join(out_dir, config_dir, "mops"))
     # a copy beside the raw rocprofv3 results
     with open(os.path.join(out_dir, os.path.basename(out)), "w") as fh:
         fh.write(text)
@@ -354,12 +365,13 @@ def main():
     s.add_argument("--algorithmic-bytes", type=int, default=0)
     s.add_argument("--cmd", action="append", default=[])
     s.add_argument("--util", default=None, help="rocprofv3 folder of the matrix-core / LDS counter run")
+    s.add_argument("--mops", default=None, help="rocprofv3 folder of the fp16 MFMA operation-count run")
     s.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.cmd == "run":
         print(open(run(a.config, a.out_dir, a.bench_arg)).read(), end="")
         return
-    print(summarize(a.stats, a.fetch, a.write, a.config, a.copy_bytes, a.algorithmic_bytes, a.cmd, a.out, a.util), end="")
+    print(summarize(a.stats, a.fetch, a.write, a.config, a.copy_bytes, a.algorithmic_bytes, a.cmd, a.out, a.util, a.mops), end="")
 
 
 if __name__ == "__main__":
