@@ -11,9 +11,11 @@
 // all read the same KV tiles, so QK^T and PV are real matrix products and run
 // on bf16 MFMA; a per-request item has the Hq/Hkv <= 16 rows of each head.
 //
-// Persistent workgroups of 4 independent waves, two workgroups per CU (two
-// waves per SIMD): the planner cuts the work items of both passes into one
-// equal run of work per workgroup (its bin).  In an item the 4 waves are H
+// Persistent workgroups of 4 independent waves, one or two workgroups per CU
+// (the planner's choice: two on small batches, where they hide each other's
+// stalls; one on large ones, which halves the token splits): the planner
+// cuts the work items of both passes into one equal run of work per
+// workgroup (its bin).  In an item the 4 waves are H
 // heads x C column groups (up to 32 rows each; C = 2 only for items wider
 // than 32 rows) x S = 4/(H C) block stripes; the wave of stripe t reads
 // blocks t, t + S, ... of the range.  With the usual pool layout (the heads

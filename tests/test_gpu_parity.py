@@ -310,10 +310,12 @@ def test_decode_edge_lengths_and_ratios(hq, hkv):
 @pytest.mark.parametrize("kind", ["gqa", "mla"])
 def test_decode_short_requests_precision(kind):
     """Requests of 2 to 9 tokens: the output is a weighted mean of a few
-    value rows, so rounding the probabilities alone (bf16 keeps 8 bits)
-    would leave errors above the tolerance wherever the rows cancel; the
-    kernels apply each probability to about 16 bits (12 in the latent
-    kernel) and must stay within it on every element."""
+    value rows, so rounding the probabilities alone to bf16 (8 bits) would
+    leave errors above the tolerance wherever the rows cancel.  The GQA
+    kernel applies each probability to about 16 bits (two bf16 operands);
+    the latent kernel rounds it to fp16 (11 bits) and multiplies fp16 copies
+    of the value rows (exact below 65504).  Both must stay within the
+    tolerance on every element."""
     if kind == "gqa":
         shape = AttnShape(32, 8, 128, 128, 16, 1 / math.sqrt(128))
     else:
