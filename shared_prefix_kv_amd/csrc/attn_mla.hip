@@ -370,6 +370,9 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
         ph[ct] = *reinterpret_cast<const f16x8*>(lds + kOffP + buf * kPTile + (ct * 64 + lane) * 16);
+      float al[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) al[ct] = *reinterpret_cast<const float*>(lds + kOffA + buf * 256 + (16 * ct + c16) * 4);
       // The copy of stage t + 2 goes into the slot of stage t - 2, which
       // every wave finished before this barrier.  It is issued after the P
       // reads, which then reach LDS ahead of more of the score waves' key
@@ -433,9 +436,6 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
         // First stage of the item: fresh accumulators.
         products(true);
       } else {
-        float al[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) al[ct] = *reinterpret_cast<const float*>(lds + kOffA + buf * 256 + (16 * ct + c16) * 4);
         bool scale = false;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) scale |= ct < nct && al[ct] != 1.f;
