@@ -240,8 +240,9 @@ def short_record(name, torch, fca, steps, warmup, layers=4):
     fca.fca_plan(bt, sl, desc)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    create = []
     for _ in range(5):
-        fca.fca_plan(bt, sl, desc)
+        create.append(fca.fca_plan(bt, sl, desc).create_ms)
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - t0) * 1000 / 5
     for key, desc in (
@@ -279,6 +280,7 @@ def short_record(name, torch, fca, steps, warmup, layers=4):
         "speedup_vs_non_cascade": round(ms_nc / ms, 3),
         "plan_ms": round(plan_ms, 3),
         "plan_ms_per_layer_of_32": round(plan_ms / 32, 4),
+        "plan_create_call_ms": round(float(np.median(create)), 3),
         "folded_groups": int(info.num_folded_groups),
     }
     if latent:
@@ -431,8 +433,10 @@ def main():
     torch.cuda.synchronize()
     plan_ms_first = (time.perf_counter() - t0) * 1000
     t0 = time.perf_counter()
+    create = []
     for _ in range(5):
         plan = fca.fca_plan(bt, sl, desc)
+        create.append(plan.create_ms)
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - t0) * 1000 / 5
     info = plan.info
@@ -615,6 +619,7 @@ def main():
         "grouped_mfma_frac_of_peak": round(grouped_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "plan_ms": round(plan_ms, 3),
         "plan_ms_per_layer_of_32": round(plan_ms / 32, 4),
+        "plan_create_call_ms": round(float(np.median(create)), 3),
         "plan_ms_first_call": round(plan_ms_first, 3),
         "roofline": roofline,
     }

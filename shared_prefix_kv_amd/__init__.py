@@ -10,6 +10,7 @@ libfca.so is missing, ``lib()`` raises.
 from __future__ import annotations
 
 import ctypes
+import time
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -308,6 +309,7 @@ class Plan:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=block_tables.device)
         self.workspace = workspace  # must outlive the plan
         h = ctypes.c_void_p()
+        t0 = time.perf_counter()
         _check(
             lib().fca_plan_create(
                 _ptr(block_tables),
@@ -322,6 +324,9 @@ class Plan:
                 ctypes.byref(h),
             )
         )
+        # host time of the C call: discovery, its one read-back, planning and
+        # the upload; the two table kernels queued last run asynchronously
+        self.create_ms = (time.perf_counter() - t0) * 1000.0
         self._h = h
         info = PlanInfo()
         _check(lib().fca_plan_get_info(self._h, ctypes.byref(info)))
