@@ -355,6 +355,47 @@ def test_decode_empty_batch_and_all_empty():
     assert (out.float() == 0).all() and torch.isneginf(lse).all()
 
 
+def test_plan_and_decode_largest_batch():
+    """The largest batch the library takes (8192 requests), all in one tree:
+    a 3-block root shared by every request, 64 branches of 2 more blocks,
+    128 samples per branch with a suffix of 1 to 16 tokens.  Discovery sorts
+    all 8192 members in one workgroup's LDS; the grouping must equal the
+    oracle's and every request's decode must match the oracle."""
+    shape = AttnShape(4, 1, 128, 128, 16, 1 / math.sqrt(128))
+    B, branches, W = 8192, 64, 6
+    per = B // branches
+    rng = np.random.default_rng(8192)
+    sfx = rng.integers(1, 17, size=B).astype(np.int32)
+    n_used = 3 + 2 * branches + B
+    nb = n_used + 64
+    ids = rng.permutation(nb).astype(np.int32)
+    tables = rng.integers(0, nb, size=(B, W)).astype(np.int32)  # entries past a request's blocks: arbitrary
+    for i in range(B):
+        br = i // per
+        tables[i, :3] = ids[:3]
+        tables[i, 3:5] = ids[3 + 2 * br : 5 + 2 * br]
+        tables[i, 5] = ids[3 + 2 * branches + i]
+    order = rng.permutation(B)  # members of a branch are not contiguous in the batch
+    tables, lens = tables[order], (5 * 16 + sfx)[order].astype(np.int32)
+    say("largest batch: B", B, "blocks", nb)
+    bt, sl = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    p = fca.fca_plan(bt, sl, fca.desc_from_shape(shape, nb, auto_fold=False))
+    exp = group(tables, lens, 16)
+    assert with_block_ids(p.export(), tables) == exp
+    assert p.info.num_groups == 1 + branches
+    say("largest batch: groups", p.info.num_groups, "equal to the oracle's")
+    case = small_case(shape, tables, lens, nb, seed=8193)
+    ref, ref_lse = A.attend(case["q"], case["k"], case["v"], tables, lens, shape)
+    b = _B(shape, tables, lens, nb)
+    vals = upload(case)
+    for cascade, fold in MODES:
+        _, out, lse = run_decode(b, vals, cascade=cascade, auto_fold=fold)
+        rep = assert_close(bf16_tensor_to_f64(out), ref, f"largest batch cascade={cascade} fold={fold}")
+        assert_lse_close(lse.cpu().numpy(), ref_lse, "largest batch")
+        say("largest batch", "cascade" if cascade else "non-cascade", "fold" if fold else "keep", rep)
+        del out, lse
+
+
 def test_decode_strided_pool():
     """Pools that are slices of a larger buffer (head/block strides)."""
     b = build_batch(CONFIGS["tiny"])
