@@ -216,6 +216,18 @@ def read_peak(torch, fca):
     return gbps
 
 
+def token_row_pools(pools):
+    """The same pools as token rows, [blocks][slots][kv heads][dims] (the
+    descriptor's default row strides), rearranged on the device."""
+    out = []
+    for k, v in pools:
+        nb, H, c, bs, e = k.shape
+        kr = k.permute(0, 3, 1, 2, 4).reshape(nb, bs, H, c * e).contiguous()
+        vr = v.permute(0, 3, 1, 2).contiguous() if v is not None else None
+        out.append((kr, vr))
+    return out
+
+
 def short_record(name, torch, fca, steps, warmup, layers=4):
     """Cascade vs non-cascade on another workload: decode time per step, the
     logical-KV rate, unique-KV GB/s, the byte ratio R and the speedup."""
@@ -267,6 +279,13 @@ def short_record(name, torch, fca, steps, warmup, layers=4):
                 "suffix_GBps": round(pb["suffix"] / (t["suffix_ms"] / 1000.0) / 1e9, 1) if t["suffix_ms"] > 0 else None,
             }
         del plan
+    # The same plan over pools of token rows.
+    rpools = token_row_pools(pools)
+    plan = fca.fca_plan(bt, sl, fca.desc_from_shape(sh, batch.num_blocks, token_rows=True))
+    plan.decode_workspace(out.device)
+    warm(plan, qs, rpools, out, lse, warmup, torch, fca)
+    ms_rows, _ = time_steps(plan, qs, rpools, out, lse, steps, torch, fca)
+    del plan, rpools
     ms, info = res["fca"]
     ms_nc, _ = res["non_cascade"]
     tok_bytes = sh.kv_bytes_per_token()
@@ -274,6 +293,7 @@ def short_record(name, torch, fca, steps, warmup, layers=4):
         "workload": f"{cfg.name}: {cfg.description}",
         "fca_us_per_step": round(ms * 1000, 2),
         "non_cascade_us_per_step": round(ms_nc * 1000, 2),
+        "token_rows_us_per_step": round(ms_rows * 1000, 2),
         "logical_kv_tokens_per_s": round(int(info.logical_tokens) / (ms / 1000.0), 1),
         "unique_kv_GBps": round(int(info.unique_tokens) * tok_bytes / (ms / 1000.0) / 1e9, 1),
         "byte_ratio_R": round(int(info.logical_tokens) / max(int(info.unique_tokens), 1), 3),
@@ -646,6 +666,25 @@ def main():
             "keep_groups_ms_per_step": round(ms_kg, 5),
         }
         del plan_kg
+
+    if not args.profile_only:
+        # The same batch over pools of token rows ([blocks][slots][kv heads]
+        # [dims]), which the kernels gather into the tile arrangement.
+        rpools = token_row_pools(pools)
+        plan_r = fca.fca_plan(bt, sl, fca.desc_from_shape(sh, batch.num_blocks, token_rows=True,
+                                                          cascade=not args.no_cascade))
+        plan_r.decode_workspace(out.device)
+        warm(plan_r, qs, rpools, out, lse, warmup, torch, fca)
+        ms_r, _ = time_steps(plan_r, qs, rpools, out, lse, steps, torch, fca)
+        log(f"fca decode from token-row pools: {ms_r * 1000:.1f} us/step")
+        result["token_rows"] = {
+            "layout": "[blocks][slots][kv_heads][dims]",
+            "ms_per_step": round(ms_r, 5),
+            "value": round(logical / (ms_r / 1000.0), 1),
+            "time_over_tiles": round(ms_r / ms, 4),
+        }
+        del plan_r, rpools
+        torch.cuda.empty_cache()
 
     if not args.no_noncascade and not args.profile_only:
         desc_nc = fca.desc_from_shape(sh, batch.num_blocks, cascade=False)

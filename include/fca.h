@@ -82,18 +82,41 @@ typedef enum fca_status {
 /*
  * Shape and cache layout of one attention layer.
  *
- * Cache layout (bf16, elements, d = head-dim index, t = slot in the block):
- *   key  (blk, h, t, d) at k_cache[blk*k_stride_block + h*k_stride_head
- *                                  + (d/8)*(block_size*8) + t*8 + d%8]
- *   value(blk, h, t, d) at v_cache[blk*v_stride_block + h*v_stride_head
- *                                  + d*block_size + t]
- * i.e. inside one (block, head) tile keys are stored in 16-byte chunks of 8
- * head dims, chunk-major, and values are stored transposed (one row of
- * block_size tokens per value dim).  With v_aliases_k = 1 (latent caches)
- * the values are the first head_dim_v key dims of the same tile and v_cache
- * is ignored.  Strides are in elements; a tile must not straddle strides
- * (k_stride_head >= head_dim_qk*block_size, and so on), and every tile must
- * start on a 16-byte boundary.
+ * Cache layout (bf16, elements, d = head-dim index, t = slot in the block).
+ * Two layouts are read; k_stride_token chooses:
+ *
+ *   tiles (k_stride_token = v_stride_token = 0):
+ *     key  (blk, h, t, d) at k_cache[blk*k_stride_block + h*k_stride_head
+ *                                    + (d/8)*(block_size*8) + t*8 + d%8]
+ *     value(blk, h, t, d) at v_cache[blk*v_stride_block + h*v_stride_head
+ *                                    + d*block_size + t]
+ *     i.e. inside one (block, head) tile keys are stored in 16-byte chunks
+ *     of 8 head dims, chunk-major, and values transposed (one row of
+ *     block_size tokens per value dim).  A tile must not straddle strides
+ *     (k_stride_head >= head_dim_qk*block_size, and so on).
+ *
+ *   token rows (k_stride_token > 0): each (block, head, slot) holds one row
+ *   of head dims with unit stride,
+ *     key  (blk, h, t, d) at k_cache[blk*k_stride_block + h*k_stride_head
+ *                                    + t*k_stride_token + d]
+ *     value(blk, h, t, d) at v_cache[blk*v_stride_block + h*v_stride_head
+ *                                    + t*v_stride_token + d]
+ *     e.g. [num_blocks][block_size][num_kv_heads][head_dim] (token stride
+ *     num_kv_heads*head_dim, head stride head_dim) or
+ *     [num_blocks][num_kv_heads][block_size][head_dim] (token stride
+ *     head_dim, head stride block_size*head_dim).  Both token strides are
+ *     set (GQA), and every stride is at least the row width (GQA: token,
+ *     head and block strides >= 128; latent: token stride in
+ *     [576, 2^20], block stride >= 576, head stride >= 0); the caller keeps
+ *     rows of different (block, head, slot) from overlapping.  All
+ *     block_size rows of a referenced block are read, also past a
+ *     request's length.  The kernels gather the rows into the tile
+ *     arrangement on the way into LDS; fca_kv_append writes rows.
+ *
+ * With v_aliases_k = 1 (latent caches) the values are the first head_dim_v
+ * key dims of the same tile or row, and v_cache, v_stride_* are ignored.
+ * Strides are in elements and must be multiples of 8 (every tile and every
+ * row starts on a 16-byte boundary, as must the pools).
  *
  * Supported (others return FCA_ERR_UNSUPPORTED):
  *   - GQA:  head_dim_qk = head_dim_v = 128, block_size = 16,
@@ -118,6 +141,8 @@ typedef struct fca_attn_desc {
   int64_t k_stride_head;
   int64_t v_stride_block;
   int64_t v_stride_head;
+  int64_t k_stride_token; /* 0: tile layout; > 0: token rows (see above) */
+  int64_t v_stride_token; /* 0 with k_stride_token = 0; ignored when v_aliases_k */
   int32_t v_aliases_k;
   float scale;
   uint32_t flags; /* FCA_PLAN_* */

@@ -80,6 +80,8 @@ class AttnDesc(ctypes.Structure):
         ("k_stride_head", ctypes.c_int64),
         ("v_stride_block", ctypes.c_int64),
         ("v_stride_head", ctypes.c_int64),
+        ("k_stride_token", ctypes.c_int64),
+        ("v_stride_token", ctypes.c_int64),
         ("v_aliases_k", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("flags", ctypes.c_uint32),
@@ -203,8 +205,15 @@ def make_desc(
     separate_passes=False,
     out_f32=False,
     auto_fold=True,
+    token_rows=False,
 ) -> AttnDesc:
-    """Descriptor for the documented cache layout (default: dense pools).
+    """Descriptor for one of the two documented cache layouts.
+
+    Tiles (default): ``k_strides`` / ``v_strides`` are (block, head) strides,
+    default dense pools ``[num_blocks][num_kv_heads][tile]``.
+    Token rows (``token_rows=True``): they are (block, head, token) strides,
+    default ``[num_blocks][block_size][num_kv_heads][head_dim]``.
+
     ``auto_fold=False`` keeps every discovered group (FCA_PLAN_KEEP_GROUPS);
     by default the library folds groups that cannot pay for their partial
     rows (GQA caches)."""
@@ -212,13 +221,17 @@ def make_desc(
     d.num_q_heads, d.num_kv_heads = num_q_heads, num_kv_heads
     d.head_dim_qk, d.head_dim_v = head_dim_qk, head_dim_v
     d.block_size, d.num_blocks = block_size, num_blocks
-    ksh = head_dim_qk * block_size
-    d.k_stride_block, d.k_stride_head = k_strides if k_strides else (num_kv_heads * ksh, ksh)
-    vsh = head_dim_v * block_size
+
+    def strides(given, dim):
+        if token_rows:
+            return tuple(given) if given else (block_size * num_kv_heads * dim, dim, num_kv_heads * dim)
+        return tuple(given) + (0,) if given else (num_kv_heads * dim * block_size, dim * block_size, 0)
+
+    d.k_stride_block, d.k_stride_head, d.k_stride_token = strides(k_strides, head_dim_qk)
     if v_aliases_k:
-        d.v_stride_block, d.v_stride_head = d.k_stride_block, d.k_stride_head
+        d.v_stride_block, d.v_stride_head, d.v_stride_token = d.k_stride_block, d.k_stride_head, 0
     else:
-        d.v_stride_block, d.v_stride_head = v_strides if v_strides else (num_kv_heads * vsh, vsh)
+        d.v_stride_block, d.v_stride_head, d.v_stride_token = strides(v_strides, head_dim_v)
     d.v_aliases_k = int(bool(v_aliases_k))
     d.scale = float(scale)
     d.flags = (
@@ -231,7 +244,9 @@ def make_desc(
     return d
 
 
-def desc_from_shape(shape, num_blocks, cascade=True, separate_passes=False, out_f32=False, auto_fold=True) -> AttnDesc:
+def desc_from_shape(
+    shape, num_blocks, cascade=True, separate_passes=False, out_f32=False, auto_fold=True, token_rows=False
+) -> AttnDesc:
     return make_desc(
         shape.num_q_heads,
         shape.num_kv_heads,
@@ -245,6 +260,7 @@ def desc_from_shape(shape, num_blocks, cascade=True, separate_passes=False, out_
         separate_passes=separate_passes,
         out_f32=out_f32,
         auto_fold=auto_fold,
+        token_rows=token_rows,
     )
 
 
@@ -265,9 +281,13 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _pool_extent(num_blocks, stride_block, stride_head, num_heads, tile):
-    """Elements a pool of `num_blocks` blocks spans: the last tile's end."""
-    return (num_blocks - 1) * stride_block + (num_heads - 1) * stride_head + tile
+def _pool_extent(d: AttnDesc, stride_block, stride_head, stride_token, dim):
+    """Elements a pool of ``d.num_blocks`` blocks spans: the end of its last
+    tile, or of its last token row."""
+    last = (d.num_blocks - 1) * stride_block + (d.num_kv_heads - 1) * stride_head
+    if stride_token:
+        return last + (d.block_size - 1) * stride_token + dim
+    return last + dim * d.block_size
 
 
 def _span(t):
@@ -284,12 +304,12 @@ def _check_pool(d: AttnDesc, k_cache, v_cache):
 
     assert k_cache is not None and k_cache.dtype == torch.bfloat16, "k_cache must be a bf16 tensor"
     assert k_cache.data_ptr() % 16 == 0, "k_cache must be 16-byte aligned"
-    need_k = _pool_extent(d.num_blocks, d.k_stride_block, d.k_stride_head, d.num_kv_heads, d.head_dim_qk * d.block_size)
+    need_k = _pool_extent(d, d.k_stride_block, d.k_stride_head, d.k_stride_token, d.head_dim_qk)
     assert _span(k_cache) >= need_k, f"k_cache spans {_span(k_cache)} elements, the descriptor needs {need_k}"
     if not d.v_aliases_k:
         assert v_cache is not None and v_cache.dtype == torch.bfloat16, "v_cache must be a bf16 tensor"
         assert v_cache.data_ptr() % 16 == 0, "v_cache must be 16-byte aligned"
-        need_v = _pool_extent(d.num_blocks, d.v_stride_block, d.v_stride_head, d.num_kv_heads, d.head_dim_v * d.block_size)
+        need_v = _pool_extent(d, d.v_stride_block, d.v_stride_head, d.v_stride_token, d.head_dim_v)
         assert _span(v_cache) >= need_v, f"v_cache spans {_span(v_cache)} elements, the descriptor needs {need_v}"
 
 

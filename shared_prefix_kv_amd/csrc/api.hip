@@ -60,22 +60,39 @@ fca_status check_desc(const fca_attn_desc* d, Kind* kind) {
                    FCA_PLAN_KEEP_GROUPS))
     return fail(FCA_ERR_INVALID_ARG, "unknown flag bits 0x%x", d->flags);
   const int r = d->num_q_heads / d->num_kv_heads;
+  const bool rows = d->k_stride_token != 0;  // token rows, else tiles
+  if (d->k_stride_token < 0 || d->v_stride_token < 0)
+    return fail(FCA_ERR_INVALID_ARG, "token strides must not be negative");
   if (d->head_dim_qk == 128 && d->head_dim_v == 128 && d->block_size == 16 && !d->v_aliases_k) {
     if (r > 16) return fail(FCA_ERR_UNSUPPORTED, "GQA ratio %d > 16 is not built", r);
-    if (d->k_stride_head < 128 * 16 || d->v_stride_head < 128 * 16 ||
-        d->k_stride_block < (int64_t)d->num_kv_heads * d->k_stride_head ||
-        d->v_stride_block < (int64_t)d->num_kv_heads * d->v_stride_head)
+    if (rows != (d->v_stride_token != 0))
+      return fail(FCA_ERR_INVALID_ARG, "k_stride_token and v_stride_token must both be 0 (tiles) or both positive");
+    if (rows) {
+      if (d->k_stride_token < 128 || d->v_stride_token < 128 || d->k_stride_head < 128 || d->v_stride_head < 128 ||
+          d->k_stride_block < 128 || d->v_stride_block < 128)
+        return fail(FCA_ERR_INVALID_ARG, "cache strides are shorter than a 128-dim row");
+    } else if (d->k_stride_head < 128 * 16 || d->v_stride_head < 128 * 16 ||
+               d->k_stride_block < (int64_t)d->num_kv_heads * d->k_stride_head ||
+               d->v_stride_block < (int64_t)d->num_kv_heads * d->v_stride_head) {
       return fail(FCA_ERR_INVALID_ARG, "cache strides overlap tiles");
-    if ((d->k_stride_head | d->k_stride_block | d->v_stride_head | d->v_stride_block) % 8)
-      return fail(FCA_ERR_INVALID_ARG, "cache strides must keep 16-byte tile alignment");
+    }
+    if ((d->k_stride_head | d->k_stride_block | d->v_stride_head | d->v_stride_block | d->k_stride_token |
+         d->v_stride_token) % 8)
+      return fail(FCA_ERR_INVALID_ARG, "cache strides must keep 16-byte alignment");
     *kind = kGqa;
     return FCA_OK;
   }
   if (d->head_dim_qk == 576 && d->head_dim_v == 512 && d->block_size == 64 && d->v_aliases_k) {
-    if (d->k_stride_head < 576 * 64 || d->k_stride_block < (int64_t)d->num_kv_heads * d->k_stride_head)
+    if (rows) {
+      if (d->k_stride_token < 576 || d->k_stride_token > (1 << 20))
+        return fail(FCA_ERR_INVALID_ARG, "latent k_stride_token must lie in [576, 2^20]");
+      if (d->k_stride_head < 0 || d->k_stride_block < 576)
+        return fail(FCA_ERR_INVALID_ARG, "latent cache strides are shorter than a 576-dim row");
+    } else if (d->k_stride_head < 576 * 64 || d->k_stride_block < (int64_t)d->num_kv_heads * d->k_stride_head) {
       return fail(FCA_ERR_INVALID_ARG, "cache strides overlap tiles");
-    if ((d->k_stride_head | d->k_stride_block) % 8)
-      return fail(FCA_ERR_INVALID_ARG, "cache strides must keep 16-byte tile alignment");
+    }
+    if ((d->k_stride_head | d->k_stride_block | d->k_stride_token) % 8)
+      return fail(FCA_ERR_INVALID_ARG, "cache strides must keep 16-byte alignment");
     *kind = kMla;
     return FCA_OK;
   }
@@ -538,6 +555,8 @@ fca_status decode_params(const fca_plan_s* P, const void* q_dev, const void* k_c
   gp->k_stride_head = P->desc.k_stride_head;
   gp->v_stride_block = P->desc.v_stride_block;
   gp->v_stride_head = P->desc.v_stride_head;
+  gp->k_stride_token = P->desc.k_stride_token;
+  gp->v_stride_token = P->desc.v_aliases_k ? 0 : P->desc.v_stride_token;
   gp->part = part;
   gp->items = reinterpret_cast<const WorkItem*>(P->sched + S.items);
   gp->bins = nullptr;
@@ -825,6 +844,8 @@ fca_status fca_kv_append_layers(const fca_attn_desc* desc, int32_t n_layers, con
   p.k_stride_head = desc->k_stride_head;
   p.v_stride_block = alias ? 0 : desc->v_stride_block;
   p.v_stride_head = alias ? 0 : desc->v_stride_head;
+  p.k_stride_token = desc->k_stride_token;
+  p.v_stride_token = alias ? 0 : desc->v_stride_token;
   p.batch = batch;
   p.num_kv_heads = desc->num_kv_heads;
   p.max_blocks = max_blocks;

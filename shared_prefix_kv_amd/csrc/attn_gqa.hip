@@ -28,7 +28,12 @@
 // ahead of the math: per item, an entry with its Q rows, then one entry per
 // (block, head) tile (K tile then V tile, 4 KiB each), all copied with
 // global_load_lds_dwordx4 (16 bytes per lane, 1 KiB contiguous per
-// instruction).  Before using an entry the wave waits until at most the
+// instruction in the tile layout).  From a pool of token rows (one row of
+// 128 dims per (block, head, slot)) each copy instruction moves 4 whole rows
+// of keys or values, so LDS holds both token-major, with the 16-byte chunks
+// of each row permuted by an XOR with the token index (keys: chunk ^ t,
+// values: chunk ^ 2 (t % 8)) so that the operand reads hit distinct banks;
+// values are read transposed (ds_read_b64_tr_b16).  Before using an entry the wave waits until at most the
 // operations of the one entry issued after it are in flight (the count is
 // known exactly; partial stores only add to it, which makes the wait longer,
 // never wrong).  Block IDs and item descriptors come in through scalar loads
@@ -165,6 +170,35 @@ __device__ __forceinline__ Role role_of(const WorkItem& it, int wave) {
   return r;
 }
 
+// The 8 V^T operands of a block from a token-major value tile in LDS (16
+// rows of 128 dims, 16-byte chunk c of token t at chunk c ^ 2 (t % 8) of its
+// row): ds_read_b64_tr_b16, where lane (g, c16) addresses dims
+// 4 (c16 % 4) .. + 3 of sub-tile dt (dims 16 dt .. 16 dt + 15) of token
+// t = 4 g + c16 / 4 and receives dim c16 of tokens 4 g .. 4 g + 3 -- the
+// operand the tile layout gives by a plain read.  Those 8 bytes sit at
+// 256 t + 32 (dt ^ (t % 8)) + 8 (c16 % 4).  One block that waits for its own
+// results.
+__device__ __forceinline__ void read_vt_rows(const char* vt, int g, int c16, u32x2 (&r)[8]) {
+  const int t = 4 * g + (c16 >> 2);
+  const uint32_t a = (uint32_t)(uintptr_t)vt + t * 256 + (c16 & 3) * 8;
+  uint32_t ad[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) ad[dt] = a + 32 * (dt ^ (t & 7));
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n"
+      "ds_read_b64_tr_b16 %1, %9\n"
+      "ds_read_b64_tr_b16 %2, %10\n"
+      "ds_read_b64_tr_b16 %3, %11\n"
+      "ds_read_b64_tr_b16 %4, %12\n"
+      "ds_read_b64_tr_b16 %5, %13\n"
+      "ds_read_b64_tr_b16 %6, %14\n"
+      "ds_read_b64_tr_b16 %7, %15\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+      : "memory");
+}
+
 // Arguments the first copies need, passed ahead of the parameter block so
 // that they arrive preloaded in scalar registers.
 struct CopyArgs {
@@ -175,6 +209,9 @@ struct CopyArgs {
   int64_t ksb, ksh, vsb, vsh;  // strides in elements: key block / head, value block / head
 };
 
+// ROWS: the pools hold token rows (Pm.k_stride_token, Pm.v_stride_token),
+// else tiles.
+template <bool ROWS>
 __device__ __forceinline__ void stream_body(const CopyArgs& ca, const GqaParams& Pm) {
   constexpr int kWaveBytes = kRing * kSlotBytes;
   __shared__ __attribute__((aligned(1024))) char lds[kWaves * kWaveBytes];
@@ -265,8 +302,28 @@ __device__ __forceinline__ void stream_body(const CopyArgs& ca, const GqaParams&
       dk = 0;
     } else {
       const int hd = dit.kv_head + dr.hh;
-      const char* ksrc = ca.k + ((int64_t)cur_id * ca.ksb + (int64_t)hd * ca.ksh) * 2 + lane * 16;
-      const char* vsrc = ca.v + ((int64_t)cur_id * ca.vsb + (int64_t)hd * ca.vsh) * 2 + lane * 16;
+      // Tiles: instruction i copies bytes [1024 i, 1024 i + 1024) of each
+      // tile.  Token rows: instruction i copies rows 4 i .. 4 i + 3; lane l
+      // fills LDS chunk l % 16 of row t = 4 i + l / 16 from the row's chunk
+      // (l % 16) ^ t (keys) or (l % 16) ^ 2 (t % 8) (values).
+      const char* kbase = ca.k + ((int64_t)cur_id * ca.ksb + (int64_t)hd * ca.ksh) * 2;
+      const char* vbase = ca.v + ((int64_t)cur_id * ca.vsb + (int64_t)hd * ca.vsh) * 2;
+      auto ksrc = [&](int i) -> const char* {
+        if constexpr (ROWS) {
+          const int t = 4 * i + (lane >> 4);
+          return kbase + (int64_t)t * Pm.k_stride_token * 2 + ((lane & 15) ^ t) * 16;
+        } else {
+          return kbase + lane * 16 + i * 1024;
+        }
+      };
+      auto vsrc = [&](int i) -> const char* {
+        if constexpr (ROWS) {
+          const int t = 4 * i + (lane >> 4);
+          return vbase + (int64_t)t * Pm.v_stride_token * 2 + ((lane & 15) ^ (2 * (t & 7))) * 16;
+        } else {
+          return vbase + lane * 16 + i * 1024;
+        }
+      };
       // A tile that exactly one wave reads (the planner's kItemStream: a
       // suffix of a cascade plan, or a group whose query rows fit one wave)
       // streams through the caches with the non-temporal policy.  Other
@@ -277,18 +334,18 @@ __device__ __forceinline__ void stream_body(const CopyArgs& ca, const GqaParams&
       if (dit.flags & kItemStream) {
 #pragma unroll
         for (int i = 0; i < kTileBytes / 1024; ++i)
-          __builtin_amdgcn_global_load_lds(ksrc + i * 1024, (lds_void*)(dst + i * 1024), 16, 0, kCachePolicyNT);
+          __builtin_amdgcn_global_load_lds(ksrc(i), (lds_void*)(dst + i * 1024), 16, 0, kCachePolicyNT);
 #pragma unroll
         for (int i = 0; i < kTileBytes / 1024; ++i)
-          __builtin_amdgcn_global_load_lds(vsrc + i * 1024, (lds_void*)(dst + kTileBytes + i * 1024), 16, 0,
+          __builtin_amdgcn_global_load_lds(vsrc(i), (lds_void*)(dst + kTileBytes + i * 1024), 16, 0,
                                            kCachePolicyNT);
       } else {
 #pragma unroll
         for (int i = 0; i < kTileBytes / 1024; ++i)
-          __builtin_amdgcn_global_load_lds(ksrc + i * 1024, (lds_void*)(dst + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(ksrc(i), (lds_void*)(dst + i * 1024), 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < kTileBytes / 1024; ++i)
-          __builtin_amdgcn_global_load_lds(vsrc + i * 1024, (lds_void*)(dst + kTileBytes + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vsrc(i), (lds_void*)(dst + kTileBytes + i * 1024), 16, 0, 0);
       }
       last_ops = kTileOps;
       if (++dk == dr.nblk)
@@ -358,12 +415,26 @@ __device__ __forceinline__ void stream_body(const CopyArgs& ca, const GqaParams&
           // All twelve LDS reads first; V is consumed after the softmax.
           bf16x8 ka[4];
           bf16x4 va[8];
+          if constexpr (ROWS) {
+            // chunk 4 ks + g of token c16, stored at chunk (4 ks + g) ^ c16
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            ka[ks] = *reinterpret_cast<const bf16x8*>(kt + ((4 * ks + g) * kBS + c16) * 16);
+            for (int ks = 0; ks < 4; ++ks)
+              ka[ks] = *reinterpret_cast<const bf16x8*>(kt + c16 * kQRowBytes + ((4 * ks + g) ^ c16) * 16);
+          } else {
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-            va[dt] = *reinterpret_cast<const bf16x4*>(vt + ((16 * dt + c16) * kBS + 4 * g) * 2);
+            for (int ks = 0; ks < 4; ++ks)
+              ka[ks] = *reinterpret_cast<const bf16x8*>(kt + ((4 * ks + g) * kBS + c16) * 16);
+          }
+          if constexpr (ROWS) {
+            u32x2 vr[8];
+            read_vt_rows(vt, g, c16, vr);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) va[dt] = __builtin_bit_cast(bf16x4, vr[dt]);
+          } else {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+              va[dt] = *reinterpret_cast<const bf16x4*>(vt + ((16 * dt + c16) * kBS + 4 * g) * 2);
+          }
           f32x4 s[NCT];
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
@@ -456,14 +527,29 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fca_attention_kernel(const Bin
                                                                       int64_t ksh, int64_t vsb, int64_t vsh,
                                                                       GqaParams p) {
   const CopyArgs ca{bins, items, k, v, ksb, ksh, vsb, vsh};
-  stream_body(ca, p);
+  stream_body<false>(ca, p);
+}
+
+// The same for pools of token rows.
+__global__ __launch_bounds__(kWaves * 64, 2) void fca_attention_rows_kernel(const BinHead* __restrict__ bins,
+                                                                           const WorkItem* __restrict__ items,
+                                                                           const char* k, const char* v,
+                                                                           int64_t ksb, int64_t ksh, int64_t vsb,
+                                                                           int64_t vsh, GqaParams p) {
+  const CopyArgs ca{bins, items, k, v, ksb, ksh, vsb, vsh};
+  stream_body<true>(ca, p);
 }
 
 hipError_t launch_attention(const GqaParams& p, int n_bins, hipStream_t s) {
   if (n_bins <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fca_attention_kernel, dim3(n_bins), dim3(kWaves * 64), 0, s, p.bins, p.items,
-                     static_cast<const char*>(p.k), static_cast<const char*>(p.v), p.k_stride_block,
-                     p.k_stride_head, p.v_stride_block, p.v_stride_head, p);
+  if (p.k_stride_token != 0)
+    hipLaunchKernelGGL(fca_attention_rows_kernel, dim3(n_bins), dim3(kWaves * 64), 0, s, p.bins, p.items,
+                       static_cast<const char*>(p.k), static_cast<const char*>(p.v), p.k_stride_block,
+                       p.k_stride_head, p.v_stride_block, p.v_stride_head, p);
+  else
+    hipLaunchKernelGGL(fca_attention_kernel, dim3(n_bins), dim3(kWaves * 64), 0, s, p.bins, p.items,
+                       static_cast<const char*>(p.k), static_cast<const char*>(p.v), p.k_stride_block,
+                       p.k_stride_head, p.v_stride_block, p.v_stride_head, p);
   return hipGetLastError();
 }
 

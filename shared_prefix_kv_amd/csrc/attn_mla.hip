@@ -166,8 +166,11 @@ __device__ __forceinline__ int item_stages(const Item& it) { return (it.tok_end 
 // Copy cursor: the stages of the bin's items in order, two ahead of the
 // score waves.  Each wave copies instructions [d0, d0 + N) of a stage:
 // instruction i moves chunks 2i and 2i + 1 (32 tokens x 16 B each) of the
-// cache tile into LDS bytes [1024 i, 1024 i + 1024) of the slot.
-template <int N>
+// stage into LDS bytes [1024 i, 1024 i + 1024) of the slot.  From a tile
+// (ROWS false) each chunk is 512 contiguous bytes; from token rows (ROWS
+// true) lane l gathers 16 bytes of token l % 32 of the stage, so the LDS
+// arrangement is the same.
+template <int N, bool ROWS>
 struct Copier {
   cint32* items;
   int di, ds, dns, i_end;
@@ -186,21 +189,36 @@ struct Copier {
     const int id = bt[(int64_t)it.request * P.W + t0 / kBS];
     const char* tile = static_cast<const char*>(P.k) +
                        ((int64_t)id * P.k_stride_block + (int64_t)it.kv_head * P.k_stride_head) * 2;
-    // Raw buffer over the tile (MUBUF loads to LDS: counted by vmcnt alone).
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile), (short)0, kBS * kDq * 2, kBufferWord3);
-    const int voff = (lane >> 5) * (kBS * 16) + (lane & 31) * 16;
-    const int half = ((t0 / kStage) & 1) * kChunk;
+    if constexpr (ROWS) {
+      // Raw buffer over the stage's 32 rows; the plan checks that
+      // 64 * k_stride_token bytes stay far inside 32-bit offsets.
+      const int rb = (int)P.k_stride_token * 2;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(tile + (int64_t)(t0 % kBS) * rb), (short)0, (kStage - 1) * rb + kDq * 2, kBufferWord3);
+      const int voff = (lane & 31) * rb + (lane >> 5) * 16;
 #pragma unroll
-    for (int i = 0; i < N; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (d0 + i) * 1024), 16, voff,
-                                               half + (d0 + i) * 2 * (kBS * 16), 0, 0);
+      for (int i = 0; i < N; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (d0 + i) * 1024), 16, voff, (d0 + i) * 32,
+                                                 0, 0);
+    } else {
+      // Raw buffer over the tile (MUBUF loads to LDS: counted by vmcnt alone).
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile), (short)0, kBS * kDq * 2, kBufferWord3);
+      const int voff = (lane >> 5) * (kBS * 16) + (lane & 31) * 16;
+      const int half = ((t0 / kStage) & 1) * kChunk;
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (d0 + i) * 1024), 16, voff,
+                                                 half + (d0 + i) * 2 * (kBS * 16), 0, 0);
+    }
     next();
   }
 };
 
 }  // namespace
 
+// ROWS: the pool holds token rows (P.k_stride_token), else tiles.
+template <bool ROWS>
 __device__ __forceinline__ void mla_body(GqaParams P) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
 
@@ -338,7 +356,7 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
     // ---------------- value wave: dims 128 v .. 128 v + 127 of all rows ----------------
     const int v = wave - kQkWaves;
     cint32* bt = (cint32*)(P.bt);
-    Copier<kDmaP> cp{items, i_begin, 0, 0, i_end, load_item(items, i_begin)};
+    Copier<kDmaP, ROWS> cp{items, i_begin, 0, 0, i_end, load_item(items, i_begin)};
     cp.dns = item_stages(cp.it);
     const int d0 = v * kDmaP;
     cp.issue(P, bt, lds, d0, lane);
@@ -472,15 +490,17 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
 
 // One entry per pass, so that kernel traces tell the two launches of a decode
 // apart; both run the same code.
-__global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_grouped_kernel(GqaParams P) { mla_body(P); }
-__global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_suffix_kernel(GqaParams P) { mla_body(P); }
+__global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_grouped_kernel(GqaParams P) { mla_body<false>(P); }
+__global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_suffix_kernel(GqaParams P) { mla_body<false>(P); }
+__global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_grouped_rows_kernel(GqaParams P) { mla_body<true>(P); }
+__global__ __launch_bounds__(kWaves * 64, 1) void fca_mla_suffix_rows_kernel(GqaParams P) { mla_body<true>(P); }
 
 hipError_t launch_mla(const GqaParams& p, int n_bins, bool grouped_pass, hipStream_t s) {
   if (n_bins <= 0) return hipSuccess;
-  if (grouped_pass)
-    hipLaunchKernelGGL(fca_mla_grouped_kernel, dim3(n_bins), dim3(kWaves * 64), 0, s, p);
-  else
-    hipLaunchKernelGGL(fca_mla_suffix_kernel, dim3(n_bins), dim3(kWaves * 64), 0, s, p);
+  const bool rows = p.k_stride_token != 0;
+  auto* kern = grouped_pass ? (rows ? fca_mla_grouped_rows_kernel : fca_mla_grouped_kernel)
+                            : (rows ? fca_mla_suffix_rows_kernel : fca_mla_suffix_kernel);
+  hipLaunchKernelGGL(kern, dim3(n_bins), dim3(kWaves * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -59,6 +59,7 @@ struct GqaParams {
   const void* k;
   const void* v;
   int64_t k_stride_block, k_stride_head, v_stride_block, v_stride_head;
+  int64_t k_stride_token, v_stride_token;  // 0: tile layout; > 0: token rows
   PartialPtrs part;
 };
 
@@ -131,6 +132,7 @@ struct AppendParams {
   const int32_t* seq_lens;
   const int32_t* cow_dst;  // may be null
   int64_t k_stride_block, k_stride_head, v_stride_block, v_stride_head;
+  int64_t k_stride_token, v_stride_token;  // 0: tile layout; > 0: token rows
   int32_t batch, num_kv_heads, max_blocks, num_blocks;
 };
 

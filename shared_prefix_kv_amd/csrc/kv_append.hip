@@ -28,8 +28,10 @@
 // of one token, so slot t's pieces come from the new token and later ones are
 // skipped; a value piece is 8 tokens of one dim, and the one holding slot t
 // is merged from the source (slots before t), the new value (slot t) and the
-// target (slots after t).  Each target byte is written once.  Without a copy
-// only the new token's bytes are written.  Requests whose length or block
+// target (slots after t).  In a pool of token rows every piece is 8 dims of
+// one token, keys and values alike, so slot t's pieces come from the new
+// token and later slots are skipped.  Each target byte is written once.
+// Without a copy only the new token's bytes are written.  Requests whose length or block
 // IDs are out of range are skipped; the commit launch sets a bit of *status
 // for them.
 
@@ -72,6 +74,25 @@ __device__ __forceinline__ bool append_target(const int32_t* bt, int64_t stride,
   return true;
 }
 
+// One pool of token rows: slots tok0 .. tok0 + n_tok - 1 of every head of
+// block blk, in 16-byte pieces (8 dims of one token) taken from block cur,
+// except slot t, which takes the new row (fresh: [num_kv_heads][D]).
+template <int D>
+__device__ __forceinline__ void rows_copy(const uint16_t* fresh, uint16_t* cache, int64_t sb, int64_t sh, int64_t st,
+                                          int num_kv_heads, int cur, int blk, int tok0, int n_tok, int t, int tid) {
+  constexpr int kRow = D / 8;  // pieces per row
+  const int per_head = kRow * n_tok;
+  for (int c = tid; c < num_kv_heads * per_head; c += kAppendThreads) {
+    const int h = c / per_head;
+    const int r = c - h * per_head;
+    const int tok = tok0 + r / kRow, dc = r % kRow;
+    const int64_t off = (int64_t)h * sh + (int64_t)tok * st + dc * 8;
+    const uint4 piece = tok == t ? *reinterpret_cast<const uint4*>(fresh + h * D + dc * 8)
+                                 : *reinterpret_cast<const uint4*>(cache + (int64_t)cur * sb + off);
+    *reinterpret_cast<uint4*>(cache + (int64_t)blk * sb + off) = piece;
+  }
+}
+
 template <int DQK, int DV, int BS, bool ALIAS>
 __device__ __forceinline__ void append_body(const AppendParams& p) {
   static_assert(DQK % 8 == 0 && DV % 8 == 0 && BS % 8 == 0, "16-byte pieces");
@@ -88,6 +109,20 @@ __device__ __forceinline__ void append_body(const AppendParams& p) {
   const uint16_t* vn = ALIAS ? nullptr : p.v_new[layer] + (int64_t)i * p.num_kv_heads * DV;
   uint16_t* kc = p.k_cache[layer];
   uint16_t* vc = ALIAS ? nullptr : p.v_cache[layer];
+
+  if (p.k_stride_token != 0) {
+    // Token rows: key (h, tok, d) at h * k_stride_head + tok * k_stride_token + d.
+    // Slots 0 .. t of the copy target, or slot t alone in place.
+    const int blk = dst >= 0 ? dst : cur;
+    const int tok0 = dst >= 0 ? 0 : t;
+    const int n_tok = t + 1 - tok0;
+    rows_copy<DQK>(kn, kc, p.k_stride_block, p.k_stride_head, p.k_stride_token, p.num_kv_heads, cur, blk, tok0, n_tok,
+                   t, tid);
+    if constexpr (!ALIAS)
+      rows_copy<DV>(vn, vc, p.v_stride_block, p.v_stride_head, p.v_stride_token, p.num_kv_heads, cur, blk, tok0,
+                    n_tok, t, tid);
+    return;
+  }
 
   if (dst >= 0) {
     const int per_head = kKPieces + kVPieces;

@@ -81,6 +81,55 @@ def test_workspace_size_and_validation():
         fca.plan_workspace_size(4, 4, d)
 
 
+def test_token_row_descriptors():
+    """Token-row pools: the default strides of both orders are accepted, and
+    mixed, negative, short or misaligned token strides are rejected."""
+    d = gqa_desc(token_rows=True)
+    assert (d.k_stride_block, d.k_stride_head, d.k_stride_token) == (16 * 8 * 128, 128, 8 * 128)
+    assert (d.v_stride_block, d.v_stride_head, d.v_stride_token) == (16 * 8 * 128, 128, 8 * 128)
+    fca.plan_workspace_size(4, 4, d)
+    fca.plan_workspace_size(4, 4, gqa_desc(token_rows=True, k_strides=(8 * 16 * 128, 16 * 128, 128),
+                                           v_strides=(8 * 16 * 128, 16 * 128, 128)))
+    tiles = gqa_desc()
+    assert tiles.k_stride_token == 0 and tiles.v_stride_token == 0
+    bad = []
+    d = gqa_desc(token_rows=True)
+    d.v_stride_token = 0  # keys in rows, values in tiles
+    bad.append(d)
+    d = gqa_desc()
+    d.v_stride_token = 1024  # the other way round
+    bad.append(d)
+    d = gqa_desc(token_rows=True)
+    d.k_stride_token = -1024
+    bad.append(d)
+    d = gqa_desc(token_rows=True)
+    d.k_stride_token = 64  # shorter than a row
+    bad.append(d)
+    d = gqa_desc(token_rows=True)
+    d.v_stride_token = 1028  # not a multiple of 8 elements
+    bad.append(d)
+    d = gqa_desc(token_rows=True)
+    d.k_stride_head = 0
+    bad.append(d)
+    for d in bad:
+        with pytest.raises(fca.FcaError) as e:
+            fca.plan_workspace_size(4, 4, d)
+        assert e.value.status == 1
+    mla = dict(num_q_heads=128, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, block_size=64, num_blocks=10,
+               scale=0.04, v_aliases_k=True, token_rows=True)
+    d = fca.make_desc(**mla)
+    assert (d.k_stride_block, d.k_stride_head, d.k_stride_token) == (64 * 576, 576, 576)
+    assert d.v_stride_token == 0
+    fca.plan_workspace_size(4, 4, d)
+    for field, value in (("k_stride_token", 520), ("k_stride_token", (1 << 20) + 8), ("k_stride_block", 8),
+                         ("k_stride_head", -8)):
+        d = fca.make_desc(**mla)
+        setattr(d, field, value)
+        with pytest.raises(fca.FcaError) as e:
+            fca.plan_workspace_size(4, 4, d)
+        assert e.value.status == 1, field
+
+
 def test_create_rejects_bad_args_before_device():
     L = fca.lib()
     d = gqa_desc()
