@@ -46,11 +46,22 @@ int env_int(const char* name, int dflt) {
 // Split-schedule targets (developer tuning knobs).
 struct Tuning {
   int bins_per_cu;  // attention workgroups per compute unit; 0: chosen from the batch's bytes
+  int wide_cost;    // cost of a stage of a two-column-group lane, in hundredths of another
 };
+
+// A GQA stage is one (block, head) K+V tile per wave.  In a lane of more
+// than 32 query rows its two column-group waves each load every tile and
+// take two 16-column product tiles, and a stage took 1.1-1.2x the time of a
+// stage of a per-request lane (4 rows) on MI355X; the equal-work cut weighs
+// it accordingly (long_rl attention launch 544 -> 519 us; 1.10-1.20 within
+// 1 % of each other on forest_mixed).  Lanes of up to 32 rows keep weight
+// 1: weighing them too made the Llama-3-8B batch slower.
+constexpr int kWideStageCost = 115;
 
 Tuning tuning() {
   Tuning t;
   t.bins_per_cu = env_int("FCA_TUNE_BINS_PER_CU", 0);
+  t.wide_cost = env_int("FCA_TUNE_WIDE_COST", kWideStageCost);
   return t;
 }
 
@@ -285,6 +296,7 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
     int64_t stages;
     int64_t base;
     int splits;
+    int cost;  // of one stage in the cut (hundredths)
   };
   // Appends the lanes of one unit; returns the index of its first lane.
   auto add_lanes = [&](std::vector<Lane>& lanes, int tok0, int tok_end, int request, int member_off,
@@ -300,9 +312,11 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
     for (int hb = 0; hb < hkv / H; ++hb)
       for (int c = 0; c < chunks; ++c) {
         const int col0 = c * icols, col1 = std::min(ncols, (c + 1) * icols);
-        const int S = mla ? 1 : kItemWaves / (H * (col1 - col0 > kWaveCols ? 2 : 1));
+        const int C = col1 - col0 > kWaveCols ? 2 : 1;
+        const int S = mla ? 1 : kItemWaves / (H * C);
+        const int cost = !mla && C == 2 ? t.wide_cost : 100;
         lanes.push_back(Lane{request, member_off, ncols, tok0, tok_end, hb * H, H, col0, col1, S,
-                             one_reader ? kItemStream : 0, ceil_div(nblk, S), 0, 0});
+                             one_reader ? kItemStream : 0, ceil_div(nblk, S), 0, 0, cost});
       }
     *H_out = H;
     *chunks_out = chunks;
@@ -318,11 +332,12 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
   P->bins.assign(1, 0);
   P->launches.clear();
   auto cut = [&](size_t l0, size_t l1, PassSet passes) {
-    int64_t W = 0;
+    int64_t W = 0, n_st = 0;  // cost and stages of the launch
     for (size_t k = l0; k < l1; ++k) {
-      W += all[k].stages;
+      W += all[k].stages * all[k].cost;
+      n_st += all[k].stages;
     }
-    const int64_t nb = std::min<int64_t>(W, (int64_t)n_cu_ * bpc);
+    const int64_t nb = std::min<int64_t>(n_st, (int64_t)n_cu_ * bpc);
     if (nb == 0) return;
     // every bin boundary cuts at most one lane: items <= lanes + bins
     P->items.reserve(P->items.size() + (l1 - l0) + (size_t)nb);
@@ -330,12 +345,17 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
     P->bins.reserve(P->bins.size() + (size_t)nb);
     P->launches.push_back(Launch{(int)P->bins.size() - 1, (int)nb, passes});
     size_t li = l0;
-    int64_t lpos = 0, pos = 0;
+    int64_t lpos = 0, pos = 0, rem = n_st;
     for (int64_t b = 0; b < nb; ++b) {
+      // Bin b ends at cost (b + 1) W / nb, rounded up to whole stages; it
+      // takes at least one stage and leaves at least one for each later bin.
       const int64_t end = (b + 1) * W / nb;
-      while (pos < end) {
+      const int64_t cap = rem - (nb - 1 - b);
+      int64_t got = 0;
+      while ((pos < end || got == 0) && got < cap) {
         Lane& L = all[li];
-        const int64_t take = std::min(L.stages - lpos, end - pos);
+        const int64_t want = pos < end ? ceil_div(end - pos, (int64_t)L.cost) : 1;
+        const int64_t take = std::min({L.stages - lpos, want, cap - got});
         const int64_t stok = (int64_t)L.S * bs;  // tokens per stage
         WorkItem it{};
         it.request = L.request;
@@ -352,7 +372,9 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
         it.flags = L.stream;
         P->items.push_back(it);
         item_lane.push_back((int)li);
-        pos += take;
+        pos += take * L.cost;
+        got += take;
+        rem -= take;
         lpos += take;
         if (lpos == L.stages) {
           ++li;
