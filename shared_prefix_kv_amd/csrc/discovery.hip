@@ -254,22 +254,48 @@ __global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W4, Discovery
       // Bitonic sort of skey[0, N), padded with the largest key.
       int N = 1;
       while (N < n) N <<= 1;
-      for (int x = n + tid; x < N; x += kTreeThreads) skey[x] = ~0ull;
-      __syncthreads();
-      for (int size = 2; size <= N; size <<= 1)
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-          for (int t = tid; t < N / 2; t += kTreeThreads) {
-            const int a = 2 * t - (t & (stride - 1));
-            const int b = a + stride;
-            const bool up = (a & size) == 0;
-            const uint64_t ka = skey[a], kb = skey[b];
-            if ((ka > kb) == up) {
-              skey[a] = kb;
-              skey[b] = ka;
+      if (N <= kTreeThreads) {
+        // One key per thread, in a register: partners within a wave
+        // (stride < 64) are exchanged by shuffles, the others through LDS.
+        uint64_t key = tid < n ? skey[tid] : ~0ull;
+        __syncthreads();
+        for (int size = 2; size <= N; size <<= 1)
+          for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            uint64_t other;
+            if (stride >= 64) {
+              if (tid < N) skey[tid] = key;
+              __syncthreads();
+              other = tid < N ? skey[tid ^ stride] : key;
+              __syncthreads();
+            } else {
+              other = (uint64_t)__shfl_xor((long long)key, stride);
             }
+            // The lower index of a pair keeps the smaller key in an
+            // ascending run (tid & size == 0), the larger in a descending one.
+            const bool lower = (tid & stride) == 0;
+            const bool up = (tid & size) == 0;
+            key = (lower == up) ? (key < other ? key : other) : (key < other ? other : key);
           }
-          __syncthreads();
-        }
+        if (tid < N) skey[tid] = key;
+        __syncthreads();
+      } else {
+        for (int x = n + tid; x < N; x += kTreeThreads) skey[x] = ~0ull;
+        __syncthreads();
+        for (int size = 2; size <= N; size <<= 1)
+          for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = tid; t < N / 2; t += kTreeThreads) {
+              const int a = 2 * t - (t & (stride - 1));
+              const int b = a + stride;
+              const bool up = (a & size) == 0;
+              const uint64_t ka = skey[a], kb = skey[b];
+              if ((ka > kb) == up) {
+                skey[a] = kb;
+                skey[b] = ka;
+              }
+            }
+            __syncthreads();
+          }
+      }
     }
     // Part bounds.  One part: its leader is the smallest key (the members are
     // not sorted then, so the leader is found by its key).
