@@ -241,3 +241,87 @@ def test_append_token_rows_bitexact(shape, layout):
         rep = assert_close(bf16_tensor_to_f64(out), ref, f"decode after row append step {step}")
         assert_lse_close(lse.cpu().numpy(), ref_lse, "decode after row append")
         say("step", step, rep)
+
+
+def test_token_rows_layers_graph_no_alloc_and_append_layers():
+    """Token-row pools through the other entry points: two layers decoded by
+    one fca_decode_layers call captured in a HIP graph (three replays with
+    new queries, each equal to an eager call bit for bit), the no-allocation
+    decode equal to fca_decode, and fca_kv_append_layers over both layers'
+    pools (bit-exact against the oracle's append), all against the oracle."""
+    b = build_batch(CONFIGS["llama3_8b"])
+    sh = b.shape
+    n_layers = 2
+    vns = [fill_values_numpy(b, poison=True) for _ in range(n_layers)]  # batch.rng advances per layer
+    caches, descs = [], []
+    for vn in vns:
+        kr, ks = to_rows(logical_k(vn["k"]), "bthd", 0)
+        vr, vs = to_rows(logical_v(vn["v"]), "bthd", 0)
+        caches.append((to_device_bf16(kr), to_device_bf16(vr)))
+        descs.append(rows_desc(sh, b.num_blocks, ks, vs))
+    desc = descs[0]
+    bt = torch.from_numpy(b.block_tables).cuda()
+    sl = torch.from_numpy(b.seq_lens).cuda()
+    p = fca.fca_plan(bt, sl, desc)
+    shape_out = (b.batch, sh.num_q_heads, sh.head_dim_v)
+    q_static = [to_device_bf16(vn["q"]) for vn in vns]
+    outs_g = [torch.empty(shape_out, dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
+    outs_e = [torch.empty_like(o) for o in outs_g]
+    ws = p.decode_workspace(q_static[0].device)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        p.decode_layers(q_static, caches, outs_g, workspace=ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        p.decode_layers(q_static, caches, outs_g, workspace=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(17)
+    for rep in range(3):
+        q_new = [f32_to_bf16_bits(rng.standard_normal(vn["q"].shape, dtype=np.float32)) for vn in vns]
+        for qs_, qn in zip(q_static, q_new):
+            qs_.copy_(to_device_bf16(qn))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        p.decode_layers([to_device_bf16(qn) for qn in q_new], caches, outs_e, workspace=torch.empty_like(ws))
+        torch.cuda.synchronize()
+        for l in range(n_layers):
+            assert torch.equal(outs_g[l].view(torch.int16), outs_e[l].view(torch.int16)), f"replay {rep} layer {l}"
+    for l in range(n_layers):
+        ref, _ = A.attend(q_new[l], vns[l]["k"], vns[l]["v"], b.block_tables, b.seq_lens, sh)
+        rep = assert_close(bf16_tensor_to_f64(outs_g[l]), ref, f"rows layers, layer {l}")
+        say("rows decode_layers layer", l, rep)
+    del graph
+    # no allocation: equal to fca_decode on the same plan
+    out_w = torch.empty(shape_out, dtype=torch.bfloat16, device="cuda")
+    out_s = torch.empty(shape_out, dtype=torch.bfloat16, device="cuda")
+    p.decode(q_static[0], caches[0][0], caches[0][1], out=out_w)
+    p.decode_no_alloc(q_static[0], caches[0][0], caches[0][1], out_s)
+    torch.cuda.synchronize()
+    assert torch.equal(out_w.view(torch.int16), out_s.view(torch.int16))
+    # one appended token per request into both layers' row pools, no copies
+    tables = np.pad(b.block_tables, ((0, 0), (0, 1)))  # room for a block past the longest request
+    lens = b.seq_lens.copy()
+    free = sorted(set(range(b.num_blocks)) - set(int(x) for x in tables.ravel()))
+    for i, L in enumerate(lens):
+        if L % sh.block_size == 0:
+            tables[i, L // sh.block_size] = free.pop()
+    knews = [f32_to_bf16_bits(rng.standard_normal((b.batch, sh.num_kv_heads, 128), dtype=np.float32))
+             for _ in range(n_layers)]
+    vnews = [f32_to_bf16_bits(rng.standard_normal((b.batch, sh.num_kv_heads, 128), dtype=np.float32))
+             for _ in range(n_layers)]
+    bt2 = torch.from_numpy(tables).cuda()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fca.kv_append_layers([to_device_bf16(k) for k in knews], [to_device_bf16(v) for v in vnews], caches, bt2,
+                         torch.from_numpy(lens).cuda(), desc, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for l in range(n_layers):
+        k2, v2, t2 = KV.append(vns[l]["k"], vns[l]["v"], tables, lens, knews[l], vnews[l], sh.block_size, None)
+        assert (bt2.cpu().numpy() == t2).all()
+        assert (tiles_k(from_rows(to_bits(caches[l][0]), "bthd", 128)) == k2).all(), f"layer {l}: keys"
+        assert (tiles_v(from_rows(to_bits(caches[l][1]), "bthd", 128)) == v2).all(), f"layer {l}: values"
+    say("rows append layers ok")
