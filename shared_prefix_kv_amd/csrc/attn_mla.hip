@@ -133,6 +133,42 @@ __device__ __forceinline__ void read_vt(const char* kt, u32x2 (&r)[8][2]) {
 }
 static_assert(2 * kChunk == 1024 && 16 * 16 == 256 && kPvTiles == 8, "read_vt offsets");
 
+// Stage arrangement of a token-row pool (see Copier): 9 groups of 8 chunks,
+// group G holding 128 bytes of each of the 32 tokens (4 KiB), the 16-byte
+// chunk p of token t's row at position p ^ swz(t) with swz(t) = (t / 2) % 8,
+// which spreads the 16 lanes of an operand read over all banks.
+constexpr int kRowGroup = kStage * 128;  // bytes of one 8-chunk group
+__device__ __forceinline__ int swz(int t) { return (t >> 1) & 7; }
+
+// The 16 V^T operands from a token-row stage: ds_read_b64_tr_b16 at
+// a[dt % 4] + 4096 (dt / 4) + 2048 tt.
+__device__ __forceinline__ void read_vt_rows(const uint32_t (&a)[4], u32x2 (&r)[8][2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:0\n"
+      "ds_read_b64_tr_b16 %1, %16 offset:2048\n"
+      "ds_read_b64_tr_b16 %2, %17 offset:0\n"
+      "ds_read_b64_tr_b16 %3, %17 offset:2048\n"
+      "ds_read_b64_tr_b16 %4, %18 offset:0\n"
+      "ds_read_b64_tr_b16 %5, %18 offset:2048\n"
+      "ds_read_b64_tr_b16 %6, %19 offset:0\n"
+      "ds_read_b64_tr_b16 %7, %19 offset:2048\n"
+      "ds_read_b64_tr_b16 %8, %16 offset:4096\n"
+      "ds_read_b64_tr_b16 %9, %16 offset:6144\n"
+      "ds_read_b64_tr_b16 %10, %17 offset:4096\n"
+      "ds_read_b64_tr_b16 %11, %17 offset:6144\n"
+      "ds_read_b64_tr_b16 %12, %18 offset:4096\n"
+      "ds_read_b64_tr_b16 %13, %18 offset:6144\n"
+      "ds_read_b64_tr_b16 %14, %19 offset:4096\n"
+      "ds_read_b64_tr_b16 %15, %19 offset:6144\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[2][0]), "=&v"(r[2][1]),
+        "=&v"(r[3][0]), "=&v"(r[3][1]), "=&v"(r[4][0]), "=&v"(r[4][1]), "=&v"(r[5][0]), "=&v"(r[5][1]),
+        "=&v"(r[6][0]), "=&v"(r[6][1]), "=&v"(r[7][0]), "=&v"(r[7][1])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+static_assert(kRowGroup == 4096 && 16 * 128 == 2048 && kStageBytes == 9 * kRowGroup, "read_vt_rows offsets");
+
 // Workgroup barrier for LDS hand-offs: this wave's LDS operations are done,
 // then s_barrier.  The empty asm statements keep the compiler from moving
 // memory accesses across it.  Copies into LDS are waited for separately.
@@ -166,10 +202,12 @@ __device__ __forceinline__ int item_stages(const Item& it) { return (it.tok_end 
 // Copy cursor: the stages of the bin's items in order, two ahead of the
 // score waves.  Each wave copies instructions [d0, d0 + N) of a stage:
 // instruction i moves chunks 2i and 2i + 1 (32 tokens x 16 B each) of the
-// stage into LDS bytes [1024 i, 1024 i + 1024) of the slot.  From a tile
-// (ROWS false) each chunk is 512 contiguous bytes; from token rows (ROWS
-// true) lane l gathers 16 bytes of token l % 32 of the stage, so the LDS
-// arrangement is the same.
+// stage into LDS bytes [1024 i, 1024 i + 1024) of the slot; each chunk is
+// 512 contiguous bytes of the tile.  From token rows (ROWS) the stage is
+// arranged by 8-chunk groups instead (kRowGroup): instruction i copies 128
+// bytes of each of tokens 8 (i % 4) .. + 7 of group i / 4, 8 lanes per token
+// reading one 128-byte segment of its row, lane l filling position l % 8
+// from chunk (l % 8) ^ swz(t).
 template <int N, bool ROWS>
 struct Copier {
   cint32* items;
@@ -195,11 +233,17 @@ struct Copier {
       const int rb = (int)P.k_stride_token * 2;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<char*>(tile + (int64_t)(t0 % kBS) * rb), (short)0, (kStage - 1) * rb + kDq * 2, kBufferWord3);
-      const int voff = (lane & 31) * rb + (lane >> 5) * 16;
+      // token t = 8 (i % 4) + l / 8: swz(t) = 4 (i % 2) + l / 16, so the lane
+      // part of the offset depends on i only through i % 2.
+      const int vrow = (lane >> 3) * rb;
+      const int voff0 = vrow + 16 * ((lane & 7) ^ (lane >> 4));
+      const int voff1 = vrow + 16 * ((lane & 7) ^ (4 + (lane >> 4)));
 #pragma unroll
-      for (int i = 0; i < N; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + (d0 + i) * 1024), 16, voff, (d0 + i) * 32,
-                                                 0, 0);
+      for (int i = 0; i < N; ++i) {
+        const int ii = d0 + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(slot + ii * 1024), 16, (ii & 1) ? voff1 : voff0,
+                                                 8 * (ii & 3) * rb + 128 * (ii >> 2), 0, 0);
+      }
     } else {
       // Raw buffer over the tile (MUBUF loads to LDS: counted by vmcnt alone).
       const __amdgpu_buffer_rsrc_t rs =
@@ -276,15 +320,27 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
       if (active) {
         // S^T = K Q^T over 18 d-steps; the key operands are read from LDS
         // in 6 batches of 3 d-steps, one batch ahead of the products.
-        const char* kt = lds + (t % kSlots) * kStageBytes + g * kChunk + c16 * 16;
+        // Key operand of d-step ks, tokens c16 and 16 + c16: chunk 4 ks + g.
+        // Tiles: kt + 4 ks kChunk (+ 256).  Rows: group ks / 2, position
+        // (4 (ks % 2) + g) ^ swz(c16): kr[ks % 2] + 4096 (ks / 2) (+ 2048).
+        const char* stage = lds + (t % kSlots) * kStageBytes;
+        const char* kt = stage + g * kChunk + c16 * 16;
+        const char* kr0 = stage + c16 * 128 + ((g ^ swz(c16)) * 16);
+        const char* kr1 = stage + c16 * 128 + (((4 + g) ^ swz(c16)) * 16);
+        auto key = [&](int ks, int half) -> bf16x8 {
+          if constexpr (ROWS)
+            return *reinterpret_cast<const bf16x8*>(((ks & 1) ? kr1 : kr0) + (ks >> 1) * kRowGroup + half * 2048);
+          else
+            return *reinterpret_cast<const bf16x8*>(kt + 4 * ks * kChunk + half * 256);
+        };
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
         constexpr int kB = 3;
         __builtin_amdgcn_s_setprio(1);  // the score products go first on the shared MFMA pipe
         bf16x8 ka[2][2 * kB];
 #pragma unroll
         for (int i = 0; i < kB; ++i) {
-          ka[0][2 * i] = *reinterpret_cast<const bf16x8*>(kt + 4 * i * kChunk);
-          ka[0][2 * i + 1] = *reinterpret_cast<const bf16x8*>(kt + 4 * i * kChunk + 16 * 16);
+          ka[0][2 * i] = key(i, 0);
+          ka[0][2 * i + 1] = key(i, 1);
         }
 #pragma unroll
         for (int b = 0; b < kKs / kB; ++b) {
@@ -293,8 +349,8 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
 #pragma unroll
             for (int i = 0; i < kB; ++i) {
               const int ks = (b + 1) * kB + i;
-              ka[(b + 1) & 1][2 * i] = *reinterpret_cast<const bf16x8*>(kt + 4 * ks * kChunk);
-              ka[(b + 1) & 1][2 * i + 1] = *reinterpret_cast<const bf16x8*>(kt + 4 * ks * kChunk + 16 * 16);
+              ka[(b + 1) & 1][2 * i] = key(ks, 0);
+              ka[(b + 1) & 1][2 * i + 1] = key(ks, 1);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -368,6 +424,14 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
     // tile: token 4 g + c16 / 4, dims 4 (c16 % 4) .. + 3; it receives dim
     // c16 of tokens 4 g .. 4 g + 3.
     const int tr_off = ((c16 & 3) >> 1) * kChunk + (4 * g + (c16 >> 2)) * 16 + (c16 & 1) * 8;
+    // Token rows: chunk 16 v + 2 dt + (c16 % 4) / 2 of token t = 16 tt + 4 g +
+    // c16 / 4 sits in group 2 v + dt / 4 at position (2 (dt % 4) + (c16 % 4) /
+    // 2) ^ swz(t), and swz(t) does not depend on tt.
+    uint32_t tr_rows[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      tr_rows[j] = (uint32_t)(2 * v * kRowGroup + (4 * g + (c16 >> 2)) * 128 +
+                              (((2 * j + ((c16 & 3) >> 1)) ^ swz(4 * g + (c16 >> 2))) * 16) + (c16 & 1) * 8);
 
     for (int t = 0; t <= N; ++t) {
       if (t + 1 < N)
@@ -396,9 +460,15 @@ __device__ __forceinline__ void mla_body(GqaParams P) {
       // reads, which then reach LDS ahead of more of the score waves' key
       // reads (2 % faster than copying first).
       if (t + 2 < N) cp.issue(P, bt, lds + ((t + 2) % kSlots) * kStageBytes, d0, lane);
-      const char* kt = lds + ((t - 1) % kSlots) * kStageBytes + (2 * v * kPvTiles) * kChunk + tr_off;
       u32x2 vr[kPvTiles][2];
-      read_vt(kt, vr);
+      if constexpr (ROWS) {
+        const uint32_t sb = (uint32_t)(uintptr_t)(lds + ((t - 1) % kSlots) * kStageBytes);
+        const uint32_t a[4] = {sb + tr_rows[0], sb + tr_rows[1], sb + tr_rows[2], sb + tr_rows[3]};
+        read_vt_rows(a, vr);
+      } else {
+        const char* kt = lds + ((t - 1) % kSlots) * kStageBytes + (2 * v * kPvTiles) * kChunk + tr_off;
+        read_vt(kt, vr);
+      }
       const int nvalid = it.tok_end - (it.tok_begin + cs * kStage);
       if (nvalid < kStage) {
         // Tokens past the range: zero their values (the operands are masked
