@@ -433,7 +433,55 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
     std::vector<std::vector<int>> die(kXcds);
     for (int b = 0; b < nb; ++b) die[b % kXcds].push_back(b);
     auto by_load = [&](int a, int b) { return load[a] != load[b] ? load[a] < load[b] : a < b; };
-    for (size_t ui = 0; ui < n_large; ++ui) {
+    // When every large unit has the same number of chunks C, the bins of
+    // each die are grouped into tuples of C, the units are laid end to end
+    // and the stream is cut into one equal run per tuple; chunk c of a piece
+    // goes to bin c of its tuple.  Whole pieces of about T per unit instead
+    // left bins of up to 1.5 T (the latent per-request pass: 30 stages
+    // against a mean of 20.7, the launch ending at 40 us against 28).
+    bool same_c = n_large > 0;
+    for (size_t ui = 1; ui < n_large && same_c; ++ui)
+      same_c = units[ui].l1 - units[ui].l0 == units[0].l1 - units[0].l0;
+    const int Cu = same_c ? (int)(units[0].l1 - units[0].l0) : 0;
+    std::vector<int> tuple_bin;  // bins of tuple k: [k C, k C + C)
+    if (same_c)
+      for (int j = 0;; ++j) {  // tuple j of every die in turn: consecutive tuples on different dies
+        bool any = false;
+        for (int x = 0; x < kXcds; ++x)
+          if ((int)die[x].size() >= (j + 1) * Cu) {
+            for (int c = 0; c < Cu; ++c) tuple_bin.push_back(die[x][j * Cu + c]);
+            any = true;
+          }
+        if (!any) break;
+      }
+    const int64_t n_tuples = same_c ? (int64_t)(tuple_bin.size() / Cu) : 0;
+    if (n_tuples > 0) {
+      int64_t Wl = 0;  // stages of one chunk, summed over the large units
+      for (size_t ui = 0; ui < n_large; ++ui) Wl += all[units[ui].l0].stages;
+      const int64_t nt = std::min<int64_t>(n_tuples, Wl);
+      size_t ui = 0;
+      int64_t upos = 0, pos = 0;
+      for (int64_t k = 0; k < nt; ++k) {
+        const int64_t end = (k + 1) * Wl / nt;
+        while (pos < end) {
+          const Unit& u = units[ui];
+          const int64_t n = all[u.l0].stages;
+          const int64_t take = std::min(n - upos, end - pos);
+          for (int c = 0; c < Cu; ++c) {
+            const int b = tuple_bin[k * Cu + c];
+            placed.push_back(Piece{b, (int)(u.l0 + c), upos, upos + take});
+            load[b] += take;
+          }
+          pos += take;
+          upos += take;
+          if (upos == n) {
+            ++ui;
+            upos = 0;
+          }
+        }
+      }
+    }
+    for (size_t ui = 0; ui < (n_tuples > 0 ? 0 : n_large); ++ui) {
       const Unit& u = units[ui];
       const int64_t n = all[u.l0].stages;
       const int64_t pieces = std::max<int64_t>(1, std::min<int64_t>(n, std::llround(n / T)));
