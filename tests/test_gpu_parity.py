@@ -396,6 +396,37 @@ def test_plan_and_decode_largest_batch():
         del out, lse
 
 
+@pytest.mark.parametrize("token_rows", [False, True], ids=["tiles", "rows"])
+@pytest.mark.parametrize("name", ["tiny", "llama3_8b"])
+def test_decode_one_workgroup_per_unit(name, token_rows, monkeypatch):
+    """The plan shape of large batches (one attention workgroup per compute
+    unit, so every lane is cut into half as many token pieces) forced on
+    small batches (FCA_TUNE_BINS_PER_CU=1), in both cache layouts, with
+    every group kept and with the default decision, against the oracle."""
+    monkeypatch.setenv("FCA_TUNE_BINS_PER_CU", "1")
+    b = build_batch(CONFIGS[name])
+    vn = fill_values_numpy(b, poison=True)
+    sh = b.shape
+    say("one workgroup per unit", name, "rows" if token_rows else "tiles")
+    ref, ref_lse = A.attend(vn["q"], vn["k"], vn["v"], b.block_tables, b.seq_lens, sh)
+    k, v = vn["k"], vn["v"]
+    if token_rows:  # [blocks][slots][kv heads][dims]
+        k = np.ascontiguousarray(k.transpose(0, 3, 1, 2, 4)).reshape(b.num_blocks, 16, sh.num_kv_heads, 128)
+        v = np.ascontiguousarray(v.transpose(0, 3, 1, 2))
+    kd, vd, qd = to_device_bf16(k), to_device_bf16(v), to_device_bf16(vn["q"])
+    bt, sl = dev_tables(b)
+    for fold in (False, True):
+        p = fca.fca_plan(bt, sl, fca.desc_from_shape(sh, b.num_blocks, auto_fold=fold, token_rows=token_rows))
+        check_schedule(b, p)
+        out = torch.empty((b.batch, sh.num_q_heads, sh.head_dim_v), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((b.batch, sh.num_q_heads), dtype=torch.float32, device="cuda")
+        fca.fca_decode(qd, kd, vd, p, out=out, lse=lse)
+        torch.cuda.synchronize()
+        rep = assert_close(bf16_tensor_to_f64(out), ref, f"{name} one workgroup per unit fold={fold}")
+        assert_lse_close(lse.cpu().numpy(), ref_lse, name)
+        say(name, "fold", fold, rep, "groups", p.info.num_groups)
+
+
 def test_decode_strided_pool():
     """Pools that are slices of a larger buffer (head/block strides)."""
     b = build_batch(CONFIGS["tiny"])
