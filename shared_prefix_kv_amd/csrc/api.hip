@@ -123,7 +123,7 @@ Layout make_layout(int B, int W) {
   size_t off = align_up(L.header + L.readback_bytes);
   L.W4 = (W + 3) / 4 * 4;
   L.bt = off;
-  off = align_up(off + b * (size_t)L.W4 * 4);
+  off = align_up(off + b * (size_t)L.W4 * 4 + kLcpTail * 4);
   L.state = off;
   off = align_up(off + kStateArrays * b * 4);
   L.total = off;

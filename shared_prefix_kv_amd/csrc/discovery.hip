@@ -191,6 +191,7 @@ __global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W4, Discovery
   constexpr int kLcpGroup = LCP_LANES;
   constexpr int kGroups = 64 / LCP_LANES;  // members per wave
   constexpr int kLcpSpan = LCP_LANES * LCP_LOADS * 4;
+  static_assert(kLcpSpan <= kLcpTail, "loads past the compared range stay inside the workspace");
   const int i = blockIdx.x;
   if (p.root[i] != i) return;  // not a tree root (uniform over the workgroup)
 
@@ -348,14 +349,17 @@ __global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W4, Discovery
         int found = INT_MAX;
         for (int base = a0; __ballot(busy) != 0; base += kLcpSpan) {
           if (busy) {
+            // Unconditional loads from one address per row plus immediate
+            // offsets (entries past cap are read but not compared; the
+            // workspace keeps kLcpTail entries after the last row), which
+            // leaves registers for LCP_LOADS loads of both rows in flight.
             i32x4 va[LCP_LOADS], vb[LCP_LOADS];
+            const int32_t* rkb = rk + base + 4 * gl;
+            const int32_t* rlb = rl + base + 4 * gl;
 #pragma unroll
             for (int u = 0; u < LCP_LOADS; ++u) {
-              const int pos = base + 4 * (kLcpGroup * u + gl);
-              if (pos < cap) {
-                va[u] = *reinterpret_cast<const i32x4*>(rk + pos);
-                vb[u] = *reinterpret_cast<const i32x4*>(rl + pos);
-              }
+              va[u] = *reinterpret_cast<const i32x4*>(rkb + 4 * kLcpGroup * u);
+              vb[u] = *reinterpret_cast<const i32x4*>(rlb + 4 * kLcpGroup * u);
             }
             int first = INT_MAX;
 #pragma unroll
@@ -480,19 +484,21 @@ hipError_t launch_discovery(const int32_t* bt_in, int64_t bt_stride, const int32
   if (cascade) {
     hipLaunchKernelGGL(k_roots, dim3((B + 3) / 4), dim3(256), 0, s, B, W4, p);
     hipLaunchKernelGGL(k_lcp0, dim3((B + 3) / 4), dim3(256), 0, s, B, W4, p);
-    // lanes per compared row (developer tuning knob): 4 (default: most
-    // members in flight; measured fastest on the two-level forest), 8 or 16
-    static const int lcp_lanes = [] {
-      const char* v = getenv("FCA_TUNE_LCP_LANES");
-      const int x = v ? atoi(v) : 4;
-      return (x == 8 || x == 16) ? x : 4;
+    // Lanes per compared row x loads in flight per lane (developer tuning
+    // knob FCA_TUNE_LCP = 44, 84 or 48): 4 lanes x 4 loads by default (most
+    // members in flight; the common-prefix step of forest_mixed's second
+    // round took 13-15 us with 4 or 8 loads, 84 against 116 VGPRs).
+    static const int lcp = [] {
+      const char* v = getenv("FCA_TUNE_LCP");
+      const int x = v ? atoi(v) : 44;
+      return (x == 48 || x == 84) ? x : 44;
     }();
-    if (lcp_lanes == 4)
+    if (lcp == 44)
       hipLaunchKernelGGL((k_trees<4, 4>), dim3(B), dim3(kTreeThreads), 0, s, B, W4, p);
-    else if (lcp_lanes == 8)
+    else if (lcp == 84)
       hipLaunchKernelGGL((k_trees<8, 4>), dim3(B), dim3(kTreeThreads), 0, s, B, W4, p);
     else
-      hipLaunchKernelGGL((k_trees<16, 4>), dim3(B), dim3(kTreeThreads), 0, s, B, W4, p);
+      hipLaunchKernelGGL((k_trees<4, 8>), dim3(B), dim3(kTreeThreads), 0, s, B, W4, p);
   }
   return hipGetLastError();
 }

@@ -14,6 +14,10 @@ namespace fca {
 
 constexpr int kMaxBatch = 8192;
 constexpr int kMaxTableWidth = 1 << 20;
+// Entries of the plan workspace after the last row of the block-table copy:
+// the common-prefix step of discovery reads up to one span of 4 x lanes x
+// loads entries (at most 128) past the compared range.
+constexpr int kLcpTail = 256;
 constexpr int kAttnLgWaves = 2;                 // log2 of the waves of an attention workgroup
 constexpr int kAttnWaves = 1 << kAttnLgWaves;   // waves that share one work item
 constexpr int kItemColsGqa = 64;                // query rows of one GQA work item at most
