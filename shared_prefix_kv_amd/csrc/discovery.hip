@@ -158,6 +158,10 @@ __global__ __launch_bounds__(256) void k_lcp0(int B, int W4, DiscoveryPtrs p) {
 
 constexpr int kTreeThreads = 1024;
 constexpr int kTreeWaves = kTreeThreads / 64;
+constexpr int kHashBits = 11;  // part table of trees of up to kTreeThreads members
+constexpr int kHashSlots = 1 << kHashBits;
+constexpr int kPosBits = 10;   // member position in that table's leader field
+static_assert(kHashSlots == 2 * kTreeThreads && (1 << kPosBits) == kTreeThreads, "part table");
 constexpr int kIdxBits = 13;  // request index in a sort key (kMaxBatch = 8192)
 static_assert((1 << kIdxBits) >= kMaxBatch, "request index field");
 constexpr uint64_t kIdxMask = (1u << kIdxBits) - 1;
@@ -196,6 +200,7 @@ __global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W4, Discovery
   if (p.root[i] != i) return;  // not a tree root (uniform over the workgroup)
 
   __shared__ uint64_t skey[kMaxBatch];  // active members; sorted keys during a round
+  static_assert(kTreeThreads + kHashSlots + kHashSlots / 2 * 2 <= kMaxBatch, "part table inside skey");
   __shared__ int16_t sbeg[kMaxBatch];   // part start (position) of each sorted member
   __shared__ int16_t scnt[kMaxBatch];   // part size
   __shared__ int32_t sdiff[kMaxBatch];  // common prefix with the part's leader; d* at the leader
@@ -251,7 +256,40 @@ __global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W4, Discovery
     }
     __syncthreads();
     const bool one_part = (kmin >> kIdxBits) == (kmax >> kIdxBits);
-    if (!one_part) {
+    // Up to kTreeThreads members: the parts are found through a hash table of
+    // their (node, block) keys in LDS (the unused upper part of skey), one
+    // member per thread, each part led by its smallest request; larger trees
+    // sort their keys.
+    const bool hashed = !one_part && n <= kTreeThreads;
+    if (hashed) {
+      unsigned long long* tkey = reinterpret_cast<unsigned long long*>(skey + kTreeThreads);
+      unsigned int* tlead = reinterpret_cast<unsigned int*>(skey + kTreeThreads + kHashSlots);
+      unsigned int* tcnt = tlead + kHashSlots;
+      for (int i = tid; i < kHashSlots; i += kTreeThreads) {
+        tkey[i] = ~0ull;
+        tlead[i] = ~0u;
+        tcnt[i] = 0u;
+      }
+      __syncthreads();
+      int slot = 0;
+      if (tid < n) {
+        const unsigned long long part = skey[tid] >> kIdxBits;  // < 2^44: never the empty key
+        int h = (int)((part * 0x9E3779B97F4A7C15ull) >> (64 - kHashBits));
+        for (;;) {  // at most n of the kHashSlots = 2 kTreeThreads slots are taken
+          const unsigned long long prev = atomicCAS(&tkey[h], ~0ull, part);
+          if (prev == ~0ull || prev == part) break;
+          h = (h + 1) & (kHashSlots - 1);
+        }
+        slot = h;
+        atomicMin(&tlead[h], (unsigned)(((skey[tid] & kIdxMask) << kPosBits) | (uint64_t)tid));
+        atomicAdd(&tcnt[h], 1u);
+      }
+      __syncthreads();
+      if (tid < n) {
+        sbeg[tid] = (int16_t)(tlead[slot] & ((1u << kPosBits) - 1));
+        scnt[tid] = (int16_t)tcnt[slot];
+      }
+    } else if (!one_part) {
       // Bitonic sort of skey[0, N), padded with the largest key.
       int N = 1;
       while (N < n) N <<= 1;
@@ -300,7 +338,7 @@ __global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W4, Discovery
     }
     // Part bounds.  One part: its leader is the smallest key (the members are
     // not sorted then, so the leader is found by its key).
-    for (int x = tid; x < n; x += kTreeThreads) {
+    for (int x = tid; x < n && !hashed; x += kTreeThreads) {
       int b0, cnt;
       if (one_part) {
         b0 = -1;
