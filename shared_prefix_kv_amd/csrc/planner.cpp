@@ -620,6 +620,8 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
   if (row > INT32_MAX) return pfail(err, FCA_ERR_UNSUPPORTED, "too many partial rows");
   P->items_g.clear();
   P->items_s.clear();
+  P->items_g.reserve(P->items.size());
+  P->items_s.reserve(P->items.size());
   for (size_t k = 0; k < P->items.size(); ++k) {
     WorkItem& it = P->items[k];
     const Lane& L = all[item_lane[k]];
@@ -627,6 +629,7 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
     (it.member_off >= 0 ? P->items_g : P->items_s).push_back(it);
   }
   P->lanes.clear();
+  P->lanes.reserve(all.size());
   for (const Lane& L : all)
     P->lanes.push_back(LaneMeta{(int32_t)L.base, L.splits, L.kv0, L.H, L.col0, L.col1 - L.col0, 0, 0});
 
