@@ -462,12 +462,6 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
       delete P;
       return hip_fail(e, "schedule upload");
     }
-    e = launch_bin_heads(reinterpret_cast<BinHead*>(P->sched + S.heads), (int)n_heads,
-                         reinterpret_cast<const int32_t*>(P->ws + P->L.bt), P->L.W4, P->desc.block_size, s);
-    if (e != hipSuccess) {
-      delete P;
-      return hip_fail(e, "bin heads");
-    }
     {
       TableParams tp;
       tp.req = reinterpret_cast<const ReqMeta*>(P->sched + S.req);
@@ -480,10 +474,15 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
       tp.src_span = reinterpret_cast<int2*>(P->sched + S.src_span);
       tp.src_row = reinterpret_cast<int32_t*>(P->sched + S.src_row);
       tp.total = reinterpret_cast<int32_t*>(P->sched + S.counter);
-      e = launch_merge_tables(tp, s);
+      tp.heads = reinterpret_cast<BinHead*>(P->sched + S.heads);
+      tp.n_bins = (int32_t)n_heads;
+      tp.bt = reinterpret_cast<const int32_t*>(P->ws + P->L.bt);
+      tp.W4 = P->L.W4;
+      tp.bs = P->desc.block_size;
+      e = launch_plan_tables(tp, s);
       if (e != hipSuccess) {
         delete P;
-        return hip_fail(e, "merge tables");
+        return hip_fail(e, "plan tables");
       }
     }
     *out = P;

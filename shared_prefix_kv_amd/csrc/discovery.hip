@@ -492,25 +492,6 @@ __global__ __launch_bounds__(kTreeThreads) void k_trees(int B, int W4, Discovery
 
 }  // namespace
 
-// One thread per bin: the block IDs of the first four blocks of its first
-// item (block IDs are validated by k_prepare).
-__global__ __launch_bounds__(256) void k_bin_heads(BinHead* __restrict__ heads, int n_bins,
-                                                   const int32_t* __restrict__ bt, int W4, int bs) {
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b >= n_bins) return;
-  BinHead& h = heads[b];
-  const WorkItem& it = h.first;
-  const int nblk = (it.tok_end - it.tok_begin + bs - 1) / bs;
-  for (int j = 0; j < 4; ++j)
-    h.id[j] = j < nblk ? bt[(int64_t)it.request * W4 + it.tok_begin / bs + j] : 0;
-}
-
-hipError_t launch_bin_heads(BinHead* heads, int n_bins, const int32_t* bt, int W4, int bs, hipStream_t s) {
-  if (n_bins <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bin_heads, dim3((n_bins + 255) / 256), dim3(256), 0, s, heads, n_bins, bt, W4, bs);
-  return hipGetLastError();
-}
-
 hipError_t launch_discovery(const int32_t* bt_in, int64_t bt_stride, const int32_t* lens_in, int B, int W, int W4,
                             int block_size, int num_blocks, bool cascade, const DiscoveryPtrs& p, hipStream_t s) {
   hipLaunchKernelGGL(k_init_header, dim3(1), dim3(64), 0, s, p.header);

@@ -43,9 +43,6 @@ struct PartialPtrs {
   float* l;
 };
 
-// Fills id[] of every bin head from the block-table copy (plan time).
-hipError_t launch_bin_heads(BinHead* heads, int n_bins, const int32_t* bt, int W, int bs, hipStream_t s);
-
 struct GqaParams {
   const WorkItem* items;    // grouped by bin
   const BinHead* bins;      // one per workgroup
@@ -72,9 +69,12 @@ hipError_t launch_attention(const GqaParams& p, int n_bins, hipStream_t s);
 // picks the kernel entry the launch is traced under (same code).
 hipError_t launch_mla(const GqaParams& p, int n_bins, bool grouped_pass, hipStream_t s);
 
-// Merge tables built at plan time (plan_tables.hip) from the planner's
-// metadata: src_span [B * Hq] (start, count) into src_row [total rows];
-// *total (zero before the launch) ends at the number of rows.
+// Device tables built at plan time (plan_tables.hip), in one launch:
+//   * merge tables from the planner's metadata: src_span [B * Hq] (start,
+//     count) into src_row [total rows]; *total (zero before the launch) ends
+//     at the number of rows;
+//   * id[] of every bin head: the first block IDs of its first item, from
+//     the block-table copy bt (row stride W4, block size bs).
 struct TableParams {
   const ReqMeta* req;
   const GroupMeta* grp;
@@ -83,9 +83,13 @@ struct TableParams {
   int2* src_span;
   int32_t* src_row;
   int32_t* total;
+  BinHead* heads;
+  int32_t n_bins;
+  const int32_t* bt;
+  int32_t W4, bs;
 };
 
-hipError_t launch_merge_tables(const TableParams& p, hipStream_t s);
+hipError_t launch_plan_tables(const TableParams& p, hipStream_t s);
 
 struct MergeParams {
   // Partial rows of (request i, query head h), in merge order (deepest

@@ -13,7 +13,12 @@
 // add on a counter, and every thread writes its rows -- instead of the host
 // walking B x Hq paths at every plan.  Where a pair's rows sit in src_row
 // depends on the order in which waves reach the counter; what they are, and
-// their order, does not.
+// their order, does not.  The same launch fills the first block IDs of every
+// workgroup's bin head (its last blocks, one thread per bin), so the plan's
+// device tables cost one launch after the upload.
+
+#include <algorithm>
+#include <climits>
 
 #include "fca_internal.h"
 
@@ -37,7 +42,20 @@ __device__ __forceinline__ void path_units(const TableParams& p, int i, int h, F
   if (rq.sfx_lane >= 0) f(rq.sfx_lane + (kvh / rq.sfx_H) * rq.sfx_chunks + rr / p.item_cols, rr);
 }
 
-__global__ __launch_bounds__(kTableThreads) void k_merge_table(TableParams p) {
+// Blocks [0, table_blocks) build the merge tables, the rest the bin heads.
+__global__ __launch_bounds__(kTableThreads) void k_plan_tables(TableParams p, int table_blocks) {
+  if ((int)blockIdx.x >= table_blocks) {
+    // Block IDs of blocks 0..3 of the bin's first item (validated by
+    // discovery), 0 past its end.
+    const int b = ((int)blockIdx.x - table_blocks) * kTableThreads + threadIdx.x;
+    if (b >= p.n_bins) return;
+    BinHead& h = p.heads[b];
+    const WorkItem& it = h.first;
+    const int nblk = (it.tok_end - it.tok_begin + p.bs - 1) / p.bs;
+    for (int j = 0; j < 4; ++j)
+      h.id[j] = j < nblk ? p.bt[(int64_t)it.request * p.W4 + it.tok_begin / p.bs + j] : 0;
+    return;
+  }
   const int64_t pair = (int64_t)blockIdx.x * kTableThreads + threadIdx.x;
   const int64_t n = (int64_t)p.B * p.Hq;
   const int lane = threadIdx.x & 63;
@@ -72,11 +90,14 @@ __global__ __launch_bounds__(kTableThreads) void k_merge_table(TableParams p) {
 
 }  // namespace
 
-hipError_t launch_merge_tables(const TableParams& p, hipStream_t s) {
+hipError_t launch_plan_tables(const TableParams& p, hipStream_t s) {
   const int64_t n = (int64_t)p.B * p.Hq;
-  if (n == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((n + kTableThreads - 1) / kTableThreads);
-  hipLaunchKernelGGL(k_merge_table, dim3(grid), dim3(kTableThreads), 0, s, p);
+  const int64_t table_blocks = (n + kTableThreads - 1) / kTableThreads;
+  const int64_t head_blocks = ((int64_t)std::max(p.n_bins, 0) + kTableThreads - 1) / kTableThreads;
+  if (table_blocks + head_blocks == 0) return hipSuccess;
+  if (table_blocks + head_blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_plan_tables, dim3((unsigned)(table_blocks + head_blocks)), dim3(kTableThreads), 0, s, p,
+                     (int)table_blocks);
   return hipGetLastError();
 }
 
