@@ -116,6 +116,28 @@ fca_status check_readback(const PlanHost& P, const DiscoveryView& d, std::string
   return FCA_OK;
 }
 
+// Values grouped by key in [0, n), each group in the order the values come
+// (a counting sort; two flat arrays instead of one vector per key).
+struct KeyLists {
+  std::vector<int> at;   // [n + 1]: group k is val[at[k], at[k + 1])
+  std::vector<int> val;
+  // key(j) for j in [0, m): a key in [0, n), or -1 to leave value j out
+  template <class Key>
+  void build(int n, int m, Key key) {
+    at.assign((size_t)n + 1, 0);
+    for (int j = 0; j < m; ++j)
+      if (key(j) >= 0) ++at[(size_t)key(j) + 1];
+    for (int k = 0; k < n; ++k) at[(size_t)k + 1] += at[k];
+    val.resize(at[n]);
+    std::vector<int> fill(at.begin(), at.end() - 1);
+    for (int j = 0; j < m; ++j)
+      if (key(j) >= 0) val[fill[key(j)]++] = j;
+  }
+  int size(int k) const { return at[(size_t)k + 1] - at[k]; }
+  const int* begin(int k) const { return val.data() + at[k]; }
+  const int* end(int k) const { return val.data() + at[(size_t)k + 1]; }
+};
+
 }  // namespace
 
 fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std::string* err) {
@@ -150,7 +172,6 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
   P->groups.assign(G, fca_group_record{});
   P->grp.assign(G, GroupMeta{});
   std::vector<int> count(G);
-  std::vector<std::vector<int>> children(G), direct(G);
   std::vector<int> roots;
   int max_depth = -1;
   for (int c = 0; c < G; ++c) {
@@ -162,16 +183,13 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
     gr.block_end = x[4];
     count[c] = x[5];
     max_depth = std::max(max_depth, gr.depth);
-    if (gr.parent >= 0)
-      children[gr.parent].push_back(c);
-    else
-      roots.push_back(c);
+    if (gr.parent < 0) roots.push_back(c);
   }
   std::vector<int> deepest_c(B);
-  for (int i = 0; i < B; ++i) {
-    deepest_c[i] = deep[i] >= 0 ? canon[deep[i]] : -1;
-    if (deepest_c[i] >= 0) direct[deepest_c[i]].push_back(i);
-  }
+  for (int i = 0; i < B; ++i) deepest_c[i] = deep[i] >= 0 ? canon[deep[i]] : -1;
+  KeyLists children, direct;  // child groups of each group; requests whose deepest group it is
+  children.build(G, G, [&](int c) { return P->groups[c].parent; });
+  direct.build(G, B, [&](int i) { return deepest_c[i]; });
 
   // Depth-first member order: every group is the contiguous range [r0, r1).
   P->perm.clear();
@@ -182,14 +200,14 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
     for (int root : roots) {
       stack.push_back({root, 0});
       r0[root] = (int)P->perm.size();
-      for (int i : direct[root]) P->perm.push_back(i);
+      P->perm.insert(P->perm.end(), direct.begin(root), direct.end(root));
       while (!stack.empty()) {
         auto& top = stack.back();
         const int c = top.first;
-        if (top.second < children[c].size()) {
-          const int ch = children[c][top.second++];
+        if ((int)top.second < children.size(c)) {
+          const int ch = children.begin(c)[top.second++];
           r0[ch] = (int)P->perm.size();
-          for (int i : direct[ch]) P->perm.push_back(i);
+          P->perm.insert(P->perm.end(), direct.begin(ch), direct.end(ch));
           stack.push_back({ch, 0});
         } else {
           r1[c] = (int)P->perm.size();
@@ -209,11 +227,11 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
     if (r1[c] - r0[c] != count[c] || count[c] < 2)
       return pfail(err, FCA_ERR_HIP, "inconsistent discovery output (group %d: %d members, range %d)", c, count[c],
                   r1[c] - r0[c]);
-    P->groups[c].member_begin = (int32_t)P->members.size();
+    const size_t at = P->members.size();
+    P->groups[c].member_begin = (int32_t)at;
     P->groups[c].member_count = count[c];
-    std::vector<int> m(P->perm.begin() + r0[c], P->perm.begin() + r1[c]);
-    std::sort(m.begin(), m.end());
-    P->members.insert(P->members.end(), m.begin(), m.end());
+    P->members.insert(P->members.end(), P->perm.begin() + r0[c], P->perm.begin() + r1[c]);
+    std::sort(P->members.begin() + at, P->members.end());
   }
 
   // Activation (GQA caches, unless FCA_PLAN_KEEP_GROUPS): a group is read
@@ -242,7 +260,8 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
     const double row_cost = 4.0 * (4.0 * P->desc.head_dim_v + 8.0);
     for (int c = G - 1; c >= 0; --c) {  // children come after their parents
       bool leaves_folded = true;
-      for (int ch : children[c]) leaves_folded = leaves_folded && P->folded[ch];
+      for (const int* ch = children.begin(c); ch != children.end(c); ++ch)
+        leaves_folded = leaves_folded && P->folded[*ch];
       if (!leaves_folded) continue;
       const double T = (double)(P->groups[c].block_end - P->groups[c].block_begin) * bs;
       const double saved = (count[c] - 1) * T * tok_bytes;
@@ -531,7 +550,14 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
           s0 += take;
         }
       }
-    std::stable_sort(placed.begin(), placed.end(), [](const Piece& a, const Piece& b) { return a.bin < b.bin; });
+    {  // stable counting sort by bin
+      std::vector<int> at((size_t)nb + 1, 0);
+      for (const Piece& e : placed) ++at[(size_t)e.bin + 1];
+      for (int b = 0; b < nb; ++b) at[(size_t)b + 1] += at[b];
+      std::vector<Piece> by_bin(placed.size());
+      for (const Piece& e : placed) by_bin[at[e.bin]++] = e;
+      placed.swap(by_bin);
+    }
     const int first = (int)P->bins.size() - 1;
     int used = 0;
     P->items.reserve(P->items.size() + placed.size());
