@@ -71,7 +71,9 @@ __device__ __forceinline__ void store_row(void* out, int32_t out_f32, int64_t at
 // at once after two dependent loads; the value rows
 // are then accumulated two at a time (lanes 0-31 take even sources, lanes
 // 32-63 odd ones, each lane DV/32 value dims), eight rows in flight per
-// wave, and the two halves are added at the end.
+// wave, and the two halves are added at the end.  (Sixteen rows in flight
+// for 128-dim rows measured slower on MI355X: the extra registers cost more
+// occupancy than the fewer round trips saved.)
 template <int DV>
 __device__ __forceinline__ void merge_body(const MergeParams& P) {
   constexpr int VPL = DV / 32;  // floats per lane
@@ -89,21 +91,27 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
   float acc[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) acc[v] = 0.f;
+  // Value rows of sources s .. s + 2U - 1 (even ones in the lower half
+  // wave, odd ones in the upper); slots past the sources are not loaded
+  // and get weight 0.
+  float x[U][VPL];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) x[u][v] = 0.f;
 
   for (int base = 0; base < n_src; base += 64) {
     const int j = base + lane;
     const int row = j < n_src ? P.src_row[off0 + j] : -1;
     const int cnt = min(64, n_src - base);
-    const int row0 = __builtin_amdgcn_readlane(row, 0);  // a valid row for idle slots
-    // Value rows of sources s .. s + 2U - 1 (even ones in the lower half
-    // wave, odd ones in the upper); they depend on the row indices only.
-    float x[U][VPL];
     auto load_rows = [&](int s) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int se = s + 2 * u;
-        const int re = se < cnt ? __builtin_amdgcn_readlane(row, se) : row0;
-        const int ro = se + 1 < cnt ? __builtin_amdgcn_readlane(row, se + 1) : row0;
+        if (se >= cnt) continue;  // wave-uniform
+        const int re = __builtin_amdgcn_readlane(row, se);
+        // a missing odd source: the upper half loads the even row (weight 0)
+        const int ro = se + 1 < cnt ? __builtin_amdgcn_readlane(row, se + 1) : re;
         const float* src = P.part.o + (int64_t)(half ? ro : re) * DV + hl * VPL;
 #pragma unroll
         for (int v = 0; v < VPL; v += 4) {
