@@ -37,6 +37,12 @@ HBM_PEAK_GBPS = 8000.0
 RIDGE_FLOP_PER_BYTE = 312.0  # 2.5 PFLOP/s bf16 over 8 TB/s
 COPY_BYTES = 1 << 30
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# kernel entry of each pass when the two passes are launched one after the
+# other (the latent-cache plans always; GQA plans with separate passes)
+PASS_KERNELS = {
+    "gqa": ("fca_attention_grouped_kernel", "fca_attention_suffix_kernel"),
+    "mla": ("fca_mla_grouped_kernel", "fca_mla_suffix_kernel"),
+}
 
 
 def log(*a):
@@ -63,6 +69,12 @@ def parse():
         "--no-cascade",
         action="store_true",
         help="time the non-cascade plan as the main one (to profile the baseline's launches)",
+    )
+    ap.add_argument(
+        "--separate-passes",
+        action="store_true",
+        help="time the plan that launches the grouped and the per-request pass one after the other as the main "
+        "one (to profile each pass's launch)",
     )
     ap.add_argument(
         "--group-sweep",
@@ -228,9 +240,48 @@ def token_row_pools(pools):
     return out
 
 
+def pass_traffic(name, pb, latent, main, sep=None):
+    """Each pass's own launch and the merge, measured by counters, from the
+    committed rocprofv3 summaries of the same sources (None where there are
+    none): the passes from `sep` or else from the summary of the workload's
+    plan with one launch per pass (latent-cache plans always launch them so:
+    their timed plan's summary `main`), the merge from `main`.  Per launch:
+    HBM bytes (FETCH_SIZE + WRITE_SIZE, calibrated), the median duration, and
+    the algorithmic bytes over that duration against the 8 TB/s peak."""
+    from shared_prefix_kv_amd.profiling import load_traffic
+
+    if sep is None:
+        sep = main if latent else load_traffic(name + ".separate_passes")
+    names = dict(zip(("grouped", "suffix"), PASS_KERNELS["mla" if latent else "gqa"]), merge="fca_merge_kernel")
+    src = {"grouped": sep, "suffix": sep, "merge": main}
+    pt = {}
+    for pname, kname in names.items():
+        d = src[pname]
+        t = d["traffic"].get(kname) if d else None
+        us = d.get("launch_us", {}).get(kname) if d else None
+        if t and us and pb[pname] > 0:
+            moved = t["fetch_bytes"] + t["write_bytes"]
+            rate = pb[pname] / (us * 1e-6) / 1e9
+            pt[pname] = {
+                "kernel": kname,
+                "launch_us_profiled": round(us, 2),
+                "traffic": int(moved),
+                "algorithmic_bytes": int(pb[pname]),
+                "traffic_over_algorithmic": round(moved / pb[pname], 4),
+                "algorithmic_GBps": round(rate, 1),
+                "algorithmic_frac_of_hbm_peak": round(rate / HBM_PEAK_GBPS, 4),
+            }
+    if "suffix" in pt and "merge" in pt:
+        us = pt["suffix"]["launch_us_profiled"] + pt["merge"]["launch_us_profiled"]
+        rate = (pb["suffix"] + pb["merge"]) / (us * 1e-6) / 1e9
+        pt["suffix_plus_merge"] = {"algorithmic_GBps": round(rate, 1), "algorithmic_frac_of_hbm_peak": round(rate / HBM_PEAK_GBPS, 4)}
+    return pt or None
+
+
 def short_record(name, torch, fca, steps, warmup, layers=4):
     """Cascade vs non-cascade on another workload: decode time per step, the
     logical-KV rate, unique-KV GB/s, the byte ratio R and the speedup."""
+    from shared_prefix_kv_amd.profiling import load_traffic
     from workloads import CONFIGS, build_batch
     from workloads.values import fill_values_torch
 
@@ -266,10 +317,12 @@ def short_record(name, torch, fca, steps, warmup, layers=4):
         warm(plan, qs, pools, out, lse, warmup, torch, fca)
         ms, _ = time_steps(plan, qs, pools, out, lse, steps, torch, fca)
         res[key] = (ms, plan.info)
+        if key == "fca":
+            pb_fca = pass_bytes(batch, plan, None)
         if key == "fca" and sh.v_aliases_k:
             # Latent cache: the two passes are separate launches; time each.
             t = plan.time_launches(qs[0], pools, 10, out, lse)
-            pb = pass_bytes(batch, plan, None)
+            pb = pb_fca
             launch = {k[:-3]: round(v, 5) for k, v in t.items() if k.endswith("_ms") and v > 0}
             g_tf = pb["grouped_flops"] / (t["grouped_ms"] / 1000.0) / 1e12 if t["grouped_ms"] > 0 else 0.0
             latent = {
@@ -305,6 +358,9 @@ def short_record(name, torch, fca, steps, warmup, layers=4):
     }
     if latent:
         rec["latent"] = latent
+    pt = pass_traffic(name, pb_fca, sh.v_aliases_k, load_traffic(name))
+    if pt:
+        rec["pass_traffic"] = pt
     del pools, qs
     torch.cuda.empty_cache()
     return rec
@@ -447,7 +503,7 @@ def main():
 
     bt = torch.from_numpy(batch.block_tables).cuda()
     sl = torch.from_numpy(batch.seq_lens).cuda()
-    desc = fca.desc_from_shape(sh, batch.num_blocks, cascade=not args.no_cascade)
+    desc = fca.desc_from_shape(sh, batch.num_blocks, cascade=not args.no_cascade, separate_passes=args.separate_passes)
     t0 = time.perf_counter()
     plan = fca.fca_plan(bt, sl, desc)
     torch.cuda.synchronize()
@@ -534,7 +590,7 @@ def main():
     launches = [(merge_kernel, "merge", pb["merge"], 0)]
     if two_launches:
         # the latent-cache kernel, one entry name per pass
-        g_name, s_name = ("fca_mla_grouped_kernel", "fca_mla_suffix_kernel") if sh.v_aliases_k else ("fca_attention_kernel",) * 2
+        g_name, s_name = PASS_KERNELS["mla" if sh.v_aliases_k else "gqa"]
         launches += [
             (g_name, "grouped", pb["grouped"], pb["grouped_flops"]),
             (s_name, "suffix", pb["suffix"], pb["suffix_flops"]),
@@ -578,7 +634,8 @@ def main():
     # only while the library sources are the ones it was taken with.
     from shared_prefix_kv_amd.profiling import load_traffic
 
-    tr = load_traffic(cfg.name + (".non_cascade" if args.no_cascade else ""))
+    variant = ".non_cascade" if args.no_cascade else ".separate_passes" if args.separate_passes else ""
+    tr = load_traffic(cfg.name + variant)
     if tr and dom_name == tr["kernel"] and dom_name in tr["traffic"]:
         t = tr["traffic"][dom_name]
         roofline["traffic"] = int(t["fetch_bytes"] + t["write_bytes"])
@@ -643,6 +700,11 @@ def main():
         "plan_ms_first_call": round(plan_ms_first, 3),
         "roofline": roofline,
     }
+
+    if not args.no_cascade:
+        pt = pass_traffic(cfg.name, pb, sh.v_aliases_k, tr, sep=tr if two_launches else None)
+        if pt:
+            result["pass_traffic"] = pt
 
     if not args.profile_only:
         warm(plan_sep, qs, pools, out, lse, warmup, torch, fca)

@@ -577,7 +577,7 @@ hipError_t launch_pass(const fca_plan_s* P, GqaParams gp, int k, hipStream_t s) 
   const Launch& ln = P->launches[k];
   gp.bins = reinterpret_cast<const BinHead*>(P->sched + P->SL.heads) + ln.bin0;
   return P->kind == kMla ? launch_mla(gp, ln.n_bins, ln.passes == kGroupedPass, s)
-                         : launch_attention(gp, ln.n_bins, s);
+                         : launch_attention(gp, ln.n_bins, ln.passes, s);
 }
 
 // Adds the time of attention launch `k` to the profile's per-pass sums.

@@ -530,7 +530,27 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fca_attention_kernel(const Bin
   stream_body<false>(ca, p);
 }
 
-// The same for pools of token rows.
+// Plans that launch the two passes one after the other: the same body under
+// one entry name per pass, so that kernel traces and counters tell the
+// passes apart.
+__global__ __launch_bounds__(kWaves * 64, 2) void fca_attention_grouped_kernel(const BinHead* __restrict__ bins,
+                                                                              const WorkItem* __restrict__ items,
+                                                                              const char* k, const char* v,
+                                                                              int64_t ksb, int64_t ksh, int64_t vsb,
+                                                                              int64_t vsh, GqaParams p) {
+  const CopyArgs ca{bins, items, k, v, ksb, ksh, vsb, vsh};
+  stream_body<false>(ca, p);
+}
+__global__ __launch_bounds__(kWaves * 64, 2) void fca_attention_suffix_kernel(const BinHead* __restrict__ bins,
+                                                                             const WorkItem* __restrict__ items,
+                                                                             const char* k, const char* v,
+                                                                             int64_t ksb, int64_t ksh, int64_t vsb,
+                                                                             int64_t vsh, GqaParams p) {
+  const CopyArgs ca{bins, items, k, v, ksb, ksh, vsb, vsh};
+  stream_body<false>(ca, p);
+}
+
+// The same for pools of token rows (every pass).
 __global__ __launch_bounds__(kWaves * 64, 2) void fca_attention_rows_kernel(const BinHead* __restrict__ bins,
                                                                            const WorkItem* __restrict__ items,
                                                                            const char* k, const char* v,
@@ -540,16 +560,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void fca_attention_rows_kernel(cons
   stream_body<true>(ca, p);
 }
 
-hipError_t launch_attention(const GqaParams& p, int n_bins, hipStream_t s) {
+hipError_t launch_attention(const GqaParams& p, int n_bins, PassSet passes, hipStream_t s) {
   if (n_bins <= 0) return hipSuccess;
-  if (p.k_stride_token != 0)
-    hipLaunchKernelGGL(fca_attention_rows_kernel, dim3(n_bins), dim3(kWaves * 64), 0, s, p.bins, p.items,
-                       static_cast<const char*>(p.k), static_cast<const char*>(p.v), p.k_stride_block,
-                       p.k_stride_head, p.v_stride_block, p.v_stride_head, p);
-  else
-    hipLaunchKernelGGL(fca_attention_kernel, dim3(n_bins), dim3(kWaves * 64), 0, s, p.bins, p.items,
-                       static_cast<const char*>(p.k), static_cast<const char*>(p.v), p.k_stride_block,
-                       p.k_stride_head, p.v_stride_block, p.v_stride_head, p);
+  const auto kernel = p.k_stride_token != 0   ? fca_attention_rows_kernel
+                      : passes == kGroupedPass ? fca_attention_grouped_kernel
+                      : passes == kSuffixPass  ? fca_attention_suffix_kernel
+                                               : fca_attention_kernel;
+  hipLaunchKernelGGL(kernel, dim3(n_bins), dim3(kWaves * 64), 0, s, p.bins, p.items,
+                     static_cast<const char*>(p.k), static_cast<const char*>(p.v), p.k_stride_block,
+                     p.k_stride_head, p.v_stride_block, p.v_stride_head, p);
   return hipGetLastError();
 }
 

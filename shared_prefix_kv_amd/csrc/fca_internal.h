@@ -61,8 +61,9 @@ struct GqaParams {
 };
 
 // Grouped and per-request work items, one persistent workgroup per bin
-// (bins [0, n_bins) of p.bins).
-hipError_t launch_attention(const GqaParams& p, int n_bins, hipStream_t s);
+// (bins [0, n_bins) of p.bins).  `passes` names the launch's passes; it
+// picks the kernel entry the launch is traced under (same code).
+hipError_t launch_attention(const GqaParams& p, int n_bins, PassSet passes, hipStream_t s);
 
 // The same for a latent cache (576-wide keys, values = first 512 dims,
 // 64-token blocks): items of up to 128 query rows of one head.  `grouped_pass`

@@ -38,10 +38,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
 ATTENTION = "fca_attention_kernel"  # both passes in one launch
+GQA_GROUPED = "fca_attention_grouped_kernel"  # plans with one launch per pass: grouped pass
+GQA_SUFFIX = "fca_attention_suffix_kernel"  # plans with one launch per pass: per-request pass
 MLA_GROUPED = "fca_mla_grouped_kernel"  # latent cache: grouped-pass launch
 MLA_SUFFIX = "fca_mla_suffix_kernel"  # latent cache: per-request-pass launch
 MERGE = "fca_merge_kernel"
 CALIBRATION = "mul"  # torch.mul elementwise kernel of the calibration copy
+ATTENTION_KERNELS = (ATTENTION, GQA_GROUPED, GQA_SUFFIX, MLA_GROUPED, MLA_SUFFIX)
 
 
 def source_sha256() -> str:
@@ -162,7 +165,7 @@ def _raw_counters(dirpath: str, counter: str) -> dict[str, list[float]]:
 def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_bytes, cmds, out, util_dir=None,
               mops_dir=None):
     stats = kernel_stats(stats_dir)
-    att_kernels = [k for k in (ATTENTION, MLA_GROUPED, MLA_SUFFIX) if kernel_durations(stats_dir, k)]
+    att_kernels = [k for k in ATTENTION_KERNELS if kernel_durations(stats_dir, k)]
     if not att_kernels:
         raise RuntimeError("no attention kernel in the kernel trace")
     durations = {k: kernel_durations(stats_dir, k) for k in att_kernels + [MERGE]}
@@ -246,6 +249,7 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
         source_sha256=source_sha256(),
         kernel=kernel,
         avg_launch_us=statistics.median(durations[kernel]),
+        launch_us={k: statistics.median(d) for k, d in durations.items() if d},
         fetch_factor=f_factor,
         write_factor=w_factor,
         traffic=res,
@@ -261,7 +265,7 @@ def summarize(stats_dir, fetch_dir, write_dir, config, copy_bytes, algorithmic_b
 def load_traffic(config: str):
     """Calibrated traffic per attention dispatch from the committed summary,
     or None if there is none or the sources changed since it was taken."""
-    paths = [os.path.join(ROOT, "profiles", f"{k}.{config}.txt") for k in (ATTENTION, MLA_GROUPED, MLA_SUFFIX)]
+    paths = [os.path.join(ROOT, "profiles", f"{k}.{config}.txt") for k in ATTENTION_KERNELS]
     paths = [p for p in paths if os.path.exists(p)]
     if not paths:
         return None
@@ -293,7 +297,8 @@ def run(config: str, out_dir: str, extra: list[str], timeout_s: int = 300) -> st
     import sys
 
     out_dir = os.path.abspath(out_dir)
-    config_dir = config + ("_non_cascade" if "--no-cascade" in extra else "")
+    variant = "non_cascade" if "--no-cascade" in extra else "separate_passes" if "--separate-passes" in extra else ""
+    config_dir = config + ("_" + variant if variant else "")
     bench = [sys.executable, os.path.join(ROOT, "bench.py"), "--config", config, "--profile-only", "--copy-calibration",
              "--no-cpu-baseline", *extra]
     env = dict(os.environ, TMPDIR="/tmp")
@@ -322,7 +327,7 @@ def run(config: str, out_dir: str, extra: list[str], timeout_s: int = 300) -> st
         with open(tmp, "w") as fh:
             fh.write(json.dumps(line["roofline"]))
     kernel = _dominant_kernel(os.path.join(out_dir, config_dir, "stats"))
-    label = config + (".non_cascade" if "--no-cascade" in extra else "")
+    label = config + ("." + variant if variant else "")
     out = os.path.join(ROOT, "profiles", f"{kernel}.{label}.txt")
     summ = [
         f"python3 -m shared_prefix_kv_amd.profiling summarize --stats {out_dir}/{config_dir}/stats --fetch "
@@ -345,7 +350,7 @@ COPY_BYTES = 1 << 30  # the calibration copy bench.py launches (--copy-calibrati
 
 
 def _dominant_kernel(stats_dir: str) -> str:
-    ks = [k for k in (ATTENTION, MLA_GROUPED, MLA_SUFFIX) if kernel_durations(stats_dir, k)]
+    ks = [k for k in ATTENTION_KERNELS if kernel_durations(stats_dir, k)]
     return max(ks, key=lambda k: statistics.median(kernel_durations(stats_dir, k)))
 
 
