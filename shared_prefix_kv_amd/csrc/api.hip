@@ -134,7 +134,22 @@ Layout make_layout(int B, int W) {
 struct SchedLayout {
   size_t items, heads, perm, req, grp, lanes, counter, upload;  // uploaded from the host: [0, upload)
   size_t src_span, src_row, total;                              // merge tables, built on the device
+  int32_t src_stride;  // > 0: fixed-stride merge table (entries per (request, head))
+  size_t src_rows;     // entries of src_row
 };
+
+// Merge-table stride for a plan: the bound on any (request, head)'s partial
+// rows when it fits one wave's lanes and the padding stays modest (at most
+// twice the rows, or 64 Ki entries), else 0 (packed tables).  Developer knob:
+// FCA_TUNE_MERGE_PACKED=1 keeps packed tables.
+int32_t merge_stride(int64_t pairs, int64_t rows, int64_t most) {
+  const char* v = getenv("FCA_TUNE_MERGE_PACKED");
+  if (v && atoi(v) == 1) return 0;
+  if (most < 1 || most > 64) return 0;
+  const int64_t entries = pairs * most;
+  if (entries > std::max<int64_t>(2 * rows, rows + (1 << 16)) || entries > INT32_MAX) return 0;
+  return (int32_t)most;
+}
 
 
 DiscoveryPtrs discovery_ptrs(char* ws, const Layout& L, int B) {
@@ -419,8 +434,11 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
     S.lanes = place(P->lanes.size() * sizeof(LaneMeta));
     S.counter = place(4);  // zero in the upload: the merge-table kernel's row counter
     S.upload = off;
-    S.src_span = place((size_t)P->B * P->desc.num_q_heads * 8);
-    S.src_row = place((size_t)P->info.num_partial_rows * 4);
+    const int64_t pairs = (int64_t)P->B * P->desc.num_q_heads;
+    S.src_stride = merge_stride(pairs, P->info.num_partial_rows, P->max_pair_sources);
+    S.src_rows = (size_t)std::max<int64_t>(P->info.num_partial_rows, pairs * S.src_stride);
+    S.src_span = place((size_t)pairs * 8);
+    S.src_row = place(S.src_rows * 4);
     S.total = off;
     P->dev = dev;
     P->stream = s;
@@ -474,6 +492,7 @@ fca_status fca_plan_create(const int32_t* block_tables_dev, int64_t bt_row_strid
       tp.src_span = reinterpret_cast<int2*>(P->sched + S.src_span);
       tp.src_row = reinterpret_cast<int32_t*>(P->sched + S.src_row);
       tp.total = reinterpret_cast<int32_t*>(P->sched + S.counter);
+      tp.stride = S.src_stride;
       tp.heads = reinterpret_cast<BinHead*>(P->sched + S.heads);
       tp.n_bins = (int32_t)n_heads;
       tp.bt = reinterpret_cast<const int32_t*>(P->ws + P->L.bt);
@@ -562,6 +581,7 @@ fca_status decode_params(const fca_plan_s* P, const void* q_dev, const void* k_c
 
   mp->src_span = reinterpret_cast<const int2*>(P->sched + S.src_span);
   mp->src_row = reinterpret_cast<const int32_t*>(P->sched + S.src_row);
+  mp->src_stride = S.src_stride;
   mp->B = P->B;
   mp->Hq = P->desc.num_q_heads;
   mp->Dv = P->desc.head_dim_v;
@@ -1001,7 +1021,7 @@ fca_status fca_plan_export_schedule(fca_plan plan, fca_work_item* grouped, fca_w
     // the merge tables as the device built them, in (request, head) order
     const size_t pairs = (size_t)P->B * P->desc.num_q_heads;
     std::vector<int2> span(pairs);
-    std::vector<int32_t> rows((size_t)P->info.num_partial_rows);
+    std::vector<int32_t> rows(P->SL.src_rows);
     hipError_t e = hipMemcpyAsync(span.data(), P->sched + P->SL.src_span, pairs * sizeof(int2), hipMemcpyDeviceToHost,
                                   P->stream);
     if (e == hipSuccess && !rows.empty())

@@ -72,8 +72,10 @@ hipError_t launch_mla(const GqaParams& p, int n_bins, bool grouped_pass, hipStre
 
 // Device tables built at plan time (plan_tables.hip), in one launch:
 //   * merge tables from the planner's metadata: src_span [B * Hq] (start,
-//     count) into src_row [total rows]; *total (zero before the launch) ends
-//     at the number of rows;
+//     count) into src_row.  With stride > 0 pair q's rows start at q * stride
+//     and the rest of its stride holds -1 (every pair has at most stride
+//     rows); with stride 0 they are packed, placed through *total (zero
+//     before the launch), which ends at the number of rows;
 //   * id[] of every bin head: the first block IDs of its first item, from
 //     the block-table copy bt (row stride W4, block size bs).
 struct TableParams {
@@ -84,6 +86,7 @@ struct TableParams {
   int2* src_span;
   int32_t* src_row;
   int32_t* total;
+  int32_t stride;
   BinHead* heads;
   int32_t n_bins;
   const int32_t* bt;
@@ -95,9 +98,13 @@ hipError_t launch_plan_tables(const TableParams& p, hipStream_t s);
 struct MergeParams {
   // Partial rows of (request i, query head h), in merge order (deepest
   // group's splits, then its ancestors', then the suffix's):
-  // src_row[s.x .. s.x + s.y), s = src_span[i * Hq + h].
+  // src_row[s.x .. s.x + s.y), s = src_span[i * Hq + h].  With
+  // src_stride > 0 (at most 64), s.x = (i * Hq + h) * src_stride and the
+  // entries after s.y hold -1 up to the stride, so the merge reads the rows
+  // without the span.
   const int2* src_span;
   const int32_t* src_row;
+  int32_t src_stride;
   int32_t B, Hq, Dv;
   PartialPtrs part;
   void* out;

@@ -83,9 +83,19 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
   const int hl = lane & 31;
   const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= (int64_t)P.B * P.Hq) return;
-  const int2 span = P.src_span[pair];
-  const int off0 = span.x;
-  const int n_src = span.y;
+  // Fixed-stride tables: the row indices come straight from the pair's
+  // slot (valid ones first, -1 after), one memory round trip fewer.
+  const bool strided = P.src_stride > 0;
+  int off0, n_src, row_first = -1;
+  if (strided) {
+    off0 = (int)(pair * P.src_stride);
+    row_first = lane < P.src_stride ? P.src_row[off0 + lane] : -1;
+    n_src = __popcll(__ballot(row_first >= 0));
+  } else {
+    const int2 span = P.src_span[pair];
+    off0 = span.x;
+    n_src = span.y;
+  }
 
   float M = -INFINITY, L = 0.f;
   float acc[VPL];
@@ -102,7 +112,8 @@ __device__ __forceinline__ void merge_body(const MergeParams& P) {
 
   for (int base = 0; base < n_src; base += 64) {
     const int j = base + lane;
-    const int row = j < n_src ? P.src_row[off0 + j] : -1;
+    // (strided: n_src <= 64, one batch, already loaded)
+    const int row = strided ? row_first : j < n_src ? P.src_row[off0 + j] : -1;
     const int cnt = min(64, n_src - base);
     auto load_rows = [&](int s) {
 #pragma unroll

@@ -65,18 +65,27 @@ __global__ __launch_bounds__(kTableThreads) void k_plan_tables(TableParams p, in
     h = (int)(pair - (int64_t)i * p.Hq);
     path_units(p, i, h, [&](int lane_id, int) { cnt += p.lanes[lane_id].splits; });
   }
-  // inclusive prefix sum of the counts over the wave
-  int incl = cnt;
+  int start;
+  if (p.stride > 0) {
+    // fixed stride: the pair's rows, then -1 up to the stride
+    if (pair >= n) return;
+    start = (int)(pair * p.stride);
+    for (int k = cnt; k < p.stride; ++k) p.src_row[start + k] = -1;
+  } else {
+    // packed: inclusive prefix sum of the counts over the wave, one atomic
+    // add per wave for its room
+    int incl = cnt;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d);
-    if (lane >= d) incl += v;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    int base = 0;
+    if (lane == 63) base = atomicAdd(p.total, incl);
+    base = __shfl(base, 63);
+    if (pair >= n) return;
+    start = base + incl - cnt;
   }
-  int base = 0;
-  if (lane == 63) base = atomicAdd(p.total, incl);
-  base = __shfl(base, 63);
-  if (pair >= n) return;
-  const int start = base + incl - cnt;
   p.src_span[pair] = make_int2(start, cnt);
   const int kvh = h / p.r;
   int32_t* out = p.src_row + start;

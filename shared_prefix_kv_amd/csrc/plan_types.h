@@ -137,6 +137,7 @@ struct PlanHost {
   std::vector<GroupMeta> grp;
   std::vector<LaneMeta> lanes;  // grouped lanes, then suffix lanes
   int item_cols = kItemColsGqa;  // query rows per column chunk
+  int64_t max_pair_sources = 0;  // upper bound of the partial rows one (request, head) merges
   fca_plan_info info{};
 };
 

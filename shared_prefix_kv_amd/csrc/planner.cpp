@@ -659,6 +659,32 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
   for (const Lane& L : all)
     P->lanes.push_back(LaneMeta{(int32_t)L.base, L.splits, L.kv0, L.H, L.col0, L.col1 - L.col0, 0, 0});
 
+  // The most partial rows one (request, head) can merge: per request, the
+  // most splits of any lane of each group on its path plus the most of any
+  // lane of its suffix.
+  {
+    std::vector<int32_t> gmax(G, 0);
+    for (int c = 0; c < G; ++c) {
+      const GroupMeta& gm = P->grp[c];
+      if (gm.lane0 < 0) continue;  // folded
+      const int n = (hkv / gm.H) * gm.chunks;
+      for (int k = 0; k < n; ++k) gmax[c] = std::max(gmax[c], P->lanes[gm.lane0 + k].splits);
+    }
+    int64_t most = 0;
+    for (const ReqMeta& rq : P->req) {
+      int64_t n = 0;
+      for (int g = rq.deepest; g >= 0; g = P->grp[g].parent) n += gmax[g];
+      if (rq.sfx_lane >= 0) {
+        const int m = (hkv / rq.sfx_H) * rq.sfx_chunks;
+        int32_t most_s = 0;
+        for (int k = 0; k < m; ++k) most_s = std::max(most_s, P->lanes[rq.sfx_lane + k].splits);
+        n += most_s;
+      }
+      most = std::max(most, n);
+    }
+    P->max_pair_sources = most;
+  }
+
   // Merge sources: every partial row is read by exactly one (request, query
   // head), so there are as many sources as rows.  The table itself (per
   // (request, head) the rows of its path, for_each_source order) is built on

@@ -71,6 +71,7 @@ void print_plan(const PlanHost& P) {
   off.push_back((int32_t)src.size());
   print_ints("src_off", off);
   print_ints("src", src);
+  printf("max_pair_sources %lld\n", (long long)P.max_pair_sources);
   // bins: items per persistent workgroup, and the launches
   print_ints("bins", P.bins);
   printf("launches %zu", P.launches.size());

@@ -159,6 +159,8 @@ def check_plan(res, shape, tables, lens, exp, keep_groups, cascade):
     assert info["unique_tokens"] == sum((g["block_end"] - g["block_begin"]) * bs for g in kept) + sum(
         r[1] for r in ex["requests"])
     assert info["num_merge_sources"] == sum(len(v) for row in res["schedule"]["sources"] for v in row)
+    # the bound the fixed-stride merge table is sized by covers every (request, head)
+    assert res["max_pair_sources"][0] >= max((len(v) for row in res["schedule"]["sources"] for v in row), default=0)
     assert info["decode_workspace_bytes"] >= info["num_partial_rows"] * (shape.head_dim_v * 4 + 8)
     bins, launches = res["bins"][1:], res["launches"][1:]
     assert bins[0] == 0 and all(a < b for a, b in zip(bins, bins[1:]))  # no empty bin
