@@ -100,7 +100,7 @@ fca_status check_desc(const fca_attn_desc* d, Kind* kind) {
               d->head_dim_qk, d->head_dim_v, d->block_size, d->v_aliases_k);
 }
 
-constexpr int kStateArrays = 9;  // per-request discovery state (DiscoveryPtrs)
+constexpr int kStateArrays = 10;  // per-request discovery state (DiscoveryPtrs)
 
 // Caller-owned plan workspace: discovery read-back region, table copy and
 // discovery state.  Its size depends only on (batch, max_blocks).
@@ -161,7 +161,8 @@ DiscoveryPtrs discovery_ptrs(char* ws, const Layout& L, int B) {
   p.records = reinterpret_cast<int32_t*>(ws + L.records);
   p.bt = reinterpret_cast<int32_t*>(ws + L.bt);
   int32_t* st = reinterpret_cast<int32_t*>(ws + L.state);
-  int32_t** arr[] = {&p.nfull, &p.root, &p.depth_at, &p.node, &p.gdepth, &p.gparent, &p.active, &p.lcp0, &p.ngid};
+  int32_t** arr[] = {&p.nfull, &p.root, &p.depth_at, &p.node, &p.gdepth, &p.gparent, &p.active, &p.lcp0, &p.ngid,
+                     &p.first};
   for (int a = 0; a < kStateArrays; ++a) *arr[a] = st + (size_t)a * B;
   return p;
 }

@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256) void k_prepare(const int32_t* __restrict__ bt_
       }
       p.lens[i] = Lc;
       p.nfull[i] = Lc / bs;
+      p.first[i] = Lc / bs > 0 ? id : -1;
       p.deepest[i] = -1;
       p.sfx_begin[i] = 0;
       p.root[i] = -1;
@@ -93,12 +94,13 @@ __global__ __launch_bounds__(256) void k_roots(int B, int W4, DiscoveryPtrs p) {
   const int i = (int)((blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= B) return;
-  if (p.nfull[i] == 0) return;  // root stays -1: nothing to share
-  const int key = p.bt[(int64_t)i * W4];
+  const int key = p.first[i];
+  if (key < 0) return;  // no full block: root stays -1, nothing to share
   int found = i;
+  // first block IDs are contiguous: 64 candidates in 256 bytes per load
   for (int k0 = 0; k0 <= i; k0 += 64) {
     const int k = k0 + lane;
-    const bool hit = k <= i && p.nfull[k] > 0 && p.bt[(int64_t)k * W4] == key;
+    const bool hit = k <= i && p.first[k] == key;
     const unsigned long long mask = __ballot(hit);
     if (mask) {
       found = k0 + __ffsll((long long)mask) - 1;

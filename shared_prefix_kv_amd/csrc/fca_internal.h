@@ -28,6 +28,7 @@ struct DiscoveryPtrs {
   int32_t* active;
   int32_t* lcp0;       // common prefix (full blocks) of each request with its tree's root
   int32_t* ngid;
+  int32_t* first;      // first block ID of each request with a full block, else -1
 };
 
 // W: table width (entries per row the caller's tables use); W4: row stride of
