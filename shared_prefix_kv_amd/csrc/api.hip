@@ -1016,32 +1016,42 @@ fca_status fca_plan_export_schedule(fca_plan plan, fca_work_item* grouped, fca_w
                                     int32_t* src) {
   if (!plan) return fail(FCA_ERR_INVALID_ARG, "plan is NULL");
   const fca_plan_s* P = plan;
-  if (grouped) std::memcpy(grouped, P->items_g.data(), P->items_g.size() * sizeof(WorkItem));
-  if (suffix) std::memcpy(suffix, P->items_s.data(), P->items_s.size() * sizeof(WorkItem));
-  if ((src_off || src) && P->B > 0) {
-    // the merge tables as the device built them, in (request, head) order
-    const size_t pairs = (size_t)P->B * P->desc.num_q_heads;
-    std::vector<int2> span(pairs);
-    std::vector<int32_t> rows(P->SL.src_rows);
-    hipError_t e = hipMemcpyAsync(span.data(), P->sched + P->SL.src_span, pairs * sizeof(int2), hipMemcpyDeviceToHost,
-                                  P->stream);
-    if (e == hipSuccess && !rows.empty())
-      e = hipMemcpyAsync(rows.data(), P->sched + P->SL.src_row, rows.size() * 4, hipMemcpyDeviceToHost, P->stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(P->stream);
-    if (e != hipSuccess) return hip_fail(e, "merge table read-back");
-    int64_t n = 0;
-    for (size_t q = 0; q < pairs; ++q) {
-      if (span[q].x < 0 || span[q].y < 0 || (size_t)span[q].x + span[q].y > rows.size())
-        return fail(FCA_ERR_HIP, "merge table entry %zu out of range", q);
-      if (src_off) src_off[q] = (int32_t)n;
-      if (src) std::memcpy(src + n, rows.data() + span[q].x, (size_t)span[q].y * 4);
-      n += span[q].y;
+  try {
+    if (grouped) {
+      const std::vector<WorkItem> v = pass_items(*P, true);
+      std::memcpy(grouped, v.data(), v.size() * sizeof(WorkItem));
     }
-    if (src_off) src_off[pairs] = (int32_t)n;
-  } else if (src_off) {
-    src_off[0] = 0;
+    if (suffix) {
+      const std::vector<WorkItem> v = pass_items(*P, false);
+      std::memcpy(suffix, v.data(), v.size() * sizeof(WorkItem));
+    }
+    if ((src_off || src) && P->B > 0) {
+      // the merge tables as the device built them, in (request, head) order
+      const size_t pairs = (size_t)P->B * P->desc.num_q_heads;
+      std::vector<int2> span(pairs);
+      std::vector<int32_t> rows(P->SL.src_rows);
+      hipError_t e = hipMemcpyAsync(span.data(), P->sched + P->SL.src_span, pairs * sizeof(int2), hipMemcpyDeviceToHost,
+                                    P->stream);
+      if (e == hipSuccess && !rows.empty())
+        e = hipMemcpyAsync(rows.data(), P->sched + P->SL.src_row, rows.size() * 4, hipMemcpyDeviceToHost, P->stream);
+      if (e == hipSuccess) e = hipStreamSynchronize(P->stream);
+      if (e != hipSuccess) return hip_fail(e, "merge table read-back");
+      int64_t n = 0;
+      for (size_t q = 0; q < pairs; ++q) {
+        if (span[q].x < 0 || span[q].y < 0 || (size_t)span[q].x + span[q].y > rows.size())
+          return fail(FCA_ERR_HIP, "merge table entry %zu out of range", q);
+        if (src_off) src_off[q] = (int32_t)n;
+        if (src) std::memcpy(src + n, rows.data() + span[q].x, (size_t)span[q].y * 4);
+        n += span[q].y;
+      }
+      if (src_off) src_off[pairs] = (int32_t)n;
+    } else if (src_off) {
+      src_off[0] = 0;
+    }
+    return FCA_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(FCA_ERR_HOST_ALLOC, "host allocation failed");
   }
-  return FCA_OK;
 }
 
 void fca_plan_destroy(fca_plan plan) { delete plan; }

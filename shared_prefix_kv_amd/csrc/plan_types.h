@@ -128,8 +128,7 @@ struct PlanHost {
   std::vector<int32_t> members;   // ascending per group
   std::vector<int32_t> folded;    // per group: read per request (activation heuristic)
   std::vector<int32_t> req3;      // per request: suffix_block_begin, suffix_tokens, deepest
-  std::vector<WorkItem> items_g, items_s;  // host copies of each pass's items, in bin order
-  std::vector<WorkItem> items;             // what the device runs: all launches' items
+  std::vector<WorkItem> items;             // what the device runs: all launches' items (in bin order)
   std::vector<int32_t> bins;               // bin b runs items [bins[b], bins[b + 1])
   std::vector<Launch> launches;            // one (both passes) or two (grouped, suffix)
   std::vector<int32_t> perm;
@@ -140,6 +139,15 @@ struct PlanHost {
   int64_t max_pair_sources = 0;  // upper bound of the partial rows one (request, head) merges
   fca_plan_info info{};
 };
+
+// The grouped items (member_off >= 0) or the per-request items of a plan, in
+// bin order (what the export reports for each pass).
+inline std::vector<WorkItem> pass_items(const PlanHost& P, bool grouped) {
+  std::vector<WorkItem> v;
+  for (const WorkItem& it : P.items)
+    if ((it.member_off >= 0) == grouped) v.push_back(it);
+  return v;
+}
 
 // Builds P's grouping and schedule from a discovery read-back, for a device
 // with n_cu compute units.  P.desc, P.kind, P.B, P.W and P.r must be set.

@@ -644,15 +644,12 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
     row += (int64_t)L.splits * L.H * (L.col1 - L.col0);
   }
   if (row > INT32_MAX) return pfail(err, FCA_ERR_UNSUPPORTED, "too many partial rows");
-  P->items_g.clear();
-  P->items_s.clear();
-  P->items_g.reserve(P->items.size());
-  P->items_s.reserve(P->items.size());
+  int64_t n_grouped_items = 0;
   for (size_t k = 0; k < P->items.size(); ++k) {
     WorkItem& it = P->items[k];
     const Lane& L = all[item_lane[k]];
     it.part_base = (int32_t)(L.base + (int64_t)it.part_base * L.S * L.H * (L.col1 - L.col0));
-    (it.member_off >= 0 ? P->items_g : P->items_s).push_back(it);
+    n_grouped_items += it.member_off >= 0;
   }
   P->lanes.clear();
   P->lanes.reserve(all.size());
@@ -695,8 +692,8 @@ fca_status build_plan(PlanHost& plan, const DiscoveryView& disc, int n_cu_, std:
   info.batch = B;
   info.num_groups = G;
   info.max_depth = max_depth;
-  info.num_grouped_items = (int32_t)P->items_g.size();
-  info.num_suffix_items = (int32_t)P->items_s.size();
+  info.num_grouped_items = (int32_t)n_grouped_items;
+  info.num_suffix_items = (int32_t)((int64_t)P->items.size() - n_grouped_items);
   info.num_merge_sources = (int32_t)std::min<int64_t>(sources, INT32_MAX);
   info.num_partial_rows = row;
   info.logical_tokens = logical;

@@ -58,8 +58,8 @@ void print_plan(const PlanHost& P) {
   print_ints("members", P.members);
   print_ints("folded", P.folded);
   print_ints("requests", P.req3);
-  print_items("grouped", P.items_g);
-  print_items("suffix", P.items_s);
+  print_items("grouped", pass_items(P, true));
+  print_items("suffix", pass_items(P, false));
   // merge sources in the order of fca_plan_export_schedule
   const int hq = P.desc.num_q_heads;
   std::vector<int32_t> off, src;
