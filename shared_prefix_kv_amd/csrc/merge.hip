@@ -70,14 +70,15 @@ __device__ __forceinline__ void store_row(void* out, int32_t out_f32, int64_t at
 // the pair from the plan's source table, so that all (m, l) loads are issued
 // at once after two dependent loads; the value rows
 // are then accumulated two at a time (lanes 0-31 take even sources, lanes
-// 32-63 odd ones, each lane DV/32 value dims), eight rows in flight per
-// wave, and the two halves are added at the end.  (Sixteen rows in flight
-// for 128-dim rows measured slower on MI355X: the extra registers cost more
-// occupancy than the fewer round trips saved.)
+// 32-63 odd ones, each lane DV/32 value dims), 2U rows in flight per wave,
+// and the two halves are added at the end.  U keeps the kernel at eight
+// waves per SIMD, which measured faster on MI355X than more rows per round
+// trip: 8 rows of 128 dims (16 rows: 76 VGPRs, 6 waves, 2-6 % slower), 2
+// rows of 512 dims (8 rows: 114 VGPRs, 4 waves, 7 % slower).
 template <int DV>
 __device__ __forceinline__ void merge_body(const MergeParams& P) {
-  constexpr int VPL = DV / 32;  // floats per lane
-  constexpr int U = 4;          // row pairs per batch of loads
+  constexpr int VPL = DV / 32;         // floats per lane
+  constexpr int U = DV <= 128 ? 4 : 1;  // row pairs per batch of loads
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int hl = lane & 31;
