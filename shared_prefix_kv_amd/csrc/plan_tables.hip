@@ -9,11 +9,13 @@
 // (LaneMeta: base row, splits, head block, column range of one (unit, head
 // block, column chunk) stream) and the per-request and per-group metadata;
 // one kernel turns them into the table -- a thread per (request, head)
-// counts its rows, each wave takes room for its threads' rows with one atomic
-// add on a counter, and every thread writes its rows -- instead of the host
-// walking B x Hq paths at every plan.  Where a pair's rows sit in src_row
-// depends on the order in which waves reach the counter; what they are, and
-// their order, does not.  The same launch fills the first block IDs of every
+// counts its rows and writes them -- instead of the host walking B x Hq paths
+// at every plan.  When the host has bounded every pair's count by a stride of
+// at most 64, pair q's rows sit at q * stride, padded with -1 (the merge then
+// reads them without the span); otherwise each wave takes room for its
+// threads' rows with one atomic add on a counter, so where a pair's rows sit
+// depends on the order in which waves reach it; what they are, and their
+// order, does not.  The same launch fills the first block IDs of every
 // workgroup's bin head (its last blocks, one thread per bin), so the plan's
 // device tables cost one launch after the upload.
 
@@ -86,14 +88,17 @@ __global__ __launch_bounds__(kTableThreads) void k_plan_tables(TableParams p, in
     if (pair >= n) return;
     start = base + incl - cnt;
   }
-  p.src_span[pair] = make_int2(start, cnt);
+  p.src_span[pair] = make_int2(start, p.stride > 0 ? min(cnt, (int)p.stride) : cnt);
   const int kvh = h / p.r;
   int32_t* out = p.src_row + start;
+  // the pair's room: its count (packed) or the stride, which the host sizes
+  // to a bound of every pair's count; never written past
+  const int32_t* const room = out + (p.stride > 0 ? p.stride : cnt);
   path_units(p, i, h, [&](int lane_id, int col) {
     const LaneMeta L = p.lanes[lane_id];
     const int step = L.H * L.ccols;
     int row = L.base + (kvh - L.kv0) * L.ccols + (col - L.col0);
-    for (int s = 0; s < L.splits; ++s, row += step) *out++ = row;
+    for (int s = 0; s < L.splits && out < room; ++s, row += step) *out++ = row;
   });
 }
 
